@@ -1,0 +1,96 @@
+"""Planted mistakes in the oracle (on the CPU) must be caught by its pins.
+
+Each case patches one plausible mistake into ``oracle.attention`` and checks that
+at least one pin of ``tests/test_oracle.py`` fails.  This shows the pins are
+strong enough to detect a dropped term, a wrong sign or an off-by-one index.
+"""
+
+import numpy as np
+import pytest
+
+from oracle import attention as A
+import tests.test_oracle as pins
+
+
+def _orig(name):
+    return getattr(A, name)
+
+
+def mut_scale_dropped(monkeypatch):
+    orig = _orig("scores")
+
+    def bad(q_rows, k, scale, *a, **kw):
+        return orig(q_rows, k, 1.0, *a, **kw)
+    monkeypatch.setattr(A, "scores", bad)
+
+
+def mut_bias_sign(monkeypatch):
+    orig = _orig("distance_bias")
+    monkeypatch.setattr(A, "distance_bias", lambda rows, n_k, slope: -orig(rows, n_k, slope))
+
+
+def mut_causal_off_by_one(monkeypatch):
+    orig = _orig("visible_mask")
+
+    def bad(n_q, n_k, rows, causal, ks, ke):
+        vis = orig(n_q, n_k, rows, False, ks, ke)
+        if causal:
+            j = np.arange(n_k)[None, :]
+            vis &= j < (np.asarray(rows)[:, None] + (n_k - n_q))
+        return vis
+    monkeypatch.setattr(A, "visible_mask", bad)
+
+
+def mut_causal_top_left(monkeypatch):
+    orig = _orig("visible_mask")
+
+    def bad(n_q, n_k, rows, causal, ks, ke):
+        vis = orig(n_q, n_k, rows, False, ks, ke)
+        if causal:
+            vis &= np.arange(n_k)[None, :] <= np.asarray(rows)[:, None]
+        return vis
+    monkeypatch.setattr(A, "visible_mask", bad)
+
+
+def mut_range_end_inclusive(monkeypatch):
+    orig = _orig("visible_mask")
+
+    def bad(n_q, n_k, rows, causal, ks, ke):
+        if ks is None:
+            return orig(n_q, n_k, rows, causal, ks, ke)
+        return orig(n_q, n_k, rows, causal, ks, np.asarray(ke) + 1)
+    monkeypatch.setattr(A, "visible_mask", bad)
+
+
+def mut_softmax_no_normalise(monkeypatch):
+    orig = _orig("_two_pass_softmax")
+
+    def bad(s):
+        p, m, l = orig(s)
+        return p * np.where(l > 0, l, 1.0)[:, None] ** 0.5, m, l
+    monkeypatch.setattr(A, "_two_pass_softmax", bad)
+
+
+FWD_PINS = [
+    lambda: [pins.test_forward_matches_multiprecision_brute_force(i)
+             for i in range(len(pins.CASES))],
+    lambda: pins.test_against_torch_float64_reference(True, 0.02, True, 31, 31),
+    lambda: pins.test_against_torch_float64_reference(True, None, False, 23, 50),
+    lambda: pins.test_bias_only_geometric_series(),
+    lambda: pins.test_uniform_scores_mean_of_visible_values(True),
+]
+
+
+@pytest.mark.parametrize("mutation", [
+    mut_scale_dropped, mut_bias_sign, mut_causal_off_by_one, mut_causal_top_left,
+    mut_range_end_inclusive, mut_softmax_no_normalise,
+])
+def test_planted_mistake_is_caught(monkeypatch, mutation):
+    mutation(monkeypatch)
+    caught = 0
+    for pin in FWD_PINS:
+        try:
+            pin()
+        except AssertionError:
+            caught += 1
+    assert caught >= 1, f"no pin caught {mutation.__name__}"
