@@ -1,0 +1,240 @@
+"""Exact IO-aware attention for AMD Instinct MI355X (gfx950).
+
+A thin ctypes binding over the C ABI of ``libfa.so`` (declared in ``include/fa.h``).
+The Python side only checks tensors and marshals pointers, sizes and the current
+HIP stream; every step of the computation runs in the library's HIP kernels.
+PyTorch supplies device memory and streams. If the library is not built, every
+call raises: there is no CPU or PyTorch fallback.
+
+Function names follow the C entry points: ``fa_fwd``, ``fa_bwd``,
+``fa_bwd_workspace_bytes``, ``fa_mask_summary``, ``fa_status_string``, ``fa_version``.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional, Sequence, Tuple
+
+import torch
+
+__all__ = [
+    "FaError", "fa_fwd", "fa_bwd", "fa_bwd_workspace_bytes", "fa_mask_summary",
+    "fa_status_string", "fa_version", "lib_path", "load_library",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libfa.so")
+_LIB = None
+
+FA_F32, FA_F16, FA_BF16 = 0, 1, 2
+FA_BIAS_NONE, FA_BIAS_DIST_LINEAR = 0, 1
+FA_MAX_SLOPES = 256
+_DT = {torch.float32: FA_F32, torch.float16: FA_F16, torch.bfloat16: FA_BF16}
+
+
+class FaError(RuntimeError):
+    """A non-zero status returned by the C ABI."""
+
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: status {status} ({fa_status_string(status)})")
+
+
+class MaskBiasDesc(ctypes.Structure):
+    _fields_ = [
+        ("bias_kind", ctypes.c_int32),
+        ("n_slopes", ctypes.c_int32),
+        ("slopes", ctypes.POINTER(ctypes.c_float)),
+        ("key_start", ctypes.c_void_p),
+        ("key_end", ctypes.c_void_p),
+    ]
+
+
+def lib_path() -> str:
+    return _LIB_PATH
+
+
+def load_library():
+    """Load ``libfa.so`` (raises if it has not been built)."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError(
+            f"{_LIB_PATH} is missing: build the HIP library first "
+            "(python -m exact_io_aware_flash_amd.build)")
+    lib = ctypes.CDLL(_LIB_PATH)
+    vp, i32, f32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+    desc_p = ctypes.POINTER(MaskBiasDesc)
+    lib.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32, desc_p, i32, vp]
+    lib.fa_fwd.restype = i32
+    lib.fa_bwd_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
+    lib.fa_bwd_workspace_bytes.restype = ctypes.c_size_t
+    lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, ctypes.c_size_t,
+                           i32, i32, i32, i32, i32, f32, i32, desc_p, i32, vp]
+    lib.fa_bwd.restype = i32
+    lib.fa_mask_summary.argtypes = [vp, vp, i32, i32, i32, vp, vp]
+    lib.fa_mask_summary.restype = i32
+    lib.fa_status_string.argtypes = [i32]
+    lib.fa_status_string.restype = ctypes.c_char_p
+    lib.fa_version.argtypes = []
+    lib.fa_version.restype = ctypes.c_char_p
+    _LIB = lib
+    return lib
+
+
+def fa_status_string(status: int) -> str:
+    return load_library().fa_status_string(int(status)).decode()
+
+
+def fa_version() -> str:
+    return load_library().fa_version().decode()
+
+
+def fa_bwd_workspace_bytes(B: int, H: int, N_q: int, N_k: int, d: int) -> int:
+    return int(load_library().fa_bwd_workspace_bytes(B, H, N_q, N_k, d))
+
+
+def _stream_ptr(stream: Optional[torch.cuda.Stream]) -> int:
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return int(s.cuda_stream)
+
+
+def _check_dev(name: str, t: torch.Tensor, dtype=None, shape=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _desc(bias_slopes, key_start, key_end, H, N_q):
+    """Build the mask/bias descriptor; returns (desc or None, keepalive)."""
+    if bias_slopes is None and key_start is None and key_end is None:
+        return None, None
+    d = MaskBiasDesc()
+    keep = []
+    d.bias_kind = FA_BIAS_NONE
+    d.n_slopes = 1
+    d.slopes = None
+    if bias_slopes is not None:
+        sl = [float(x) for x in (bias_slopes if isinstance(bias_slopes, Sequence)
+                                 else [bias_slopes])]
+        arr = (ctypes.c_float * len(sl))(*sl)
+        keep.append(arr)
+        d.bias_kind = FA_BIAS_DIST_LINEAR
+        d.n_slopes = len(sl)
+        d.slopes = ctypes.cast(arr, ctypes.POINTER(ctypes.c_float))
+    if (key_start is None) != (key_end is None):
+        raise ValueError("key_start and key_end must be given together")
+    if key_start is not None:
+        _check_dev("key_start", key_start, torch.int32, (N_q,))
+        _check_dev("key_end", key_end, torch.int32, (N_q,))
+        d.key_start = key_start.data_ptr()
+        d.key_end = key_end.data_ptr()
+    return d, keep
+
+
+def fa_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
+           scale: Optional[float] = None, bias_slopes=None,
+           key_start: Optional[torch.Tensor] = None, key_end: Optional[torch.Tensor] = None,
+           out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+           stream: Optional[torch.cuda.Stream] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Exact attention forward on the GPU: returns (O [B,H,N_q,d], LSE [B,H,N_q] float32).
+
+    q: [B,H,N_q,d], k/v: [B,H,N_k,d], all of one dtype (float32, float16, bfloat16).
+    ``bias_slopes``: float or a list of 1 or H floats, bias = slope * |i - j|.
+    ``key_start``/``key_end``: int32 [N_q] device tensors, row i sees keys in [start, end).
+    """
+    lib = load_library()
+    _check_dev("q", q)
+    if q.dim() != 4:
+        raise ValueError("q must be [B, H, N_q, d]")
+    B, H, N_q, d = q.shape
+    N_k = k.shape[2]
+    if q.dtype not in _DT:
+        raise ValueError(f"unsupported dtype {q.dtype}")
+    _check_dev("k", k, q.dtype, (B, H, N_k, d))
+    _check_dev("v", v, q.dtype, (B, H, N_k, d))
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    _check_dev("out", out, q.dtype, (B, H, N_q, d))
+    if lse is None:
+        lse = torch.empty((B, H, N_q), dtype=torch.float32, device=q.device)
+    _check_dev("lse", lse, torch.float32, (B, H, N_q))
+    desc, keep = _desc(bias_slopes, key_start, key_end, H, N_q)
+    st = lib.fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                    B, H, N_q, N_k, d, float(scale), 1 if causal else 0,
+                    ctypes.byref(desc) if desc is not None else None, _DT[q.dtype],
+                    _stream_ptr(stream))
+    del keep
+    if st != 0:
+        raise FaError(st, "fa_fwd")
+    return out, lse
+
+
+def fa_bwd(dout: torch.Tensor, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+           o: torch.Tensor, lse: torch.Tensor, causal: bool = False,
+           scale: Optional[float] = None, bias_slopes=None,
+           key_start: Optional[torch.Tensor] = None, key_end: Optional[torch.Tensor] = None,
+           grad_dtype: torch.dtype = torch.float32, workspace: Optional[torch.Tensor] = None,
+           stream: Optional[torch.cuda.Stream] = None):
+    """Backward by recomputation: returns (dQ, dK, dV) in ``grad_dtype``.
+
+    ``o`` and ``lse`` are the outputs of :func:`fa_fwd` for the same inputs.
+    """
+    lib = load_library()
+    _check_dev("q", q)
+    B, H, N_q, d = q.shape
+    N_k = k.shape[2]
+    _check_dev("k", k, q.dtype, (B, H, N_k, d))
+    _check_dev("v", v, q.dtype, (B, H, N_k, d))
+    _check_dev("o", o, q.dtype, (B, H, N_q, d))
+    _check_dev("dout", dout, q.dtype, (B, H, N_q, d))
+    _check_dev("lse", lse, torch.float32, (B, H, N_q))
+    if grad_dtype not in (torch.float32, q.dtype):
+        raise ValueError("grad_dtype must be float32 or the input dtype")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dq = torch.empty((B, H, N_q, d), dtype=grad_dtype, device=q.device)
+    dk = torch.empty((B, H, N_k, d), dtype=grad_dtype, device=q.device)
+    dv = torch.empty((B, H, N_k, d), dtype=grad_dtype, device=q.device)
+    wsb = fa_bwd_workspace_bytes(B, H, N_q, N_k, d)
+    if workspace is None:
+        workspace = torch.empty(max(wsb, 16), dtype=torch.uint8, device=q.device)
+    desc, keep = _desc(bias_slopes, key_start, key_end, H, N_q)
+    st = lib.fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                    dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                    _DT[grad_dtype], workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                    B, H, N_q, N_k, d, float(scale), 1 if causal else 0,
+                    ctypes.byref(desc) if desc is not None else None, _DT[q.dtype],
+                    _stream_ptr(stream))
+    del keep
+    if st != 0:
+        raise FaError(st, "fa_bwd")
+    return dq, dk, dv
+
+
+def fa_mask_summary(key_start: torch.Tensor, key_end: torch.Tensor, n_k: int, block_rows: int,
+                    stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
+    """Per block of ``block_rows`` query rows: [min start, max start, min end, max end]."""
+    lib = load_library()
+    (n_q,) = key_start.shape
+    _check_dev("key_start", key_start, torch.int32, (n_q,))
+    _check_dev("key_end", key_end, torch.int32, (n_q,))
+    nb = (n_q + block_rows - 1) // max(block_rows, 1)
+    out = torch.empty((max(nb, 1), 4), dtype=torch.int32, device=key_start.device)
+    st = lib.fa_mask_summary(key_start.data_ptr(), key_end.data_ptr(), n_q, n_k, block_rows,
+                             out.data_ptr(), _stream_ptr(stream))
+    if st != 0:
+        raise FaError(st, "fa_mask_summary")
+    return out[:nb]

@@ -1,0 +1,160 @@
+// fa_api.hip -- the C ABI: argument validation, dispatch and launch (see include/fa.h).
+//
+// Every argument is checked before anything is enqueued; an invalid call returns its
+// status and launches nothing. There is no alternative code path: a combination this
+// library does not implement is reported as FA_ERR_UNSUPPORTED, never computed some
+// other way (blog "Apakah Konteks Sehari Penuh Mengalahkan Konteks Sepuluh Menit?",
+// section "Integrasinya delapan baris": a silent fallback to the slow path looks
+// exactly like a slow working model).
+#include <climits>
+#include <cmath>
+#include <cstring>
+
+#include "fa.h"
+#include "fa_internal.h"
+
+using namespace fa;
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+fa_status check_common(int B, int H, int N_q, int N_k, int d, float scale, fa_dtype dtype) {
+  if (dtype != FA_F32 && dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_DTYPE;
+  if (B < 1 || H < 1 || N_q < 1 || N_k < 1) return FA_ERR_SHAPE;
+  if (d != 64 && d != 128) return FA_ERR_HEADDIM;
+  // 32-bit indexing inside one (b, h) and for the grid
+  if ((long long)N_q * d > INT_MAX || (long long)N_k * d > INT_MAX) return FA_ERR_SHAPE;
+  if ((long long)B * H * ((N_q + 63) / 64 + 1) > INT_MAX) return FA_ERR_SHAPE;
+  if ((long long)B * H * N_q > INT_MAX) return FA_ERR_SHAPE;
+  if (!std::isfinite(scale) || !(scale > 0.f)) return FA_ERR_ARG;
+  return FA_OK;
+}
+
+// Fills the bias/mask part of an argument block; returns the status.
+template <class Args>
+fa_status read_desc(const fa_mask_bias_desc* mb, int H, bool& bias, Args& a) {
+  bias = false;
+  a.key_start = nullptr;
+  a.key_end = nullptr;
+  a.n_slopes = 1;
+  for (int i = 0; i < FA_MAX_SLOPES; ++i) a.slope2[i] = 0.f;
+  if (mb == nullptr) return FA_OK;
+  if (mb->bias_kind != FA_BIAS_NONE && mb->bias_kind != FA_BIAS_DIST_LINEAR) return FA_ERR_MASK;
+  if ((mb->key_start == nullptr) != (mb->key_end == nullptr)) return FA_ERR_MASK;
+  if (mb->key_start != nullptr) {
+    if (!aligned16(mb->key_start) || !aligned16(mb->key_end)) return FA_ERR_ALIGN;
+    a.key_start = mb->key_start;
+    a.key_end = mb->key_end;
+  }
+  if (mb->bias_kind == FA_BIAS_DIST_LINEAR) {
+    if (mb->slopes == nullptr) return FA_ERR_NULL;
+    if (mb->n_slopes != 1 && mb->n_slopes != H) return FA_ERR_MASK;
+    if (mb->n_slopes > FA_MAX_SLOPES) return FA_ERR_UNSUPPORTED;
+    for (int i = 0; i < mb->n_slopes; ++i) {
+      if (!std::isfinite(mb->slopes[i])) return FA_ERR_ARG;
+      a.slope2[i] = mb->slopes[i] * 1.4426950408889634f;
+    }
+    a.n_slopes = mb->n_slopes;
+    bias = true;
+  }
+  return FA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* fa_status_string(fa_status s) {
+  switch (s) {
+    case FA_OK: return "ok";
+    case FA_ERR_NULL: return "a required pointer is NULL";
+    case FA_ERR_SHAPE: return "invalid shape (B, H, N_q, N_k must be >= 1 and fit 32-bit indexing)";
+    case FA_ERR_DTYPE: return "unknown dtype";
+    case FA_ERR_HEADDIM: return "head dimension must be 64 or 128";
+    case FA_ERR_MASK: return "malformed mask/bias descriptor";
+    case FA_ERR_ALIGN: return "device pointer not 16-byte aligned";
+    case FA_ERR_WORKSPACE: return "workspace missing or too small";
+    case FA_ERR_UNSUPPORTED: return "combination not implemented";
+    case FA_ERR_HIP: return "HIP launch error";
+    case FA_ERR_ARG: return "scale must be finite and > 0";
+  }
+  return "unknown status";
+}
+
+const char* fa_version(void) { return "fa 0.1.0 gfx950"; }
+
+fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                 int N_q, int N_k, int d, float scale, int causal, const fa_mask_bias_desc* mb,
+                 fa_dtype dtype, void* stream) {
+  fa_status st = check_common(B, H, N_q, N_k, d, scale, dtype);
+  if (st != FA_OK) return st;
+  if (!q || !k || !v || !o) return FA_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return FA_ERR_ALIGN;
+  if (lse != nullptr && (reinterpret_cast<uintptr_t>(lse) & 3u)) return FA_ERR_ALIGN;
+  FwdArgs a;
+  std::memset(&a, 0, sizeof(a));
+  bool bias = false;
+  st = read_desc(mb, H, bias, a);
+  if (st != FA_OK) return st;
+  a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
+  a.B = B; a.H = H; a.Nq = N_q; a.Nk = N_k;
+  a.causal = causal ? 1 : 0;
+  a.sl2 = scale * 1.4426950408889634f;
+  hipError_t e = launch_fwd(dtype, d, bias, a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+size_t fa_bwd_workspace_bytes(int B, int H, int N_q, int N_k, int d) {
+  (void)N_k; (void)d;
+  if (B < 1 || H < 1 || N_q < 1) return 0;
+  // delta = rowsum(dO * O): one float per query row, rounded up to 256 bytes
+  const size_t delta = (size_t)B * H * N_q * sizeof(float);
+  return (delta + 255) & ~(size_t)255;
+}
+
+fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                 const void* dout, void* dq, void* dk, void* dv, fa_dtype grad_dtype,
+                 void* workspace, size_t workspace_bytes, int B, int H, int N_q, int N_k, int d,
+                 float scale, int causal, const fa_mask_bias_desc* mb, fa_dtype dtype,
+                 void* stream) {
+  fa_status st = check_common(B, H, N_q, N_k, d, scale, dtype);
+  if (st != FA_OK) return st;
+  if (grad_dtype != FA_F32 && grad_dtype != dtype) return FA_ERR_DTYPE;
+  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return FA_ERR_NULL;
+  const void* dev[] = {q, k, v, o, lse, dout, dq, dk, dv};
+  for (const void* p : dev)
+    if (!aligned16(p)) return FA_ERR_ALIGN;
+  if (workspace == nullptr || workspace_bytes < fa_bwd_workspace_bytes(B, H, N_q, N_k, d))
+    return FA_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return FA_ERR_ALIGN;
+  BwdArgs a;
+  std::memset(&a, 0, sizeof(a));
+  bool bias = false;
+  st = read_desc(mb, H, bias, a);
+  if (st != FA_OK) return st;
+  a.q = q; a.k = k; a.v = v; a.o = o; a.dout = dout; a.lse = lse;
+  a.delta = static_cast<float*>(workspace);
+  a.dq = dq; a.dk = dk; a.dv = dv;
+  a.B = B; a.H = H; a.Nq = N_q; a.Nk = N_k;
+  a.causal = causal ? 1 : 0;
+  a.grad_f32 = grad_dtype == FA_F32 ? 1 : 0;
+  a.scale = scale;
+  a.sl2 = scale * 1.4426950408889634f;
+  hipError_t e = launch_bwd(dtype, d, bias, a, static_cast<hipStream_t>(stream));
+  if (e == hipErrorNotSupported) return FA_ERR_UNSUPPORTED;
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+fa_status fa_mask_summary(const int32_t* key_start, const int32_t* key_end, int N_q, int N_k,
+                          int block_rows, int32_t* out, void* stream) {
+  if (!key_start || !key_end || !out) return FA_ERR_NULL;
+  if (N_q < 1 || N_k < 1) return FA_ERR_SHAPE;
+  if (block_rows < 1 || block_rows > 1024) return FA_ERR_SHAPE;
+  if (!aligned16(key_start) || !aligned16(key_end) || !aligned16(out)) return FA_ERR_ALIGN;
+  hipError_t e = launch_mask_summary(key_start, key_end, N_q, N_k, block_rows, out,
+                                     static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,556 @@
+// fa_fwd.hip -- fused exact-attention forward kernel for gfx950 (MI355X).
+//
+// Method (blog "Apakah Konteks Sehari Penuh Mengalahkan Konteks Sepuluh Menit?",
+// sections "Algoritma Flash Attention", "Pengulangan softmax online", "FA2: paralelisme",
+// "Causal masking ..."): Q is cut into row blocks and K/V into column blocks; for every
+// query block the kernel walks the key/value blocks, computes the score tile on chip,
+// keeps a running row max and row sum, rescales the output accumulator when the max
+// grows, and divides by the row sum once at the end. Tiles that hold no visible key are
+// never loaded or computed. The score matrix never leaves registers.
+//
+// gfx950 mapping (not the Hopper design the pages describe):
+//  * one workgroup = NW waves = NW*32*QSUB query rows of one (batch, head); the grid runs
+//    over (batch, head, query block) so batch 1-4 still fills 256 CUs;
+//  * each wave owns its own 32*QSUB query rows (no cross-wave reduction of scores);
+//  * scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_{bf16,f16}:
+//    a lane then holds 16 keys of ONE query row per 32x32 tile, so the row max needs one
+//    exchange between the two wave halves and the row sum none until the epilogue;
+//  * the probabilities feed O^T += V^T P^T directly from those result registers; V is
+//    stored transposed in LDS (with keys relabelled so that every lane reads 16
+//    contiguous bytes) by an in-register 4x8 transpose during the global->LDS copy;
+//  * K and V^T tiles are double-buffered in LDS: the global loads of tile j+1 are issued
+//    before tile j is computed and written to the other buffer after it;
+//  * the running max is only moved when a row's tile max exceeds it by more than 2^8
+//    (exact: numerator and denominator share the same stale max), which removes almost
+//    every rescale of the 64-128 accumulator registers per lane;
+//  * Q stays in registers for the whole loop; O^T and S^T live in registers.
+#include <type_traits>
+
+#include "fa_device.h"
+#include "fa_internal.h"
+
+namespace fa {
+
+constexpr float kTau = 8.0f;  // lazy-rescale threshold in log2 units (p <= 2^8)
+
+__device__ __host__ constexpr int align16(int x) { return (x + 15) & ~15; }
+
+template <typename T, int D_, int BC_, int QSUB_, int NW_>
+struct FwdCfg {
+  static constexpr bool kF32 = std::is_same<T, float>::value;
+  static constexpr int D = D_, BC = BC_, QSUB = QSUB_, NW = NW_;
+  static constexpr int kNT = NW * 64;
+  static constexpr int kQW = 32 * QSUB;       // query rows per wave
+  static constexpr int kBR = kQW * NW;        // query rows per workgroup
+  static constexpr int kKB = BC / 32;         // 32-key blocks per tile
+  static constexpr int kDB = D / 32;          // 32-wide d blocks of O^T
+  static constexpr int kDK = kF32 ? D / 2 : D / 16;  // MFMA k-steps over d for S^T
+  // LDS layout. 16-bit: K row-major (row stride D*2+16 bytes), V^T rows of BC keys
+  // (stride BC*2+16, 16-byte chunks XOR-swizzled by (row/16)). f32: K row stride
+  // (D+1)*4 (odd word stride), V row-major with stride (D+4)*4.
+  static constexpr int kKStride = kF32 ? (D + 1) * 4 : D * 2 + 16;
+  static constexpr int kVStride = kF32 ? (D + 4) * 4 : BC * 2 + 16;
+  static constexpr int kKBytes = align16(BC * kKStride);
+  static constexpr int kVBytes = kF32 ? BC * kVStride : D * kVStride;
+  static constexpr int kStage = kKBytes + kVBytes;
+  // global->LDS copy split: 16-byte chunks per thread
+  static constexpr int kEltPerChunk = kF32 ? 4 : 8;
+  static constexpr int kRowChunks = D / kEltPerChunk;
+  static constexpr int kKPer = BC * kRowChunks / kNT;
+  // 16-bit V: a thread owns KQ consecutive keys x 8 d values (one chunk per key)
+  static constexpr int kKQraw = BC * kRowChunks / kNT;
+  static constexpr int kKQ = kF32 ? 1 : (kKQraw >= 4 ? 4 : kKQraw);
+  static constexpr int kVPer = kF32 ? kKPer : BC * kRowChunks / (kKQ * kNT);
+  static constexpr int kVChunksSwz = BC / 8;   // 16-byte chunks per V^T row
+  static_assert(BC % 32 == 0 && D % 32 == 0, "tile shape");
+  static_assert(kKPer >= 1 && kKPer * kNT == BC * kRowChunks, "K copy split");
+  static_assert(kF32 || (kKQ >= 2 && kVPer * kKQ * kNT == BC * kRowChunks), "V copy split");
+  static_assert(2 * kStage <= 160 * 1024, "LDS budget");
+};
+
+// Keys inside a tile are relabelled in V^T so that the 8 keys one lane feeds to a
+// P.V MFMA step are contiguous: swap bits 2 and 3 of the tile-local key index.
+__device__ constexpr int vt_pos(int key) {
+  return (key & ~12) | ((key & 4) << 1) | ((key & 8) >> 1);
+}
+
+template <class C>
+__device__ inline int vt_off(int row, int chunk) {
+  return row * C::kVStride + 16 * (chunk ^ ((row >> 4) & (C::kVChunksSwz - 1)));
+}
+
+// ---------------------------------------------------------------------------------
+// work mapping: workgroup -> (bh, query block); heaviest (causal: last) blocks first
+// ---------------------------------------------------------------------------------
+__device__ inline void map_block(int L, int BH, int nblk, int sched, int& bh, int& qb) {
+  if (sched == kSchedXcd) {
+    // blocks are handed to the 8 XCDs round-robin; keep every (b,h) on one XCD so its
+    // K/V stays in that XCD's L2, and walk each head's blocks heaviest first.
+    int x = L & 7, s = L >> 3;
+    bh = x + 8 * (s / nblk);
+    qb = nblk - 1 - (s % nblk);
+  } else {
+    bh = L / nblk;
+    qb = nblk - 1 - (L % nblk);
+  }
+}
+
+__device__ inline int wave_min(int v) {
+  for (int o = 32; o >= 1; o >>= 1) v = min(v, __shfl_xor(v, o, 64));
+  return v;
+}
+__device__ inline int wave_max(int v) {
+  for (int o = 32; o >= 1; o >>= 1) v = max(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+template <typename T, int D, int BC, int QSUB, int NW, bool BIAS>
+__global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
+                          amdgpu_waves_per_eu(1, 1)))
+void fwd_kernel(const FwdArgs a) {
+  using C = FwdCfg<T, D, BC, QSUB, NW>;
+  using E = Elt<T>;
+  constexpr bool F32 = C::kF32;
+  __shared__ __attribute__((aligned(16))) char smem[2 * C::kStage];
+  __shared__ int wg_win[NW][2];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wid = tid >> 6;
+  const int n = lane & 31, h = lane >> 5;
+  const int Nq = a.Nq, Nk = a.Nk;
+  const int off = Nk - Nq;  // bottom-right aligned causal diagonal
+  const bool causal = a.causal != 0;
+  const bool ranged = a.key_start != nullptr;
+
+  int bh, qb;
+  map_block(blockIdx.x, a.B * a.H, a.nqb, a.sched, bh, qb);
+  const int head = bh % a.H;
+  const int q0 = qb * C::kBR;
+  const T* __restrict__ Q = static_cast<const T*>(a.q) + (size_t)bh * Nq * D;
+  const T* __restrict__ K = static_cast<const T*>(a.k) + (size_t)bh * Nk * D;
+  const T* __restrict__ V = static_cast<const T*>(a.v) + (size_t)bh * Nk * D;
+  T* __restrict__ O = static_cast<T*>(a.o) + (size_t)bh * Nq * D;
+  const float sl2 = a.sl2;
+  const float slope2 = BIAS ? a.slope2[a.n_slopes == 1 ? 0 : head] : 0.f;
+
+  // ---- this lane's query rows and key intervals ----------------------------------
+  const int wq0 = q0 + wid * C::kQW;
+  int qrow[QSUB], kst[QSUB], ken[QSUB];
+  int w_min_s = Nk, w_max_s = 0, w_min_e = Nk, w_max_e = 0;
+#pragma unroll
+  for (int qs = 0; qs < QSUB; ++qs) {
+    qrow[qs] = wq0 + qs * 32 + n;
+    kst[qs] = 0;
+    ken[qs] = Nk;
+    if (ranged) {
+      if (qrow[qs] < Nq) {
+        kst[qs] = min(max(a.key_start[qrow[qs]], 0), Nk);
+        ken[qs] = min(max(a.key_end[qrow[qs]], 0), Nk);
+        w_min_s = min(w_min_s, kst[qs]);
+        w_max_s = max(w_max_s, kst[qs]);
+        w_min_e = min(w_min_e, ken[qs]);
+        w_max_e = max(w_max_e, ken[qs]);
+      }
+    }
+  }
+  const bool wave_live = wq0 < Nq;
+  const int wq_last = min(wq0 + C::kQW, Nq) - 1;
+  // keys [w_lo, w_hi) may be visible to some row of this wave; keys < w_full_c are
+  // visible (causally) to every row of the wave
+  int w_lo = 0, w_hi = Nk, w_full_c = Nk;
+  if (causal) {
+    w_hi = min(w_hi, wq_last + off + 1);
+    w_full_c = max(0, min(Nk, wq0 + off + 1));
+  }
+  if (ranged) {
+    w_min_s = wave_min(w_min_s);
+    w_max_s = wave_max(w_max_s);
+    w_min_e = wave_min(w_min_e);
+    w_max_e = wave_max(w_max_e);
+    w_lo = max(w_lo, w_min_s);
+    w_hi = min(w_hi, w_max_e);
+  }
+  if (!wave_live || w_hi <= w_lo) { w_lo = Nk; w_hi = 0; }
+  if (lane == 0) { wg_win[wid][0] = w_lo; wg_win[wid][1] = w_hi; }
+  __syncthreads();
+  int g_lo = Nk, g_hi = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) { g_lo = min(g_lo, wg_win[w][0]); g_hi = max(g_hi, wg_win[w][1]); }
+  const int t_lo = g_hi > g_lo ? g_lo / BC : 0;
+  const int t_hi = g_hi > g_lo ? (g_hi + BC - 1) / BC : 0;
+
+  // ---- Q fragments in registers (B operand of S^T = K Q^T) -----------------------
+  u32x4 qf[QSUB][F32 ? 1 : C::kDK];
+  float qf1[QSUB][F32 ? C::kDK : 1];
+#pragma unroll
+  for (int qs = 0; qs < QSUB; ++qs) {
+    const bool ok = qrow[qs] < Nq;
+    if constexpr (F32) {
+#pragma unroll
+      for (int ks = 0; ks < C::kDK; ++ks)
+        qf1[qs][ks] = ok ? reinterpret_cast<const float*>(Q)[(size_t)qrow[qs] * D + 2 * ks + h] : 0.f;
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < C::kDK; ++ks)
+        qf[qs][ks] = ok ? ldg16(Q + (size_t)qrow[qs] * D + 16 * ks + 8 * h) : u32x4{0, 0, 0, 0};
+    }
+  }
+
+  // ---- running state ---------------------------------------------------------------
+  f32x16 o[QSUB][C::kDB];
+  float m2[QSUB], l[QSUB];
+#pragma unroll
+  for (int qs = 0; qs < QSUB; ++qs) {
+    m2[qs] = kNegInf;
+    l[qs] = 0.f;
+#pragma unroll
+    for (int db = 0; db < C::kDB; ++db) o[qs][db] = f32x16{};
+  }
+
+  // ---- global -> register -> LDS copy of one K/V tile ------------------------------
+  u32x4 kreg[C::kKPer];
+  u32x4 vreg[C::kVPer][F32 ? 1 : C::kKQ];
+
+  auto load_tile = [&](int t) {
+    const int kt0 = t * BC;
+#pragma unroll
+    for (int i = 0; i < C::kKPer; ++i) {
+      const int c = tid + i * C::kNT;
+      const int row = c / C::kRowChunks, col = c % C::kRowChunks;
+      const int key = kt0 + row;
+      kreg[i] = key < Nk ? ldg16(K + (size_t)key * D + col * C::kEltPerChunk) : u32x4{0, 0, 0, 0};
+    }
+    if constexpr (F32) {
+#pragma unroll
+      for (int i = 0; i < C::kVPer; ++i) {
+        const int c = tid + i * C::kNT;
+        const int row = c / C::kRowChunks, col = c % C::kRowChunks;
+        const int key = kt0 + row;
+        vreg[i][0] = key < Nk ? ldg16(V + (size_t)key * D + col * 4) : u32x4{0, 0, 0, 0};
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < C::kVPer; ++i) {
+        const int b = tid + i * C::kNT;
+        const int grp = b / C::kRowChunks, col = b % C::kRowChunks;
+#pragma unroll
+        for (int e = 0; e < C::kKQ; ++e) {
+          const int key = kt0 + grp * C::kKQ + e;
+          vreg[i][e] = key < Nk ? ldg16(V + (size_t)key * D + col * 8) : u32x4{0, 0, 0, 0};
+        }
+      }
+    }
+  };
+
+  auto store_tile = [&](int stage) {
+    char* Ks = smem + stage * C::kStage;
+    char* Vs = Ks + C::kKBytes;
+    if constexpr (F32) {
+#pragma unroll
+      for (int i = 0; i < C::kKPer; ++i) {
+        const int c = tid + i * C::kNT;
+        const int row = c / C::kRowChunks, col = c % C::kRowChunks;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) lds_st4(Ks, row * C::kKStride + (col * 4 + e) * 4, kreg[i][e]);
+      }
+#pragma unroll
+      for (int i = 0; i < C::kVPer; ++i) {
+        const int c = tid + i * C::kNT;
+        const int row = c / C::kRowChunks, col = c % C::kRowChunks;
+        lds_st16(Vs, row * C::kVStride + col * 16, vreg[i][0]);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < C::kKPer; ++i) {
+        const int c = tid + i * C::kNT;
+        const int row = c / C::kRowChunks, col = c % C::kRowChunks;
+        lds_st16(Ks, row * C::kKStride + col * 16, kreg[i]);
+      }
+      // V^T: the thread holds keys grp*KQ .. +KQ-1, d values col*8 .. col*8+7
+#pragma unroll
+      for (int i = 0; i < C::kVPer; ++i) {
+        const int b = tid + i * C::kNT;
+        const int grp = b / C::kRowChunks, col = b % C::kRowChunks;
+        const int pos = vt_pos(grp * C::kKQ);  // KQ consecutive keys -> KQ consecutive slots
+#pragma unroll
+        for (int dd = 0; dd < 8; ++dd) {
+          const int row = col * 8 + dd;
+          const int w = dd >> 1;
+          const int byte = vt_off<C>(row, pos >> 3) + (pos & 7) * 2;
+          if constexpr (C::kKQ == 4) {
+            u32x2 val;
+            val[0] = (dd & 1) ? pack_hi(vreg[i][0][w], vreg[i][1][w]) : pack_lo(vreg[i][0][w], vreg[i][1][w]);
+            val[1] = (dd & 1) ? pack_hi(vreg[i][2][w], vreg[i][3][w]) : pack_lo(vreg[i][2][w], vreg[i][3][w]);
+            lds_st8(Vs, byte, val);
+          } else {
+            const uint32_t val = (dd & 1) ? pack_hi(vreg[i][0][w], vreg[i][1][w]) : pack_lo(vreg[i][0][w], vreg[i][1][w]);
+            lds_st4(Vs, byte, val);
+          }
+        }
+      }
+    }
+  };
+
+  if (t_lo < t_hi) {
+    load_tile(t_lo);
+    store_tile(0);
+  }
+  __syncthreads();
+
+  for (int t = t_lo; t < t_hi; ++t) {
+    const int stage = (t - t_lo) & 1;
+    const bool more = t + 1 < t_hi;
+    if (more) load_tile(t + 1);
+
+    const int kt0 = t * BC;
+    const int kt1 = kt0 + BC;
+    const bool skip = kt0 >= w_hi || kt1 <= w_lo;
+    if (!skip) {
+      const bool full = kt1 <= Nk && kt1 <= w_full_c &&
+                        (!ranged || (w_max_s <= kt0 && w_min_e >= kt1));
+      const char* Ks = smem + stage * C::kStage;
+      const char* Vs = Ks + C::kKBytes;
+
+      // ---- S^T = K Q^T ---------------------------------------------------------
+      f32x16 s[QSUB][C::kKB];
+#pragma unroll
+      for (int qs = 0; qs < QSUB; ++qs)
+#pragma unroll
+        for (int kb = 0; kb < C::kKB; ++kb) s[qs][kb] = f32x16{};
+#pragma unroll
+      for (int kb = 0; kb < C::kKB; ++kb) {
+#pragma unroll
+        for (int ks = 0; ks < C::kDK; ++ks) {
+          if constexpr (F32) {
+            const float av = *reinterpret_cast<const float*>(
+                Ks + (kb * 32 + n) * C::kKStride + (2 * ks + h) * 4);
+#pragma unroll
+            for (int qs = 0; qs < QSUB; ++qs) s[qs][kb] = E::mma1(av, qf1[qs][ks], s[qs][kb]);
+          } else {
+            const u32x4 av = lds_ld16(Ks, (kb * 32 + n) * C::kKStride + 32 * ks + 16 * h);
+#pragma unroll
+            for (int qs = 0; qs < QSUB; ++qs) s[qs][kb] = E::mma(av, qf[qs][ks], s[qs][kb]);
+          }
+        }
+      }
+
+      // ---- bias and masking (masking only on partially visible tiles) ----------
+      if constexpr (BIAS) {
+#pragma unroll
+        for (int qs = 0; qs < QSUB; ++qs) {
+          const float base = (float)(qrow[qs] - kt0 - 4 * h);
+#pragma unroll
+          for (int kb = 0; kb < C::kKB; ++kb)
+#pragma unroll
+            for (int g = 0; g < 16; ++g) {
+              const float dist = base - (float)(kb * 32 + 8 * (g / 4) + (g % 4));
+              s[qs][kb][g] = __builtin_fmaf(s[qs][kb][g], sl2, slope2 * __builtin_fabsf(dist));
+            }
+        }
+      }
+      if (!full) {
+#pragma unroll
+        for (int qs = 0; qs < QSUB; ++qs) {
+          const int lo = kst[qs], hi = min(ken[qs], Nk);
+          const int cl = causal ? qrow[qs] + off : Nk;
+#pragma unroll
+          for (int kb = 0; kb < C::kKB; ++kb)
+#pragma unroll
+            for (int g = 0; g < 16; ++g) {
+              const int j = kt0 + kb * 32 + res_row(g, h);
+              const bool vis = j >= lo && j < hi && j <= cl;
+              s[qs][kb][g] = vis ? s[qs][kb][g] : kNegInf;
+            }
+        }
+      }
+
+      // ---- online softmax: tile row max, lazy rescale, exponentials, row sums -----
+      float tmax[QSUB];
+      bool need = false;
+#pragma unroll
+      for (int qs = 0; qs < QSUB; ++qs) {
+        float mx = kNegInf;
+#pragma unroll
+        for (int kb = 0; kb < C::kKB; ++kb)
+#pragma unroll
+          for (int g = 0; g < 16; ++g) mx = __builtin_fmaxf(mx, s[qs][kb][g]);
+        mx = __builtin_fmaxf(mx, xhalf(mx));
+        tmax[qs] = BIAS ? mx : mx * sl2;
+        need |= tmax[qs] > m2[qs] + kTau;
+      }
+      if (wave_any(need)) {
+#pragma unroll
+        for (int qs = 0; qs < QSUB; ++qs) {
+          const float mnew = __builtin_fmaxf(m2[qs], tmax[qs]);
+          const float alpha = mnew == kNegInf ? 1.f : fast_exp2(m2[qs] - mnew);
+          l[qs] *= alpha;
+#pragma unroll
+          for (int db = 0; db < C::kDB; ++db) o[qs][db] *= alpha;
+          m2[qs] = mnew;
+        }
+      }
+#pragma unroll
+      for (int qs = 0; qs < QSUB; ++qs) {
+        const float nb = m2[qs] == kNegInf ? 0.f : -m2[qs];
+        float rs = 0.f;
+#pragma unroll
+        for (int kb = 0; kb < C::kKB; ++kb)
+#pragma unroll
+          for (int g = 0; g < 16; ++g) {
+            const float x = BIAS ? s[qs][kb][g] + nb : __builtin_fmaf(s[qs][kb][g], sl2, nb);
+            const float p = fast_exp2(x);
+            s[qs][kb][g] = p;
+            rs += p;
+          }
+        l[qs] += rs;
+      }
+
+      // ---- O^T += V^T P^T ---------------------------------------------------------
+#pragma unroll
+      for (int kb = 0; kb < C::kKB; ++kb) {
+        if constexpr (F32) {
+#pragma unroll
+          for (int g = 0; g < 16; ++g) {
+            const int key = kb * 32 + res_row(g, h);
+#pragma unroll
+            for (int db = 0; db < C::kDB; ++db) {
+              const float av = *reinterpret_cast<const float*>(
+                  Vs + key * C::kVStride + (db * 32 + n) * 4);
+#pragma unroll
+              for (int qs = 0; qs < QSUB; ++qs) o[qs][db] = E::mma1(av, s[qs][kb][g], o[qs][db]);
+            }
+          }
+        } else {
+#pragma unroll
+          for (int st = 0; st < 2; ++st) {
+            u32x4 pb[QSUB];
+#pragma unroll
+            for (int qs = 0; qs < QSUB; ++qs) {
+#pragma unroll
+              for (int w = 0; w < 4; ++w)
+                pb[qs][w] = E::pack2(s[qs][kb][8 * st + 2 * w], s[qs][kb][8 * st + 2 * w + 1]);
+            }
+#pragma unroll
+            for (int db = 0; db < C::kDB; ++db) {
+              const u32x4 av = lds_ld16(Vs, vt_off<C>(db * 32 + n, 4 * kb + 2 * st + h));
+#pragma unroll
+              for (int qs = 0; qs < QSUB; ++qs) o[qs][db] = E::mma(av, pb[qs], o[qs][db]);
+            }
+          }
+        }
+      }
+    }
+
+    if (more) store_tile(stage ^ 1);
+    __syncthreads();
+  }
+
+  // ---- epilogue: O = O^T / l, LSE = (m + log2 l) ln 2 -------------------------------
+#pragma unroll
+  for (int qs = 0; qs < QSUB; ++qs) {
+    const float lt = l[qs] + xhalf(l[qs]);
+    const float inv = lt > 0.f ? 1.f / lt : 0.f;
+    const int row = qrow[qs];
+    if (row < Nq) {
+#pragma unroll
+      for (int db = 0; db < C::kDB; ++db) {
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int d0 = db * 32 + 8 * g4 + 4 * h;
+          const float v0 = o[qs][db][4 * g4 + 0] * inv, v1 = o[qs][db][4 * g4 + 1] * inv;
+          const float v2 = o[qs][db][4 * g4 + 2] * inv, v3 = o[qs][db][4 * g4 + 3] * inv;
+          if constexpr (F32) {
+            *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(O) + (size_t)row * D + d0) =
+                f32x4{v0, v1, v2, v3};
+          } else {
+            stg8(O + (size_t)row * D + d0, u32x2{E::pack2(v0, v1), E::pack2(v2, v3)});
+          }
+        }
+      }
+      if (h == 0 && a.lse != nullptr) {
+        const float lse = lt > 0.f ? (m2[qs] + __builtin_amdgcn_logf(lt)) * kLn2 : kNegInf;
+        a.lse[(size_t)bh * Nq + row] = lse;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------
+// key-range summary: out[4r..4r+3] = min/max of clamped start and end over rows of block r
+// ---------------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void mask_summary_kernel(const int32_t* __restrict__ ks,
+                                                           const int32_t* __restrict__ ke,
+                                                           int Nq, int Nk, int block,
+                                                           int32_t* __restrict__ out) {
+  __shared__ int red[4][4];
+  const int r = blockIdx.x;
+  const int r0 = r * block, r1 = min(Nq, r0 + block);
+  int mn_s = Nk, mx_s = 0, mn_e = Nk, mx_e = 0;
+  for (int i = r0 + (int)threadIdx.x; i < r1; i += 256) {
+    const int s = min(max(ks[i], 0), Nk), e = min(max(ke[i], 0), Nk);
+    mn_s = min(mn_s, s); mx_s = max(mx_s, s); mn_e = min(mn_e, e); mx_e = max(mx_e, e);
+  }
+  mn_s = wave_min(mn_s); mx_s = wave_max(mx_s); mn_e = wave_min(mn_e); mx_e = wave_max(mx_e);
+  const int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) { red[w][0] = mn_s; red[w][1] = mx_s; red[w][2] = mn_e; red[w][3] = mx_e; }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int i = 1; i < 4; ++i) {
+      red[0][0] = min(red[0][0], red[i][0]); red[0][1] = max(red[0][1], red[i][1]);
+      red[0][2] = min(red[0][2], red[i][2]); red[0][3] = max(red[0][3], red[i][3]);
+    }
+    for (int i = 0; i < 4; ++i) out[4 * r + i] = red[0][i];
+  }
+}
+
+hipError_t launch_mask_summary(const int32_t* ks, const int32_t* ke, int Nq, int Nk, int block,
+                               int32_t* out, hipStream_t st) {
+  const int nb = (Nq + block - 1) / block;
+  hipLaunchKernelGGL(mask_summary_kernel, dim3(nb), dim3(256), 0, st, ks, ke, Nq, Nk, block, out);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------------
+// tile configurations per (dtype, d) and the launcher
+// ---------------------------------------------------------------------------------
+template <typename T, int D, int BC, int QSUB, int NW>
+static hipError_t launch_cfg(bool bias, FwdArgs& a, hipStream_t st) {
+  using C = FwdCfg<T, D, BC, QSUB, NW>;
+  a.nqb = (a.Nq + C::kBR - 1) / C::kBR;
+  const int BH = a.B * a.H;
+  a.sched = (BH % 8 == 0) ? kSchedXcd : kSchedHeadMajor;
+  const dim3 grid((unsigned)(BH * a.nqb)), block(C::kNT);
+  if (bias)
+    hipLaunchKernelGGL((fwd_kernel<T, D, BC, QSUB, NW, true>), grid, block, 0, st, a);
+  else
+    hipLaunchKernelGGL((fwd_kernel<T, D, BC, QSUB, NW, false>), grid, block, 0, st, a);
+  return hipGetLastError();
+}
+
+// (BC keys per tile, QSUB 32-row sub-blocks per wave, NW waves)
+#define FA_FWD_CFG_16_D128 128, 64, 2, 4
+#define FA_FWD_CFG_16_D64 64, 64, 2, 4
+#define FA_FWD_CFG_32_D128 128, 32, 1, 4
+#define FA_FWD_CFG_32_D64 64, 32, 1, 4
+
+int fwd_block_rows(fa_dtype dt, int d) {
+  (void)d;
+  return dt == FA_F32 ? FwdCfg<float, 64, 32, 1, 4>::kBR : FwdCfg<__bf16, 128, 64, 2, 4>::kBR;
+}
+
+hipError_t launch_fwd(fa_dtype dt, int d, bool bias, FwdArgs& a, hipStream_t st) {
+  switch (dt) {
+    case FA_BF16:
+      return d == 128 ? launch_cfg<__bf16, FA_FWD_CFG_16_D128>(bias, a, st)
+                      : launch_cfg<__bf16, FA_FWD_CFG_16_D64>(bias, a, st);
+    case FA_F16:
+      return d == 128 ? launch_cfg<_Float16, FA_FWD_CFG_16_D128>(bias, a, st)
+                      : launch_cfg<_Float16, FA_FWD_CFG_16_D64>(bias, a, st);
+    case FA_F32:
+      return d == 128 ? launch_cfg<float, FA_FWD_CFG_32_D128>(bias, a, st)
+                      : launch_cfg<float, FA_FWD_CFG_32_D64>(bias, a, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace fa

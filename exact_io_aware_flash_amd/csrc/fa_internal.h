@@ -1,0 +1,69 @@
+// fa_internal.h -- host/device argument blocks and launcher declarations (library-private).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "fa.h"
+
+namespace fa {
+
+// Work-to-workgroup mapping of the forward/backward grids.
+enum Sched : int {
+  kSchedHeadMajor = 0,  // block L -> head L / nblk, heaviest query block first
+  kSchedXcd = 1         // heads pinned to one of the 8 XCDs (L % 8), heaviest first
+};
+
+struct FwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  const int32_t* key_start;  // NULL: no key-range mask
+  const int32_t* key_end;
+  int B, H, Nq, Nk;
+  int causal;
+  int nqb;     // query blocks per (b, h)
+  int sched;   // Sched
+  int n_slopes;
+  float sl2;   // scale * log2(e)
+  float slope2[FA_MAX_SLOPES];  // bias slope * log2(e), per head or broadcast
+};
+
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dout;
+  const float* lse;
+  float* delta;   // [B,H,Nq] rowsum(dO * O), workspace
+  void* dq;
+  void* dk;
+  void* dv;
+  const int32_t* key_start;
+  const int32_t* key_end;
+  int B, H, Nq, Nk;
+  int causal;
+  int nblk;      // blocks per (b, h) along the parallel axis of the kernel
+  int sched;
+  int grad_f32;  // 1: gradients written as float32, else in the input type
+  int n_slopes;
+  float scale;
+  float sl2;
+  float slope2[FA_MAX_SLOPES];
+};
+
+// Launchers (return hipSuccess or the launch error). dtype-specialised in the .hip files.
+hipError_t launch_fwd(fa_dtype dt, int d, bool bias, FwdArgs& a, hipStream_t st);
+hipError_t launch_bwd(fa_dtype dt, int d, bool bias, BwdArgs& a, hipStream_t st);
+hipError_t launch_mask_summary(const int32_t* ks, const int32_t* ke, int Nq, int Nk, int block,
+                               int32_t* out, hipStream_t st);
+
+// Query rows per forward workgroup for (dtype, d): fixes the grid size.
+int fwd_block_rows(fa_dtype dt, int d);
+int bwd_key_block(fa_dtype dt, int d);
+int bwd_query_block(fa_dtype dt, int d);
+
+}  // namespace fa

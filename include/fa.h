@@ -1,0 +1,158 @@
+/*
+ * fa.h -- C ABI of the exact-attention library for AMD Instinct MI355X (gfx950).
+ *
+ * The library computes exact scaled-dot-product attention
+ *
+ *     O = softmax(scale * Q K^T + bias, masked) V
+ *
+ * the tiled, IO-aware way: Q is cut into row blocks and K/V into column blocks,
+ * each score tile lives only in registers, a running row max and row sum rescale
+ * the output accumulator (online softmax), and the N x N score matrix never
+ * reaches device memory. The backward pass recomputes the score tiles from Q, K
+ * and the saved log-sum-exp.
+ *
+ * Sources (pages cited by title and section):
+ *  - "Apakah Konteks Sehari Penuh Mengalahkan Konteks Sepuluh Menit? Perhatian
+ *    Kilat dan Pertanyaan Panjang Urutan" (marketmaker.cc blog on Flash
+ *    Attention): sections "Algoritma Flash Attention" (tiling and the per-block
+ *    loop), "Pengulangan softmax online" (running max/sum rescaling),
+ *    "Backward pass: menghitung ulang, bukan menyimpan" (keep only O and the
+ *    softmax statistics, recompute tiles), "FA2: paralelisme" (deferred
+ *    normalisation, parallelism over query blocks, per-wave query rows),
+ *    "Causal masking adalah tempat perdagangan mendapat diskon" (skip tiles in
+ *    the future), "Integrasinya delapan baris" ((batch, heads, seq, head_dim)
+ *    layout; causal is a flag; never fall back silently to a slow path).
+ *  - scifaro.com "related papers: FlashMask: Efficient and Rich Mask Extension
+ *    of FlashAttention": attention with an additive bias on the query-key scores.
+ *  - briefgpt.xyz page for arXiv 2307.08691, FlashAttention abstract: the
+ *    tiled method extends to block-sparse attention.
+ *
+ * Conventions shared by every entry point
+ *  - Tensors are dense, contiguous [B, H, N, d] with d innermost (element
+ *    (b,h,n,c) at ((b*H + h)*N + n)*d + c). LSE is [B, H, N_q] float32.
+ *  - Pointers named "device" must be device memory of the current HIP device,
+ *    16-byte aligned. The caller owns every buffer; the library allocates and
+ *    frees nothing and keeps no state between calls.
+ *  - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and
+ *    the calls return without synchronising. Inputs must stay valid until the
+ *    stream has passed the call.
+ *  - Arguments are validated before anything is enqueued. On any error the
+ *    call returns a non-zero fa_status and enqueues nothing; there is no
+ *    fallback to another algorithm. A launch failure returns FA_ERR_HIP.
+ */
+#ifndef FA_H
+#define FA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Symbols of the shared library (it is built with hidden default visibility). */
+#define FA_API __attribute__((visibility("default")))
+
+typedef enum fa_status {
+  FA_OK = 0,
+  FA_ERR_NULL = 1,        /* a required pointer is NULL */
+  FA_ERR_SHAPE = 2,       /* B, H, N_q or N_k < 1, or a size overflows 32-bit indexing */
+  FA_ERR_DTYPE = 3,       /* unknown dtype or gradient dtype */
+  FA_ERR_HEADDIM = 4,     /* d not in {64, 128} */
+  FA_ERR_MASK = 5,        /* malformed mask/bias descriptor */
+  FA_ERR_ALIGN = 6,       /* a device pointer is not 16-byte aligned */
+  FA_ERR_WORKSPACE = 7,   /* workspace NULL or smaller than fa_bwd_workspace_bytes() */
+  FA_ERR_UNSUPPORTED = 8, /* a valid combination this build does not implement */
+  FA_ERR_HIP = 9,         /* the HIP runtime reported an error at launch */
+  FA_ERR_ARG = 10         /* scale not finite or not positive; a slope not finite */
+} fa_status;
+
+typedef enum fa_dtype { FA_F32 = 0, FA_F16 = 1, FA_BF16 = 2 } fa_dtype;
+
+typedef enum fa_bias_kind {
+  FA_BIAS_NONE = 0,
+  /* bias(h, i, j) = slopes[h] * |i - j|, i and j absolute row/column indices,
+     generated on the fly (never stored); added after scaling (see fa_fwd). */
+  FA_BIAS_DIST_LINEAR = 1
+} fa_bias_kind;
+
+#define FA_MAX_SLOPES 256
+
+/* Optional bias and key-range mask.
+ *  bias_kind : fa_bias_kind.
+ *  slopes    : HOST pointer to n_slopes floats (read during the call only);
+ *              n_slopes == 1 applies slopes[0] to every head, n_slopes == H gives
+ *              one slope per head (H <= FA_MAX_SLOPES). Ignored for FA_BIAS_NONE.
+ *  key_start, key_end : DEVICE pointers to N_q int32 each, or both NULL.
+ *              Query row i attends exactly to keys j with
+ *              key_start[i] <= j < key_end[i] (one interval per row, shared by
+ *              every batch and head). Any int32 values are allowed: the interval
+ *              is intersected with [0, N_k); an empty interval gives an empty row.
+ *  A row with no visible key (after causal and range masking) gets O = 0 and
+ *  LSE = -inf. */
+typedef struct fa_mask_bias_desc {
+  int32_t bias_kind;
+  int32_t n_slopes;
+  const float* slopes;
+  const int32_t* key_start;
+  const int32_t* key_end;
+} fa_mask_bias_desc;
+
+/* Forward pass.
+ *  q [B,H,N_q,d], k and v [B,H,N_k,d]: device, element type `dtype`.
+ *  o [B,H,N_q,d]: device, output, element type `dtype` (rounded to nearest even).
+ *  lse [B,H,N_q]: device float32 output, natural-log log-sum-exp of each row's
+ *                 scaled, biased, masked scores (saved for fa_bwd); may be NULL.
+ *  d in {64, 128}; N_q, N_k >= 1 (any value: tail tiles are masked).
+ *  scale > 0 and finite (1/sqrt(d) is the usual choice); otherwise FA_ERR_ARG.
+ *  causal != 0: query i sees key j only if j <= i + (N_k - N_q) (bottom-right
+ *               aligned diagonal; identical to the usual rule when N_q == N_k).
+ *  mb: NULL for no bias and no range mask.
+ *  Math: s_ij = scale * q_i.k_j + bias(h,i,j), -inf where masked;
+ *        O_i = sum_j softmax(s_i)_j v_j ; LSE_i = log sum_j exp(s_ij).
+ *  Accumulation is float32 (bf16/f16 inputs go through bf16/f16 MFMA with the
+ *  probabilities rounded to the input type before the P.V product). */
+FA_API fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                 int B, int H, int N_q, int N_k, int d, float scale, int causal,
+                 const fa_mask_bias_desc* mb, fa_dtype dtype, void* stream);
+
+/* Bytes of device workspace fa_bwd needs for these sizes (caller allocates). */
+FA_API size_t fa_bwd_workspace_bytes(int B, int H, int N_q, int N_k, int d);
+
+/* Backward pass by recomputation.
+ *  q, k, v, o, dout: device, element type `dtype`, same shapes as in fa_fwd;
+ *  lse: device float32 [B,H,N_q] exactly as written by fa_fwd for these inputs.
+ *  dq [B,H,N_q,d], dk and dv [B,H,N_k,d]: device outputs of type `grad_dtype`
+ *  (FA_F32 or `dtype`); they are fully overwritten.
+ *  workspace: device, at least fa_bwd_workspace_bytes(...) bytes, 16-byte aligned;
+ *  its contents on entry do not matter.
+ *  Gradients of L = sum(O * dout): dV = P^T dO; dP = dO V^T; D_i = rowsum(dO_i * O_i);
+ *  dS = P * (dP - D); dQ = scale * dS K; dK = scale * dS^T Q, with
+ *  P = exp(S - LSE) recomputed tile by tile. No gradient flows to bias or mask. */
+FA_API fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                 const void* dout, void* dq, void* dk, void* dv, fa_dtype grad_dtype,
+                 void* workspace, size_t workspace_bytes,
+                 int B, int H, int N_q, int N_k, int d, float scale, int causal,
+                 const fa_mask_bias_desc* mb, fa_dtype dtype, void* stream);
+
+/* Key-range summary of consecutive blocks of `block_rows` query rows.
+ *  key_start, key_end: device int32 [N_q] (same meaning as in fa_mask_bias_desc).
+ *  out: device int32 [ceil(N_q / block_rows) * 4]; block r gets
+ *       {min start, max start, min end, max end} after clamping to [0, N_k].
+ *  A column tile [c0, c1) is fully masked for block r if c1 <= min start or
+ *  c0 >= max end, and fully visible if max start <= c0 and min end >= c1.
+ *  block_rows in [1, 1024]. */
+FA_API fa_status fa_mask_summary(const int32_t* key_start, const int32_t* key_end, int N_q, int N_k,
+                          int block_rows, int32_t* out, void* stream);
+
+/* Static description of a status code (never NULL). */
+FA_API const char* fa_status_string(fa_status s);
+
+/* Library version string, e.g. "fa 0.1.0 gfx950". */
+FA_API const char* fa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H */

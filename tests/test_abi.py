@@ -1,0 +1,146 @@
+"""The C ABI without a GPU: the library loads, exports every declared entry point,
+and rejects invalid arguments before launching anything (no compute calls here)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import exact_io_aware_flash_amd as fa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(fa.lib_path()),
+                                reason="libfa.so not built (run __graft_entry__.build())")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa_[a-z_]+)\s*\(", src)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for want in ("fa_fwd", "fa_bwd", "fa_bwd_workspace_bytes", "fa_mask_summary",
+                 "fa_status_string", "fa_version"):
+        assert want in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(fa.lib_path())
+    for name in declared_functions():
+        assert hasattr(lib, name), f"{name} missing from libfa.so"
+
+
+def test_status_strings_and_version():
+    lib = fa.load_library()
+    for code in range(0, 11):
+        s = fa.fa_status_string(code)
+        assert isinstance(s, str) and s
+    assert fa.fa_status_string(0) == "ok"
+    assert "gfx950" in fa.fa_version()
+    assert lib.fa_status_string(999) is not None
+
+
+def test_workspace_bytes():
+    assert fa.fa_bwd_workspace_bytes(2, 16, 8192, 8192, 128) == 2 * 16 * 8192 * 4
+    assert fa.fa_bwd_workspace_bytes(1, 1, 3, 5, 64) == 256
+    assert fa.fa_bwd_workspace_bytes(0, 1, 3, 5, 64) == 0
+
+
+# Fake, never-dereferenced device addresses: validation fails before any HIP call.
+P = 0x7F0000000000
+MIS = P + 8
+
+
+def fwd(**kw):
+    lib = fa.load_library()
+    a = dict(q=P, k=P, v=P, o=P, lse=P, B=1, H=1, Nq=16, Nk=16, d=64, scale=0.125, causal=0,
+             mb=None, dtype=fa.FA_BF16, stream=None)
+    a.update(kw)
+    return lib.fa_fwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["Nq"],
+                      a["Nk"], a["d"], a["scale"], a["causal"], a["mb"], a["dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), 1), (dict(o=None), 1),
+    (dict(B=0), 2), (dict(H=-1), 2), (dict(Nq=0), 2), (dict(Nk=0), 2),
+    (dict(Nq=1 << 30, d=128), 2),
+    (dict(dtype=7), 3),
+    (dict(d=96), 4), (dict(d=256), 4), (dict(d=0), 4),
+    (dict(k=MIS), 6), (dict(o=MIS), 6),
+    (dict(scale=0.0), 10), (dict(scale=-1.0), 10), (dict(scale=float("nan")), 10),
+    (dict(scale=float("inf")), 10),
+])
+def test_fwd_rejects_invalid_arguments(kw, status):
+    assert fwd(**kw) == status
+
+
+def test_fwd_rejects_malformed_descriptors():
+    d = fa.MaskBiasDesc()
+    d.bias_kind = 5
+    assert fwd(mb=ctypes.byref(d)) == 5
+    d = fa.MaskBiasDesc()
+    d.key_start = P
+    d.key_end = None
+    assert fwd(mb=ctypes.byref(d)) == 5
+    d = fa.MaskBiasDesc()
+    d.bias_kind = fa.FA_BIAS_DIST_LINEAR
+    d.n_slopes = 1
+    d.slopes = None
+    assert fwd(mb=ctypes.byref(d)) == 1
+    arr = (ctypes.c_float * 3)(1, 2, 3)
+    d.slopes = ctypes.cast(arr, ctypes.POINTER(ctypes.c_float))
+    d.n_slopes = 3
+    assert fwd(mb=ctypes.byref(d), H=4) == 5  # neither 1 nor H slopes
+    d.n_slopes = 1
+    arr[0] = float("nan")
+    assert fwd(mb=ctypes.byref(d)) == 10
+    d = fa.MaskBiasDesc()
+    d.key_start = MIS
+    d.key_end = P
+    assert fwd(mb=ctypes.byref(d)) == 6
+
+
+def bwd(**kw):
+    lib = fa.load_library()
+    a = dict(q=P, k=P, v=P, o=P, lse=P, do=P, dq=P, dk=P, dv=P, gdt=fa.FA_F32, ws=P, wsb=1 << 20,
+             B=1, H=1, Nq=16, Nk=16, d=128, scale=0.1, causal=1, mb=None, dtype=fa.FA_BF16,
+             stream=None)
+    a.update(kw)
+    return lib.fa_bwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["do"], a["dq"], a["dk"],
+                      a["dv"], a["gdt"], a["ws"], a["wsb"], a["B"], a["H"], a["Nq"], a["Nk"],
+                      a["d"], a["scale"], a["causal"], a["mb"], a["dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(do=None), 1), (dict(lse=None), 1), (dict(dk=None), 1),
+    (dict(gdt=fa.FA_F16), 3),
+    (dict(ws=None), 7), (dict(wsb=16), 7),
+    (dict(d=32), 4), (dict(Nk=0), 2),
+    (dict(dv=MIS), 6), (dict(ws=MIS), 6),
+    (dict(scale=0.0), 10),
+])
+def test_bwd_rejects_invalid_arguments(kw, status):
+    assert bwd(**kw) == status
+
+
+@pytest.mark.parametrize("args,status", [
+    ((None, P, 10, 10, 4, P, None), 1),
+    ((P, P, 0, 10, 4, P, None), 2),
+    ((P, P, 10, 10, 0, P, None), 2),
+    ((P, P, 10, 10, 2048, P, None), 2),
+    ((P, MIS, 10, 10, 4, P, None), 6),
+])
+def test_mask_summary_rejects_invalid_arguments(args, status):
+    assert fa.load_library().fa_mask_summary(*args) == status
+
+
+def test_python_binding_refuses_cpu_tensors():
+    import torch
+    q = torch.zeros(1, 1, 4, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        fa.fa_fwd(q, q, q)
