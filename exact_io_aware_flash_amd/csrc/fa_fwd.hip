@@ -104,9 +104,9 @@ __device__ inline int wave_max(int v) {
   return v;
 }
 
-template <typename T, int D, int BC, int QSUB, int NW, bool BIAS>
+template <typename T, int D, int BC, int QSUB, int NW, int WPE, bool BIAS>
 __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
-                          amdgpu_waves_per_eu(1, 1)))
+                          amdgpu_waves_per_eu(WPE, WPE)))
 void fwd_kernel(const FwdArgs a) {
   using C = FwdCfg<T, D, BC, QSUB, NW>;
   using E = Elt<T>;
@@ -184,15 +184,13 @@ void fwd_kernel(const FwdArgs a) {
   float qf1[QSUB][F32 ? C::kDK : 1];
 #pragma unroll
   for (int qs = 0; qs < QSUB; ++qs) {
-    const bool ok = qrow[qs] < Nq;
+    const size_t r = (size_t)min(qrow[qs], Nq - 1);  // rows past the end are never stored
     if constexpr (F32) {
 #pragma unroll
-      for (int ks = 0; ks < C::kDK; ++ks)
-        qf1[qs][ks] = ok ? reinterpret_cast<const float*>(Q)[(size_t)qrow[qs] * D + 2 * ks + h] : 0.f;
+      for (int ks = 0; ks < C::kDK; ++ks) qf1[qs][ks] = Q[r * D + 2 * ks + h];
     } else {
 #pragma unroll
-      for (int ks = 0; ks < C::kDK; ++ks)
-        qf[qs][ks] = ok ? ldg16(Q + (size_t)qrow[qs] * D + 16 * ks + 8 * h) : u32x4{0, 0, 0, 0};
+      for (int ks = 0; ks < C::kDK; ++ks) qf[qs][ks] = ldg16(Q + r * D + 16 * ks + 8 * h);
     }
   }
 
@@ -217,16 +215,16 @@ void fwd_kernel(const FwdArgs a) {
     for (int i = 0; i < C::kKPer; ++i) {
       const int c = tid + i * C::kNT;
       const int row = c / C::kRowChunks, col = c % C::kRowChunks;
-      const int key = kt0 + row;
-      kreg[i] = key < Nk ? ldg16(K + (size_t)key * D + col * C::kEltPerChunk) : u32x4{0, 0, 0, 0};
+      const int key = min(kt0 + row, Nk - 1);
+      kreg[i] = ldg16(K + (size_t)key * D + col * C::kEltPerChunk);
     }
     if constexpr (F32) {
 #pragma unroll
       for (int i = 0; i < C::kVPer; ++i) {
         const int c = tid + i * C::kNT;
         const int row = c / C::kRowChunks, col = c % C::kRowChunks;
-        const int key = kt0 + row;
-        vreg[i][0] = key < Nk ? ldg16(V + (size_t)key * D + col * 4) : u32x4{0, 0, 0, 0};
+        const int key = min(kt0 + row, Nk - 1);
+        vreg[i][0] = ldg16(V + (size_t)key * D + col * 4);
       }
     } else {
 #pragma unroll
@@ -235,8 +233,8 @@ void fwd_kernel(const FwdArgs a) {
         const int grp = b / C::kRowChunks, col = b % C::kRowChunks;
 #pragma unroll
         for (int e = 0; e < C::kKQ; ++e) {
-          const int key = kt0 + grp * C::kKQ + e;
-          vreg[i][e] = key < Nk ? ldg16(V + (size_t)key * D + col * 8) : u32x4{0, 0, 0, 0};
+          const int key = min(kt0 + grp * C::kKQ + e, Nk - 1);
+          vreg[i][e] = ldg16(V + (size_t)key * D + col * 8);
         }
       }
     }
@@ -513,7 +511,7 @@ hipError_t launch_mask_summary(const int32_t* ks, const int32_t* ke, int Nq, int
 // ---------------------------------------------------------------------------------
 // tile configurations per (dtype, d) and the launcher
 // ---------------------------------------------------------------------------------
-template <typename T, int D, int BC, int QSUB, int NW>
+template <typename T, int D, int BC, int QSUB, int NW, int WPE>
 static hipError_t launch_cfg(bool bias, FwdArgs& a, hipStream_t st) {
   using C = FwdCfg<T, D, BC, QSUB, NW>;
   a.nqb = (a.Nq + C::kBR - 1) / C::kBR;
@@ -521,22 +519,22 @@ static hipError_t launch_cfg(bool bias, FwdArgs& a, hipStream_t st) {
   a.sched = (BH % 8 == 0) ? kSchedXcd : kSchedHeadMajor;
   const dim3 grid((unsigned)(BH * a.nqb)), block(C::kNT);
   if (bias)
-    hipLaunchKernelGGL((fwd_kernel<T, D, BC, QSUB, NW, true>), grid, block, 0, st, a);
+    hipLaunchKernelGGL((fwd_kernel<T, D, BC, QSUB, NW, WPE, true>), grid, block, 0, st, a);
   else
-    hipLaunchKernelGGL((fwd_kernel<T, D, BC, QSUB, NW, false>), grid, block, 0, st, a);
+    hipLaunchKernelGGL((fwd_kernel<T, D, BC, QSUB, NW, WPE, false>), grid, block, 0, st, a);
   return hipGetLastError();
 }
 
-// (BC keys per tile, QSUB 32-row sub-blocks per wave, NW waves)
-#define FA_FWD_CFG_16_D128 128, 64, 2, 4
-#define FA_FWD_CFG_16_D64 64, 64, 2, 4
-#define FA_FWD_CFG_32_D128 128, 32, 1, 4
-#define FA_FWD_CFG_32_D64 64, 32, 1, 4
+// (d, BC keys per tile, QSUB 32-row sub-blocks per wave, NW waves, waves per SIMD)
+#ifndef FA_FWD_CFG_16_D128
+#define FA_FWD_CFG_16_D128 128, 64, 1, 8, 2
+#endif
+#ifndef FA_FWD_CFG_16_D64
+#define FA_FWD_CFG_16_D64 64, 128, 1, 8, 2
+#endif
+#define FA_FWD_CFG_32_D128 128, 32, 1, 4, 1
+#define FA_FWD_CFG_32_D64 64, 32, 1, 4, 1
 
-int fwd_block_rows(fa_dtype dt, int d) {
-  (void)d;
-  return dt == FA_F32 ? FwdCfg<float, 64, 32, 1, 4>::kBR : FwdCfg<__bf16, 128, 64, 2, 4>::kBR;
-}
 
 hipError_t launch_fwd(fa_dtype dt, int d, bool bias, FwdArgs& a, hipStream_t st) {
   switch (dt) {
