@@ -108,9 +108,9 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
 size_t fa_bwd_workspace_bytes(int B, int H, int N_q, int N_k, int d) {
   (void)N_k; (void)d;
   if (B < 1 || H < 1 || N_q < 1) return 0;
-  // delta = rowsum(dO * O): one float per query row, rounded up to 256 bytes
-  const size_t delta = (size_t)B * H * N_q * sizeof(float);
-  return (delta + 255) & ~(size_t)255;
+  // delta = rowsum(dO * O) (one float per query row) + the key-range summary of every
+  // 64-row query tile (4 int32), each rounded up to 256 bytes
+  return bwd_workspace_bytes(B, H, N_q);
 }
 
 fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
@@ -122,9 +122,10 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, con
   if (st != FA_OK) return st;
   if (grad_dtype != FA_F32 && grad_dtype != dtype) return FA_ERR_DTYPE;
   if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return FA_ERR_NULL;
-  const void* dev[] = {q, k, v, o, lse, dout, dq, dk, dv};
+  const void* dev[] = {q, k, v, o, dout, dq, dk, dv};
   for (const void* p : dev)
     if (!aligned16(p)) return FA_ERR_ALIGN;
+  if (reinterpret_cast<uintptr_t>(lse) & 3u) return FA_ERR_ALIGN;
   if (workspace == nullptr || workspace_bytes < fa_bwd_workspace_bytes(B, H, N_q, N_k, d))
     return FA_ERR_WORKSPACE;
   if (!aligned16(workspace)) return FA_ERR_ALIGN;
@@ -135,6 +136,7 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, con
   if (st != FA_OK) return st;
   a.q = q; a.k = k; a.v = v; a.o = o; a.dout = dout; a.lse = lse;
   a.delta = static_cast<float*>(workspace);
+  a.qsum = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + bwd_qsum_offset(B, H, N_q));
   a.dq = dq; a.dk = dk; a.dv = dv;
   a.B = B; a.H = H; a.Nq = N_q; a.Nk = N_k;
   a.causal = causal ? 1 : 0;

@@ -1,8 +1,560 @@
-// fa_bwd.hip -- recompute-based backward kernels (placeholder until the kernels land).
+// fa_bwd.hip -- recompute-based attention backward for gfx950 (MI355X).
+//
+// Method (blog "Apakah Konteks Sehari Penuh Mengalahkan Konteks Sepuluh Menit?", section
+// "Backward pass: menghitung ulang, bukan menyimpan"): only O and the softmax statistics
+// (here the log-sum-exp) are kept from the forward pass; every score tile is recomputed
+// from Q and K, P = exp(S - LSE). The gradient formulas are the textbook softmax
+// Jacobian: dV = P^T dO, dP = dO V^T, D = rowsum(dO * O), dS = P * (dP - D),
+// dQ = scale * dS K, dK = scale * dS^T Q.
+//
+// Three launches, no atomics, deterministic:
+//  1. prep:  D_i = rowsum(dO_i * O_i) in float32 (one HBM pass);
+//  2. dkdv:  one workgroup per (b, h, block of 32*NW keys); each wave keeps its 32 keys'
+//            K and V rows in registers and accumulates dK^T/dV^T while walking the query
+//            tiles. S = Q K^T and dP = dO V^T come out with the key on the lane and the
+//            query on the register, so P^T and dS^T feed the dV/dK products straight from
+//            registers; Q and dO are staged in LDS both row-major (A operands of S, dP)
+//            and transposed (B operands of dV, dK);
+//  3. dq:    forward-shaped: one workgroup per (b, h, block of 32*NW queries); Q, dO, LSE
+//            and D of the wave's 32 queries stay in registers; K (row-major and
+//            transposed) and V tiles are double-buffered in LDS; dQ^T += K^T dS^T.
+// The dq pass recomputes S and dP a second time (7 matrix products instead of 5) in
+// exchange for no float32 atomics on dQ.
+#include <type_traits>
+
+#include "fa_device.h"
 #include "fa_internal.h"
 
 namespace fa {
 
-hipError_t launch_bwd(fa_dtype, int, bool, BwdArgs&, hipStream_t) { return hipErrorNotSupported; }
+// ---------------------------------------------------------------------------------
+// 1. D = rowsum(dO * O)
+// ---------------------------------------------------------------------------------
+template <typename T, int D>
+__global__ __launch_bounds__(256) void bwd_prep_kernel(const T* __restrict__ o,
+                                                       const T* __restrict__ dout,
+                                                       float* __restrict__ delta, int rows) {
+  constexpr int TPR = D / 8;  // threads per row, 8 elements (16 bytes) each
+  constexpr int RPB = 256 / TPR;
+  const int row = blockIdx.x * RPB + (int)threadIdx.x / TPR;
+  const int c = threadIdx.x % TPR;
+  float acc = 0.f;
+  if (row < rows) {
+    const u32x4 x = ldg16(o + (size_t)row * D + c * 8);
+    const u32x4 y = ldg16(dout + (size_t)row * D + c * 8);
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const uint32_t xw = x[w], yw = y[w];
+      const float x0 = (float)__builtin_bit_cast(T, (uint16_t)(xw & 0xffffu));
+      const float x1 = (float)__builtin_bit_cast(T, (uint16_t)(xw >> 16));
+      const float y0 = (float)__builtin_bit_cast(T, (uint16_t)(yw & 0xffffu));
+      const float y1 = (float)__builtin_bit_cast(T, (uint16_t)(yw >> 16));
+      acc = __builtin_fmaf(x0, y0, acc);
+      acc = __builtin_fmaf(x1, y1, acc);
+    }
+  }
+#pragma unroll
+  for (int s = TPR / 2; s >= 1; s >>= 1) acc += __shfl_xor(acc, s, 64);
+  if (row < rows && c == 0) delta[row] = acc;
+}
+
+// Stores 4 consecutive float gradients (converted as requested).
+template <typename T>
+__device__ inline void store_grad4(void* base, size_t idx, bool f32, float v0, float v1, float v2,
+                                   float v3) {
+  if (f32) {
+    *reinterpret_cast<f32x4*>(static_cast<float*>(base) + idx) = f32x4{v0, v1, v2, v3};
+  } else {
+    stg8(static_cast<T*>(base) + idx, u32x2{Elt<T>::pack2(v0, v1), Elt<T>::pack2(v2, v3)});
+  }
+}
+
+// ---------------------------------------------------------------------------------
+// 2. dK, dV: key-block-outer
+// ---------------------------------------------------------------------------------
+template <int D, int BR>
+struct DkdvLds {
+  static constexpr int NS = D * 2 + 16;   // row-major tile row stride (bytes)
+  static constexpr int TS = BR * 2 + 16;  // transposed tile row stride (D rows)
+  static constexpr int NB = BR * NS;
+  static constexpr int TB = D * TS;
+  static constexpr int QN = 0, QT = NB, DN = NB + TB, DT = 2 * NB + TB;
+  static constexpr int LSE = 2 * NB + 2 * TB, DLT = LSE + BR * 4, KS = DLT + BR * 4,
+                       KE = KS + BR * 4;
+  static constexpr int STAGE = KE + BR * 4;
+};
+
+template <typename T, int D, int BR, int NW, int WPE, bool BIAS>
+__global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
+                          amdgpu_waves_per_eu(WPE, WPE)))
+void bwd_dkdv_kernel(const BwdArgs a) {
+  using E = Elt<T>;
+  using L = DkdvLds<D, BR>;
+  constexpr int NT = NW * 64, BK = 32 * NW, QB = BR / 32, DK = D / 16, DB = D / 32;
+  using TC = TileCopy<BR, D, NT>;
+  static_assert(2 * L::STAGE <= 160 * 1024, "LDS budget");
+  __shared__ __attribute__((aligned(16))) char smem[2 * L::STAGE];
+  __shared__ int win[2];
+
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6, n = lane & 31, h = lane >> 5;
+  const int Nq = a.Nq, Nk = a.Nk, off = Nk - Nq;
+  const bool causal = a.causal != 0, ranged = a.key_start != nullptr;
+  int bh, kb;
+  map_block(blockIdx.x, a.B * a.H, a.nblk, a.sched, false, bh, kb);
+  const int head = bh % a.H;
+  const T* Q = static_cast<const T*>(a.q) + (size_t)bh * Nq * D;
+  const T* K = static_cast<const T*>(a.k) + (size_t)bh * Nk * D;
+  const T* V = static_cast<const T*>(a.v) + (size_t)bh * Nk * D;
+  const T* dO = static_cast<const T*>(a.dout) + (size_t)bh * Nq * D;
+  const float* lse = a.lse + (size_t)bh * Nq;
+  const float* dlt = a.delta + (size_t)bh * Nq;
+  const float sl2 = a.sl2;
+  const float slope2 = BIAS ? a.slope2[a.n_slopes == 1 ? 0 : head] : 0.f;
+
+  const int k0 = kb * BK, k1 = min(k0 + BK, Nk);
+  const int kw0 = k0 + 32 * wid, kw1 = min(kw0 + 32, Nk);
+  const int key = kw0 + n;  // this lane's key (column of S)
+
+  // K and V rows of the wave's keys: B operands of S = Q K^T and dP = dO V^T
+  u32x4 kf[DK], vf[DK];
+  {
+    const size_t r = (size_t)min(key, Nk - 1);
+#pragma unroll
+    for (int ks = 0; ks < DK; ++ks) {
+      kf[ks] = ldg16(K + r * D + 16 * ks + 8 * h);
+      vf[ks] = ldg16(V + r * D + 16 * ks + 8 * h);
+    }
+  }
+
+  // query tiles that can see a key of this block
+  const int nqt = (Nq + BR - 1) / BR;
+  int t_lo = 0, t_hi = nqt;
+  if (causal) t_lo = max(0, k0 - off) / BR;
+  if (causal && k0 - off >= Nq) t_hi = 0;
+  if (ranged) {
+    if (tid < 64) {
+      int lo = nqt, hi = -1;
+      for (int t = lane; t < nqt; t += 64) {
+        const int* s = a.qsum + 4 * t;  // {min start, max start, min end, max end}
+        if (!(k1 <= s[0] || k0 >= s[3])) { lo = min(lo, t); hi = max(hi, t); }
+      }
+      lo = wave_min(lo);
+      hi = wave_max(hi);
+      if (lane == 0) { win[0] = lo; win[1] = hi + 1; }
+    }
+    __syncthreads();
+    t_lo = max(t_lo, win[0]);
+    t_hi = min(t_hi, win[1]);
+  }
+  if (k0 >= Nk) t_hi = t_lo;
+
+  f32x16 dv[DB], dk[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) { dv[db] = f32x16{}; dk[db] = f32x16{}; }
+
+  TC tq, tdo;
+  float lse_r = 0.f, dlt_r = 0.f;
+  int ks_r = 0, ke_r = 0;
+  auto load_tile = [&](int t) {
+    const int q0t = t * BR;
+    tq.load(Q, q0t, Nq, tid);
+    tdo.load(dO, q0t, Nq, tid);
+    if (tid < BR) {
+      const int r = min(q0t + tid, Nq - 1);
+      lse_r = lse[r] * kLog2e;
+      dlt_r = dlt[r];
+      if (ranged) {
+        ks_r = min(max(a.key_start[r], 0), Nk);
+        ke_r = min(max(a.key_end[r], 0), Nk);
+      }
+    }
+  };
+  auto store_tile = [&](int stage) {
+    char* s = smem + stage * L::STAGE;
+    tq.template store_natural<L::NS>(s + L::QN, tid);
+    tq.template store_T<L::TS>(s + L::QT, tid);
+    tdo.template store_natural<L::NS>(s + L::DN, tid);
+    tdo.template store_T<L::TS>(s + L::DT, tid);
+    if (tid < BR) {
+      reinterpret_cast<float*>(s + L::LSE)[tid] = lse_r;
+      reinterpret_cast<float*>(s + L::DLT)[tid] = dlt_r;
+      reinterpret_cast<int*>(s + L::KS)[tid] = ks_r;
+      reinterpret_cast<int*>(s + L::KE)[tid] = ke_r;
+    }
+  };
+
+  if (t_lo < t_hi) {
+    load_tile(t_lo);
+    store_tile(0);
+  }
+  __syncthreads();
+
+  for (int t = t_lo; t < t_hi; ++t) {
+    const int stage = (t - t_lo) & 1;
+    const bool more = t + 1 < t_hi;
+    if (more) load_tile(t + 1);
+    const int q0t = t * BR;
+    const char* s = smem + stage * L::STAGE;
+
+    // classify the tile for this wave's keys [kw0, kw1)
+    bool skip = kw0 >= Nk;
+    bool full = q0t + BR <= Nq && kw0 + 32 <= Nk;
+    if (causal) {
+      skip |= q0t + BR - 1 + off < kw0;
+      full &= q0t + off >= kw0 + 31;
+    }
+    if (ranged) {
+      const int* sm = a.qsum + 4 * t;
+      skip |= kw1 <= sm[0] || kw0 >= sm[3];
+      full &= sm[1] <= kw0 && sm[2] >= kw0 + 32;
+    }
+    if (!skip) {
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        f32x16 sc = f32x16{}, dp = f32x16{};
+#pragma unroll
+        for (int ks = 0; ks < DK; ++ks) {
+          const int o = (32 * qb + n) * L::NS + 32 * ks + 16 * h;
+          sc = E::mma(lds_ld16(s + L::QN, o), kf[ks], sc);
+          dp = E::mma(lds_ld16(s + L::DN, o), vf[ks], dp);
+        }
+        // per-query statistics of the 16 queries this lane holds (rows res_row(g, h))
+        f32x4 l4[4], d4[4];
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const int r0 = 32 * qb + 8 * q4 + 4 * h;
+          l4[q4] = *reinterpret_cast<const f32x4*>(s + L::LSE + r0 * 4);
+          d4[q4] = *reinterpret_cast<const f32x4*>(s + L::DLT + r0 * 4);
+        }
+        float p[16], ds[16];
+#pragma unroll
+        for (int g = 0; g < 16; ++g) {
+          const float lq = l4[g / 4][g % 4];
+          float x;
+          if constexpr (BIAS) {
+            const float dist = (float)(q0t + 32 * qb + 4 * h - key) + (float)(8 * (g / 4) + (g % 4));
+            x = __builtin_fmaf(sc[g], sl2, __builtin_fmaf(slope2, __builtin_fabsf(dist), -lq));
+          } else {
+            x = __builtin_fmaf(sc[g], sl2, -lq);
+          }
+          p[g] = fast_exp2(x);
+        }
+        if (!full) {
+          int4 st4[4], en4[4];
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4) {
+            const int r0 = 32 * qb + 8 * q4 + 4 * h;
+            st4[q4] = *reinterpret_cast<const int4*>(s + L::KS + r0 * 4);
+            en4[q4] = *reinterpret_cast<const int4*>(s + L::KE + r0 * 4);
+          }
+#pragma unroll
+          for (int g = 0; g < 16; ++g) {
+            const int qi = q0t + 32 * qb + res_row(g, h);
+            const int sti = (&st4[g / 4].x)[g % 4], eni = (&en4[g / 4].x)[g % 4];
+            bool vis = qi < Nq && key < Nk;
+            if (causal) vis = vis && key <= qi + off;
+            if (ranged) vis = vis && key >= sti && key < eni;
+            p[g] = vis ? p[g] : 0.f;
+          }
+        }
+#pragma unroll
+        for (int g = 0; g < 16; ++g) ds[g] = p[g] * (dp[g] - d4[g / 4][g % 4]);
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+          u32x4 pa, da;
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            pa[w] = E::pack2(p[8 * st + 2 * w], p[8 * st + 2 * w + 1]);
+            da[w] = E::pack2(ds[8 * st + 2 * w], ds[8 * st + 2 * w + 1]);
+          }
+#pragma unroll
+          for (int db = 0; db < DB; ++db) {
+            const int o = TC::template t_off<L::TS>(32 * db + n, 4 * qb + 2 * st + h);
+            dv[db] = E::mma(pa, lds_ld16(s + L::DT, o), dv[db]);
+            dk[db] = E::mma(da, lds_ld16(s + L::QT, o), dk[db]);
+          }
+        }
+      }
+    }
+    if (more) store_tile(stage ^ 1);
+    __syncthreads();
+  }
+
+  // epilogue: lane holds column d = 32*db + n for keys kw0 + res_row(g, h)
+  const float scale = a.scale;
+#pragma unroll
+  for (int db = 0; db < DB; ++db) {
+#pragma unroll
+    for (int g = 0; g < 16; ++g) {
+      const int kr = kw0 + res_row(g, h);
+      if (kr < Nk) {
+        const size_t idx = ((size_t)bh * Nk + kr) * D + 32 * db + n;
+        if (a.grad_f32) {
+          static_cast<float*>(a.dk)[idx] = dk[db][g] * scale;
+          static_cast<float*>(a.dv)[idx] = dv[db][g];
+        } else {
+          static_cast<T*>(a.dk)[idx] = (T)(dk[db][g] * scale);
+          static_cast<T*>(a.dv)[idx] = (T)dv[db][g];
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------
+// 3. dQ: query-block-outer
+// ---------------------------------------------------------------------------------
+template <int D, int BC>
+struct DqLds {
+  static constexpr int NS = D * 2 + 16;
+  static constexpr int TS = BC * 2 + 16;
+  static constexpr int NB = BC * NS;
+  static constexpr int KN = 0, VN = NB, KT = 2 * NB;
+  static constexpr int STAGE = 2 * NB + D * TS;
+};
+
+template <typename T, int D, int BC, int NW, int WPE, bool BIAS>
+__global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
+                          amdgpu_waves_per_eu(WPE, WPE)))
+void bwd_dq_kernel(const BwdArgs a) {
+  using E = Elt<T>;
+  using L = DqLds<D, BC>;
+  constexpr int NT = NW * 64, BRQ = 32 * NW, KB = BC / 32, DK = D / 16, DB = D / 32;
+  using TC = TileCopy<BC, D, NT>;
+  static_assert(2 * L::STAGE <= 160 * 1024, "LDS budget");
+  __shared__ __attribute__((aligned(16))) char smem[2 * L::STAGE];
+  __shared__ int wg_win[NW][2];
+
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6, n = lane & 31, h = lane >> 5;
+  const int Nq = a.Nq, Nk = a.Nk, off = Nk - Nq;
+  const bool causal = a.causal != 0, ranged = a.key_start != nullptr;
+  int bh, qb;
+  map_block(blockIdx.x, a.B * a.H, a.nblk, a.sched, true, bh, qb);
+  const int head = bh % a.H;
+  const T* Q = static_cast<const T*>(a.q) + (size_t)bh * Nq * D;
+  const T* K = static_cast<const T*>(a.k) + (size_t)bh * Nk * D;
+  const T* V = static_cast<const T*>(a.v) + (size_t)bh * Nk * D;
+  const T* dO = static_cast<const T*>(a.dout) + (size_t)bh * Nq * D;
+  const float sl2 = a.sl2;
+  const float slope2 = BIAS ? a.slope2[a.n_slopes == 1 ? 0 : head] : 0.f;
+
+  const int q0 = qb * BRQ, wq0 = q0 + 32 * wid;
+  const int qrow = wq0 + n;
+  const size_t qr = (size_t)min(qrow, Nq - 1);
+  u32x4 qf[DK], dof[DK];
+#pragma unroll
+  for (int ks = 0; ks < DK; ++ks) {
+    qf[ks] = ldg16(Q + qr * D + 16 * ks + 8 * h);
+    dof[ks] = ldg16(dO + qr * D + 16 * ks + 8 * h);
+  }
+  const float lq = a.lse[(size_t)bh * Nq + qr] * kLog2e;
+  const float dq_d = a.delta[(size_t)bh * Nq + qr];
+
+  // key window of this wave / workgroup (same rules as the forward pass)
+  int kst = 0, ken = Nk;
+  int w_min_s = Nk, w_max_s = 0, w_min_e = Nk, w_max_e = 0;
+  if (ranged && qrow < Nq) {
+    kst = min(max(a.key_start[qrow], 0), Nk);
+    ken = min(max(a.key_end[qrow], 0), Nk);
+    w_min_s = kst; w_max_s = kst; w_min_e = ken; w_max_e = ken;
+  }
+  const bool wave_live = wq0 < Nq;
+  const int wq_last = min(wq0 + 32, Nq) - 1;
+  int w_lo = 0, w_hi = Nk, w_full_c = Nk;
+  if (causal) {
+    w_hi = min(w_hi, wq_last + off + 1);
+    w_full_c = max(0, min(Nk, wq0 + off + 1));
+  }
+  if (ranged) {
+    w_min_s = wave_min(w_min_s);
+    w_max_s = wave_max(w_max_s);
+    w_min_e = wave_min(w_min_e);
+    w_max_e = wave_max(w_max_e);
+    w_lo = max(w_lo, w_min_s);
+    w_hi = min(w_hi, w_max_e);
+  }
+  if (!wave_live || w_hi <= w_lo) { w_lo = Nk; w_hi = 0; }
+  if (lane == 0) { wg_win[wid][0] = w_lo; wg_win[wid][1] = w_hi; }
+  __syncthreads();
+  int g_lo = Nk, g_hi = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) { g_lo = min(g_lo, wg_win[w][0]); g_hi = max(g_hi, wg_win[w][1]); }
+  const int t_lo = g_hi > g_lo ? g_lo / BC : 0;
+  const int t_hi = g_hi > g_lo ? (g_hi + BC - 1) / BC : 0;
+
+  f32x16 dqa[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) dqa[db] = f32x16{};
+
+  TC tk, tv;
+  auto load_tile = [&](int t) {
+    tk.load(K, t * BC, Nk, tid);
+    tv.load(V, t * BC, Nk, tid);
+  };
+  auto store_tile = [&](int stage) {
+    char* s = smem + stage * L::STAGE;
+    tk.template store_natural<L::NS>(s + L::KN, tid);
+    tk.template store_T<L::TS>(s + L::KT, tid);
+    tv.template store_natural<L::NS>(s + L::VN, tid);
+  };
+
+  if (t_lo < t_hi) {
+    load_tile(t_lo);
+    store_tile(0);
+  }
+  __syncthreads();
+
+  for (int t = t_lo; t < t_hi; ++t) {
+    const int stage = (t - t_lo) & 1;
+    const bool more = t + 1 < t_hi;
+    if (more) load_tile(t + 1);
+    const int kt0 = t * BC, kt1 = kt0 + BC;
+    const bool skip = kt0 >= w_hi || kt1 <= w_lo;
+    if (!skip) {
+      const bool full = kt1 <= Nk && kt1 <= w_full_c &&
+                        (!ranged || (w_max_s <= kt0 && w_min_e >= kt1));
+      const char* s = smem + stage * L::STAGE;
+      f32x16 sc[KB], dp[KB];
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        sc[kb] = f32x16{};
+        dp[kb] = f32x16{};
+#pragma unroll
+        for (int ks = 0; ks < DK; ++ks) {
+          const int o = (kb * 32 + n) * L::NS + 32 * ks + 16 * h;
+          sc[kb] = E::mma(lds_ld16(s + L::KN, o), qf[ks], sc[kb]);
+          dp[kb] = E::mma(lds_ld16(s + L::VN, o), dof[ks], dp[kb]);
+        }
+      }
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+#pragma unroll
+        for (int g = 0; g < 16; ++g) {
+          float x;
+          if constexpr (BIAS) {
+            const float dist = (float)(qrow - kt0 - 4 * h) - (float)(kb * 32 + 8 * (g / 4) + (g % 4));
+            x = __builtin_fmaf(sc[kb][g], sl2, __builtin_fmaf(slope2, __builtin_fabsf(dist), -lq));
+          } else {
+            x = __builtin_fmaf(sc[kb][g], sl2, -lq);
+          }
+          sc[kb][g] = fast_exp2(x);
+        }
+        if (!full) {
+          const int cl = causal ? qrow + off : Nk;
+          const int hi = min(ken, Nk);
+#pragma unroll
+          for (int g = 0; g < 16; ++g) {
+            const int j = kt0 + kb * 32 + res_row(g, h);
+            const bool vis = j >= kst && j < hi && j <= cl;
+            sc[kb][g] = vis ? sc[kb][g] : 0.f;
+          }
+        }
+#pragma unroll
+        for (int g = 0; g < 16; ++g) sc[kb][g] = sc[kb][g] * (dp[kb][g] - dq_d);  // dS^T
+      }
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+          u32x4 da;
+#pragma unroll
+          for (int w = 0; w < 4; ++w) da[w] = E::pack2(sc[kb][8 * st + 2 * w], sc[kb][8 * st + 2 * w + 1]);
+#pragma unroll
+          for (int db = 0; db < DB; ++db) {
+            const int o = TC::template t_off<L::TS>(32 * db + n, 4 * kb + 2 * st + h);
+            dqa[db] = E::mma(lds_ld16(s + L::KT, o), da, dqa[db]);
+          }
+        }
+      }
+    }
+    if (more) store_tile(stage ^ 1);
+    __syncthreads();
+  }
+
+  // epilogue: lane holds query qrow, registers d = 32*db + res_row(g, h)
+  if (qrow < Nq) {
+    const float scale = a.scale;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int d0 = db * 32 + 8 * g4 + 4 * h;
+        store_grad4<T>(a.dq, ((size_t)bh * Nq + qrow) * D + d0, a.grad_f32 != 0,
+                       dqa[db][4 * g4] * scale, dqa[db][4 * g4 + 1] * scale,
+                       dqa[db][4 * g4 + 2] * scale, dqa[db][4 * g4 + 3] * scale);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------
+// launch
+// ---------------------------------------------------------------------------------
+constexpr int kDkdvBR = 64;  // query rows per LDS tile of the dK/dV pass
+
+size_t bwd_qsum_offset(int B, int H, int Nq) {
+  return (((size_t)B * H * Nq * sizeof(float)) + 255) & ~(size_t)255;
+}
+size_t bwd_workspace_bytes(int B, int H, int Nq) {
+  const size_t nt = (size_t)(Nq + kDkdvBR - 1) / kDkdvBR;
+  return bwd_qsum_offset(B, H, Nq) + ((nt * 4 * sizeof(int32_t) + 255) & ~(size_t)255);
+}
+
+template <typename T, int D, int DKDV_NW, int DKDV_WPE, int DQ_BC, int DQ_NW, int DQ_WPE>
+static hipError_t launch_bwd_t(bool bias, BwdArgs& a, hipStream_t st) {
+  const int BH = a.B * a.H;
+  const int rows = BH * a.Nq;
+  constexpr int RPB = 256 / (D / 8);
+  hipLaunchKernelGGL((bwd_prep_kernel<T, D>), dim3((rows + RPB - 1) / RPB), dim3(256), 0, st,
+                     static_cast<const T*>(a.o), static_cast<const T*>(a.dout), a.delta, rows);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (a.key_start != nullptr) {
+    e = launch_mask_summary(a.key_start, a.key_end, a.Nq, a.Nk, kDkdvBR, a.qsum, st);
+    if (e != hipSuccess) return e;
+  }
+  const int sched = (BH % 8 == 0) ? 1 : 0;
+  // dK, dV
+  {
+    constexpr int BK = 32 * DKDV_NW;
+    BwdArgs b = a;
+    b.nblk = (a.Nk + BK - 1) / BK;
+    b.sched = sched;
+    const dim3 grid((unsigned)(BH * b.nblk)), block(DKDV_NW * 64);
+    if (bias)
+      hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, kDkdvBR, DKDV_NW, DKDV_WPE, true>), grid, block, 0, st, b);
+    else
+      hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, kDkdvBR, DKDV_NW, DKDV_WPE, false>), grid, block, 0, st, b);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  // dQ
+  {
+    constexpr int BRQ = 32 * DQ_NW;
+    BwdArgs b = a;
+    b.nblk = (a.Nq + BRQ - 1) / BRQ;
+    b.sched = sched;
+    const dim3 grid((unsigned)(BH * b.nblk)), block(DQ_NW * 64);
+    if (bias)
+      hipLaunchKernelGGL((bwd_dq_kernel<T, D, DQ_BC, DQ_NW, DQ_WPE, true>), grid, block, 0, st, b);
+    else
+      hipLaunchKernelGGL((bwd_dq_kernel<T, D, DQ_BC, DQ_NW, DQ_WPE, false>), grid, block, 0, st, b);
+    e = hipGetLastError();
+  }
+  return e;
+}
+
+hipError_t launch_bwd(fa_dtype dt, int d, bool bias, BwdArgs& a, hipStream_t st) {
+  switch (dt) {
+    case FA_BF16:
+      return d == 128 ? launch_bwd_t<__bf16, 128, 4, 1, 64, 8, 2>(bias, a, st)
+                      : launch_bwd_t<__bf16, 64, 4, 1, 128, 8, 2>(bias, a, st);
+    case FA_F16:
+      return d == 128 ? launch_bwd_t<_Float16, 128, 4, 1, 64, 8, 2>(bias, a, st)
+                      : launch_bwd_t<_Float16, 64, 4, 1, 128, 8, 2>(bias, a, st);
+    default:
+      return hipErrorNotSupported;  // float32 backward is not implemented
+  }
+}
 
 }  // namespace fa

@@ -100,3 +100,111 @@ __device__ inline uint32_t pack_lo(uint32_t a, uint32_t b) { return perm(b, a, 0
 __device__ inline uint32_t pack_hi(uint32_t a, uint32_t b) { return perm(b, a, 0x07060302u); }
 
 }  // namespace fa
+
+namespace fa {
+
+__device__ __host__ constexpr int align16(int x) { return (x + 15) & ~15; }
+
+// Rows inside a 32-row block are relabelled in transposed LDS tiles so that the 8 rows
+// one lane feeds to an MFMA step (rows 8*(t/4) + 4*h + t%4 + 16*s of the 32x32 result
+// layout) sit in 8 consecutive slots: swap bits 2 and 3 of the row index.
+__device__ constexpr int tr_pos(int r) { return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1); }
+
+__device__ inline int wave_min(int v) {
+  for (int o = 32; o >= 1; o >>= 1) v = min(v, __shfl_xor(v, o, 64));
+  return v;
+}
+__device__ inline int wave_max(int v) {
+  for (int o = 32; o >= 1; o >>= 1) v = max(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+// A [ROWS x D] tile of 16-bit elements copied global -> registers -> LDS by NT threads.
+// Thread b owns KQ consecutive rows of one 16-byte column chunk, so the same registers
+// can be written row-major ("natural": row stride NSTRIDE bytes) and transposed
+// ("T": D rows of ROWS slots, row stride TSTRIDE bytes, 16-byte chunks XOR-swizzled by
+// (row/16), slot of row r = tr_pos(r)). Global reads of a warp cover whole rows.
+template <int ROWS, int D, int NT>
+struct TileCopy {
+  static constexpr int kRowChunks = D / 8;
+  static constexpr int kRaw = ROWS * kRowChunks / NT;
+  static constexpr int KQ = kRaw >= 4 ? 4 : kRaw;
+  static constexpr int kGroups = KQ > 0 ? kRaw / KQ : 0;
+  static constexpr int kTChunks = ROWS / 8;
+  static_assert(KQ >= 2 && kGroups * KQ * NT == ROWS * kRowChunks, "tile copy split");
+
+  u32x4 r[kGroups][KQ];
+
+  template <typename T>
+  __device__ inline void load(const T* base, int row0, int nrows, int tid) {
+#pragma unroll
+    for (int i = 0; i < kGroups; ++i) {
+      const int b = tid + i * NT;
+      const int grp = b / kRowChunks, col = b % kRowChunks;
+#pragma unroll
+      for (int e = 0; e < KQ; ++e) {
+        const int row = min(row0 + grp * KQ + e, nrows - 1);  // rows past the end: masked
+        r[i][e] = ldg16(base + (size_t)row * D + col * 8);
+      }
+    }
+  }
+
+  template <int NSTRIDE>
+  __device__ inline void store_natural(char* lds, int tid) const {
+#pragma unroll
+    for (int i = 0; i < kGroups; ++i) {
+      const int b = tid + i * NT;
+      const int grp = b / kRowChunks, col = b % kRowChunks;
+#pragma unroll
+      for (int e = 0; e < KQ; ++e) lds_st16(lds, (grp * KQ + e) * NSTRIDE + col * 16, r[i][e]);
+    }
+  }
+
+  template <int TSTRIDE>
+  __device__ static inline int t_off(int row, int chunk) {
+    return row * TSTRIDE + 16 * (chunk ^ ((row >> 4) & (kTChunks - 1)));
+  }
+
+  template <int TSTRIDE>
+  __device__ inline void store_T(char* lds, int tid) const {
+#pragma unroll
+    for (int i = 0; i < kGroups; ++i) {
+      const int b = tid + i * NT;
+      const int grp = b / kRowChunks, col = b % kRowChunks;
+      const int pos = tr_pos(grp * KQ);  // KQ consecutive rows -> KQ consecutive slots
+#pragma unroll
+      for (int dd = 0; dd < 8; ++dd) {
+        const int row = col * 8 + dd;
+        const int w = dd >> 1;
+        const int byte = t_off<TSTRIDE>(row, pos >> 3) + (pos & 7) * 2;
+        if constexpr (KQ == 4) {
+          u32x2 val;
+          val[0] = (dd & 1) ? pack_hi(r[i][0][w], r[i][1][w]) : pack_lo(r[i][0][w], r[i][1][w]);
+          val[1] = (dd & 1) ? pack_hi(r[i][2][w], r[i][3][w]) : pack_lo(r[i][2][w], r[i][3][w]);
+          lds_st8(lds, byte, val);
+        } else {
+          lds_st4(lds, byte, (dd & 1) ? pack_hi(r[i][0][w], r[i][1][w]) : pack_lo(r[i][0][w], r[i][1][w]));
+        }
+      }
+    }
+  }
+};
+
+// Workgroup -> (bh, block along the kernel's parallel axis), heaviest block first.
+// With kSchedXcd every (b, h) stays on one of the 8 XCDs (blocks are dealt to XCDs
+// round-robin), so its K/V (or Q/dO) is shared through that XCD's L2.
+__device__ inline void map_block(int L, int BH, int nblk, int sched, bool reverse, int& bh, int& blk) {
+  int s;
+  if (sched == 1) {
+    const int x = L & 7;
+    s = L >> 3;
+    bh = x + 8 * (s / nblk);
+  } else {
+    s = L;
+    bh = L / nblk;
+  }
+  const int r = s % nblk;
+  blk = reverse ? nblk - 1 - r : r;
+}
+
+}  // namespace fa

@@ -33,8 +33,6 @@ namespace fa {
 
 constexpr float kTau = 8.0f;  // lazy-rescale threshold in log2 units (p <= 2^8)
 
-__device__ __host__ constexpr int align16(int x) { return (x + 15) & ~15; }
-
 template <typename T, int D_, int BC_, int QSUB_, int NW_>
 struct FwdCfg {
   static constexpr bool kF32 = std::is_same<T, float>::value;
@@ -70,38 +68,11 @@ struct FwdCfg {
 
 // Keys inside a tile are relabelled in V^T so that the 8 keys one lane feeds to a
 // P.V MFMA step are contiguous: swap bits 2 and 3 of the tile-local key index.
-__device__ constexpr int vt_pos(int key) {
-  return (key & ~12) | ((key & 4) << 1) | ((key & 8) >> 1);
-}
+__device__ constexpr int vt_pos(int key) { return tr_pos(key); }
 
 template <class C>
 __device__ inline int vt_off(int row, int chunk) {
   return row * C::kVStride + 16 * (chunk ^ ((row >> 4) & (C::kVChunksSwz - 1)));
-}
-
-// ---------------------------------------------------------------------------------
-// work mapping: workgroup -> (bh, query block); heaviest (causal: last) blocks first
-// ---------------------------------------------------------------------------------
-__device__ inline void map_block(int L, int BH, int nblk, int sched, int& bh, int& qb) {
-  if (sched == kSchedXcd) {
-    // blocks are handed to the 8 XCDs round-robin; keep every (b,h) on one XCD so its
-    // K/V stays in that XCD's L2, and walk each head's blocks heaviest first.
-    int x = L & 7, s = L >> 3;
-    bh = x + 8 * (s / nblk);
-    qb = nblk - 1 - (s % nblk);
-  } else {
-    bh = L / nblk;
-    qb = nblk - 1 - (L % nblk);
-  }
-}
-
-__device__ inline int wave_min(int v) {
-  for (int o = 32; o >= 1; o >>= 1) v = min(v, __shfl_xor(v, o, 64));
-  return v;
-}
-__device__ inline int wave_max(int v) {
-  for (int o = 32; o >= 1; o >>= 1) v = max(v, __shfl_xor(v, o, 64));
-  return v;
 }
 
 template <typename T, int D, int BC, int QSUB, int NW, int WPE, bool BIAS>
@@ -123,7 +94,7 @@ void fwd_kernel(const FwdArgs a) {
   const bool ranged = a.key_start != nullptr;
 
   int bh, qb;
-  map_block(blockIdx.x, a.B * a.H, a.nqb, a.sched, bh, qb);
+  map_block(blockIdx.x, a.B * a.H, a.nqb, a.sched, true, bh, qb);
   const int head = bh % a.H;
   const int q0 = qb * C::kBR;
   const T* __restrict__ Q = static_cast<const T*>(a.q) + (size_t)bh * Nq * D;

@@ -39,6 +39,7 @@ struct BwdArgs {
   const void* dout;
   const float* lse;
   float* delta;   // [B,H,Nq] rowsum(dO * O), workspace
+  int32_t* qsum;  // key-range summary per query tile of the dK/dV pass, workspace
   void* dq;
   void* dk;
   void* dv;
@@ -61,9 +62,8 @@ hipError_t launch_bwd(fa_dtype dt, int d, bool bias, BwdArgs& a, hipStream_t st)
 hipError_t launch_mask_summary(const int32_t* ks, const int32_t* ke, int Nq, int Nk, int block,
                                int32_t* out, hipStream_t st);
 
-// Query rows per forward workgroup for (dtype, d): fixes the grid size.
-int fwd_block_rows(fa_dtype dt, int d);
-int bwd_key_block(fa_dtype dt, int d);
-int bwd_query_block(fa_dtype dt, int d);
+// Backward workspace layout: delta at offset 0, key-range summary at bwd_qsum_offset.
+size_t bwd_qsum_offset(int B, int H, int Nq);
+size_t bwd_workspace_bytes(int B, int H, int Nq);
 
 }  // namespace fa
