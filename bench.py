@@ -1,0 +1,225 @@
+#!/usr/bin/env python3
+"""Benchmark of the exact-attention hot path on one MI355X.
+
+One step = one forward pass (fa_fwd) plus one recompute backward pass (fa_bwd's three
+launches) over the bf16 causal workload B=2, H=16, N=8192, d=128 with synthetic
+Gaussian Q, K, V, dO already resident in HBM. Prints ONE JSON line.
+
+FLOP convention: forward 4*B*H*N_q*N_k*d halved for causal; backward 2.5x forward.
+The roofline object describes the dominant kernel, timed with HIP events recorded on
+the stream the kernels run on; its achieved rate uses the algorithmic FLOPs of that
+kernel (see ALG_FLOPS below). The CPU baseline times the float64 oracle (fwd + bwd)
+on a bounded sample of whole (b, h) heads of the same workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "attention fwd(+bwd) TFLOP/s and % of MI355X bf16 MFMA peak, B·H·N²·d sweep"
+PEAK_BF16_TFLOPS = 2516.6  # 256 CU x 2.4 GHz x 4096 dense bf16 FLOP/clk/CU (published 2.5 PFLOP/s)
+PEAK_HBM_GBS = 8000.0
+
+# HBM traffic of the kernels from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs (bytes per
+# launch, already scaled by the copy-kernel calibration factor), keyed by the sha256 of
+# the kernel source they were measured on. A changed source means stale counters -> null.
+TRAFFIC = {}
+
+
+def src_hash(*names) -> str:
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "exact_io_aware_flash_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+KERNEL_SRC = {
+    "fwd": ("fa_fwd.hip", "fa_device.h"),
+    "bwd_prep": ("fa_bwd.hip", "fa_device.h"),
+    "bwd_dkdv": ("fa_bwd.hip", "fa_device.h"),
+    "bwd_dq": ("fa_bwd.hip", "fa_device.h"),
+}
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="target wall time of the CPU-oracle sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE={world}); "
+              "the attention kernels shard over (batch, head) with no exchange, so a multi-GPU "
+              "figure is N independent copies of this one.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import exact_io_aware_flash_amd as fa
+    from synth import CONFIGS, qkv_inputs
+
+    fa.load_library()  # fails loudly if the HIP library is missing
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+
+    w = CONFIGS[5]
+    B, H, N, d = w.B, w.H, w.N_q, w.d
+    q, k, v, do = (t.to(dev) for t in qkv_inputs(w))
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    grads = tuple(torch.empty((B, H, N, d), dtype=torch.float32, device=dev) for _ in range(3))
+    ws = torch.empty(fa.fa_bwd_workspace_bytes(B, H, N, N, d), dtype=torch.uint8, device=dev)
+    kw = dict(causal=True, scale=w.scale)
+
+    phases = [("bwd_prep", fa.FA_BWD_PREP), ("bwd_dkdv", fa.FA_BWD_DKDV), ("bwd_dq", fa.FA_BWD_DQ)]
+    names = ["fwd"] + [p[0] for p in phases]
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0][0].record()
+        fa.fa_fwd(q, k, v, out=o, lse=lse, **kw)
+        for i, (_, ph) in enumerate(phases):
+            if ev is not None:
+                ev[i][1].record()
+                ev[i + 1][0].record()
+            fa.fa_bwd(do, q, k, v, o, lse, grads=grads, workspace=ws, phases=ph, **kw)
+        if ev is not None:
+            ev[len(phases)][1].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    events = [[[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in names]
+              for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        step(events[s])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    kern_ms = {n: float(np.mean([events[s][i][0].elapsed_time(events[s][i][1])
+                                 for s in range(args.steps)])) for i, n in enumerate(names)}
+
+    fwd_flops = 4.0 * B * H * N * N * d / 2.0
+    bwd_flops = 2.5 * fwd_flops
+    step_flops = fwd_flops + bwd_flops
+    value = step_flops / (ms_per_step * 1e-3) / 1e12
+
+    # algorithmic work per launch: 2*d FLOP per visible (query, key) pair and product;
+    # causal with N_q == N_k has N(N+1)/2 visible pairs per head
+    pairs = B * H * N * (N + 1) / 2.0
+    ALG_FLOPS = {
+        "fwd": 4.0 * d * pairs,          # S = QK^T, O = PV
+        "bwd_dkdv": 8.0 * d * pairs,     # S, dP = dO V^T, dV = P^T dO, dK = dS^T Q
+        "bwd_dq": 2.0 * d * pairs,       # dQ = dS K (its S and dP recomputation is overhead)
+    }
+    prep_bytes = 2.0 * B * H * N * d * 2 + 4.0 * B * H * N
+    kernels = {}
+    for n in names:
+        t = kern_ms[n] * 1e-3
+        ent = {"avg_us": round(kern_ms[n] * 1e3, 2)}
+        if n in ALG_FLOPS:
+            ent["alg_tflops"] = round(ALG_FLOPS[n] / t / 1e12, 1)
+            ent["frac_bf16_peak"] = round(ALG_FLOPS[n] / t / 1e12 / PEAK_BF16_TFLOPS, 4)
+        else:
+            ent["alg_gbs"] = round(prep_bytes / t / 1e9, 1)
+        kernels[n] = ent
+    dom = max((n for n in names if n in ALG_FLOPS), key=lambda n: kern_ms[n])
+    achieved = ALG_FLOPS[dom] / (kern_ms[dom] * 1e-3) / 1e12
+    tr = TRAFFIC.get(dom)
+    traffic = None
+    if tr is not None and tr[0] == src_hash(*KERNEL_SRC[dom]):
+        traffic = tr[1]
+    roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 1),
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w, q, k, v, do, args.cpu_seconds)
+
+    fwd_tflops = fwd_flops / (kern_ms["fwd"] * 1e-3) / 1e12
+    bwd_ms = sum(kern_ms[p[0]] for p in phases)
+    line = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "exact attention fwd+bwd, bf16 causal B2 H16 N8192 d128",
+                   "B": B, "H": H, "N": N, "d": d, "causal": True,
+                   "grad_dtype": "f32", "flop_convention": "fwd 4BHN^2d/2, bwd 2.5x fwd"},
+        "frac_of_bf16_peak": round(value / PEAK_BF16_TFLOPS, 4),
+        "fwd_tflops": round(fwd_tflops, 1),
+        "fwd_frac_of_bf16_peak": round(fwd_tflops / PEAK_BF16_TFLOPS, 4),
+        "bwd_tflops": round(bwd_flops / (bwd_ms * 1e-3) / 1e12, 1),
+        "kernels": kernels,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline(w, q, k, v, do, seconds):
+    """The float64 oracle (fwd + bwd) on whole heads of the same inputs, until `seconds`."""
+    import numpy as np
+
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((p.get("num_threads", 1) for p in threadpool_info()
+                       if p.get("internal_api") in ("openblas", "mkl", "blis")), default=1)
+    except Exception:  # pragma: no cover - threadpoolctl missing
+        threads = len(os.sched_getaffinity(0))
+    heads = [(b, h) for b in range(w.B) for h in range(w.H)]
+    done = 0
+    el = 0.0
+    for (b, h) in heads:
+        one = lambda t: t[b:b + 1, h:h + 1].float().cpu().double().numpy()  # noqa: E731
+        qn, kn, vn, don = one(q), one(k), one(v), one(do)
+        t_start = time.perf_counter()
+        oracle.attention_forward(qn, kn, vn, w.scale, causal=True)
+        oracle.attention_backward(qn, kn, vn, don, w.scale, causal=True)
+        el += time.perf_counter() - t_start
+        done += 1
+        if el >= seconds:
+            break
+    per_head = 4.0 * w.N_q * w.N_k * w.d / 2.0 * 3.5  # fwd + bwd, same convention
+    return {"value": round(done * per_head / el / 1e12, 5), "unit": "TFLOP/s",
+            "cores": int(threads), "kind": "oracle",
+            "sample": f"float64 numpy oracle fwd+bwd of {done} of {len(heads)} (b,h) heads "
+                      f"at full N={w.N_q} ({el:.1f} s of oracle wall time)"}
+
+
+if __name__ == "__main__":
+    main()

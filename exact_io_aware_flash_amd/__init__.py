@@ -21,6 +21,7 @@ import torch
 
 __all__ = [
     "FaError", "fa_fwd", "fa_bwd", "fa_bwd_workspace_bytes", "fa_mask_summary",
+    "FA_BWD_PREP", "FA_BWD_DKDV", "FA_BWD_DQ", "FA_BWD_ALL",
     "fa_status_string", "fa_version", "lib_path", "load_library",
 ]
 
@@ -31,6 +32,7 @@ _LIB = None
 FA_F32, FA_F16, FA_BF16 = 0, 1, 2
 FA_BIAS_NONE, FA_BIAS_DIST_LINEAR = 0, 1
 FA_MAX_SLOPES = 256
+FA_BWD_PREP, FA_BWD_DKDV, FA_BWD_DQ, FA_BWD_ALL = 1, 2, 4, 7
 _DT = {torch.float32: FA_F32, torch.float16: FA_F16, torch.bfloat16: FA_BF16}
 
 
@@ -75,6 +77,10 @@ def load_library():
     lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, ctypes.c_size_t,
                            i32, i32, i32, i32, i32, f32, i32, desc_p, i32, vp]
     lib.fa_bwd.restype = i32
+    lib.fa_bwd_phases.argtypes = [i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp,
+                                  ctypes.c_size_t, i32, i32, i32, i32, i32, f32, i32, desc_p,
+                                  i32, vp]
+    lib.fa_bwd_phases.restype = i32
     lib.fa_mask_summary.argtypes = [vp, vp, i32, i32, i32, vp, vp]
     lib.fa_mask_summary.restype = i32
     lib.fa_status_string.argtypes = [i32]
@@ -187,10 +193,12 @@ def fa_bwd(dout: torch.Tensor, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor
            scale: Optional[float] = None, bias_slopes=None,
            key_start: Optional[torch.Tensor] = None, key_end: Optional[torch.Tensor] = None,
            grad_dtype: torch.dtype = torch.float32, workspace: Optional[torch.Tensor] = None,
-           stream: Optional[torch.cuda.Stream] = None):
+           grads=None, phases: int = FA_BWD_ALL, stream: Optional[torch.cuda.Stream] = None):
     """Backward by recomputation: returns (dQ, dK, dV) in ``grad_dtype``.
 
     ``o`` and ``lse`` are the outputs of :func:`fa_fwd` for the same inputs.
+    ``grads``: optional preallocated (dq, dk, dv); ``phases``: subset of FA_BWD_ALL
+    (``fa_bwd_phases``), e.g. to run or time the launches separately with one workspace.
     """
     lib = load_library()
     _check_dev("q", q)
@@ -205,14 +213,20 @@ def fa_bwd(dout: torch.Tensor, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor
         raise ValueError("grad_dtype must be float32 or the input dtype")
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    dq = torch.empty((B, H, N_q, d), dtype=grad_dtype, device=q.device)
-    dk = torch.empty((B, H, N_k, d), dtype=grad_dtype, device=q.device)
-    dv = torch.empty((B, H, N_k, d), dtype=grad_dtype, device=q.device)
+    if grads is None:
+        dq = torch.empty((B, H, N_q, d), dtype=grad_dtype, device=q.device)
+        dk = torch.empty((B, H, N_k, d), dtype=grad_dtype, device=q.device)
+        dv = torch.empty((B, H, N_k, d), dtype=grad_dtype, device=q.device)
+    else:
+        dq, dk, dv = grads
+        _check_dev("dq", dq, grad_dtype, (B, H, N_q, d))
+        _check_dev("dk", dk, grad_dtype, (B, H, N_k, d))
+        _check_dev("dv", dv, grad_dtype, (B, H, N_k, d))
     wsb = fa_bwd_workspace_bytes(B, H, N_q, N_k, d)
     if workspace is None:
         workspace = torch.empty(max(wsb, 16), dtype=torch.uint8, device=q.device)
     desc, keep = _desc(bias_slopes, key_start, key_end, H, N_q)
-    st = lib.fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+    st = lib.fa_bwd_phases(int(phases), q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
                     dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
                     _DT[grad_dtype], workspace.data_ptr(), workspace.numel() * workspace.element_size(),
                     B, H, N_q, N_k, d, float(scale), 1 if causal else 0,
@@ -220,7 +234,7 @@ def fa_bwd(dout: torch.Tensor, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor
                     _stream_ptr(stream))
     del keep
     if st != 0:
-        raise FaError(st, "fa_bwd")
+        raise FaError(st, "fa_bwd_phases")
     return dq, dk, dv
 
 

@@ -77,7 +77,7 @@ const char* fa_status_string(fa_status s) {
     case FA_ERR_WORKSPACE: return "workspace missing or too small";
     case FA_ERR_UNSUPPORTED: return "combination not implemented";
     case FA_ERR_HIP: return "HIP launch error";
-    case FA_ERR_ARG: return "scale must be finite and > 0";
+    case FA_ERR_ARG: return "invalid scalar argument (scale must be finite and > 0)";
   }
   return "unknown status";
 }
@@ -118,6 +118,16 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, con
                  void* workspace, size_t workspace_bytes, int B, int H, int N_q, int N_k, int d,
                  float scale, int causal, const fa_mask_bias_desc* mb, fa_dtype dtype,
                  void* stream) {
+  return fa_bwd_phases(FA_BWD_ALL, q, k, v, o, lse, dout, dq, dk, dv, grad_dtype, workspace,
+                       workspace_bytes, B, H, N_q, N_k, d, scale, causal, mb, dtype, stream);
+}
+
+fa_status fa_bwd_phases(int phases, const void* q, const void* k, const void* v, const void* o,
+                        const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                        fa_dtype grad_dtype, void* workspace, size_t workspace_bytes, int B,
+                        int H, int N_q, int N_k, int d, float scale, int causal,
+                        const fa_mask_bias_desc* mb, fa_dtype dtype, void* stream) {
+  if (phases < 1 || (phases & ~FA_BWD_ALL) != 0) return FA_ERR_ARG;
   fa_status st = check_common(B, H, N_q, N_k, d, scale, dtype);
   if (st != FA_OK) return st;
   if (grad_dtype != FA_F32 && grad_dtype != dtype) return FA_ERR_DTYPE;
@@ -143,7 +153,7 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, con
   a.grad_f32 = grad_dtype == FA_F32 ? 1 : 0;
   a.scale = scale;
   a.sl2 = scale * 1.4426950408889634f;
-  hipError_t e = launch_bwd(dtype, d, bias, a, static_cast<hipStream_t>(stream));
+  hipError_t e = launch_bwd(dtype, d, bias, phases, a, static_cast<hipStream_t>(stream));
   if (e == hipErrorNotSupported) return FA_ERR_UNSUPPORTED;
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }

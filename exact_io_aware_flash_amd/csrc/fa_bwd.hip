@@ -501,21 +501,24 @@ size_t bwd_workspace_bytes(int B, int H, int Nq) {
 }
 
 template <typename T, int D, int DKDV_NW, int DKDV_WPE, int DQ_BC, int DQ_NW, int DQ_WPE>
-static hipError_t launch_bwd_t(bool bias, BwdArgs& a, hipStream_t st) {
+static hipError_t launch_bwd_t(bool bias, int phases, BwdArgs& a, hipStream_t st) {
   const int BH = a.B * a.H;
   const int rows = BH * a.Nq;
   constexpr int RPB = 256 / (D / 8);
-  hipLaunchKernelGGL((bwd_prep_kernel<T, D>), dim3((rows + RPB - 1) / RPB), dim3(256), 0, st,
-                     static_cast<const T*>(a.o), static_cast<const T*>(a.dout), a.delta, rows);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  if (a.key_start != nullptr) {
-    e = launch_mask_summary(a.key_start, a.key_end, a.Nq, a.Nk, kDkdvBR, a.qsum, st);
+  hipError_t e = hipSuccess;
+  if (phases & FA_BWD_PREP) {
+    hipLaunchKernelGGL((bwd_prep_kernel<T, D>), dim3((rows + RPB - 1) / RPB), dim3(256), 0, st,
+                       static_cast<const T*>(a.o), static_cast<const T*>(a.dout), a.delta, rows);
+    e = hipGetLastError();
     if (e != hipSuccess) return e;
+    if (a.key_start != nullptr) {
+      e = launch_mask_summary(a.key_start, a.key_end, a.Nq, a.Nk, kDkdvBR, a.qsum, st);
+      if (e != hipSuccess) return e;
+    }
   }
   const int sched = (BH % 8 == 0) ? 1 : 0;
   // dK, dV
-  {
+  if (phases & FA_BWD_DKDV) {
     constexpr int BK = 32 * DKDV_NW;
     BwdArgs b = a;
     b.nblk = (a.Nk + BK - 1) / BK;
@@ -529,7 +532,7 @@ static hipError_t launch_bwd_t(bool bias, BwdArgs& a, hipStream_t st) {
     if (e != hipSuccess) return e;
   }
   // dQ
-  {
+  if (phases & FA_BWD_DQ) {
     constexpr int BRQ = 32 * DQ_NW;
     BwdArgs b = a;
     b.nblk = (a.Nq + BRQ - 1) / BRQ;
@@ -544,14 +547,14 @@ static hipError_t launch_bwd_t(bool bias, BwdArgs& a, hipStream_t st) {
   return e;
 }
 
-hipError_t launch_bwd(fa_dtype dt, int d, bool bias, BwdArgs& a, hipStream_t st) {
+hipError_t launch_bwd(fa_dtype dt, int d, bool bias, int phases, BwdArgs& a, hipStream_t st) {
   switch (dt) {
     case FA_BF16:
-      return d == 128 ? launch_bwd_t<__bf16, 128, 4, 1, 64, 8, 2>(bias, a, st)
-                      : launch_bwd_t<__bf16, 64, 4, 1, 128, 8, 2>(bias, a, st);
+      return d == 128 ? launch_bwd_t<__bf16, 128, 4, 1, 64, 8, 2>(bias, phases, a, st)
+                      : launch_bwd_t<__bf16, 64, 4, 1, 128, 8, 2>(bias, phases, a, st);
     case FA_F16:
-      return d == 128 ? launch_bwd_t<_Float16, 128, 4, 1, 64, 8, 2>(bias, a, st)
-                      : launch_bwd_t<_Float16, 64, 4, 1, 128, 8, 2>(bias, a, st);
+      return d == 128 ? launch_bwd_t<_Float16, 128, 4, 1, 64, 8, 2>(bias, phases, a, st)
+                      : launch_bwd_t<_Float16, 64, 4, 1, 128, 8, 2>(bias, phases, a, st);
     default:
       return hipErrorNotSupported;  // float32 backward is not implemented
   }

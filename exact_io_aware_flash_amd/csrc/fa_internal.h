@@ -58,7 +58,7 @@ struct BwdArgs {
 
 // Launchers (return hipSuccess or the launch error). dtype-specialised in the .hip files.
 hipError_t launch_fwd(fa_dtype dt, int d, bool bias, FwdArgs& a, hipStream_t st);
-hipError_t launch_bwd(fa_dtype dt, int d, bool bias, BwdArgs& a, hipStream_t st);
+hipError_t launch_bwd(fa_dtype dt, int d, bool bias, int phases, BwdArgs& a, hipStream_t st);
 hipError_t launch_mask_summary(const int32_t* ks, const int32_t* ke, int Nq, int Nk, int block,
                                int32_t* out, hipStream_t st);
 

@@ -64,7 +64,7 @@ typedef enum fa_status {
   FA_ERR_WORKSPACE = 7,   /* workspace NULL or smaller than fa_bwd_workspace_bytes() */
   FA_ERR_UNSUPPORTED = 8, /* a valid combination this build does not implement */
   FA_ERR_HIP = 9,         /* the HIP runtime reported an error at launch */
-  FA_ERR_ARG = 10         /* scale not finite or not positive; a slope not finite */
+  FA_ERR_ARG = 10         /* scale not finite or not positive; a slope not finite; bad phase set */
 } fa_status;
 
 typedef enum fa_dtype { FA_F32 = 0, FA_F16 = 1, FA_BF16 = 2 } fa_dtype;
@@ -134,6 +134,24 @@ FA_API fa_status fa_bwd(const void* q, const void* k, const void* v, const void*
                  void* workspace, size_t workspace_bytes,
                  int B, int H, int N_q, int N_k, int d, float scale, int causal,
                  const fa_mask_bias_desc* mb, fa_dtype dtype, void* stream);
+
+/* The launches of fa_bwd, selectable for callers that schedule or time them apart:
+ *  FA_BWD_PREP: D = rowsum(dO * O) and the key-range summary, into the workspace;
+ *  FA_BWD_DKDV: dK and dV (needs a completed FA_BWD_PREP on the same workspace);
+ *  FA_BWD_DQ:   dQ (needs a completed FA_BWD_PREP on the same workspace).
+ *  Phases given together run in that order. fa_bwd(...) is fa_bwd_phases(FA_BWD_ALL, ...).
+ *  `phases` must be a non-empty subset of FA_BWD_ALL (else FA_ERR_ARG); the other
+ *  arguments are validated exactly as for fa_bwd. */
+#define FA_BWD_PREP 1
+#define FA_BWD_DKDV 2
+#define FA_BWD_DQ 4
+#define FA_BWD_ALL 7
+FA_API fa_status fa_bwd_phases(int phases, const void* q, const void* k, const void* v,
+                               const void* o, const float* lse, const void* dout, void* dq,
+                               void* dk, void* dv, fa_dtype grad_dtype, void* workspace,
+                               size_t workspace_bytes, int B, int H, int N_q, int N_k, int d,
+                               float scale, int causal, const fa_mask_bias_desc* mb,
+                               fa_dtype dtype, void* stream);
 
 /* Key-range summary of consecutive blocks of `block_rows` query rows.
  *  key_start, key_end: device int32 [N_q] (same meaning as in fa_mask_bias_desc).
