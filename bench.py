@@ -32,7 +32,12 @@ PEAK_HBM_GBS = 8000.0
 # HBM traffic of the kernels from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs (bytes per
 # launch, already scaled by the copy-kernel calibration factor), keyed by the sha256 of
 # the kernel source they were measured on. A changed source means stale counters -> null.
-TRAFFIC = {}
+TRAFFIC = {
+    # kernel: (source hash, bytes read, bytes written) -- profiles/attention_fwd_bwd_bf16_causal_B2H16N8192d128.md
+    "fwd": ("834439fd4ed25003", 267.2e6, 68.2e6),
+    "bwd_dkdv": ("646d13d8bac097a2", 274.7e6, 268.4e6),
+    "bwd_dq": ("646d13d8bac097a2", 401.2e6, 138.3e6),
+}
 
 
 def src_hash(*names) -> str:
@@ -59,7 +64,22 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target wall time of the CPU-oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 256 MiB device-to-device copy 5 times (the known-size "
+                         "reference for scaling FETCH_SIZE/WRITE_SIZE counters)")
     return ap.parse_args()
+
+
+def calibrate_copy():
+    import torch
+    n = 256 << 20
+    src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 5}), flush=True)
 
 
 def main():
@@ -70,6 +90,9 @@ def main():
               "the attention kernels shard over (batch, head) with no exchange, so a multi-GPU "
               "figure is N independent copies of this one.", file=sys.stderr)
         sys.exit(2)
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
 
     import numpy as np
     import torch
@@ -149,10 +172,17 @@ def main():
         kernels[n] = ent
     dom = max((n for n in names if n in ALG_FLOPS), key=lambda n: kern_ms[n])
     achieved = ALG_FLOPS[dom] / (kern_ms[dom] * 1e-3) / 1e12
-    tr = TRAFFIC.get(dom)
-    traffic = None
-    if tr is not None and tr[0] == src_hash(*KERNEL_SRC[dom]):
-        traffic = tr[1]
+    def traffic_of(n):
+        tr = TRAFFIC.get(n)
+        if tr is None or tr[0] != src_hash(*KERNEL_SRC[n]):
+            return None  # no counters for this kernel source
+        return tr[1] + tr[2]
+    for n in names:
+        t = traffic_of(n)
+        if t is not None:
+            kernels[n]["hbm_bytes"] = t
+            kernels[n]["hbm_gbs"] = round(t / (kern_ms[n] * 1e-3) / 1e9, 1)
+    traffic = traffic_of(dom)
     roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 1),
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic}
