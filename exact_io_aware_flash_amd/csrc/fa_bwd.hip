@@ -192,6 +192,10 @@ void bwd_dkdv_kernel(const BwdArgs a) {
   for (int t = t_lo; t < t_hi; ++t) {
     const int stage = (t - t_lo) & 1;
     const bool more = t + 1 < t_hi;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) { pin_agpr(dv[db]); pin_agpr(dk[db]); }
+#pragma unroll
+    for (int ks = 0; ks < DK; ++ks) { pin_agpr(kf[ks]); pin_agpr(vf[ks]); }
     if (more) load_tile(t + 1);
     const int q0t = t * BR;
     const char* s = smem + stage * L::STAGE;

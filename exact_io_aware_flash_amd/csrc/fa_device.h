@@ -91,6 +91,14 @@ __device__ inline void lds_st4(char* base, int off, uint32_t v) {
   *reinterpret_cast<uint32_t*>(base + off) = v;
 }
 
+// Register-class pins (empty asm, no instruction emitted): keep a value in the
+// accumulation registers (AGPRs) or in the vector registers at this point. MFMA reads
+// its operands and accumulator from either class; values only ever touched by MFMA are
+// pinned to AGPRs so that kernels with more live state than 256 VGPRs do not shuttle
+// them between the two register files every iteration.
+__device__ inline void pin_agpr(f32x16& x) { asm volatile("" : "+a"(x)); }
+__device__ inline void pin_agpr(u32x4& x) { asm volatile("" : "+a"(x)); }
+
 // Byte permute: result byte k = byte sel_k of the 8-byte value {hi:lo}.
 __device__ inline uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel) {
   return __builtin_amdgcn_perm(hi, lo, sel);
