@@ -33,6 +33,11 @@ template <typename T> struct Elt;
 
 template <> struct Elt<__bf16> {
   static constexpr int kBytes = 2;
+  // acc + lo(w) + hi(w) for a word of two packed elements (v_dot2c_f32_bf16 with 1.0)
+  __device__ static inline float sum2(uint32_t w, float acc) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w),
+                                           __builtin_bit_cast(bf16x2, 0x3f803f80u), acc, false);
+  }
   __device__ static inline f32x16 mma(u32x4 a, u32x4 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
                                                    __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
@@ -46,6 +51,10 @@ template <> struct Elt<__bf16> {
 
 template <> struct Elt<_Float16> {
   static constexpr int kBytes = 2;
+  __device__ static inline float sum2(uint32_t w, float acc) {
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w),
+                                  __builtin_bit_cast(f16x2, 0x3c003c00u), acc, false);
+  }
   __device__ static inline f32x16 mma(u32x4 a, u32x4 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
                                                   __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
@@ -69,6 +78,9 @@ __device__ constexpr int res_row(int g, int h) { return 8 * (g / 4) + 4 * h + (g
 // Cross-half exchange: value held by lane l ^ 32 (the other half of the same column).
 __device__ inline float xhalf(float v) { return __shfl_xor(v, 32, 64); }
 
+__device__ inline float xhalf_max(float v) { return __builtin_fmaxf(v, xhalf(v)); }
+__device__ inline float xhalf_sum(float v) { return v + xhalf(v); }
+
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 __device__ inline bool wave_any(bool p) { return __builtin_amdgcn_ballot_w64(p) != 0; }
@@ -89,6 +101,17 @@ __device__ inline void lds_st8(char* base, int off, u32x2 v) {
 }
 __device__ inline void lds_st4(char* base, int off, uint32_t v) {
   *reinterpret_cast<uint32_t*>(base + off) = v;
+}
+
+// Transposing LDS load (ds_read_b64_tr_b16). Within each group of 16 lanes, lane j
+// receives 4 elements: element k is element (j % 4) of the 8 bytes addressed by lane
+// 4*k + j/4 of the group. Lanes that address 4 consecutive rows x 4 consecutive 16-bit
+// columns of a row-major tile thus gather a column slice (4 rows) per lane.
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+__device__ inline u32x2 lds_ld8_tr(const char* base, int off) {
+  const s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4*)(base + off));
+  return __builtin_bit_cast(u32x2, r);
 }
 
 // Register-class pins (empty asm, no instruction emitted): keep a value in the

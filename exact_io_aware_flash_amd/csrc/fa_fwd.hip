@@ -445,6 +445,249 @@ void fwd_kernel(const FwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------------
+// 16-bit forward. K and V tiles are row-major in LDS and double-buffered: the global
+// loads of tile j+1 are in flight while tile j is computed; one barrier per tile. Two
+// waves share a SIMD, so one wave's softmax overlaps the other's MFMAs.
+// ---------------------------------------------------------------------------------
+template <int D_, int BC_, int NW_>
+struct Fwd16Cfg {
+  static constexpr int D = D_, BC = BC_, NW = NW_;
+  static constexpr int kNT = NW * 64;
+  static constexpr int kBR = 32 * NW;       // query rows per workgroup
+  static constexpr int kKB = BC / 32;       // 32-key blocks per tile
+  static constexpr int kDB = D / 32;        // 32-wide d blocks of O^T
+  static constexpr int kDK = D / 16;        // k-steps over d for S^T
+  // K and V are both stored row-major. K rows are read 16 bytes per lane (row stride
+  // 2*D+16 keeps 16 lanes on distinct banks); V is gathered with the transposing load
+  // (row stride 2*D+64 keeps the 4-row x 32-byte footprint of a 16-lane group on
+  // distinct banks). Both strides were chosen from measured LDS bank-conflict counts.
+  static constexpr int kKS = D * 2 + 16;    // K row stride (bytes)
+  static constexpr int kVS = D * 2 + 64;    // V row stride (bytes)
+  static constexpr int kKBytes = BC * kKS;
+  static constexpr int kVBytes = BC * kVS;
+  static_assert(2 * (kKBytes + kVBytes) <= 160 * 1024, "LDS budget");
+};
+
+template <typename T, int D, int BC, int NW, bool BIAS>
+__global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
+                          amdgpu_waves_per_eu(2, 2)))
+void fwd16_kernel(const FwdArgs a) {
+  using C = Fwd16Cfg<D, BC, NW>;
+  using E = Elt<T>;
+  using TC = TileCopy<BC, D, C::kNT>;
+  constexpr int KB = C::kKB, DB = C::kDB, DK = C::kDK;
+  __shared__ __attribute__((aligned(16))) char ks_mem[2 * C::kKBytes];
+  __shared__ __attribute__((aligned(16))) char vs_mem[2 * C::kVBytes];
+  __shared__ int wg_win[NW][2];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wid = tid >> 6;
+  const int n = lane & 31, h = lane >> 5;
+  const int Nq = a.Nq, Nk = a.Nk;
+  const int off = Nk - Nq;
+  const bool causal = a.causal != 0;
+  const bool ranged = a.key_start != nullptr;
+
+  int bh, qb;
+  map_block(blockIdx.x, a.B * a.H, a.nqb, a.sched, true, bh, qb);
+  const int head = bh % a.H;
+  const T* __restrict__ Q = static_cast<const T*>(a.q) + (size_t)bh * Nq * D;
+  const T* __restrict__ K = static_cast<const T*>(a.k) + (size_t)bh * Nk * D;
+  const T* __restrict__ V = static_cast<const T*>(a.v) + (size_t)bh * Nk * D;
+  T* __restrict__ O = static_cast<T*>(a.o) + (size_t)bh * Nq * D;
+  const float sl2 = a.sl2;
+  const float slope2 = BIAS ? a.slope2[a.n_slopes == 1 ? 0 : head] : 0.f;
+
+  // ---- rows, key intervals, windows (as in the generic kernel) --------------------
+  const int wq0 = qb * C::kBR + wid * 32;
+  const int qrow = wq0 + n;
+  int kst = 0, ken = Nk;
+  int w_min_s = Nk, w_max_s = 0, w_min_e = Nk, w_max_e = 0;
+  if (ranged && qrow < Nq) {
+    kst = min(max(a.key_start[qrow], 0), Nk);
+    ken = min(max(a.key_end[qrow], 0), Nk);
+    w_min_s = kst; w_max_s = kst; w_min_e = ken; w_max_e = ken;
+  }
+  const bool wave_live = wq0 < Nq;
+  const int wq_last = min(wq0 + 32, Nq) - 1;
+  int w_lo = 0, w_hi = Nk, w_full_c = Nk;
+  if (causal) {
+    w_hi = min(w_hi, wq_last + off + 1);
+    w_full_c = max(0, min(Nk, wq0 + off + 1));
+  }
+  if (ranged) {
+    w_min_s = wave_min(w_min_s);
+    w_max_s = wave_max(w_max_s);
+    w_min_e = wave_min(w_min_e);
+    w_max_e = wave_max(w_max_e);
+    w_lo = max(w_lo, w_min_s);
+    w_hi = min(w_hi, w_max_e);
+  }
+  if (!wave_live || w_hi <= w_lo) { w_lo = Nk; w_hi = 0; }
+  if (lane == 0) { wg_win[wid][0] = w_lo; wg_win[wid][1] = w_hi; }
+  __syncthreads();
+  int g_lo = Nk, g_hi = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) { g_lo = min(g_lo, wg_win[w][0]); g_hi = max(g_hi, wg_win[w][1]); }
+  const int t_lo = g_hi > g_lo ? g_lo / BC : 0;
+  const int t_hi = g_hi > g_lo ? (g_hi + BC - 1) / BC : 0;
+  // wave-uniform tile tests (scalar branches)
+  auto live_tile = [&](int t) { return t < t_hi && t * BC < w_hi && (t + 1) * BC > w_lo; };
+  auto full_tile = [&](int t) {
+    const int k0 = t * BC, k1 = k0 + BC;
+    return k1 <= Nk && k1 <= w_full_c && (!ranged || (w_max_s <= k0 && w_min_e >= k1));
+  };
+
+  // ---- Q fragments (B operand of S^T = K Q^T) -------------------------------------
+  u32x4 qf[DK];
+  {
+    const size_t r = (size_t)min(qrow, Nq - 1);  // rows past the end are never stored
+#pragma unroll
+    for (int ks = 0; ks < DK; ++ks) qf[ks] = ldg16(Q + r * D + 16 * ks + 8 * h);
+  }
+
+  // ---- per-lane LDS offsets; everything else is a compile-time immediate ----------
+  // K (A operand of S^T): lane n reads key row kb*32+n, d = 16*ks + 8*h .. +7.
+  const int k_lane = n * C::kKS + 16 * h;  // + kb*32*KS + 32*ks
+  // V (A operand of O^T = V^T P^T) by transposing loads: for MFMA k-slots 8h+4p .. +3
+  // (p = 0, 1) a lane needs keys 32kb + 16st + 8p + 4h + {0..3} at d = 32db + n; lane
+  // 4k+q of its 16-lane group addresses key row (.. + k), columns 16*(n/16) + 4q .. +3.
+  const int v_lane = (((lane >> 2) & 3) + 4 * h) * C::kVS + (16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * 2;
+  auto v_imm = [](int db, int kb, int st, int p) { return (32 * kb + 16 * st + 8 * p) * C::kVS + 64 * db; };
+  auto vfrag = [&](const char* Vs, int db, int kb, int st) {
+    const u32x2 lo = lds_ld8_tr(Vs, v_lane + v_imm(db, kb, st, 0));
+    const u32x2 hi = lds_ld8_tr(Vs, v_lane + v_imm(db, kb, st, 1));
+    return u32x4{lo[0], lo[1], hi[0], hi[1]};
+  };
+
+  f32x16 o[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) o[db] = f32x16{};
+  float m2 = kNegInf, l = 0.f;
+
+  TC tk, tv;
+  // One key tile: S^T = K Q^T, (bias), (mask), running max, exponentials, O^T += V^T P^T.
+  // Full and partially visible tiles get separate straight-line bodies (MASK) so that no
+  // register merges are needed inside a tile.
+  auto tile = [&](int t, auto mask_tag) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    const char* Ks = ks_mem + (t & 1) * C::kKBytes;
+    const char* Vs = vs_mem + (t & 1) * C::kVBytes;
+    const int kt0 = t * BC;
+    f32x16 sc[KB];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      sc[kb] = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < DK; ++ks)
+        sc[kb] = E::mma(lds_ld16(Ks, k_lane + kb * 32 * C::kKS + 32 * ks), qf[ks], sc[kb]);
+    }
+    if constexpr (BIAS) {
+      const float base = (float)(qrow - kt0 - 4 * h);
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int g = 0; g < 16; ++g) {
+          const float dist = base - (float)(kb * 32 + 8 * (g / 4) + (g % 4));
+          sc[kb][g] = __builtin_fmaf(sc[kb][g], sl2, slope2 * __builtin_fabsf(dist));
+        }
+    }
+    if constexpr (MASK) {
+      // visible keys of this row inside the tile: tile-local [lo, hi)
+      const int lo = kst - kt0;
+      const int hi = min(min(ken, Nk), causal ? qrow + off + 1 : Nk) - kt0;
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int g = 0; g < 16; ++g) {
+          const int j = kb * 32 + res_row(g, h);
+          sc[kb][g] = (j >= lo && j < hi) ? sc[kb][g] : kNegInf;
+        }
+    }
+    float mx = kNegInf;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int g = 0; g < 16; ++g) mx = __builtin_fmaxf(mx, sc[kb][g]);
+    mx = xhalf_max(mx);
+    const float tmax = BIAS ? mx : mx * sl2;
+    if (__builtin_expect(wave_any(tmax > m2 + kTau), 0)) {  // rare after the first tiles
+      const float mnew = __builtin_fmaxf(m2, tmax);
+      const float alpha = mnew == kNegInf ? 1.f : fast_exp2(m2 - mnew);
+      l *= alpha;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) o[db] *= alpha;
+      m2 = mnew;
+    }
+    const float nb = m2 == kNegInf ? 0.f : -m2;
+    u32x4 pb[KB][2];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int st = 0; st < 2; ++st)
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const int g = 8 * st + 2 * w;
+          const float x0 = BIAS ? sc[kb][g] + nb : __builtin_fmaf(sc[kb][g], sl2, nb);
+          const float x1 = BIAS ? sc[kb][g + 1] + nb : __builtin_fmaf(sc[kb][g + 1], sl2, nb);
+          const float p0 = fast_exp2(x0), p1 = fast_exp2(x1);
+          pb[kb][st][w] = E::pack2(p0, p1);
+          l += p0 + p1;  // float32 row sum (the LSE needs the unrounded probabilities)
+        }
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int st = 0; st < 2; ++st)
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+          o[db] = E::mma(vfrag(Vs, db, kb, st), pb[kb][st], o[db]);
+  };
+
+  if (t_lo < t_hi) {
+    tk.load(K, t_lo * BC, Nk, tid);
+    tv.load(V, t_lo * BC, Nk, tid);
+    tk.template store_natural<C::kKS>(ks_mem + (t_lo & 1) * C::kKBytes, tid);
+    tv.template store_natural<C::kVS>(vs_mem + (t_lo & 1) * C::kVBytes, tid);
+  }
+  __syncthreads();
+  for (int t = t_lo; t < t_hi; ++t) {
+    const bool more = t + 1 < t_hi;
+    if (more) {  // next tile in flight while this one is computed
+      tk.load(K, (t + 1) * BC, Nk, tid);
+      tv.load(V, (t + 1) * BC, Nk, tid);
+    }
+    if (live_tile(t)) {
+      if (full_tile(t))
+        tile(t, std::false_type{});
+      else
+        tile(t, std::true_type{});
+    }
+    if (more) {
+      tk.template store_natural<C::kKS>(ks_mem + ((t + 1) & 1) * C::kKBytes, tid);
+      tv.template store_natural<C::kVS>(vs_mem + ((t + 1) & 1) * C::kVBytes, tid);
+    }
+    __syncthreads();
+  }
+
+  // ---- epilogue -----------------------------------------------------------------------
+  const float lt = xhalf_sum(l);
+  const float inv = lt > 0.f ? 1.f / lt : 0.f;
+  if (qrow < Nq) {
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int d0 = db * 32 + 8 * g4 + 4 * h;
+        stg8(O + (size_t)qrow * D + d0,
+             u32x2{E::pack2(o[db][4 * g4] * inv, o[db][4 * g4 + 1] * inv),
+                   E::pack2(o[db][4 * g4 + 2] * inv, o[db][4 * g4 + 3] * inv)});
+      }
+    if (h == 0 && a.lse != nullptr)
+      a.lse[(size_t)bh * Nq + qrow] = lt > 0.f ? (m2 + __builtin_amdgcn_logf(lt)) * kLn2 : kNegInf;
+  }
+}
+
+// ---------------------------------------------------------------------------------
 // key-range summary: out[4r..4r+3] = min/max of clamped start and end over rows of block r
 // ---------------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void mask_summary_kernel(const int32_t* __restrict__ ks,
@@ -496,25 +739,34 @@ static hipError_t launch_cfg(bool bias, FwdArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
-// (d, BC keys per tile, QSUB 32-row sub-blocks per wave, NW waves, waves per SIMD)
-#ifndef FA_FWD_CFG_16_D128
-#define FA_FWD_CFG_16_D128 128, 64, 1, 8, 2
-#endif
-#ifndef FA_FWD_CFG_16_D64
-#define FA_FWD_CFG_16_D64 64, 128, 1, 8, 2
-#endif
+// float32 configurations (d, BC keys per tile, QSUB 32-row sub-blocks per wave, NW waves,
+// waves per SIMD); 16-bit types use fwd16_kernel below
 #define FA_FWD_CFG_32_D128 128, 32, 1, 4, 1
 #define FA_FWD_CFG_32_D64 64, 32, 1, 4, 1
 
 
+template <typename T, int D, int BC, int NW>
+static hipError_t launch16(bool bias, FwdArgs& a, hipStream_t st) {
+  using C = Fwd16Cfg<D, BC, NW>;
+  a.nqb = (a.Nq + C::kBR - 1) / C::kBR;
+  const int BH = a.B * a.H;
+  a.sched = (BH % 8 == 0) ? kSchedXcd : kSchedHeadMajor;
+  const dim3 grid((unsigned)(BH * a.nqb)), block(C::kNT);
+  if (bias)
+    hipLaunchKernelGGL((fwd16_kernel<T, D, BC, NW, true>), grid, block, 0, st, a);
+  else
+    hipLaunchKernelGGL((fwd16_kernel<T, D, BC, NW, false>), grid, block, 0, st, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_fwd(fa_dtype dt, int d, bool bias, FwdArgs& a, hipStream_t st) {
   switch (dt) {
     case FA_BF16:
-      return d == 128 ? launch_cfg<__bf16, FA_FWD_CFG_16_D128>(bias, a, st)
-                      : launch_cfg<__bf16, FA_FWD_CFG_16_D64>(bias, a, st);
+      return d == 128 ? launch16<__bf16, 128, 64, 8>(bias, a, st)
+                      : launch16<__bf16, 64, 64, 4>(bias, a, st);
     case FA_F16:
-      return d == 128 ? launch_cfg<_Float16, FA_FWD_CFG_16_D128>(bias, a, st)
-                      : launch_cfg<_Float16, FA_FWD_CFG_16_D64>(bias, a, st);
+      return d == 128 ? launch16<_Float16, 128, 64, 8>(bias, a, st)
+                      : launch16<_Float16, 64, 64, 4>(bias, a, st);
     case FA_F32:
       return d == 128 ? launch_cfg<float, FA_FWD_CFG_32_D128>(bias, a, st)
                       : launch_cfg<float, FA_FWD_CFG_32_D64>(bias, a, st);
