@@ -31,7 +31,10 @@
 
 namespace fa {
 
-constexpr float kTau = 8.0f;  // lazy-rescale threshold in log2 units (p <= 2^8)
+constexpr float kTau = 8.0f;
+#ifndef FA_FWD_PRIO
+#define FA_FWD_PRIO false
+#endif  // lazy-rescale threshold in log2 units (p <= 2^8)
 
 template <typename T, int D_, int BC_, int QSUB_, int NW_>
 struct FwdCfg {
@@ -575,13 +578,21 @@ void fwd16_kernel(const FwdArgs a) {
     const char* Vs = vs_mem + (t & 1) * C::kVBytes;
     const int kt0 = t * BC;
     f32x16 sc[KB];
+    // The wave issuing MFMAs gets priority, so the two waves sharing a SIMD drift out of
+    // phase: one runs its softmax on the VALU while the other keeps the MFMA unit busy.
+    if constexpr (FA_FWD_PRIO) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
+      // all K operands of this 32-key block are requested before the first MFMA uses
+      // one, so the LDS latency is paid once per block instead of once per MFMA pair
+      u32x4 kf[DK];
+#pragma unroll
+      for (int ks = 0; ks < DK; ++ks) kf[ks] = lds_ld16(Ks, k_lane + kb * 32 * C::kKS + 32 * ks);
       sc[kb] = f32x16{};
 #pragma unroll
-      for (int ks = 0; ks < DK; ++ks)
-        sc[kb] = E::mma(lds_ld16(Ks, k_lane + kb * 32 * C::kKS + 32 * ks), qf[ks], sc[kb]);
+      for (int ks = 0; ks < DK; ++ks) sc[kb] = E::mma(kf[ks], qf[ks], sc[kb]);
     }
+    if constexpr (FA_FWD_PRIO) __builtin_amdgcn_s_setprio(0);
     if constexpr (BIAS) {
       const float base = (float)(qrow - kt0 - 4 * h);
 #pragma unroll
@@ -634,13 +645,18 @@ void fwd16_kernel(const FwdArgs a) {
           pb[kb][st][w] = E::pack2(p0, p1);
           l += p0 + p1;  // float32 row sum (the LSE needs the unrounded probabilities)
         }
+    if constexpr (FA_FWD_PRIO) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-      for (int st = 0; st < 2; ++st)
+      for (int st = 0; st < 2; ++st) {
+        u32x4 vf[DB];  // V operands of this 16-key step, requested together
 #pragma unroll
-        for (int db = 0; db < DB; ++db)
-          o[db] = E::mma(vfrag(Vs, db, kb, st), pb[kb][st], o[db]);
+        for (int db = 0; db < DB; ++db) vf[db] = vfrag(Vs, db, kb, st);
+#pragma unroll
+        for (int db = 0; db < DB; ++db) o[db] = E::mma(vf[db], pb[kb][st], o[db]);
+      }
+    if constexpr (FA_FWD_PRIO) __builtin_amdgcn_s_setprio(0);
   };
 
   if (t_lo < t_hi) {
@@ -745,6 +761,9 @@ static hipError_t launch_cfg(bool bias, FwdArgs& a, hipStream_t st) {
 #define FA_FWD_CFG_32_D64 64, 32, 1, 4, 1
 
 
+#ifndef FA_FWD_NW128
+#define FA_FWD_NW128 8  // waves per workgroup of the d = 128 forward
+#endif
 template <typename T, int D, int BC, int NW>
 static hipError_t launch16(bool bias, FwdArgs& a, hipStream_t st) {
   using C = Fwd16Cfg<D, BC, NW>;
@@ -762,10 +781,10 @@ static hipError_t launch16(bool bias, FwdArgs& a, hipStream_t st) {
 hipError_t launch_fwd(fa_dtype dt, int d, bool bias, FwdArgs& a, hipStream_t st) {
   switch (dt) {
     case FA_BF16:
-      return d == 128 ? launch16<__bf16, 128, 64, 8>(bias, a, st)
+      return d == 128 ? launch16<__bf16, 128, 64, FA_FWD_NW128>(bias, a, st)
                       : launch16<__bf16, 64, 64, 4>(bias, a, st);
     case FA_F16:
-      return d == 128 ? launch16<_Float16, 128, 64, 8>(bias, a, st)
+      return d == 128 ? launch16<_Float16, 128, 64, FA_FWD_NW128>(bias, a, st)
                       : launch16<_Float16, 64, 64, 4>(bias, a, st);
     case FA_F32:
       return d == 128 ? launch_cfg<float, FA_FWD_CFG_32_D128>(bias, a, st)
