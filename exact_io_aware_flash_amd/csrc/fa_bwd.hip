@@ -70,17 +70,45 @@ __device__ inline void store_grad4(void* base, size_t idx, bool f32, float v0, f
 }
 
 // ---------------------------------------------------------------------------------
+// Shared LDS conventions: a tile needed as rows (16 bytes per lane, MFMA A operand) is
+// stored row-major with row stride 2*D+16; a tile whose columns are gathered with the
+// transposing load (MFMA operand over the tile's rows) is stored row-major with row stride
+// 2*D+64. Both strides are bank-conflict-free for their access (measured); a tile used
+// both ways is stored twice with plain 16-byte writes.
+// ---------------------------------------------------------------------------------
+template <int D>
+struct BwdStrides {
+  static constexpr int RS = D * 2 + 16;  // row-read copy
+  static constexpr int TS = D * 2 + 64;  // transposing-read copy
+};
+
+// 8 consecutive 16-bit values of column d = 32*db + n over the 8 rows that MFMA k-slots
+// 8h .. 8h+7 stand for (rows r0 + 16*st + 8*p + 4*h + {0..3}, p = 0, 1), gathered with two
+// transposing loads from a row-major tile of row stride TS.
+template <int TS>
+__device__ inline u32x4 col_frag(const char* base, int lane_off, int r0, int st, int db) {
+  const int o = lane_off + (r0 + 16 * st) * TS + 64 * db;
+  const u32x2 lo = lds_ld8_tr(base, o);
+  const u32x2 hi = lds_ld8_tr(base, o + 8 * TS);
+  return u32x4{lo[0], lo[1], hi[0], hi[1]};
+}
+template <int TS>
+__device__ inline int col_lane_off(int lane) {
+  const int h = lane >> 5;
+  return (((lane >> 2) & 3) + 4 * h) * TS + (16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * 2;
+}
+
+// ---------------------------------------------------------------------------------
 // 2. dK, dV: key-block-outer
 // ---------------------------------------------------------------------------------
 template <int D, int BR>
 struct DkdvLds {
-  static constexpr int NS = D * 2 + 16;   // row-major tile row stride (bytes)
-  static constexpr int TS = BR * 2 + 16;  // transposed tile row stride (D rows)
-  static constexpr int NB = BR * NS;
-  static constexpr int TB = D * TS;
-  static constexpr int QN = 0, QT = NB, DN = NB + TB, DT = 2 * NB + TB;
-  static constexpr int LSE = 2 * NB + 2 * TB, DLT = LSE + BR * 4, KS = DLT + BR * 4,
-                       KE = KS + BR * 4;
+  static constexpr int RS = BwdStrides<D>::RS, TS = BwdStrides<D>::TS;
+  static constexpr int QR = 0;                 // Q rows (A operand of S = Q K^T)
+  static constexpr int QT = QR + BR * RS;      // Q for column gathers (B operand of dK)
+  static constexpr int DR = QT + BR * TS;      // dO rows (A operand of dP = dO V^T)
+  static constexpr int DT = DR + BR * RS;      // dO for column gathers (B operand of dV)
+  static constexpr int LSE = DT + BR * TS, DLT = LSE + BR * 4, KS = DLT + BR * 4, KE = KS + BR * 4;
   static constexpr int STAGE = KE + BR * 4;
 };
 
@@ -135,8 +163,8 @@ void bwd_dkdv_kernel(const BwdArgs a) {
     if (tid < 64) {
       int lo = nqt, hi = -1;
       for (int t = lane; t < nqt; t += 64) {
-        const int* s = a.qsum + 4 * t;  // {min start, max start, min end, max end}
-        if (!(k1 <= s[0] || k0 >= s[3])) { lo = min(lo, t); hi = max(hi, t); }
+        const int* sm = a.qsum + 4 * t;  // {min start, max start, min end, max end}
+        if (!(k1 <= sm[0] || k0 >= sm[3])) { lo = min(lo, t); hi = max(hi, t); }
       }
       lo = wave_min(lo);
       hi = wave_max(hi);
@@ -151,6 +179,9 @@ void bwd_dkdv_kernel(const BwdArgs a) {
   f32x16 dv[DB], dk[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) { dv[db] = f32x16{}; dk[db] = f32x16{}; }
+
+  const int r_lane = n * L::RS + 16 * h;        // + (32*qb)*RS + 32*ks
+  const int t_lane = col_lane_off<L::TS>(lane);  // column gathers
 
   TC tq, tdo;
   float lse_r = 0.f, dlt_r = 0.f;
@@ -170,16 +201,98 @@ void bwd_dkdv_kernel(const BwdArgs a) {
     }
   };
   auto store_tile = [&](int stage) {
-    char* s = smem + stage * L::STAGE;
-    tq.template store_natural<L::NS>(s + L::QN, tid);
-    tq.template store_T<L::TS>(s + L::QT, tid);
-    tdo.template store_natural<L::NS>(s + L::DN, tid);
-    tdo.template store_T<L::TS>(s + L::DT, tid);
+    char* sb = smem + stage * L::STAGE;
+    tq.template store_natural<L::RS>(sb + L::QR, tid);
+    tq.template store_natural<L::TS>(sb + L::QT, tid);
+    tdo.template store_natural<L::RS>(sb + L::DR, tid);
+    tdo.template store_natural<L::TS>(sb + L::DT, tid);
     if (tid < BR) {
-      reinterpret_cast<float*>(s + L::LSE)[tid] = lse_r;
-      reinterpret_cast<float*>(s + L::DLT)[tid] = dlt_r;
-      reinterpret_cast<int*>(s + L::KS)[tid] = ks_r;
-      reinterpret_cast<int*>(s + L::KE)[tid] = ke_r;
+      reinterpret_cast<float*>(sb + L::LSE)[tid] = lse_r;
+      reinterpret_cast<float*>(sb + L::DLT)[tid] = dlt_r;
+      reinterpret_cast<int*>(sb + L::KS)[tid] = ks_r;
+      reinterpret_cast<int*>(sb + L::KE)[tid] = ke_r;
+    }
+  };
+
+  // one 32-query block of a tile; MASK: per-element visibility
+  auto qblock = [&](const char* sb, int q0t, int qb, auto mask_tag) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    f32x16 sc = f32x16{}, dp = f32x16{};
+    {
+      u32x4 qa[DK], da[DK];
+#pragma unroll
+      for (int ks = 0; ks < DK; ++ks) {
+        qa[ks] = lds_ld16(sb + L::QR, r_lane + 32 * qb * L::RS + 32 * ks);
+        da[ks] = lds_ld16(sb + L::DR, r_lane + 32 * qb * L::RS + 32 * ks);
+      }
+#pragma unroll
+      for (int ks = 0; ks < DK; ++ks) {
+        sc = E::mma(qa[ks], kf[ks], sc);
+        dp = E::mma(da[ks], vf[ks], dp);
+      }
+    }
+    // statistics of the 16 queries this lane holds (rows res_row(g, h) of the block)
+    f32x4 l4[4], d4[4];
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const int r0 = 32 * qb + 8 * q4 + 4 * h;
+      l4[q4] = *reinterpret_cast<const f32x4*>(sb + L::LSE + r0 * 4);
+      d4[q4] = *reinterpret_cast<const f32x4*>(sb + L::DLT + r0 * 4);
+    }
+    float p[16], ds[16];
+#pragma unroll
+    for (int g = 0; g < 16; ++g) {
+      const float lq = l4[g / 4][g % 4];
+      float x;
+      if constexpr (BIAS) {
+        const float dist = (float)(q0t + 32 * qb + 4 * h - key) + (float)(8 * (g / 4) + (g % 4));
+        x = __builtin_fmaf(sc[g], sl2, __builtin_fmaf(slope2, __builtin_fabsf(dist), -lq));
+      } else {
+        x = __builtin_fmaf(sc[g], sl2, -lq);
+      }
+      p[g] = fast_exp2(x);
+    }
+    if constexpr (MASK) {
+      int4 st4[4], en4[4];
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int r0 = 32 * qb + 8 * q4 + 4 * h;
+        st4[q4] = *reinterpret_cast<const int4*>(sb + L::KS + r0 * 4);
+        en4[q4] = *reinterpret_cast<const int4*>(sb + L::KE + r0 * 4);
+      }
+      const int kvis = key < Nk ? 1 : 0;
+#pragma unroll
+      for (int g = 0; g < 16; ++g) {
+        const int qi = q0t + 32 * qb + res_row(g, h);
+        const int sti = (&st4[g / 4].x)[g % 4], eni = (&en4[g / 4].x)[g % 4];
+        const int lo = ranged ? sti : 0;
+        const int hi = ranged ? eni : Nk;
+        const int cmin = causal ? qi + off : Nk;
+        const bool vis = kvis && qi < Nq && key >= lo && key < hi && key <= cmin;
+        p[g] = vis ? p[g] : 0.f;
+      }
+    }
+#pragma unroll
+    for (int g = 0; g < 16; ++g) ds[g] = p[g] * (dp[g] - d4[g / 4][g % 4]);
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      u32x4 pa, dsa;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        pa[w] = E::pack2(p[8 * st + 2 * w], p[8 * st + 2 * w + 1]);
+        dsa[w] = E::pack2(ds[8 * st + 2 * w], ds[8 * st + 2 * w + 1]);
+      }
+      u32x4 ob[DB], qbf[DB];
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        ob[db] = col_frag<L::TS>(sb + L::DT, t_lane, 32 * qb, st, db);
+        qbf[db] = col_frag<L::TS>(sb + L::QT, t_lane, 32 * qb, st, db);
+      }
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        dv[db] = E::mma(pa, ob[db], dv[db]);
+        dk[db] = E::mma(dsa, qbf[db], dk[db]);
+      }
     }
   };
 
@@ -198,7 +311,7 @@ void bwd_dkdv_kernel(const BwdArgs a) {
     for (int ks = 0; ks < DK; ++ks) { pin_agpr(kf[ks]); pin_agpr(vf[ks]); }
     if (more) load_tile(t + 1);
     const int q0t = t * BR;
-    const char* s = smem + stage * L::STAGE;
+    const char* sb = smem + stage * L::STAGE;
 
     // classify the tile for this wave's keys [kw0, kw1)
     bool skip = kw0 >= Nk;
@@ -213,71 +326,12 @@ void bwd_dkdv_kernel(const BwdArgs a) {
       full &= sm[1] <= kw0 && sm[2] >= kw0 + 32;
     }
     if (!skip) {
+      if (full) {
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        f32x16 sc = f32x16{}, dp = f32x16{};
+        for (int qb = 0; qb < QB; ++qb) qblock(sb, q0t, qb, std::false_type{});
+      } else {
 #pragma unroll
-        for (int ks = 0; ks < DK; ++ks) {
-          const int o = (32 * qb + n) * L::NS + 32 * ks + 16 * h;
-          sc = E::mma(lds_ld16(s + L::QN, o), kf[ks], sc);
-          dp = E::mma(lds_ld16(s + L::DN, o), vf[ks], dp);
-        }
-        // per-query statistics of the 16 queries this lane holds (rows res_row(g, h))
-        f32x4 l4[4], d4[4];
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          const int r0 = 32 * qb + 8 * q4 + 4 * h;
-          l4[q4] = *reinterpret_cast<const f32x4*>(s + L::LSE + r0 * 4);
-          d4[q4] = *reinterpret_cast<const f32x4*>(s + L::DLT + r0 * 4);
-        }
-        float p[16], ds[16];
-#pragma unroll
-        for (int g = 0; g < 16; ++g) {
-          const float lq = l4[g / 4][g % 4];
-          float x;
-          if constexpr (BIAS) {
-            const float dist = (float)(q0t + 32 * qb + 4 * h - key) + (float)(8 * (g / 4) + (g % 4));
-            x = __builtin_fmaf(sc[g], sl2, __builtin_fmaf(slope2, __builtin_fabsf(dist), -lq));
-          } else {
-            x = __builtin_fmaf(sc[g], sl2, -lq);
-          }
-          p[g] = fast_exp2(x);
-        }
-        if (!full) {
-          int4 st4[4], en4[4];
-#pragma unroll
-          for (int q4 = 0; q4 < 4; ++q4) {
-            const int r0 = 32 * qb + 8 * q4 + 4 * h;
-            st4[q4] = *reinterpret_cast<const int4*>(s + L::KS + r0 * 4);
-            en4[q4] = *reinterpret_cast<const int4*>(s + L::KE + r0 * 4);
-          }
-#pragma unroll
-          for (int g = 0; g < 16; ++g) {
-            const int qi = q0t + 32 * qb + res_row(g, h);
-            const int sti = (&st4[g / 4].x)[g % 4], eni = (&en4[g / 4].x)[g % 4];
-            bool vis = qi < Nq && key < Nk;
-            if (causal) vis = vis && key <= qi + off;
-            if (ranged) vis = vis && key >= sti && key < eni;
-            p[g] = vis ? p[g] : 0.f;
-          }
-        }
-#pragma unroll
-        for (int g = 0; g < 16; ++g) ds[g] = p[g] * (dp[g] - d4[g / 4][g % 4]);
-#pragma unroll
-        for (int st = 0; st < 2; ++st) {
-          u32x4 pa, da;
-#pragma unroll
-          for (int w = 0; w < 4; ++w) {
-            pa[w] = E::pack2(p[8 * st + 2 * w], p[8 * st + 2 * w + 1]);
-            da[w] = E::pack2(ds[8 * st + 2 * w], ds[8 * st + 2 * w + 1]);
-          }
-#pragma unroll
-          for (int db = 0; db < DB; ++db) {
-            const int o = TC::template t_off<L::TS>(32 * db + n, 4 * qb + 2 * st + h);
-            dv[db] = E::mma(pa, lds_ld16(s + L::DT, o), dv[db]);
-            dk[db] = E::mma(da, lds_ld16(s + L::QT, o), dk[db]);
-          }
-        }
+        for (int qb = 0; qb < QB; ++qb) qblock(sb, q0t, qb, std::true_type{});
       }
     }
     if (more) store_tile(stage ^ 1);
@@ -310,11 +364,11 @@ void bwd_dkdv_kernel(const BwdArgs a) {
 // ---------------------------------------------------------------------------------
 template <int D, int BC>
 struct DqLds {
-  static constexpr int NS = D * 2 + 16;
-  static constexpr int TS = BC * 2 + 16;
-  static constexpr int NB = BC * NS;
-  static constexpr int KN = 0, VN = NB, KT = 2 * NB;
-  static constexpr int STAGE = 2 * NB + D * TS;
+  static constexpr int RS = BwdStrides<D>::RS, TS = BwdStrides<D>::TS;
+  static constexpr int KR = 0;               // K rows (A operand of S^T = K Q^T)
+  static constexpr int VR = KR + BC * RS;    // V rows (A operand of dP^T = V dO^T)
+  static constexpr int KT = VR + BC * RS;    // K for column gathers (A operand of dQ^T = K^T dS^T)
+  static constexpr int STAGE = KT + BC * TS;
 };
 
 template <typename T, int D, int BC, int NW, int WPE, bool BIAS>
@@ -390,16 +444,71 @@ void bwd_dq_kernel(const BwdArgs a) {
 #pragma unroll
   for (int db = 0; db < DB; ++db) dqa[db] = f32x16{};
 
+  const int r_lane = n * L::RS + 16 * h;
+  const int t_lane = col_lane_off<L::TS>(lane);
+
   TC tk, tv;
   auto load_tile = [&](int t) {
     tk.load(K, t * BC, Nk, tid);
     tv.load(V, t * BC, Nk, tid);
   };
   auto store_tile = [&](int stage) {
-    char* s = smem + stage * L::STAGE;
-    tk.template store_natural<L::NS>(s + L::KN, tid);
-    tk.template store_T<L::TS>(s + L::KT, tid);
-    tv.template store_natural<L::NS>(s + L::VN, tid);
+    char* sb = smem + stage * L::STAGE;
+    tk.template store_natural<L::RS>(sb + L::KR, tid);
+    tk.template store_natural<L::TS>(sb + L::KT, tid);
+    tv.template store_natural<L::RS>(sb + L::VR, tid);
+  };
+
+  auto tile = [&](const char* sb, int kt0, bool full) {
+    f32x16 sc[KB], dp[KB];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      sc[kb] = f32x16{};
+      dp[kb] = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < DK; ++ks) {
+        const int o = r_lane + kb * 32 * L::RS + 32 * ks;
+        sc[kb] = E::mma(lds_ld16(sb + L::KR, o), qf[ks], sc[kb]);
+        dp[kb] = E::mma(lds_ld16(sb + L::VR, o), dof[ks], dp[kb]);
+      }
+    }
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+#pragma unroll
+      for (int g = 0; g < 16; ++g) {
+        float x;
+        if constexpr (BIAS) {
+          const float dist = (float)(qrow - kt0 - 4 * h) - (float)(kb * 32 + 8 * (g / 4) + (g % 4));
+          x = __builtin_fmaf(sc[kb][g], sl2, __builtin_fmaf(slope2, __builtin_fabsf(dist), -lq));
+        } else {
+          x = __builtin_fmaf(sc[kb][g], sl2, -lq);
+        }
+        sc[kb][g] = fast_exp2(x);
+      }
+      if (!full) {
+        const int lo = kst - kt0;
+        const int hi = min(min(ken, Nk), causal ? qrow + off + 1 : Nk) - kt0;
+#pragma unroll
+        for (int g = 0; g < 16; ++g) {
+          const int j = kb * 32 + res_row(g, h);
+          sc[kb][g] = (j >= lo && j < hi) ? sc[kb][g] : 0.f;
+        }
+      }
+#pragma unroll
+      for (int g = 0; g < 16; ++g) sc[kb][g] = sc[kb][g] * (dp[kb][g] - dq_d);  // dS^T
+    }
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        u32x4 da;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) da[w] = E::pack2(sc[kb][8 * st + 2 * w], sc[kb][8 * st + 2 * w + 1]);
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+          dqa[db] = E::mma(col_frag<L::TS>(sb + L::KT, t_lane, 32 * kb, st, db), da, dqa[db]);
+      }
+    }
   };
 
   if (t_lo < t_hi) {
@@ -417,59 +526,8 @@ void bwd_dq_kernel(const BwdArgs a) {
     if (!skip) {
       const bool full = kt1 <= Nk && kt1 <= w_full_c &&
                         (!ranged || (w_max_s <= kt0 && w_min_e >= kt1));
-      const char* s = smem + stage * L::STAGE;
-      f32x16 sc[KB], dp[KB];
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-        sc[kb] = f32x16{};
-        dp[kb] = f32x16{};
-#pragma unroll
-        for (int ks = 0; ks < DK; ++ks) {
-          const int o = (kb * 32 + n) * L::NS + 32 * ks + 16 * h;
-          sc[kb] = E::mma(lds_ld16(s + L::KN, o), qf[ks], sc[kb]);
-          dp[kb] = E::mma(lds_ld16(s + L::VN, o), dof[ks], dp[kb]);
-        }
-      }
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-#pragma unroll
-        for (int g = 0; g < 16; ++g) {
-          float x;
-          if constexpr (BIAS) {
-            const float dist = (float)(qrow - kt0 - 4 * h) - (float)(kb * 32 + 8 * (g / 4) + (g % 4));
-            x = __builtin_fmaf(sc[kb][g], sl2, __builtin_fmaf(slope2, __builtin_fabsf(dist), -lq));
-          } else {
-            x = __builtin_fmaf(sc[kb][g], sl2, -lq);
-          }
-          sc[kb][g] = fast_exp2(x);
-        }
-        if (!full) {
-          const int cl = causal ? qrow + off : Nk;
-          const int hi = min(ken, Nk);
-#pragma unroll
-          for (int g = 0; g < 16; ++g) {
-            const int j = kt0 + kb * 32 + res_row(g, h);
-            const bool vis = j >= kst && j < hi && j <= cl;
-            sc[kb][g] = vis ? sc[kb][g] : 0.f;
-          }
-        }
-#pragma unroll
-        for (int g = 0; g < 16; ++g) sc[kb][g] = sc[kb][g] * (dp[kb][g] - dq_d);  // dS^T
-      }
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-#pragma unroll
-        for (int st = 0; st < 2; ++st) {
-          u32x4 da;
-#pragma unroll
-          for (int w = 0; w < 4; ++w) da[w] = E::pack2(sc[kb][8 * st + 2 * w], sc[kb][8 * st + 2 * w + 1]);
-#pragma unroll
-          for (int db = 0; db < DB; ++db) {
-            const int o = TC::template t_off<L::TS>(32 * db + n, 4 * kb + 2 * st + h);
-            dqa[db] = E::mma(lds_ld16(s + L::KT, o), da, dqa[db]);
-          }
-        }
-      }
+      const char* sb = smem + stage * L::STAGE;
+      tile(sb, kt0, full);
     }
     if (more) store_tile(stage ^ 1);
     __syncthreads();
