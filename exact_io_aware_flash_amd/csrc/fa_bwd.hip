@@ -124,7 +124,7 @@ void bwd_dkdv_kernel(const BwdArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[2 * L::STAGE];
   __shared__ int win[2];
 
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6, n = lane & 31, h = lane >> 5;
+  const int tid = threadIdx.x, lane = tid & 63, wid = wave_id(), n = lane & 31, h = lane >> 5;
   const int Nq = a.Nq, Nk = a.Nk, off = Nk - Nq;
   const bool causal = a.causal != 0, ranged = a.key_start != nullptr;
   int bh, kb;
@@ -383,7 +383,7 @@ void bwd_dq_kernel(const BwdArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[2 * L::STAGE];
   __shared__ int wg_win[NW][2];
 
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6, n = lane & 31, h = lane >> 5;
+  const int tid = threadIdx.x, lane = tid & 63, wid = wave_id(), n = lane & 31, h = lane >> 5;
   const int Nq = a.Nq, Nk = a.Nk, off = Nk - Nq;
   const bool causal = a.causal != 0, ranged = a.key_start != nullptr;
   int bh, qb;

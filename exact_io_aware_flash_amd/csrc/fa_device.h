@@ -75,8 +75,15 @@ template <> struct Elt<float> {
 // Result-register helpers for the 32x32 layout.
 __device__ constexpr int res_row(int g, int h) { return 8 * (g / 4) + 4 * h + (g % 4); }
 
-// Cross-half exchange: value held by lane l ^ 32 (the other half of the same column).
-__device__ inline float xhalf(float v) { return __shfl_xor(v, 32, 64); }
+// Cross-half exchange: value held by lane l ^ 32 (the other half of the same column),
+// one ds_bpermute with the byte address 4 * (l ^ 32).
+__device__ inline int lane_id() {
+  return (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+}
+__device__ inline float xhalf(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute((lane_id() ^ 32) << 2,
+                                                                __builtin_bit_cast(int, v)));
+}
 
 __device__ inline float xhalf_max(float v) { return __builtin_fmaxf(v, xhalf(v)); }
 __device__ inline float xhalf_sum(float v) { return v + xhalf(v); }
@@ -141,14 +148,78 @@ __device__ __host__ constexpr int align16(int x) { return (x + 15) & ~15; }
 // layout) sit in 8 consecutive slots: swap bits 2 and 3 of the row index.
 __device__ constexpr int tr_pos(int r) { return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1); }
 
+// Reductions over the wave. Every lane ends with the same value; reading it back from
+// the first lane tells the compiler so, and branches on it become scalar branches.
 __device__ inline int wave_min(int v) {
   for (int o = 32; o >= 1; o >>= 1) v = min(v, __shfl_xor(v, o, 64));
-  return v;
+  return __builtin_amdgcn_readfirstlane(v);
 }
 __device__ inline int wave_max(int v) {
   for (int o = 32; o >= 1; o >>= 1) v = max(v, __shfl_xor(v, o, 64));
-  return v;
+  return __builtin_amdgcn_readfirstlane(v);
 }
+// Index of the calling wave inside its workgroup, as a wave-uniform (scalar) value.
+__device__ inline int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
+
+// ---------------------------------------------------------------------------------
+// Swizzled tiles filled by direct global -> LDS loads (global_load_lds_dwordx4).
+// A tile of ROWS rows x D 16-bit elements is stored without padding (row = 2*D bytes);
+// 16-byte chunk c of tile row r sits in chunk slot c ^ swz(r). With this permutation
+// (a) 16-byte row reads by 16 lanes of 16 consecutive rows and (b) transposing 8-byte
+// reads by 16 lanes of 4 consecutive rows x 32 bytes both touch 64 distinct LDS banks.
+// swz depends on r mod 16 only.
+// ---------------------------------------------------------------------------------
+template <int D>
+__device__ constexpr int swz(int r) {
+  static_assert(D == 64 || D == 128, "head dim");
+  return D == 128 ? 4 * (r & 3) + ((r >> 2) & 3) : 4 * ((r >> 1) & 1) + ((r >> 2) & 3);
+}
+
+// Wait until at most N vector-memory operations of this wave are outstanding (direct
+// LDS loads count here; they complete in issue order).
+template <int N>
+__device__ inline void wait_vmem() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// One wave-wide direct load moves 1 KB: lane i fills bytes [16i, 16i+16) of the window
+// (the LDS address comes from the wave-uniform window base). A tile is kOps windows,
+// split evenly over the NW waves of the workgroup.
+template <int ROWS, int D, int NW>
+struct DmaTile {
+  static constexpr int kRowBytes = 2 * D;
+  static constexpr int kBytes = ROWS * kRowBytes;
+  static constexpr int kChunks = D / 8;                // 16-byte chunks per row
+  static constexpr int kRowsPerOp = 1024 / kRowBytes;  // rows one window holds
+  static constexpr int kOps = kBytes / 1024;
+  static constexpr int kOpsPerWave = kOps / NW;
+  static_assert(kOpsPerWave >= 1 && kOpsPerWave * NW == kOps, "tile split over waves");
+
+  int row[kOpsPerWave];  // tile-local row this lane loads, per window
+  int col[kOpsPerWave];  // byte offset of its chunk inside the global row
+
+  __device__ inline void init(int wid, int lane) {
+#pragma unroll
+    for (int j = 0; j < kOpsPerWave; ++j) {
+      const int u = wid * kOpsPerWave + j;
+      row[j] = u * kRowsPerOp + lane / kChunks;
+      col[j] = 16 * ((lane % kChunks) ^ swz<D>(row[j]));  // slot lane%kChunks holds this chunk
+    }
+  }
+  // this wave's share of rows [row0, row0 + ROWS) of a row-major (nrows x D) matrix;
+  // rows past the end repeat the last row (their scores are masked)
+  template <typename T>
+  __device__ inline void load(const T* base, int row0, int nrows, char* lds, int wid) const {
+#pragma unroll
+    for (int j = 0; j < kOpsPerWave; ++j) {
+      const int r = min(row0 + row[j], nrows - 1);
+      const char* g = reinterpret_cast<const char*>(base) + (size_t)r * kRowBytes + col[j];
+      __builtin_amdgcn_global_load_lds(
+          g, (__attribute__((address_space(3))) void*)(lds + (wid * kOpsPerWave + j) * 1024), 16, 0, 0);
+    }
+  }
+};
 
 // A [ROWS x D] tile of 16-bit elements copied global -> registers -> LDS by NT threads.
 // Thread b owns KQ consecutive rows of one 16-byte column chunk, so the same registers

@@ -32,9 +32,7 @@
 namespace fa {
 
 constexpr float kTau = 8.0f;
-#ifndef FA_FWD_PRIO
-#define FA_FWD_PRIO false
-#endif  // lazy-rescale threshold in log2 units (p <= 2^8)
+ // lazy-rescale threshold in log2 units (p <= 2^8)
 
 template <typename T, int D_, int BC_, int QSUB_, int NW_>
 struct FwdCfg {
@@ -89,7 +87,7 @@ void fwd_kernel(const FwdArgs a) {
   __shared__ int wg_win[NW][2];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wid = tid >> 6;
+  const int lane = tid & 63, wid = wave_id();
   const int n = lane & 31, h = lane >> 5;
   const int Nq = a.Nq, Nk = a.Nk;
   const int off = Nk - Nq;  // bottom-right aligned causal diagonal
@@ -448,10 +446,15 @@ void fwd_kernel(const FwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------------
-// 16-bit forward. K and V tiles are row-major in LDS and double-buffered: the global
-// loads of tile j+1 are in flight while tile j is computed; one barrier per tile. Two
-// waves share a SIMD, so one wave's softmax overlaps the other's MFMAs.
+// 16-bit forward. K and V tiles are copied straight from HBM into a ring of LDS stages by
+// direct loads (no staging registers), FA_FWD_STAGES - 1 tiles ahead of the one being
+// computed; one barrier per tile. Tiles are swizzled (see DmaTile): K rows feed the A
+// operand of S^T = K Q^T with 16-byte reads, V is gathered with transposing reads for
+// the A operand of O^T = V^T P^T.
 // ---------------------------------------------------------------------------------
+#ifndef FA_FWD_STAGES
+#define FA_FWD_STAGES 4
+#endif
 template <int D_, int BC_, int NW_>
 struct Fwd16Cfg {
   static constexpr int D = D_, BC = BC_, NW = NW_;
@@ -460,15 +463,11 @@ struct Fwd16Cfg {
   static constexpr int kKB = BC / 32;       // 32-key blocks per tile
   static constexpr int kDB = D / 32;        // 32-wide d blocks of O^T
   static constexpr int kDK = D / 16;        // k-steps over d for S^T
-  // K and V are both stored row-major. K rows are read 16 bytes per lane (row stride
-  // 2*D+16 keeps 16 lanes on distinct banks); V is gathered with the transposing load
-  // (row stride 2*D+64 keeps the 4-row x 32-byte footprint of a 16-lane group on
-  // distinct banks). Both strides were chosen from measured LDS bank-conflict counts.
-  static constexpr int kKS = D * 2 + 16;    // K row stride (bytes)
-  static constexpr int kVS = D * 2 + 64;    // V row stride (bytes)
-  static constexpr int kKBytes = BC * kKS;
-  static constexpr int kVBytes = BC * kVS;
-  static_assert(2 * (kKBytes + kVBytes) <= 160 * 1024, "LDS budget");
+  static constexpr int kRB = 2 * D;         // bytes per tile row
+  static constexpr int kST = FA_FWD_STAGES;
+  using Tile = DmaTile<BC, D, NW>;
+  static constexpr int kStage = 2 * Tile::kBytes;  // K tile, then V tile
+  static_assert(kST >= 2 && kST * kStage <= 160 * 1024, "LDS budget");
 };
 
 template <typename T, int D, int BC, int NW, bool BIAS>
@@ -477,14 +476,14 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
 void fwd16_kernel(const FwdArgs a) {
   using C = Fwd16Cfg<D, BC, NW>;
   using E = Elt<T>;
-  using TC = TileCopy<BC, D, C::kNT>;
-  constexpr int KB = C::kKB, DB = C::kDB, DK = C::kDK;
-  __shared__ __attribute__((aligned(16))) char ks_mem[2 * C::kKBytes];
-  __shared__ __attribute__((aligned(16))) char vs_mem[2 * C::kVBytes];
+  constexpr int KB = C::kKB, DB = C::kDB, DK = C::kDK, RB = C::kRB, ST = C::kST;
+  constexpr int P = ST - 1;                                  // tiles in flight ahead
+  constexpr int kOpsPerTile = 2 * C::Tile::kOpsPerWave;      // direct loads per wave per tile
+  __shared__ __attribute__((aligned(1024))) char smem[ST * C::kStage];
   __shared__ int wg_win[NW][2];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wid = tid >> 6;
+  const int lane = tid & 63, wid = wave_id();
   const int n = lane & 31, h = lane >> 5;
   const int Nq = a.Nq, Nk = a.Nk;
   const int off = Nk - Nq;
@@ -501,7 +500,7 @@ void fwd16_kernel(const FwdArgs a) {
   const float sl2 = a.sl2;
   const float slope2 = BIAS ? a.slope2[a.n_slopes == 1 ? 0 : head] : 0.f;
 
-  // ---- rows, key intervals, windows (as in the generic kernel) --------------------
+  // ---- rows, key intervals, windows -----------------------------------------------
   const int wq0 = qb * C::kBR + wid * 32;
   const int qrow = wq0 + n;
   int kst = 0, ken = Nk;
@@ -535,7 +534,7 @@ void fwd16_kernel(const FwdArgs a) {
   const int t_lo = g_hi > g_lo ? g_lo / BC : 0;
   const int t_hi = g_hi > g_lo ? (g_hi + BC - 1) / BC : 0;
   // wave-uniform tile tests (scalar branches)
-  auto live_tile = [&](int t) { return t < t_hi && t * BC < w_hi && (t + 1) * BC > w_lo; };
+  auto live_tile = [&](int t) { return t * BC < w_hi && (t + 1) * BC > w_lo; };
   auto full_tile = [&](int t) {
     const int k0 = t * BC, k1 = k0 + BC;
     return k1 <= Nk && k1 <= w_full_c && (!ranged || (w_max_s <= k0 && w_min_e >= k1));
@@ -549,17 +548,30 @@ void fwd16_kernel(const FwdArgs a) {
     for (int ks = 0; ks < DK; ++ks) qf[ks] = ldg16(Q + r * D + 16 * ks + 8 * h);
   }
 
-  // ---- per-lane LDS offsets; everything else is a compile-time immediate ----------
-  // K (A operand of S^T): lane n reads key row kb*32+n, d = 16*ks + 8*h .. +7.
-  const int k_lane = n * C::kKS + 16 * h;  // + kb*32*KS + 32*ks
-  // V (A operand of O^T = V^T P^T) by transposing loads: for MFMA k-slots 8h+4p .. +3
-  // (p = 0, 1) a lane needs keys 32kb + 16st + 8p + 4h + {0..3} at d = 32db + n; lane
-  // 4k+q of its 16-lane group addresses key row (.. + k), columns 16*(n/16) + 4q .. +3.
-  const int v_lane = (((lane >> 2) & 3) + 4 * h) * C::kVS + (16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * 2;
-  auto v_imm = [](int db, int kb, int st, int p) { return (32 * kb + 16 * st + 8 * p) * C::kVS + 64 * db; };
+  // ---- per-lane LDS offsets inside a swizzled tile ----------------------------------
+  // K: lane n reads key row 32kb + n, d = 16ks + 8h .. +7, i.e. chunk 2ks + h.
+  int ka[DK];
+#pragma unroll
+  for (int ks = 0; ks < DK; ++ks) ka[ks] = n * RB + 16 * ((2 * ks + h) ^ swz<D>(n));
+  // V by transposing loads: for MFMA k-slots 8h+4p .. +3 a lane needs keys
+  // 32kb + 16st + 8p + 4h + {0..3} at d = 32db + n; lane 4k+q of its 16-lane group
+  // addresses key row (.. + k) at columns 16*(n/16) + 4q .. +3 (chunk 4db + 2(n/16) +
+  // q/2, byte 8(q&1)). kb and st move whole 16-row groups, which keep the swizzle.
+  int va[DB][2];
+  {
+    const int q = (lane >> 2) & 3, g16 = (lane >> 4) & 1, lo2 = lane & 3;
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      const int r = 8 * p + 4 * h + q;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+        va[db][p] = r * RB + 16 * ((4 * db + 2 * g16 + (lo2 >> 1)) ^ swz<D>(r)) + 8 * (lo2 & 1);
+    }
+  }
   auto vfrag = [&](const char* Vs, int db, int kb, int st) {
-    const u32x2 lo = lds_ld8_tr(Vs, v_lane + v_imm(db, kb, st, 0));
-    const u32x2 hi = lds_ld8_tr(Vs, v_lane + v_imm(db, kb, st, 1));
+    const int rows = (32 * kb + 16 * st) * RB;
+    const u32x2 lo = lds_ld8_tr(Vs, rows + va[db][0]);
+    const u32x2 hi = lds_ld8_tr(Vs, rows + va[db][1]);
     return u32x4{lo[0], lo[1], hi[0], hi[1]};
   };
 
@@ -568,31 +580,20 @@ void fwd16_kernel(const FwdArgs a) {
   for (int db = 0; db < DB; ++db) o[db] = f32x16{};
   float m2 = kNegInf, l = 0.f;
 
-  TC tk, tv;
-  // One key tile: S^T = K Q^T, (bias), (mask), running max, exponentials, O^T += V^T P^T.
-  // Full and partially visible tiles get separate straight-line bodies (MASK) so that no
-  // register merges are needed inside a tile.
-  auto tile = [&](int t, auto mask_tag) {
-    constexpr bool MASK = decltype(mask_tag)::value;
-    const char* Ks = ks_mem + (t & 1) * C::kKBytes;
-    const char* Vs = vs_mem + (t & 1) * C::kVBytes;
-    const int kt0 = t * BC;
+  // One key tile: S^T = K Q^T, (bias), (mask: a small branch of its own, so both outcomes
+  // share the rest), running max, exponentials, O^T += V^T P^T.
+  auto tile = [&](const char* Ks, const char* Vs, int kt0, bool masked) __attribute__((always_inline)) {
     f32x16 sc[KB];
-    // The wave issuing MFMAs gets priority, so the two waves sharing a SIMD drift out of
-    // phase: one runs its softmax on the VALU while the other keeps the MFMA unit busy.
-    if constexpr (FA_FWD_PRIO) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
-      // all K operands of this 32-key block are requested before the first MFMA uses
-      // one, so the LDS latency is paid once per block instead of once per MFMA pair
+      // all K operands of this 32-key block are requested before the first MFMA uses one
       u32x4 kf[DK];
 #pragma unroll
-      for (int ks = 0; ks < DK; ++ks) kf[ks] = lds_ld16(Ks, k_lane + kb * 32 * C::kKS + 32 * ks);
+      for (int ks = 0; ks < DK; ++ks) kf[ks] = lds_ld16(Ks, kb * 32 * RB + ka[ks]);
       sc[kb] = f32x16{};
 #pragma unroll
       for (int ks = 0; ks < DK; ++ks) sc[kb] = E::mma(kf[ks], qf[ks], sc[kb]);
     }
-    if constexpr (FA_FWD_PRIO) __builtin_amdgcn_s_setprio(0);
     if constexpr (BIAS) {
       const float base = (float)(qrow - kt0 - 4 * h);
 #pragma unroll
@@ -603,7 +604,7 @@ void fwd16_kernel(const FwdArgs a) {
           sc[kb][g] = __builtin_fmaf(sc[kb][g], sl2, slope2 * __builtin_fabsf(dist));
         }
     }
-    if constexpr (MASK) {
+    if (masked) {
       // visible keys of this row inside the tile: tile-local [lo, hi)
       const int lo = kst - kt0;
       const int hi = min(min(ken, Nk), causal ? qrow + off + 1 : Nk) - kt0;
@@ -645,7 +646,6 @@ void fwd16_kernel(const FwdArgs a) {
           pb[kb][st][w] = E::pack2(p0, p1);
           l += p0 + p1;  // float32 row sum (the LSE needs the unrounded probabilities)
         }
-    if constexpr (FA_FWD_PRIO) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
@@ -656,33 +656,38 @@ void fwd16_kernel(const FwdArgs a) {
 #pragma unroll
         for (int db = 0; db < DB; ++db) o[db] = E::mma(vf[db], pb[kb][st], o[db]);
       }
-    if constexpr (FA_FWD_PRIO) __builtin_amdgcn_s_setprio(0);
   };
 
-  if (t_lo < t_hi) {
-    tk.load(K, t_lo * BC, Nk, tid);
-    tv.load(V, t_lo * BC, Nk, tid);
-    tk.template store_natural<C::kKS>(ks_mem + (t_lo & 1) * C::kKBytes, tid);
-    tv.template store_natural<C::kVS>(vs_mem + (t_lo & 1) * C::kVBytes, tid);
-  }
-  __syncthreads();
+  // ---- main loop: ring of ST stages, P = ST-1 tiles in flight ------------------------
+  typename C::Tile dt;
+  dt.init(wid, lane);
+  auto stage_of = [&](int t) { return smem + ((t - t_lo) % ST) * C::kStage; };
+  auto issue = [&](int t) {
+    char* sb = stage_of(t);
+    dt.load(K, t * BC, Nk, sb, wid);
+    dt.load(V, t * BC, Nk, sb + C::Tile::kBytes, wid);
+  };
+  // wait until the oldest tile in flight has landed while `later` younger tiles may stay
+  // in flight, then make every wave's part visible
+  auto land = [&](int later) {
+    if (P >= 3 && later >= 3) wait_vmem<(P >= 3 ? 3 : 0) * kOpsPerTile>();
+    else if (P >= 2 && later == 2) wait_vmem<(P >= 2 ? 2 : 0) * kOpsPerTile>();
+    else if (later == 1) wait_vmem<kOpsPerTile>();
+    else wait_vmem<0>();
+    __builtin_amdgcn_s_barrier();
+  };
+#pragma unroll
+  for (int i = 0; i < P; ++i)
+    if (t_lo + i < t_hi) issue(t_lo + i);
+  if (t_lo < t_hi) land(min(P, t_hi - t_lo) - 1);
   for (int t = t_lo; t < t_hi; ++t) {
-    const bool more = t + 1 < t_hi;
-    if (more) {  // next tile in flight while this one is computed
-      tk.load(K, (t + 1) * BC, Nk, tid);
-      tv.load(V, (t + 1) * BC, Nk, tid);
-    }
+    // the stage of tile t+P held tile t-1, which every wave finished before the barrier
+    if (t + P < t_hi) issue(t + P);
     if (live_tile(t)) {
-      if (full_tile(t))
-        tile(t, std::false_type{});
-      else
-        tile(t, std::true_type{});
+      const char* sb = stage_of(t);
+      tile(sb, sb + C::Tile::kBytes, t * BC, !full_tile(t));
     }
-    if (more) {
-      tk.template store_natural<C::kKS>(ks_mem + ((t + 1) & 1) * C::kKBytes, tid);
-      tv.template store_natural<C::kVS>(vs_mem + ((t + 1) & 1) * C::kVBytes, tid);
-    }
-    __syncthreads();
+    if (t + 1 < t_hi) land(min(t + P, t_hi - 1) - (t + 1));
   }
 
   // ---- epilogue -----------------------------------------------------------------------
