@@ -34,9 +34,9 @@ PEAK_HBM_GBS = 8000.0
 # the kernel source they were measured on. A changed source means stale counters -> null.
 TRAFFIC = {
     # kernel: (source hash, bytes read, bytes written) -- profiles/attention_fwd_bwd_bf16_causal_B2H16N8192d128.md
-    "fwd": ("834439fd4ed25003", 267.2e6, 68.2e6),
-    "bwd_dkdv": ("646d13d8bac097a2", 274.7e6, 268.4e6),
-    "bwd_dq": ("646d13d8bac097a2", 401.2e6, 138.3e6),
+    "fwd": ("f3d5f6e00480f8b8", 267.0e6, 68.2e6),
+    "bwd_dkdv": ("d1cc67f2293a6d89", 276.1e6, 268.4e6),
+    "bwd_dq": ("d1cc67f2293a6d89", 396.0e6, 134.5e6),
 }
 
 

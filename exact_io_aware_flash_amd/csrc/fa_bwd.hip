@@ -124,7 +124,7 @@ void bwd_dkdv_kernel(const BwdArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[2 * L::STAGE];
   __shared__ int win[2];
 
-  const int tid = threadIdx.x, lane = tid & 63, wid = wave_id(), n = lane & 31, h = lane >> 5;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6, n = lane & 31, h = lane >> 5;
   const int Nq = a.Nq, Nk = a.Nk, off = Nk - Nq;
   const bool causal = a.causal != 0, ranged = a.key_start != nullptr;
   int bh, kb;
@@ -410,11 +410,19 @@ void bwd_dq_kernel(const BwdArgs a) {
 
   // key window of this wave / workgroup (same rules as the forward pass)
   int kst = 0, ken = Nk;
+  // wave-uniform summaries of the rows' key intervals (rows past the end take no part);
+  // computed inside the uniform branch so they stay scalar
   int w_min_s = Nk, w_max_s = 0, w_min_e = Nk, w_max_e = 0;
-  if (ranged && qrow < Nq) {
-    kst = min(max(a.key_start[qrow], 0), Nk);
-    ken = min(max(a.key_end[qrow], 0), Nk);
-    w_min_s = kst; w_max_s = kst; w_min_e = ken; w_max_e = ken;
+  if (ranged) {
+    const bool in = qrow < Nq;
+    if (in) {
+      kst = min(max(a.key_start[qrow], 0), Nk);
+      ken = min(max(a.key_end[qrow], 0), Nk);
+    }
+    w_min_s = wave_min(in ? kst : Nk);
+    w_max_s = wave_max(in ? kst : 0);
+    w_min_e = wave_min(in ? ken : Nk);
+    w_max_e = wave_max(in ? ken : 0);
   }
   const bool wave_live = wq0 < Nq;
   const int wq_last = min(wq0 + 32, Nq) - 1;
@@ -424,10 +432,6 @@ void bwd_dq_kernel(const BwdArgs a) {
     w_full_c = max(0, min(Nk, wq0 + off + 1));
   }
   if (ranged) {
-    w_min_s = wave_min(w_min_s);
-    w_max_s = wave_max(w_max_s);
-    w_min_e = wave_min(w_min_e);
-    w_max_e = wave_max(w_max_e);
     w_lo = max(w_lo, w_min_s);
     w_hi = min(w_hi, w_max_e);
   }

@@ -108,22 +108,31 @@ void fwd_kernel(const FwdArgs a) {
   // ---- this lane's query rows and key intervals ----------------------------------
   const int wq0 = q0 + wid * C::kQW;
   int qrow[QSUB], kst[QSUB], ken[QSUB];
-  int w_min_s = Nk, w_max_s = 0, w_min_e = Nk, w_max_e = 0;
 #pragma unroll
   for (int qs = 0; qs < QSUB; ++qs) {
     qrow[qs] = wq0 + qs * 32 + n;
     kst[qs] = 0;
     ken[qs] = Nk;
-    if (ranged) {
-      if (qrow[qs] < Nq) {
-        kst[qs] = min(max(a.key_start[qrow[qs]], 0), Nk);
-        ken[qs] = min(max(a.key_end[qrow[qs]], 0), Nk);
-        w_min_s = min(w_min_s, kst[qs]);
-        w_max_s = max(w_max_s, kst[qs]);
-        w_min_e = min(w_min_e, ken[qs]);
-        w_max_e = max(w_max_e, ken[qs]);
-      }
+    if (ranged && qrow[qs] < Nq) {
+      kst[qs] = min(max(a.key_start[qrow[qs]], 0), Nk);
+      ken[qs] = min(max(a.key_end[qrow[qs]], 0), Nk);
     }
+  }
+  // wave-uniform summaries of the rows' key intervals (rows past the end take no part);
+  // per-lane partials live only inside the uniform branch, so the results stay scalar
+  int w_min_s = Nk, w_max_s = 0, w_min_e = Nk, w_max_e = 0;
+  if (ranged) {
+    int s0 = Nk, s1 = 0, e0 = Nk, e1 = 0;
+#pragma unroll
+    for (int qs = 0; qs < QSUB; ++qs)
+      if (qrow[qs] < Nq) {
+        s0 = min(s0, kst[qs]); s1 = max(s1, kst[qs]);
+        e0 = min(e0, ken[qs]); e1 = max(e1, ken[qs]);
+      }
+    w_min_s = wave_min(s0);
+    w_max_s = wave_max(s1);
+    w_min_e = wave_min(e0);
+    w_max_e = wave_max(e1);
   }
   const bool wave_live = wq0 < Nq;
   const int wq_last = min(wq0 + C::kQW, Nq) - 1;
@@ -135,10 +144,6 @@ void fwd_kernel(const FwdArgs a) {
     w_full_c = max(0, min(Nk, wq0 + off + 1));
   }
   if (ranged) {
-    w_min_s = wave_min(w_min_s);
-    w_max_s = wave_max(w_max_s);
-    w_min_e = wave_min(w_min_e);
-    w_max_e = wave_max(w_max_e);
     w_lo = max(w_lo, w_min_s);
     w_hi = min(w_hi, w_max_e);
   }
@@ -504,11 +509,19 @@ void fwd16_kernel(const FwdArgs a) {
   const int wq0 = qb * C::kBR + wid * 32;
   const int qrow = wq0 + n;
   int kst = 0, ken = Nk;
+  // wave-uniform summaries of the rows' key intervals (rows past the end take no part);
+  // computed inside the uniform branch so they stay scalar
   int w_min_s = Nk, w_max_s = 0, w_min_e = Nk, w_max_e = 0;
-  if (ranged && qrow < Nq) {
-    kst = min(max(a.key_start[qrow], 0), Nk);
-    ken = min(max(a.key_end[qrow], 0), Nk);
-    w_min_s = kst; w_max_s = kst; w_min_e = ken; w_max_e = ken;
+  if (ranged) {
+    const bool in = qrow < Nq;
+    if (in) {
+      kst = min(max(a.key_start[qrow], 0), Nk);
+      ken = min(max(a.key_end[qrow], 0), Nk);
+    }
+    w_min_s = wave_min(in ? kst : Nk);
+    w_max_s = wave_max(in ? kst : 0);
+    w_min_e = wave_min(in ? ken : Nk);
+    w_max_e = wave_max(in ? ken : 0);
   }
   const bool wave_live = wq0 < Nq;
   const int wq_last = min(wq0 + 32, Nq) - 1;
@@ -518,10 +531,6 @@ void fwd16_kernel(const FwdArgs a) {
     w_full_c = max(0, min(Nk, wq0 + off + 1));
   }
   if (ranged) {
-    w_min_s = wave_min(w_min_s);
-    w_max_s = wave_max(w_max_s);
-    w_min_e = wave_min(w_min_e);
-    w_max_e = wave_max(w_max_e);
     w_lo = max(w_lo, w_min_s);
     w_hi = min(w_hi, w_max_e);
   }
