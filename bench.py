@@ -9,7 +9,8 @@ FLOP convention: forward 4*B*H*N_q*N_k*d halved for causal; backward 2.5x forwar
 The roofline object describes the dominant kernel, timed with HIP events recorded on
 the stream the kernels run on; its achieved rate uses the algorithmic FLOPs of that
 kernel (see ALG_FLOPS below). The CPU baseline times the float64 oracle (fwd + bwd)
-on a bounded sample of whole (b, h) heads of the same workload.
+on a bounded sample of whole (b, h) heads of the same workload. A supplementary list
+times the forward on short sequences and decode-like shapes (compulsory-byte GB/s).
 """
 
 from __future__ import annotations
@@ -34,8 +35,8 @@ PEAK_HBM_GBS = 8000.0
 # the kernel source they were measured on. A changed source means stale counters -> null.
 TRAFFIC = {
     # kernel: (source hash, bytes read, bytes written) -- profiles/attention_fwd_bwd_bf16_causal_B2H16N8192d128.md
-    "fwd": ("f3d5f6e00480f8b8", 267.0e6, 68.2e6),
-    "bwd_dkdv": ("d1cc67f2293a6d89", 276.1e6, 268.4e6),
+    "fwd": ("0bba3ed4c131c112", 266.7e6, 68.2e6),
+    "bwd_dkdv": ("d1cc67f2293a6d89", 275.4e6, 268.4e6),
     "bwd_dq": ("d1cc67f2293a6d89", 396.0e6, 134.5e6),
 }
 
@@ -64,6 +65,12 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target wall time of the CPU-oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-hbm-shapes", action="store_true",
+                    help="skip the supplementary short-N and decode-like forward timings")
+    ap.add_argument("--hbm-only", action="store_true",
+                    help="only time the supplementary shapes and print them as one JSON line")
+    ap.add_argument("--hbm-filter", default="",
+                    help="time only the supplementary shapes whose name contains this text")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 256 MiB device-to-device copy 5 times (the known-size "
                          "reference for scaling FETCH_SIZE/WRITE_SIZE counters)")
@@ -92,6 +99,15 @@ def main():
         sys.exit(2)
     if args.calibrate_copy:
         calibrate_copy()
+        return
+    if args.hbm_only:
+        import torch
+        import exact_io_aware_flash_amd as fa
+        fa.load_library()  # fails loudly if the HIP library is missing
+        if not torch.cuda.is_available():
+            print("no GPU visible", file=sys.stderr)
+            sys.exit(1)
+        print(json.dumps({"hbm_shapes": hbm_shapes(fa, torch, args.hbm_filter)}), flush=True)
         return
 
     import numpy as np
@@ -187,6 +203,8 @@ def main():
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic}
 
+    hbm = None if args.no_hbm_shapes else hbm_shapes(fa, torch)
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(w, q, k, v, do, args.cpu_seconds)
@@ -216,8 +234,58 @@ def main():
         "kernels": kernels,
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "hbm_shapes": hbm,
     }
     print(json.dumps(line), flush=True)
+
+
+def hbm_shapes(fa, torch, only=""):
+    """Forward time and compulsory-byte bandwidth on short sequences and decode-like shapes.
+
+    Compulsory bytes: Q, K, V read and O written once (bf16) plus the float32 LSE. Inputs
+    are seeded Gaussian bf16 made on the device; each shape is timed with HIP events on
+    the launch stream (10 warm-up calls, median of 20)."""
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev).manual_seed(1234)
+    shapes = [("short-N", 16, 32, n, n, False) for n in (128, 256, 512)]
+    shapes += [("decode", 8, 32, nq, nk, True) for nq in (1, 16) for nk in (8192, 32768)]
+    out = []
+    for kind, B, H, nq, nk, causal in shapes:
+        d = 128
+        name = f"{kind} B{B} H{H} Nq{nq} Nk{nk} d{d}" + (" causal" if causal else "")
+        if only and only not in name:
+            continue
+        q = torch.randn((B, H, nq, d), device=dev, generator=g).to(torch.bfloat16)
+        k = torch.randn((B, H, nk, d), device=dev, generator=g).to(torch.bfloat16)
+        v = torch.randn((B, H, nk, d), device=dev, generator=g).to(torch.bfloat16)
+        o = torch.empty_like(q)
+        lse = torch.empty((B, H, nq), dtype=torch.float32, device=dev)
+        nbytes = 2 * (2 * B * H * nq * d + 2 * B * H * nk * d) + 4 * B * H * nq
+        paths = [("fa_fwd", lambda: fa.fa_fwd(q, k, v, causal=causal, out=o, lse=lse))]
+        if kind == "decode":
+            n = fa.fa_fwd_split_count(B, H, nq, nk, d, 0)
+            ws = torch.empty(max(fa.fa_fwd_split_workspace_bytes(B, H, nq, nk, d, 0), 1),
+                             dtype=torch.uint8, device=dev)
+            paths.append((f"fa_fwd_split(n={n})",
+                          lambda: fa.fa_fwd_split(q, k, v, causal=causal, out=o, lse=lse,
+                                                  workspace=ws)))
+        for path, fn in paths:
+            for _ in range(10):
+                fn()
+            ts = []
+            for _ in range(20):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                fn()
+                e1.record()
+                e1.synchronize()
+                ts.append(e0.elapsed_time(e1) * 1e3)
+            us = sorted(ts)[len(ts) // 2]
+            out.append({"shape": name, "path": path, "us": round(us, 2),
+                        "GB/s": round(nbytes / (us * 1e-6) / 1e9, 1),
+                        "frac_hbm": round(nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)})
+        del q, k, v, o, lse
+    return out
 
 
 def cpu_baseline(w, q, k, v, do, seconds):

@@ -20,7 +20,8 @@ from typing import Optional, Sequence, Tuple
 import torch
 
 __all__ = [
-    "FaError", "fa_fwd", "fa_bwd", "fa_bwd_workspace_bytes", "fa_mask_summary",
+    "FaError", "fa_fwd", "fa_fwd_split", "fa_fwd_split_count", "fa_fwd_split_workspace_bytes",
+    "fa_bwd", "fa_bwd_workspace_bytes", "fa_mask_summary",
     "FA_BWD_PREP", "FA_BWD_DKDV", "FA_BWD_DQ", "FA_BWD_ALL",
     "fa_status_string", "fa_version", "lib_path", "load_library",
 ]
@@ -72,6 +73,13 @@ def load_library():
     desc_p = ctypes.POINTER(MaskBiasDesc)
     lib.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32, desc_p, i32, vp]
     lib.fa_fwd.restype = i32
+    lib.fa_fwd_split.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32, desc_p,
+                                 i32, i32, vp, ctypes.c_size_t, vp]
+    lib.fa_fwd_split.restype = i32
+    lib.fa_fwd_split_count.argtypes = [i32, i32, i32, i32, i32, i32]
+    lib.fa_fwd_split_count.restype = i32
+    lib.fa_fwd_split_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32]
+    lib.fa_fwd_split_workspace_bytes.restype = ctypes.c_size_t
     lib.fa_bwd_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
     lib.fa_bwd_workspace_bytes.restype = ctypes.c_size_t
     lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, ctypes.c_size_t,
@@ -101,6 +109,15 @@ def fa_version() -> str:
 
 def fa_bwd_workspace_bytes(B: int, H: int, N_q: int, N_k: int, d: int) -> int:
     return int(load_library().fa_bwd_workspace_bytes(B, H, N_q, N_k, d))
+
+
+def fa_fwd_split_count(B: int, H: int, N_q: int, N_k: int, d: int, n_split: int = 0) -> int:
+    return int(load_library().fa_fwd_split_count(B, H, N_q, N_k, d, n_split))
+
+
+def fa_fwd_split_workspace_bytes(B: int, H: int, N_q: int, N_k: int, d: int,
+                                 n_split: int = 0) -> int:
+    return int(load_library().fa_fwd_split_workspace_bytes(B, H, N_q, N_k, d, n_split))
 
 
 def _stream_ptr(stream: Optional[torch.cuda.Stream]) -> int:
@@ -185,6 +202,52 @@ def fa_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = Fal
     del keep
     if st != 0:
         raise FaError(st, "fa_fwd")
+    return out, lse
+
+
+def fa_fwd_split(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
+                 scale: Optional[float] = None, bias_slopes=None,
+                 key_start: Optional[torch.Tensor] = None,
+                 key_end: Optional[torch.Tensor] = None, n_split: int = 0,
+                 workspace: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                 lse: Optional[torch.Tensor] = None,
+                 stream: Optional[torch.cuda.Stream] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Split-key forward (``fa_fwd_split``): same arguments and result as :func:`fa_fwd`,
+    with the keys of every head cut into ``n_split`` ranges (0: automatic) whose partial
+    results are merged on the GPU. ``workspace``: optional uint8 device tensor of at least
+    :func:`fa_fwd_split_workspace_bytes` bytes (allocated here when omitted).
+    """
+    lib = load_library()
+    _check_dev("q", q)
+    if q.dim() != 4:
+        raise ValueError("q must be [B, H, N_q, d]")
+    B, H, N_q, d = q.shape
+    N_k = k.shape[2]
+    if q.dtype not in _DT:
+        raise ValueError(f"unsupported dtype {q.dtype}")
+    _check_dev("k", k, q.dtype, (B, H, N_k, d))
+    _check_dev("v", v, q.dtype, (B, H, N_k, d))
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    _check_dev("out", out, q.dtype, (B, H, N_q, d))
+    if lse is None:
+        lse = torch.empty((B, H, N_q), dtype=torch.float32, device=q.device)
+    _check_dev("lse", lse, torch.float32, (B, H, N_q))
+    need = fa_fwd_split_workspace_bytes(B, H, N_q, N_k, d, n_split)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _check_dev("workspace", workspace, torch.uint8)
+    desc, keep = _desc(bias_slopes, key_start, key_end, H, N_q)
+    st = lib.fa_fwd_split(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                          lse.data_ptr(), B, H, N_q, N_k, d, float(scale), 1 if causal else 0,
+                          ctypes.byref(desc) if desc is not None else None, _DT[q.dtype],
+                          int(n_split), workspace.data_ptr(), workspace.numel(),
+                          _stream_ptr(stream))
+    del keep
+    if st != 0:
+        raise FaError(st, "fa_fwd_split")
     return out, lse
 
 

@@ -6,6 +6,7 @@
 // other way (blog "Apakah Konteks Sehari Penuh Mengalahkan Konteks Sepuluh Menit?",
 // section "Integrasinya delapan baris": a silent fallback to the slow path looks
 // exactly like a slow working model).
+#include <algorithm>
 #include <climits>
 #include <cmath>
 #include <cstring>
@@ -61,6 +62,32 @@ fa_status read_desc(const fa_mask_bias_desc* mb, int H, bool& bias, Args& a) {
   return FA_OK;
 }
 
+// Effective key-range count of the split forward and the keys per range (whole tiles).
+// n_split == 0: about two (b, h, query block, range) units per compute unit (256 CUs; two
+// small-query workgroups fit on one), each range keeping at least four 64-key tiles.
+// Measured on decode-like shapes, 512 units beat both fewer and more.
+int split_plan(int B, int H, int N_q, int N_k, int d, int n_split, int& split_keys) {
+  const long long tiles = (N_k + kFwdTileKeys - 1) / kFwdTileKeys;
+  long long n;
+  if (n_split == 0) {
+    const int rows = fwd16_rows_per_block(d, N_q);
+    const long long units = (long long)B * H * ((N_q + rows - 1) / rows);
+    const long long want = 512;
+    n = std::min(std::max((want + units - 1) / units, 1LL), std::max(tiles / 4, 1LL));
+  } else {
+    n = std::min<long long>(n_split, tiles);
+  }
+  const long long per = (tiles + n - 1) / n;
+  split_keys = (int)(per * kFwdTileKeys);
+  return (int)((N_k + split_keys - 1) / split_keys);
+}
+
+size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+size_t split_part_bytes(int B, int H, int N_q, int d, int n) {
+  return round256((size_t)n * B * H * N_q * d * sizeof(float));
+}
+
 }  // namespace
 
 extern "C" {
@@ -101,6 +128,55 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
   a.B = B; a.H = H; a.Nq = N_q; a.Nk = N_k;
   a.causal = causal ? 1 : 0;
   a.sl2 = scale * 1.4426950408889634f;
+  hipError_t e = launch_fwd(dtype, d, bias, a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+int fa_fwd_split_count(int B, int H, int N_q, int N_k, int d, int n_split) {
+  if (n_split < 0 || check_common(B, H, N_q, N_k, d, 1.f, FA_BF16) != FA_OK) return 0;
+  int sk = 0;
+  return split_plan(B, H, N_q, N_k, d, n_split, sk);
+}
+
+size_t fa_fwd_split_workspace_bytes(int B, int H, int N_q, int N_k, int d, int n_split) {
+  const int n = fa_fwd_split_count(B, H, N_q, N_k, d, n_split);
+  if (n <= 1) return 0;
+  return split_part_bytes(B, H, N_q, d, n) + round256((size_t)n * B * H * N_q * sizeof(float));
+}
+
+fa_status fa_fwd_split(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                       int H, int N_q, int N_k, int d, float scale, int causal,
+                       const fa_mask_bias_desc* mb, fa_dtype dtype, int n_split, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+  if (n_split < 0) return FA_ERR_ARG;
+  fa_status st = check_common(B, H, N_q, N_k, d, scale, dtype);
+  if (st != FA_OK) return st;
+  int split_keys = 0;
+  const int n = split_plan(B, H, N_q, N_k, d, n_split, split_keys);
+  if (n <= 1)
+    return fa_fwd(q, k, v, o, lse, B, H, N_q, N_k, d, scale, causal, mb, dtype, stream);
+  if (!q || !k || !v || !o) return FA_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return FA_ERR_ALIGN;
+  if (lse != nullptr && (reinterpret_cast<uintptr_t>(lse) & 3u)) return FA_ERR_ALIGN;
+  if (dtype == FA_F32) return FA_ERR_UNSUPPORTED;
+  if (workspace == nullptr ||
+      workspace_bytes < fa_fwd_split_workspace_bytes(B, H, N_q, N_k, d, n_split))
+    return FA_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return FA_ERR_ALIGN;
+  FwdArgs a;
+  std::memset(&a, 0, sizeof(a));
+  bool bias = false;
+  st = read_desc(mb, H, bias, a);
+  if (st != FA_OK) return st;
+  a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
+  a.B = B; a.H = H; a.Nq = N_q; a.Nk = N_k;
+  a.causal = causal ? 1 : 0;
+  a.sl2 = scale * 1.4426950408889634f;
+  a.n_split = n;
+  a.split_keys = split_keys;
+  a.o_part = static_cast<float*>(workspace);
+  a.lse_part = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                        split_part_bytes(B, H, N_q, d, n));
   hipError_t e = launch_fwd(dtype, d, bias, a, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }

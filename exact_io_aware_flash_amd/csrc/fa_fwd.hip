@@ -452,15 +452,12 @@ void fwd_kernel(const FwdArgs a) {
 
 // ---------------------------------------------------------------------------------
 // 16-bit forward. K and V tiles are copied straight from HBM into a ring of LDS stages by
-// direct loads (no staging registers), FA_FWD_STAGES - 1 tiles ahead of the one being
+// direct loads (no staging registers), ST - 1 tiles ahead of the one being
 // computed; one barrier per tile. Tiles are swizzled (see DmaTile): K rows feed the A
 // operand of S^T = K Q^T with 16-byte reads, V is gathered with transposing reads for
 // the A operand of O^T = V^T P^T.
 // ---------------------------------------------------------------------------------
-#ifndef FA_FWD_STAGES
-#define FA_FWD_STAGES 4
-#endif
-template <int D_, int BC_, int NW_>
+template <int D_, int BC_, int NW_, int ST_>
 struct Fwd16Cfg {
   static constexpr int D = D_, BC = BC_, NW = NW_;
   static constexpr int kNT = NW * 64;
@@ -469,19 +466,19 @@ struct Fwd16Cfg {
   static constexpr int kDB = D / 32;        // 32-wide d blocks of O^T
   static constexpr int kDK = D / 16;        // k-steps over d for S^T
   static constexpr int kRB = 2 * D;         // bytes per tile row
-  static constexpr int kST = FA_FWD_STAGES;
+  static constexpr int kST = ST_;            // LDS ring stages (ST-1 tiles in flight)
   using Tile = DmaTile<BC, D, NW>;
   static constexpr int kStage = 2 * Tile::kBytes;  // K tile, then V tile
   static_assert(kST >= 2 && kST * kStage <= 160 * 1024, "LDS budget");
 };
 
-template <typename T, int D, int BC, int NW, bool BIAS>
+template <typename T, int D, int BC, int NW, int ST, bool BIAS>
 __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
                           amdgpu_waves_per_eu(2, 2)))
 void fwd16_kernel(const FwdArgs a) {
-  using C = Fwd16Cfg<D, BC, NW>;
+  using C = Fwd16Cfg<D, BC, NW, ST>;
   using E = Elt<T>;
-  constexpr int KB = C::kKB, DB = C::kDB, DK = C::kDK, RB = C::kRB, ST = C::kST;
+  constexpr int KB = C::kKB, DB = C::kDB, DK = C::kDK, RB = C::kRB;
   constexpr int P = ST - 1;                                  // tiles in flight ahead
   constexpr int kOpsPerTile = 2 * C::Tile::kOpsPerWave;      // direct loads per wave per tile
   __shared__ __attribute__((aligned(1024))) char smem[ST * C::kStage];
@@ -495,8 +492,10 @@ void fwd16_kernel(const FwdArgs a) {
   const bool causal = a.causal != 0;
   const bool ranged = a.key_start != nullptr;
 
-  int bh, qb;
-  map_block(blockIdx.x, a.B * a.H, a.nqb, a.sched, true, bh, qb);
+  // work unit = (b, h, query block, key range); heaviest query blocks first
+  int bh, unit;
+  map_block(blockIdx.x, a.B * a.H, a.nqb * a.n_split, a.sched, true, bh, unit);
+  const int qb = unit / a.n_split, split = unit - qb * a.n_split;
   const int head = bh % a.H;
   const T* __restrict__ Q = static_cast<const T*>(a.q) + (size_t)bh * Nq * D;
   const T* __restrict__ K = static_cast<const T*>(a.k) + (size_t)bh * Nk * D;
@@ -533,6 +532,10 @@ void fwd16_kernel(const FwdArgs a) {
   if (ranged) {
     w_lo = max(w_lo, w_min_s);
     w_hi = min(w_hi, w_max_e);
+  }
+  if (a.n_split > 1) {  // this unit's key range (whole tiles)
+    w_lo = max(w_lo, split * a.split_keys);
+    w_hi = min(w_hi, (split + 1) * a.split_keys);
   }
   if (!wave_live || w_hi <= w_lo) { w_lo = Nk; w_hi = 0; }
   if (lane == 0) { wg_win[wid][0] = w_lo; wg_win[wid][1] = w_hi; }
@@ -702,7 +705,26 @@ void fwd16_kernel(const FwdArgs a) {
   // ---- epilogue -----------------------------------------------------------------------
   const float lt = xhalf_sum(l);
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
-  if (qrow < Nq) {
+  if (a.n_split > 1) {
+    // normalised float32 partial of this key range and its LSE (nothing visible in the
+    // range: O = 0, LSE = -inf, which gives it zero weight in the merge)
+    if (qrow < Nq) {
+      const size_t rows = (size_t)a.B * a.H * Nq;
+      const size_t row = (size_t)split * rows + (size_t)bh * Nq + qrow;
+      float* op = a.o_part + row * D;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int d0 = db * 32 + 8 * g4 + 4 * h;
+          *reinterpret_cast<f32x4*>(op + d0) =
+              f32x4{o[db][4 * g4] * inv, o[db][4 * g4 + 1] * inv, o[db][4 * g4 + 2] * inv,
+                    o[db][4 * g4 + 3] * inv};
+        }
+      if (h == 0)
+        a.lse_part[row] = lt > 0.f ? (m2 + __builtin_amdgcn_logf(lt)) * kLn2 : kNegInf;
+    }
+  } else if (qrow < Nq) {
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -769,37 +791,92 @@ static hipError_t launch_cfg(bool bias, FwdArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------------
+// Merge of split-key partials: LSE = log sum_r exp(LSE_r), O = sum_r exp(LSE_r - LSE) O_r.
+// D/4 threads per row, one float4 of the row each; n_split <= ceil(N_k / 64).
+// ---------------------------------------------------------------------------------
+template <typename T, int D>
+__global__ __launch_bounds__(256) void fwd_merge_kernel(const float* __restrict__ o_part,
+                                                        const float* __restrict__ lse_part,
+                                                        T* __restrict__ o, float* __restrict__ lse,
+                                                        int rows, int n_split) {
+  constexpr int TPR = D / 4, RPB = 256 / TPR;
+  const int r = blockIdx.x * RPB + (int)threadIdx.x / TPR;
+  const int c = ((int)threadIdx.x % TPR) * 4;
+  if (r >= rows) return;
+  float m = kNegInf;
+  for (int s = 0; s < n_split; ++s) m = __builtin_fmaxf(m, lse_part[(size_t)s * rows + r]);
+  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+  float den = 0.f;
+  if (m != kNegInf) {
+    for (int s = 0; s < n_split; ++s) {
+      const float ls = lse_part[(size_t)s * rows + r];
+      if (ls == kNegInf) continue;  // nothing visible in that range
+      const float w = fast_exp2((ls - m) * kLog2e);
+      den += w;
+      const f32x4 x = *reinterpret_cast<const f32x4*>(o_part + ((size_t)s * rows + r) * D + c);
+      acc += w * x;
+    }
+  }
+  const float inv = den > 0.f ? 1.f / den : 0.f;
+  using E = Elt<T>;
+  stg8(o + (size_t)r * D + c, u32x2{E::pack2(acc[0] * inv, acc[1] * inv),
+                                    E::pack2(acc[2] * inv, acc[3] * inv)});
+  if (c == 0 && lse != nullptr)
+    lse[r] = den > 0.f ? m + __builtin_amdgcn_logf(den) * kLn2 : kNegInf;
+}
+
+template <typename T, int D>
+static hipError_t launch_merge(const FwdArgs& a, hipStream_t st) {
+  const int rows = a.B * a.H * a.Nq;
+  constexpr int RPB = 256 / (D / 4);
+  hipLaunchKernelGGL((fwd_merge_kernel<T, D>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256),
+                     0, st, a.o_part, a.lse_part, static_cast<T*>(a.o), a.lse, rows, a.n_split);
+  return hipGetLastError();
+}
+
 // float32 configurations (d, BC keys per tile, QSUB 32-row sub-blocks per wave, NW waves,
 // waves per SIMD); 16-bit types use fwd16_kernel below
 #define FA_FWD_CFG_32_D128 128, 32, 1, 4, 1
 #define FA_FWD_CFG_32_D64 64, 32, 1, 4, 1
 
 
-#ifndef FA_FWD_NW128
-#define FA_FWD_NW128 8  // waves per workgroup of the d = 128 forward
-#endif
-template <typename T, int D, int BC, int NW>
+template <typename T, int D, int BC, int NW, int ST>
 static hipError_t launch16(bool bias, FwdArgs& a, hipStream_t st) {
-  using C = Fwd16Cfg<D, BC, NW>;
+  using C = Fwd16Cfg<D, BC, NW, ST>;
+  static_assert(kFwdTileKeys % BC == 0, "split ranges are whole tiles");
   a.nqb = (a.Nq + C::kBR - 1) / C::kBR;
+  if (a.n_split < 1) a.n_split = 1;
   const int BH = a.B * a.H;
   a.sched = (BH % 8 == 0) ? kSchedXcd : kSchedHeadMajor;
-  const dim3 grid((unsigned)(BH * a.nqb)), block(C::kNT);
+  const dim3 grid((unsigned)(BH * a.nqb * a.n_split)), block(C::kNT);
   if (bias)
-    hipLaunchKernelGGL((fwd16_kernel<T, D, BC, NW, true>), grid, block, 0, st, a);
+    hipLaunchKernelGGL((fwd16_kernel<T, D, BC, NW, ST, true>), grid, block, 0, st, a);
   else
-    hipLaunchKernelGGL((fwd16_kernel<T, D, BC, NW, false>), grid, block, 0, st, a);
-  return hipGetLastError();
+    hipLaunchKernelGGL((fwd16_kernel<T, D, BC, NW, ST, false>), grid, block, 0, st, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.n_split == 1) return e;
+  return launch_merge<T, D>(a, st);
+}
+
+// 16-bit configurations: d = 128 with 8 waves x 32 rows, 64-key tiles, 4 stages (128 KB);
+// d = 128 split over key ranges with few query rows: 4 waves, 32-key tiles, 4 stages
+// (64 KB: two workgroups, i.e. two computing waves, per compute unit); d = 64: 4 waves,
+// 64-key tiles, 4 stages (64 KB). For N_q <= kFwdFewRows both d = 128 variants hold the
+// whole head in one query block, so the host's split plan does not depend on the choice.
+template <typename T>
+static hipError_t launch16_for(int d, bool bias, FwdArgs& a, hipStream_t st) {
+  if (d == 64) return launch16<T, 64, 64, 4, 4>(bias, a, st);
+  if (a.Nq <= kFwdFewRows && a.n_split > 1) return launch16<T, 128, 32, 4, 4>(bias, a, st);
+  return launch16<T, 128, 64, 8, 4>(bias, a, st);
 }
 
 hipError_t launch_fwd(fa_dtype dt, int d, bool bias, FwdArgs& a, hipStream_t st) {
   switch (dt) {
     case FA_BF16:
-      return d == 128 ? launch16<__bf16, 128, 64, FA_FWD_NW128>(bias, a, st)
-                      : launch16<__bf16, 64, 64, 4>(bias, a, st);
+      return launch16_for<__bf16>(d, bias, a, st);
     case FA_F16:
-      return d == 128 ? launch16<_Float16, 128, 64, FA_FWD_NW128>(bias, a, st)
-                      : launch16<_Float16, 64, 64, 4>(bias, a, st);
+      return launch16_for<_Float16>(d, bias, a, st);
     case FA_F32:
       return d == 128 ? launch_cfg<float, FA_FWD_CFG_32_D128>(bias, a, st)
                       : launch_cfg<float, FA_FWD_CFG_32_D64>(bias, a, st);

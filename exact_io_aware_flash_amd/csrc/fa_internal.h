@@ -29,7 +29,21 @@ struct FwdArgs {
   int n_slopes;
   float sl2;   // scale * log2(e)
   float slope2[FA_MAX_SLOPES];  // bias slope * log2(e), per head or broadcast
+  // split-key forward (n_split > 1): keys [r * split_keys, (r+1) * split_keys) per range r
+  int n_split;
+  int split_keys;   // multiple of the 64-key tile
+  float* o_part;    // [n_split][B*H*Nq][d] float32 normalised partial outputs
+  float* lse_part;  // [n_split][B*H*Nq] float32 partial LSE (-inf: nothing visible)
 };
+
+// The split-key 16-bit forward uses a smaller workgroup (4 waves, 32-key tiles, 64 KB of
+// LDS, so two workgroups share a compute unit) when a head has at most this many rows.
+constexpr int kFwdFewRows = 64;
+// Query rows one workgroup of the 16-bit forward covers (for N_q <= kFwdFewRows a head is
+// one query block in every configuration).
+inline int fwd16_rows_per_block(int d, int Nq) { return (d == 128 && Nq > kFwdFewRows) ? 256 : 128; }
+// Split ranges are multiples of this many keys (a multiple of every forward tile).
+constexpr int kFwdTileKeys = 64;
 
 struct BwdArgs {
   const void* q;

@@ -116,6 +116,44 @@ FA_API fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, fl
                  int B, int H, int N_q, int N_k, int d, float scale, int causal,
                  const fa_mask_bias_desc* mb, fa_dtype dtype, void* stream);
 
+/* Split-key forward, for shapes with few query rows per head (decode-like: N_q small,
+ * N_k long), where one workgroup per (b, h, query block) leaves most compute units idle.
+ * The keys of every head are cut into n_split consecutive ranges (multiples of 64 keys);
+ * each (b, h, query block, range) computes a partial softmax-normalised output and its
+ * LSE into `workspace`, and a second launch merges them with the same rescaling algebra
+ * as the online softmax: LSE = log sum_r exp(LSE_r), O = sum_r exp(LSE_r - LSE) O_r.
+ * Sources: briefgpt.xyz page for arXiv 2307.08691 (its related abstract on speeding up
+ * the decode phase by spreading one sequence's keys over parallel workers); blog
+ * "Apakah Konteks Sehari Penuh...", sections "FA2: paralelisme" (parallelise along the
+ * sequence when batch x heads alone starves the GPU) and "Pengulangan softmax online"
+ * (partial results combine exactly through their running max and sum).
+ *  All arguments except the three below mean exactly what they mean for fa_fwd, and the
+ *  result equals fa_fwd's up to float32 rounding order.
+ *  n_split: requested number of key ranges; 0 picks a count from the shape. Ranges are
+ *           whole 64-key tiles of equal length (the last one shorter), so the effective
+ *           count (fa_fwd_split_count) can be lower than requested and never exceeds
+ *           ceil(N_k / 64). With an effective count of 1 the call is fa_fwd (workspace
+ *           unused, may be NULL).
+ *  workspace: device, 16-byte aligned, at least fa_fwd_split_workspace_bytes(...) bytes
+ *           for the same sizes and n_split; contents on entry do not matter; the call
+ *           overwrites it. Calls sharing one workspace must not overlap on the device.
+ *  Errors: as fa_fwd; FA_ERR_WORKSPACE if the workspace is NULL or too small (effective
+ *  count > 1); FA_ERR_UNSUPPORTED for float32 inputs with an effective count > 1;
+ *  FA_ERR_ARG if n_split < 0. */
+FA_API fa_status fa_fwd_split(const void* q, const void* k, const void* v, void* o, float* lse,
+                              int B, int H, int N_q, int N_k, int d, float scale, int causal,
+                              const fa_mask_bias_desc* mb, fa_dtype dtype, int n_split,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
+/* Effective key-range count fa_fwd_split uses for this shape and request (n_split = 0:
+ * the automatic choice, about two (b, h, query block, range) units per compute unit,
+ * at least four 64-key tiles per range). Returns 0 for invalid sizes. */
+FA_API int fa_fwd_split_count(int B, int H, int N_q, int N_k, int d, int n_split);
+
+/* Bytes of workspace fa_fwd_split needs: n * B * H * N_q * (d + 1) float32 partials for
+ * the effective count n (0 when n == 1). */
+FA_API size_t fa_fwd_split_workspace_bytes(int B, int H, int N_q, int N_k, int d, int n_split);
+
 /* Bytes of device workspace fa_bwd needs for these sizes (caller allocates). */
 FA_API size_t fa_bwd_workspace_bytes(int B, int H, int N_q, int N_k, int d);
 

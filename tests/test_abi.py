@@ -146,3 +146,54 @@ def test_python_binding_refuses_cpu_tensors():
     q = torch.zeros(1, 1, 4, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         fa.fa_fwd(q, q, q)
+
+
+# ---- split-key forward: range plan, workspace size, validation -----------------------
+
+@pytest.mark.parametrize("shape,n_req,n_eff", [
+    ((8, 32, 1, 8192, 128), 0, 2),      # 256 units -> 2 ranges of 4096 keys
+    ((8, 32, 16, 32768, 128), 0, 2),    # 256 units -> 2 ranges of 16384 keys
+    ((1, 32, 1, 32768, 128), 0, 16),    # 32 units -> 16 ranges
+    ((1, 1, 1, 8192, 128), 0, 32),      # one unit -> capped at 4 tiles per range
+    ((1, 1, 1, 100, 64), 0, 1),         # too short to split
+    ((1, 1, 1, 1000, 64), 7, 6),        # 16 tiles, 3 per range -> 6 ranges
+    ((1, 1, 1, 1000, 64), 1000, 16),    # at most one range per tile
+    ((2, 4, 300, 5000, 64), 3, 3),
+])
+def test_split_count(shape, n_req, n_eff):
+    assert fa.fa_fwd_split_count(*shape, n_req) == n_eff
+
+
+def test_split_count_rejects_invalid_sizes():
+    assert fa.fa_fwd_split_count(1, 1, 1, 1000, 96, 0) == 0
+    assert fa.fa_fwd_split_count(1, 1, 0, 1000, 64, 0) == 0
+    assert fa.fa_fwd_split_count(1, 1, 1, 1000, 64, -1) == 0
+
+
+def test_split_workspace_bytes():
+    # n * B * H * N_q * d float32 partial outputs + n * B * H * N_q float32 LSEs,
+    # each rounded up to 256 bytes; nothing when the effective count is 1
+    assert fa.fa_fwd_split_workspace_bytes(8, 32, 1, 8192, 128, 0) == 2 * 256 * 128 * 4 + 2048
+    assert fa.fa_fwd_split_workspace_bytes(1, 1, 3, 1000, 64, 7) == 4608 + 256
+    assert fa.fa_fwd_split_workspace_bytes(1, 1, 1, 100, 64, 0) == 0
+
+
+def fwd_split(**kw):
+    lib = fa.load_library()
+    a = dict(q=P, k=P, v=P, o=P, lse=P, B=1, H=2, Nq=4, Nk=4096, d=128, scale=0.1, causal=0,
+             mb=None, dtype=fa.FA_BF16, n=8, ws=P, wsb=1 << 24, stream=None)
+    a.update(kw)
+    return lib.fa_fwd_split(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["Nq"],
+                            a["Nk"], a["d"], a["scale"], a["causal"], a["mb"], a["dtype"],
+                            a["n"], a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(n=-1), 10), (dict(q=None), 1), (dict(Nq=0), 2), (dict(d=80), 4),
+    (dict(dtype=fa.FA_F32), 8),
+    (dict(ws=None), 7), (dict(wsb=1024), 7), (dict(ws=MIS), 6), (dict(v=MIS), 6),
+    (dict(scale=float("nan")), 10),
+    (dict(n=1, q=None), 1),  # effective count 1: validated as fa_fwd
+])
+def test_fwd_split_rejects_invalid_arguments(kw, status):
+    assert fwd_split(**kw) == status
