@@ -457,6 +457,14 @@ void fwd_kernel(const FwdArgs a) {
 // operand of S^T = K Q^T with 16-byte reads, V is gathered with transposing reads for
 // the A operand of O^T = V^T P^T.
 // ---------------------------------------------------------------------------------
+#ifndef FA_FWD_KFENCE
+#define FA_FWD_KFENCE 1
+#endif
+#if FA_FWD_KFENCE
+#define FA_SCHED_FENCE() __builtin_amdgcn_sched_barrier(0)
+#else
+#define FA_SCHED_FENCE() ((void)0)
+#endif
 template <int D_, int BC_, int NW_, int ST_>
 struct Fwd16Cfg {
   static constexpr int D = D_, BC = BC_, NW = NW_;
@@ -596,15 +604,22 @@ void fwd16_kernel(const FwdArgs a) {
   // share the rest), running max, exponentials, O^T += V^T P^T.
   auto tile = [&](const char* Ks, const char* Vs, int kt0, bool masked) __attribute__((always_inline)) {
     f32x16 sc[KB];
+    {
+      // Every K operand of the tile is requested before the first MFMA: the scheduler
+      // barrier keeps the compiler from re-interleaving the reads with the MFMAs, which
+      // would leave each MFMA of the first block waiting out a full LDS latency.
+      u32x4 kf[KB][DK];
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-      // all K operands of this 32-key block are requested before the first MFMA uses one
-      u32x4 kf[DK];
+      for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-      for (int ks = 0; ks < DK; ++ks) kf[ks] = lds_ld16(Ks, kb * 32 * RB + ka[ks]);
-      sc[kb] = f32x16{};
+        for (int ks = 0; ks < DK; ++ks) kf[kb][ks] = lds_ld16(Ks, kb * 32 * RB + ka[ks]);
+      FA_SCHED_FENCE();
 #pragma unroll
-      for (int ks = 0; ks < DK; ++ks) sc[kb] = E::mma(kf[ks], qf[ks], sc[kb]);
+      for (int kb = 0; kb < KB; ++kb) {
+        sc[kb] = f32x16{};
+#pragma unroll
+        for (int ks = 0; ks < DK; ++ks) sc[kb] = E::mma(kf[kb][ks], qf[ks], sc[kb]);
+      }
     }
     if constexpr (BIAS) {
       const float base = (float)(qrow - kt0 - 4 * h);
@@ -628,14 +643,17 @@ void fwd16_kernel(const FwdArgs a) {
           sc[kb][g] = (j >= lo && j < hi) ? sc[kb][g] : kNegInf;
         }
     }
+    // The lane's half of the row decides whether the running max must move: some row's
+    // max exceeds m + tau exactly when some half-row's does, so the exchange between the
+    // two wave halves is only needed in the (rare) rescale branch.
     float mx = kNegInf;
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
       for (int g = 0; g < 16; ++g) mx = __builtin_fmaxf(mx, sc[kb][g]);
-    mx = xhalf_max(mx);
-    const float tmax = BIAS ? mx : mx * sl2;
-    if (__builtin_expect(wave_any(tmax > m2 + kTau), 0)) {  // rare after the first tiles
+    const float hmax = BIAS ? mx : mx * sl2;
+    if (__builtin_expect(wave_any(hmax > m2 + kTau), 0)) {  // rare after the first tiles
+      const float tmax = xhalf_max(hmax);  // the whole row
       const float mnew = __builtin_fmaxf(m2, tmax);
       const float alpha = mnew == kNegInf ? 1.f : fast_exp2(m2 - mnew);
       l *= alpha;
