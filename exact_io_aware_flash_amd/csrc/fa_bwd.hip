@@ -101,16 +101,19 @@ __device__ inline int col_lane_off(int lane) {
 // ---------------------------------------------------------------------------------
 // 2. dK, dV: key-block-outer
 // ---------------------------------------------------------------------------------
+// Per stage: Q and dO tiles (BR rows, swizzled, filled by direct loads), then the tile's
+// LSE, D, key_start and key_end (one 4-byte direct load each, BR == 64 == lanes).
 template <int D, int BR>
 struct DkdvLds {
-  static constexpr int RS = BwdStrides<D>::RS, TS = BwdStrides<D>::TS;
-  static constexpr int QR = 0;                 // Q rows (A operand of S = Q K^T)
-  static constexpr int QT = QR + BR * RS;      // Q for column gathers (B operand of dK)
-  static constexpr int DR = QT + BR * TS;      // dO rows (A operand of dP = dO V^T)
-  static constexpr int DT = DR + BR * RS;      // dO for column gathers (B operand of dV)
-  static constexpr int LSE = DT + BR * TS, DLT = LSE + BR * 4, KS = DLT + BR * 4, KE = KS + BR * 4;
+  static constexpr int RB = 2 * D;
+  static constexpr int QT = 0, DT = BR * RB;
+  static constexpr int LSE = 2 * BR * RB, DLT = LSE + BR * 4, KS = DLT + BR * 4, KE = KS + BR * 4;
   static constexpr int STAGE = KE + BR * 4;
 };
+
+#ifndef FA_DKDV_STAGES
+#define FA_DKDV_STAGES 4
+#endif
 
 template <typename T, int D, int BR, int NW, int WPE, bool BIAS>
 __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
@@ -118,13 +121,17 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
 void bwd_dkdv_kernel(const BwdArgs a) {
   using E = Elt<T>;
   using L = DkdvLds<D, BR>;
-  constexpr int NT = NW * 64, BK = 32 * NW, QB = BR / 32, DK = D / 16, DB = D / 32;
-  using TC = TileCopy<BR, D, NT>;
-  static_assert(2 * L::STAGE <= 160 * 1024, "LDS budget");
-  __shared__ __attribute__((aligned(16))) char smem[2 * L::STAGE];
+  using Tile = DmaTile<BR, D, NW>;
+  constexpr int BK = 32 * NW, QB = BR / 32, DK = D / 16, DB = D / 32, RB = L::RB;
+  constexpr int ST = FA_DKDV_STAGES, P = ST - 1;
+  constexpr int kOpsPerTile = 2 * Tile::kOpsPerWave + 1;  // Q, dO windows + one row array
+  static_assert(BR == 64 && NW == 4, "one row array (64 entries) per wave");
+  static_assert(ST * L::STAGE <= 160 * 1024, "LDS budget");
+  __shared__ __attribute__((aligned(1024))) char smem[ST * L::STAGE];
   __shared__ int win[2];
 
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6, n = lane & 31, h = lane >> 5;
+  const int wid_s = wave_id();  // the same index as a scalar, for LDS window bases
   const int Nq = a.Nq, Nk = a.Nk, off = Nk - Nq;
   const bool causal = a.causal != 0, ranged = a.key_start != nullptr;
   int bh, kb;
@@ -134,8 +141,6 @@ void bwd_dkdv_kernel(const BwdArgs a) {
   const T* K = static_cast<const T*>(a.k) + (size_t)bh * Nk * D;
   const T* V = static_cast<const T*>(a.v) + (size_t)bh * Nk * D;
   const T* dO = static_cast<const T*>(a.dout) + (size_t)bh * Nq * D;
-  const float* lse = a.lse + (size_t)bh * Nq;
-  const float* dlt = a.delta + (size_t)bh * Nq;
   const float sl2 = a.sl2;
   const float slope2 = BIAS ? a.slope2[a.n_slopes == 1 ? 0 : head] : 0.f;
 
@@ -180,38 +185,28 @@ void bwd_dkdv_kernel(const BwdArgs a) {
 #pragma unroll
   for (int db = 0; db < DB; ++db) { dv[db] = f32x16{}; dk[db] = f32x16{}; }
 
-  const int r_lane = n * L::RS + 16 * h;        // + (32*qb)*RS + 32*ks
-  const int t_lane = col_lane_off<L::TS>(lane);  // column gathers
-
-  TC tq, tdo;
-  float lse_r = 0.f, dlt_r = 0.f;
-  int ks_r = 0, ke_r = 0;
-  auto load_tile = [&](int t) {
-    const int q0t = t * BR;
-    tq.load(Q, q0t, Nq, tid);
-    tdo.load(dO, q0t, Nq, tid);
-    if (tid < BR) {
-      const int r = min(q0t + tid, Nq - 1);
-      lse_r = lse[r] * kLog2e;
-      dlt_r = dlt[r];
-      if (ranged) {
-        ks_r = min(max(a.key_start[r], 0), Nk);
-        ke_r = min(max(a.key_end[r], 0), Nk);
-      }
+  // LDS offsets inside a swizzled tile (see DmaTile): row reads of query row 32qb + n,
+  // chunk 2ks + h (A operands of S and dP); transposing gathers of 8 query rows of one
+  // d column (B operands of dV += P^T dO and dK += dS^T Q).
+  int ra[DK];
+#pragma unroll
+  for (int ks = 0; ks < DK; ++ks) ra[ks] = n * RB + 16 * ((2 * ks + h) ^ swz<D>(n));
+  int ta[DB][2];
+  {
+    const int q = (lane >> 2) & 3, g16 = (lane >> 4) & 1, lo2 = lane & 3;
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      const int r = 8 * p + 4 * h + q;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+        ta[db][p] = r * RB + 16 * ((4 * db + 2 * g16 + (lo2 >> 1)) ^ swz<D>(r)) + 8 * (lo2 & 1);
     }
-  };
-  auto store_tile = [&](int stage) {
-    char* sb = smem + stage * L::STAGE;
-    tq.template store_natural<L::RS>(sb + L::QR, tid);
-    tq.template store_natural<L::TS>(sb + L::QT, tid);
-    tdo.template store_natural<L::RS>(sb + L::DR, tid);
-    tdo.template store_natural<L::TS>(sb + L::DT, tid);
-    if (tid < BR) {
-      reinterpret_cast<float*>(sb + L::LSE)[tid] = lse_r;
-      reinterpret_cast<float*>(sb + L::DLT)[tid] = dlt_r;
-      reinterpret_cast<int*>(sb + L::KS)[tid] = ks_r;
-      reinterpret_cast<int*>(sb + L::KE)[tid] = ke_r;
-    }
+  }
+  auto cfrag = [&](const char* base, int qb, int st, int db) {
+    const int rows = (32 * qb + 16 * st) * RB;
+    const u32x2 lo = lds_ld8_tr(base, rows + ta[db][0]);
+    const u32x2 hi = lds_ld8_tr(base, rows + ta[db][1]);
+    return u32x4{lo[0], lo[1], hi[0], hi[1]};
   };
 
   // one 32-query block of a tile; MASK: per-element visibility
@@ -222,9 +217,10 @@ void bwd_dkdv_kernel(const BwdArgs a) {
       u32x4 qa[DK], da[DK];
 #pragma unroll
       for (int ks = 0; ks < DK; ++ks) {
-        qa[ks] = lds_ld16(sb + L::QR, r_lane + 32 * qb * L::RS + 32 * ks);
-        da[ks] = lds_ld16(sb + L::DR, r_lane + 32 * qb * L::RS + 32 * ks);
+        qa[ks] = lds_ld16(sb + L::QT, 32 * qb * RB + ra[ks]);
+        da[ks] = lds_ld16(sb + L::DT, 32 * qb * RB + ra[ks]);
       }
+      sched_fence();  // all Q and dO operands in flight before the first MFMA
 #pragma unroll
       for (int ks = 0; ks < DK; ++ks) {
         sc = E::mma(qa[ks], kf[ks], sc);
@@ -242,7 +238,7 @@ void bwd_dkdv_kernel(const BwdArgs a) {
     float p[16], ds[16];
 #pragma unroll
     for (int g = 0; g < 16; ++g) {
-      const float lq = l4[g / 4][g % 4];
+      const float lq = l4[g / 4][g % 4] * kLog2e;
       float x;
       if constexpr (BIAS) {
         const float dist = (float)(q0t + 32 * qb + 4 * h - key) + (float)(8 * (g / 4) + (g % 4));
@@ -254,19 +250,20 @@ void bwd_dkdv_kernel(const BwdArgs a) {
     }
     if constexpr (MASK) {
       int4 st4[4], en4[4];
+      if (ranged) {
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const int r0 = 32 * qb + 8 * q4 + 4 * h;
-        st4[q4] = *reinterpret_cast<const int4*>(sb + L::KS + r0 * 4);
-        en4[q4] = *reinterpret_cast<const int4*>(sb + L::KE + r0 * 4);
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const int r0 = 32 * qb + 8 * q4 + 4 * h;
+          st4[q4] = *reinterpret_cast<const int4*>(sb + L::KS + r0 * 4);
+          en4[q4] = *reinterpret_cast<const int4*>(sb + L::KE + r0 * 4);
+        }
       }
       const int kvis = key < Nk ? 1 : 0;
 #pragma unroll
       for (int g = 0; g < 16; ++g) {
         const int qi = q0t + 32 * qb + res_row(g, h);
-        const int sti = (&st4[g / 4].x)[g % 4], eni = (&en4[g / 4].x)[g % 4];
-        const int lo = ranged ? sti : 0;
-        const int hi = ranged ? eni : Nk;
+        const int lo = ranged ? min(max((&st4[g / 4].x)[g % 4], 0), Nk) : 0;
+        const int hi = ranged ? min(max((&en4[g / 4].x)[g % 4], 0), Nk) : Nk;
         const int cmin = causal ? qi + off : Nk;
         const bool vis = kvis && qi < Nq && key >= lo && key < hi && key <= cmin;
         p[g] = vis ? p[g] : 0.f;
@@ -285,8 +282,8 @@ void bwd_dkdv_kernel(const BwdArgs a) {
       u32x4 ob[DB], qbf[DB];
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        ob[db] = col_frag<L::TS>(sb + L::DT, t_lane, 32 * qb, st, db);
-        qbf[db] = col_frag<L::TS>(sb + L::QT, t_lane, 32 * qb, st, db);
+        ob[db] = cfrag(sb + L::DT, qb, st, db);
+        qbf[db] = cfrag(sb + L::QT, qb, st, db);
       }
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
@@ -296,22 +293,48 @@ void bwd_dkdv_kernel(const BwdArgs a) {
     }
   };
 
-  if (t_lo < t_hi) {
-    load_tile(t_lo);
-    store_tile(0);
+  // ---- ring of ST stages, P = ST-1 query tiles in flight -------------------------------
+  Tile tile_ld;
+  tile_ld.init(wid_s, lane);
+  // wave w brings the tile's row array w: 0 LSE, 1 D, 2 key_start, 3 key_end (without a
+  // range mask waves 2 and 3 load LSE again, so that every wave issues the same count)
+  const float* arr_base;
+  {
+    const float* lse_h = a.lse + (size_t)bh * Nq;
+    const float* dlt_h = a.delta + (size_t)bh * Nq;
+    arr_base = wid_s == 0 ? lse_h : wid_s == 1 ? dlt_h
+             : ranged ? reinterpret_cast<const float*>(wid_s == 2 ? a.key_start : a.key_end) : lse_h;
   }
-  __syncthreads();
+  const int arr_off = wid_s == 0 ? L::LSE : wid_s == 1 ? L::DLT : wid_s == 2 ? L::KS : L::KE;
+  auto stage_of = [&](int t) { return smem + ((t - t_lo) % ST) * L::STAGE; };
+  auto issue = [&](int t) {
+    char* sb = stage_of(t);
+    const int q0t = t * BR;
+    tile_ld.load(Q, q0t, Nq, sb + L::QT, wid_s);
+    tile_ld.load(dO, q0t, Nq, sb + L::DT, wid_s);
+    dma4(arr_base + min(q0t + lane, Nq - 1), sb + arr_off);
+  };
+  auto land = [&](int later) {
+    if (P >= 3 && later >= 3) wait_vmem<(P >= 3 ? 3 : 0) * kOpsPerTile>();
+    else if (P >= 2 && later == 2) wait_vmem<(P >= 2 ? 2 : 0) * kOpsPerTile>();
+    else if (later == 1) wait_vmem<kOpsPerTile>();
+    else wait_vmem<0>();
+    __builtin_amdgcn_s_barrier();
+  };
+#pragma unroll
+  for (int i = 0; i < P; ++i)
+    if (t_lo + i < t_hi) issue(t_lo + i);
+  if (t_lo < t_hi) land(min(P, t_hi - t_lo) - 1);
 
   for (int t = t_lo; t < t_hi; ++t) {
-    const int stage = (t - t_lo) & 1;
-    const bool more = t + 1 < t_hi;
 #pragma unroll
     for (int db = 0; db < DB; ++db) { pin_agpr(dv[db]); pin_agpr(dk[db]); }
 #pragma unroll
     for (int ks = 0; ks < DK; ++ks) { pin_agpr(kf[ks]); pin_agpr(vf[ks]); }
-    if (more) load_tile(t + 1);
+    // the stage of tile t+P held tile t-1, which every wave finished before the barrier
+    if (t + P < t_hi) issue(t + P);
     const int q0t = t * BR;
-    const char* sb = smem + stage * L::STAGE;
+    const char* sb = stage_of(t);
 
     // classify the tile for this wave's keys [kw0, kw1)
     bool skip = kw0 >= Nk;
@@ -334,8 +357,7 @@ void bwd_dkdv_kernel(const BwdArgs a) {
         for (int qb = 0; qb < QB; ++qb) qblock(sb, q0t, qb, std::true_type{});
       }
     }
-    if (more) store_tile(stage ^ 1);
-    __syncthreads();
+    if (t + 1 < t_hi) land(min(t + P, t_hi - 1) - (t + 1));
   }
 
   // epilogue: lane holds column d = 32*db + n for keys kw0 + res_row(g, h)

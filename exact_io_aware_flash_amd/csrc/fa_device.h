@@ -175,12 +175,23 @@ __device__ constexpr int swz(int r) {
   return D == 128 ? 4 * (r & 3) + ((r >> 2) & 3) : 4 * ((r >> 1) & 1) + ((r >> 2) & 3);
 }
 
+// Scheduling fence: the compiler may not move instructions across it. Placed after a
+// batch of LDS operand reads so the reads are all in flight before the MFMAs that use
+// them (otherwise the scheduler interleaves them and each MFMA waits a full LDS latency).
+__device__ inline void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
+
 // Wait until at most N vector-memory operations of this wave are outstanding (direct
 // LDS loads count here; they complete in issue order).
 template <int N>
 __device__ inline void wait_vmem() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// One wave-wide direct load of 4 bytes per lane: lane i fills bytes [4i, 4i+4) of the
+// 256-byte window at `lds` (wave-uniform).
+__device__ inline void dma4(const void* g, char* lds) {
+  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds, 4, 0, 0);
 }
 
 // One wave-wide direct load moves 1 KB: lane i fills bytes [16i, 16i+16) of the window

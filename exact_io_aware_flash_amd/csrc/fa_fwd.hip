@@ -457,14 +457,6 @@ void fwd_kernel(const FwdArgs a) {
 // operand of S^T = K Q^T with 16-byte reads, V is gathered with transposing reads for
 // the A operand of O^T = V^T P^T.
 // ---------------------------------------------------------------------------------
-#ifndef FA_FWD_KFENCE
-#define FA_FWD_KFENCE 1
-#endif
-#if FA_FWD_KFENCE
-#define FA_SCHED_FENCE() __builtin_amdgcn_sched_barrier(0)
-#else
-#define FA_SCHED_FENCE() ((void)0)
-#endif
 template <int D_, int BC_, int NW_, int ST_>
 struct Fwd16Cfg {
   static constexpr int D = D_, BC = BC_, NW = NW_;
@@ -613,7 +605,7 @@ void fwd16_kernel(const FwdArgs a) {
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int ks = 0; ks < DK; ++ks) kf[kb][ks] = lds_ld16(Ks, kb * 32 * RB + ka[ks]);
-      FA_SCHED_FENCE();
+      sched_fence();
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
         sc[kb] = f32x16{};
