@@ -70,35 +70,6 @@ __device__ inline void store_grad4(void* base, size_t idx, bool f32, float v0, f
 }
 
 // ---------------------------------------------------------------------------------
-// Shared LDS conventions: a tile needed as rows (16 bytes per lane, MFMA A operand) is
-// stored row-major with row stride 2*D+16; a tile whose columns are gathered with the
-// transposing load (MFMA operand over the tile's rows) is stored row-major with row stride
-// 2*D+64. Both strides are bank-conflict-free for their access (measured); a tile used
-// both ways is stored twice with plain 16-byte writes.
-// ---------------------------------------------------------------------------------
-template <int D>
-struct BwdStrides {
-  static constexpr int RS = D * 2 + 16;  // row-read copy
-  static constexpr int TS = D * 2 + 64;  // transposing-read copy
-};
-
-// 8 consecutive 16-bit values of column d = 32*db + n over the 8 rows that MFMA k-slots
-// 8h .. 8h+7 stand for (rows r0 + 16*st + 8*p + 4*h + {0..3}, p = 0, 1), gathered with two
-// transposing loads from a row-major tile of row stride TS.
-template <int TS>
-__device__ inline u32x4 col_frag(const char* base, int lane_off, int r0, int st, int db) {
-  const int o = lane_off + (r0 + 16 * st) * TS + 64 * db;
-  const u32x2 lo = lds_ld8_tr(base, o);
-  const u32x2 hi = lds_ld8_tr(base, o + 8 * TS);
-  return u32x4{lo[0], lo[1], hi[0], hi[1]};
-}
-template <int TS>
-__device__ inline int col_lane_off(int lane) {
-  const int h = lane >> 5;
-  return (((lane >> 2) & 3) + 4 * h) * TS + (16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * 2;
-}
-
-// ---------------------------------------------------------------------------------
 // 2. dK, dV: key-block-outer
 // ---------------------------------------------------------------------------------
 // Per stage: Q and dO tiles (BR rows, swizzled, filled by direct loads), then the tile's
@@ -384,14 +355,19 @@ void bwd_dkdv_kernel(const BwdArgs a) {
 // ---------------------------------------------------------------------------------
 // 3. dQ: query-block-outer
 // ---------------------------------------------------------------------------------
+// Per stage: K and V tiles (BC rows each, swizzled, filled by direct loads). K is read
+// both ways: 16-byte rows (A operand of S^T = K Q^T) and transposing gathers (A operand
+// of dQ^T += K^T dS^T); V rows are the A operand of dP^T = V dO^T.
 template <int D, int BC>
 struct DqLds {
-  static constexpr int RS = BwdStrides<D>::RS, TS = BwdStrides<D>::TS;
-  static constexpr int KR = 0;               // K rows (A operand of S^T = K Q^T)
-  static constexpr int VR = KR + BC * RS;    // V rows (A operand of dP^T = V dO^T)
-  static constexpr int KT = VR + BC * RS;    // K for column gathers (A operand of dQ^T = K^T dS^T)
-  static constexpr int STAGE = KT + BC * TS;
+  static constexpr int RB = 2 * D;
+  static constexpr int KT = 0, VT = BC * RB;
+  static constexpr int STAGE = 2 * BC * RB;
 };
+
+#ifndef FA_DQ_STAGES
+#define FA_DQ_STAGES 4
+#endif
 
 template <typename T, int D, int BC, int NW, int WPE, bool BIAS>
 __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
@@ -399,10 +375,12 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
 void bwd_dq_kernel(const BwdArgs a) {
   using E = Elt<T>;
   using L = DqLds<D, BC>;
-  constexpr int NT = NW * 64, BRQ = 32 * NW, KB = BC / 32, DK = D / 16, DB = D / 32;
-  using TC = TileCopy<BC, D, NT>;
-  static_assert(2 * L::STAGE <= 160 * 1024, "LDS budget");
-  __shared__ __attribute__((aligned(16))) char smem[2 * L::STAGE];
+  using Tile = DmaTile<BC, D, NW>;
+  constexpr int BRQ = 32 * NW, KB = BC / 32, DK = D / 16, DB = D / 32, RB = L::RB;
+  constexpr int ST = FA_DQ_STAGES, P = ST - 1;
+  constexpr int kOpsPerTile = 2 * Tile::kOpsPerWave;
+  static_assert(ST * L::STAGE <= 160 * 1024, "LDS budget");
+  __shared__ __attribute__((aligned(1024))) char smem[ST * L::STAGE];
   __shared__ int wg_win[NW][2];
 
   const int tid = threadIdx.x, lane = tid & 63, wid = wave_id(), n = lane & 31, h = lane >> 5;
@@ -470,32 +448,54 @@ void bwd_dq_kernel(const BwdArgs a) {
 #pragma unroll
   for (int db = 0; db < DB; ++db) dqa[db] = f32x16{};
 
-  const int r_lane = n * L::RS + 16 * h;
-  const int t_lane = col_lane_off<L::TS>(lane);
-
-  TC tk, tv;
-  auto load_tile = [&](int t) {
-    tk.load(K, t * BC, Nk, tid);
-    tv.load(V, t * BC, Nk, tid);
+  // LDS offsets inside a swizzled tile: row reads of key row 32kb + n, chunk 2ks + h;
+  // transposing gathers of 8 keys of one d column (K^T fragments).
+  int ra[DK];
+#pragma unroll
+  for (int ks = 0; ks < DK; ++ks) ra[ks] = n * RB + 16 * ((2 * ks + h) ^ swz<D>(n));
+  int ta[DB][2];
+  {
+    const int q = (lane >> 2) & 3, g16 = (lane >> 4) & 1, lo2 = lane & 3;
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      const int r = 8 * p + 4 * h + q;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+        ta[db][p] = r * RB + 16 * ((4 * db + 2 * g16 + (lo2 >> 1)) ^ swz<D>(r)) + 8 * (lo2 & 1);
+    }
+  }
+  auto ktfrag = [&](const char* Ks, int kb, int st, int db) {
+    const int rows = (32 * kb + 16 * st) * RB;
+    const u32x2 lo = lds_ld8_tr(Ks, rows + ta[db][0]);
+    const u32x2 hi = lds_ld8_tr(Ks, rows + ta[db][1]);
+    return u32x4{lo[0], lo[1], hi[0], hi[1]};
   };
-  auto store_tile = [&](int stage) {
-    char* sb = smem + stage * L::STAGE;
-    tk.template store_natural<L::RS>(sb + L::KR, tid);
-    tk.template store_natural<L::TS>(sb + L::KT, tid);
-    tv.template store_natural<L::RS>(sb + L::VR, tid);
-  };
 
-  auto tile = [&](const char* sb, int kt0, bool full) {
+  auto tile = [&](const char* sb, int kt0, bool masked) __attribute__((always_inline)) {
+    const char* Ks = sb + L::KT;
+    const char* Vs = sb + L::VT;
     f32x16 sc[KB], dp[KB];
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
-      sc[kb] = f32x16{};
-      dp[kb] = f32x16{};
+      // each batch of 8 operands is in flight before its MFMAs (fenced), one batch of
+      // registers at a time
+      {
+        u32x4 ka[DK];
 #pragma unroll
-      for (int ks = 0; ks < DK; ++ks) {
-        const int o = r_lane + kb * 32 * L::RS + 32 * ks;
-        sc[kb] = E::mma(lds_ld16(sb + L::KR, o), qf[ks], sc[kb]);
-        dp[kb] = E::mma(lds_ld16(sb + L::VR, o), dof[ks], dp[kb]);
+        for (int ks = 0; ks < DK; ++ks) ka[ks] = lds_ld16(Ks, kb * 32 * RB + ra[ks]);
+        sched_fence();
+        sc[kb] = f32x16{};
+#pragma unroll
+        for (int ks = 0; ks < DK; ++ks) sc[kb] = E::mma(ka[ks], qf[ks], sc[kb]);
+      }
+      {
+        u32x4 va[DK];
+#pragma unroll
+        for (int ks = 0; ks < DK; ++ks) va[ks] = lds_ld16(Vs, kb * 32 * RB + ra[ks]);
+        sched_fence();
+        dp[kb] = f32x16{};
+#pragma unroll
+        for (int ks = 0; ks < DK; ++ks) dp[kb] = E::mma(va[ks], dof[ks], dp[kb]);
       }
     }
 #pragma unroll
@@ -511,7 +511,7 @@ void bwd_dq_kernel(const BwdArgs a) {
         }
         sc[kb][g] = fast_exp2(x);
       }
-      if (!full) {
+      if (masked) {
         const int lo = kst - kt0;
         const int hi = min(min(ken, Nk), causal ? qrow + off + 1 : Nk) - kt0;
 #pragma unroll
@@ -530,33 +530,45 @@ void bwd_dq_kernel(const BwdArgs a) {
         u32x4 da;
 #pragma unroll
         for (int w = 0; w < 4; ++w) da[w] = E::pack2(sc[kb][8 * st + 2 * w], sc[kb][8 * st + 2 * w + 1]);
+        u32x4 kt[DB];
 #pragma unroll
-        for (int db = 0; db < DB; ++db)
-          dqa[db] = E::mma(col_frag<L::TS>(sb + L::KT, t_lane, 32 * kb, st, db), da, dqa[db]);
+        for (int db = 0; db < DB; ++db) kt[db] = ktfrag(Ks, kb, st, db);
+#pragma unroll
+        for (int db = 0; db < DB; ++db) dqa[db] = E::mma(kt[db], da, dqa[db]);
       }
     }
   };
 
-  if (t_lo < t_hi) {
-    load_tile(t_lo);
-    store_tile(0);
-  }
-  __syncthreads();
-
+  Tile tile_ld;
+  tile_ld.init(wid, lane);
+  auto stage_of = [&](int t) { return smem + ((t - t_lo) % ST) * L::STAGE; };
+  auto issue = [&](int t) {
+    char* sb = stage_of(t);
+    tile_ld.load(K, t * BC, Nk, sb + L::KT, wid);
+    tile_ld.load(V, t * BC, Nk, sb + L::VT, wid);
+  };
+  auto land = [&](int later) {
+    if (P >= 3 && later >= 3) wait_vmem<(P >= 3 ? 3 : 0) * kOpsPerTile>();
+    else if (P >= 2 && later == 2) wait_vmem<(P >= 2 ? 2 : 0) * kOpsPerTile>();
+    else if (later == 1) wait_vmem<kOpsPerTile>();
+    else wait_vmem<0>();
+    __builtin_amdgcn_s_barrier();
+  };
+#pragma unroll
+  for (int i = 0; i < P; ++i)
+    if (t_lo + i < t_hi) issue(t_lo + i);
+  if (t_lo < t_hi) land(min(P, t_hi - t_lo) - 1);
   for (int t = t_lo; t < t_hi; ++t) {
-    const int stage = (t - t_lo) & 1;
-    const bool more = t + 1 < t_hi;
-    if (more) load_tile(t + 1);
+    // the stage of tile t+P held tile t-1, which every wave finished before the barrier
+    if (t + P < t_hi) issue(t + P);
     const int kt0 = t * BC, kt1 = kt0 + BC;
     const bool skip = kt0 >= w_hi || kt1 <= w_lo;
     if (!skip) {
       const bool full = kt1 <= Nk && kt1 <= w_full_c &&
                         (!ranged || (w_max_s <= kt0 && w_min_e >= kt1));
-      const char* sb = smem + stage * L::STAGE;
-      tile(sb, kt0, full);
+      tile(stage_of(t), kt0, !full);
     }
-    if (more) store_tile(stage ^ 1);
-    __syncthreads();
+    if (t + 1 < t_hi) land(min(t + P, t_hi - 1) - (t + 1));
   }
 
   // epilogue: lane holds query qrow, registers d = 32*db + res_row(g, h)
