@@ -35,9 +35,9 @@ PEAK_HBM_GBS = 8000.0
 # the kernel source they were measured on. A changed source means stale counters -> null.
 TRAFFIC = {
     # kernel: (source hash, bytes read, bytes written) -- profiles/attention_fwd_bwd_bf16_causal_B2H16N8192d128.md
-    "fwd": ("0bba3ed4c131c112", 266.7e6, 68.2e6),
-    "bwd_dkdv": ("d1cc67f2293a6d89", 275.4e6, 268.4e6),
-    "bwd_dq": ("d1cc67f2293a6d89", 396.0e6, 134.5e6),
+    "fwd": ("c28a501f06ec9725", 264.8e6, 68.2e6),
+    "bwd_dkdv": ("6f293c039d042386", 270.9e6, 268.4e6),
+    "bwd_dq": ("6f293c039d042386", 393.2e6, 134.2e6),
 }
 
 
