@@ -185,7 +185,8 @@ size_t fa_bwd_workspace_bytes(int B, int H, int N_q, int N_k, int d) {
   (void)N_k; (void)d;
   if (B < 1 || H < 1 || N_q < 1) return 0;
   // delta = rowsum(dO * O) (one float per query row) + the key-range summary of every
-  // 64-row query tile (4 int32), each rounded up to 256 bytes
+  // 64-row query tile (4 int32) + LSE * log2(e) (one float per query row), each rounded
+  // up to 256 bytes
   return bwd_workspace_bytes(B, H, N_q);
 }
 
@@ -223,6 +224,7 @@ fa_status fa_bwd_phases(int phases, const void* q, const void* k, const void* v,
   a.q = q; a.k = k; a.v = v; a.o = o; a.dout = dout; a.lse = lse;
   a.delta = static_cast<float*>(workspace);
   a.qsum = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + bwd_qsum_offset(B, H, N_q));
+  a.lse2 = reinterpret_cast<float*>(static_cast<char*>(workspace) + bwd_lse2_offset(B, H, N_q));
   a.dq = dq; a.dk = dk; a.dv = dv;
   a.B = B; a.H = H; a.Nq = N_q; a.Nk = N_k;
   a.causal = causal ? 1 : 0;

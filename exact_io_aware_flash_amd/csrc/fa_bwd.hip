@@ -30,10 +30,13 @@ namespace fa {
 // ---------------------------------------------------------------------------------
 // 1. D = rowsum(dO * O)
 // ---------------------------------------------------------------------------------
+// Also writes LSE * log2(e) per row (the exponent offset the dK/dV pass uses).
 template <typename T, int D>
 __global__ __launch_bounds__(256) void bwd_prep_kernel(const T* __restrict__ o,
                                                        const T* __restrict__ dout,
-                                                       float* __restrict__ delta, int rows) {
+                                                       const float* __restrict__ lse,
+                                                       float* __restrict__ delta,
+                                                       float* __restrict__ lse2, int rows) {
   constexpr int TPR = D / 8;  // threads per row, 8 elements (16 bytes) each
   constexpr int RPB = 256 / TPR;
   const int row = blockIdx.x * RPB + (int)threadIdx.x / TPR;
@@ -55,7 +58,10 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const T* __restrict__ o,
   }
 #pragma unroll
   for (int s = TPR / 2; s >= 1; s >>= 1) acc += __shfl_xor(acc, s, 64);
-  if (row < rows && c == 0) delta[row] = acc;
+  if (row < rows && c == 0) {
+    delta[row] = acc;
+    lse2[row] = lse[row] * kLog2e;
+  }
 }
 
 // Stores 4 consecutive float gradients (converted as requested).
@@ -73,7 +79,7 @@ __device__ inline void store_grad4(void* base, size_t idx, bool f32, float v0, f
 // 2. dK, dV: key-block-outer
 // ---------------------------------------------------------------------------------
 // Per stage: Q and dO tiles (BR rows, swizzled, filled by direct loads), then the tile's
-// LSE, D, key_start and key_end (one 4-byte direct load each, BR == 64 == lanes).
+// LSE*log2(e), D, key_start and key_end (one 4-byte direct load each, BR == 64 == lanes).
 template <int D, int BR>
 struct DkdvLds {
   static constexpr int RB = 2 * D;
@@ -209,7 +215,7 @@ void bwd_dkdv_kernel(const BwdArgs a) {
     float p[16], ds[16];
 #pragma unroll
     for (int g = 0; g < 16; ++g) {
-      const float lq = l4[g / 4][g % 4] * kLog2e;
+      const float lq = l4[g / 4][g % 4];  // already in log2 units
       float x;
       if constexpr (BIAS) {
         const float dist = (float)(q0t + 32 * qb + 4 * h - key) + (float)(8 * (g / 4) + (g % 4));
@@ -267,11 +273,12 @@ void bwd_dkdv_kernel(const BwdArgs a) {
   // ---- ring of ST stages, P = ST-1 query tiles in flight -------------------------------
   Tile tile_ld;
   tile_ld.init(wid_s, lane);
-  // wave w brings the tile's row array w: 0 LSE, 1 D, 2 key_start, 3 key_end (without a
-  // range mask waves 2 and 3 load LSE again, so that every wave issues the same count)
+  // wave w brings the tile's row array w: 0 LSE*log2(e), 1 D, 2 key_start, 3 key_end
+  // (without a range mask waves 2 and 3 load the first array again, so that every wave
+  // issues the same count)
   const float* arr_base;
   {
-    const float* lse_h = a.lse + (size_t)bh * Nq;
+    const float* lse_h = a.lse2 + (size_t)bh * Nq;  // LSE * log2(e), from the prep pass
     const float* dlt_h = a.delta + (size_t)bh * Nq;
     arr_base = wid_s == 0 ? lse_h : wid_s == 1 ? dlt_h
              : ranged ? reinterpret_cast<const float*>(wid_s == 2 ? a.key_start : a.key_end) : lse_h;
@@ -595,9 +602,12 @@ constexpr int kDkdvBR = 64;  // query rows per LDS tile of the dK/dV pass
 size_t bwd_qsum_offset(int B, int H, int Nq) {
   return (((size_t)B * H * Nq * sizeof(float)) + 255) & ~(size_t)255;
 }
-size_t bwd_workspace_bytes(int B, int H, int Nq) {
+size_t bwd_lse2_offset(int B, int H, int Nq) {
   const size_t nt = (size_t)(Nq + kDkdvBR - 1) / kDkdvBR;
   return bwd_qsum_offset(B, H, Nq) + ((nt * 4 * sizeof(int32_t) + 255) & ~(size_t)255);
+}
+size_t bwd_workspace_bytes(int B, int H, int Nq) {
+  return bwd_lse2_offset(B, H, Nq) + (((size_t)B * H * Nq * sizeof(float) + 255) & ~(size_t)255);
 }
 
 template <typename T, int D, int DKDV_NW, int DKDV_WPE, int DQ_BC, int DQ_NW, int DQ_WPE>
@@ -608,7 +618,8 @@ static hipError_t launch_bwd_t(bool bias, int phases, BwdArgs& a, hipStream_t st
   hipError_t e = hipSuccess;
   if (phases & FA_BWD_PREP) {
     hipLaunchKernelGGL((bwd_prep_kernel<T, D>), dim3((rows + RPB - 1) / RPB), dim3(256), 0, st,
-                       static_cast<const T*>(a.o), static_cast<const T*>(a.dout), a.delta, rows);
+                       static_cast<const T*>(a.o), static_cast<const T*>(a.dout), a.lse, a.delta,
+                       a.lse2, rows);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (a.key_start != nullptr) {

@@ -53,6 +53,7 @@ struct BwdArgs {
   const void* dout;
   const float* lse;
   float* delta;   // [B,H,Nq] rowsum(dO * O), workspace
+  float* lse2;    // [B,H,Nq] LSE * log2(e), workspace
   int32_t* qsum;  // key-range summary per query tile of the dK/dV pass, workspace
   void* dq;
   void* dk;
@@ -76,8 +77,10 @@ hipError_t launch_bwd(fa_dtype dt, int d, bool bias, int phases, BwdArgs& a, hip
 hipError_t launch_mask_summary(const int32_t* ks, const int32_t* ke, int Nq, int Nk, int block,
                                int32_t* out, hipStream_t st);
 
-// Backward workspace layout: delta at offset 0, key-range summary at bwd_qsum_offset.
+// Backward workspace layout: delta at offset 0, key-range summary at bwd_qsum_offset,
+// LSE * log2(e) at bwd_lse2_offset.
 size_t bwd_qsum_offset(int B, int H, int Nq);
+size_t bwd_lse2_offset(int B, int H, int Nq);
 size_t bwd_workspace_bytes(int B, int H, int Nq);
 
 }  // namespace fa

@@ -46,10 +46,10 @@ def test_status_strings_and_version():
 
 
 def test_workspace_bytes():
-    # delta (one float per query row) + key-range summary (4 int32 per 64-row tile),
-    # each rounded up to 256 bytes
-    assert fa.fa_bwd_workspace_bytes(2, 16, 8192, 8192, 128) == 2 * 16 * 8192 * 4 + 2048
-    assert fa.fa_bwd_workspace_bytes(1, 1, 3, 5, 64) == 512
+    # delta (one float per query row) + key-range summary (4 int32 per 64-row tile) +
+    # LSE * log2(e) (one float per query row), each rounded up to 256 bytes
+    assert fa.fa_bwd_workspace_bytes(2, 16, 8192, 8192, 128) == 2 * (2 * 16 * 8192 * 4) + 2048
+    assert fa.fa_bwd_workspace_bytes(1, 1, 3, 5, 64) == 768
     assert fa.fa_bwd_workspace_bytes(0, 1, 3, 5, 64) == 0
 
 
