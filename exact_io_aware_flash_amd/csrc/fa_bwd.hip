@@ -302,7 +302,12 @@ void bwd_dkdv_kernel(const BwdArgs a) {
 #pragma unroll
   for (int i = 0; i < P; ++i)
     if (t_lo + i < t_hi) issue(t_lo + i);
-  if (t_lo < t_hi) land(min(P, t_hi - t_lo) - 1);
+  // The K and V fragments and every prologue tile land here. Waiting for all of them
+  // (rather than for the first tile only) leaves no register load outstanding once the
+  // loop starts, so the compiler has no reason to put a full vector-memory wait, which
+  // would also wait for the ring's loads in flight, in front of the loop's MFMAs.
+  wait_vmem<0>();
+  __builtin_amdgcn_s_barrier();
 
   for (int t = t_lo; t < t_hi; ++t) {
 #pragma unroll

@@ -481,8 +481,26 @@ void fwd16_kernel(const FwdArgs a) {
   constexpr int KB = C::kKB, DB = C::kDB, DK = C::kDK, RB = C::kRB;
   constexpr int P = ST - 1;                                  // tiles in flight ahead
   constexpr int kOpsPerTile = 2 * C::Tile::kOpsPerWave;      // direct loads per wave per tile
-  __shared__ __attribute__((aligned(1024))) char smem[ST * C::kStage];
+  // One LDS array per ring stage, and a loop unrolled over the stages so that every
+  // access names its array: the compiler can then tell the stage being read from the
+  // stages the direct loads are filling, and adds no wait on those loads.
+  static_assert(ST >= 2 && ST <= 4, "two to four ring stages");
+  __shared__ __attribute__((aligned(1024))) char stg0[C::kStage];
+  __shared__ __attribute__((aligned(1024))) char stg1[C::kStage];
+  __shared__ __attribute__((aligned(1024))) char stg2[ST > 2 ? C::kStage : 1];
+  __shared__ __attribute__((aligned(1024))) char stg3[ST > 3 ? C::kStage : 1];
   __shared__ int wg_win[NW][2];
+  auto sptr = [&](auto J) -> char* {
+    constexpr int j = decltype(J)::value % ST;
+    if constexpr (j == 0) return stg0;
+    else if constexpr (j == 1) return stg1;
+    else if constexpr (j == 2) return stg2;
+    else return stg3;
+  };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  using I3 = std::integral_constant<int, 3>;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wid = wave_id();
@@ -681,11 +699,11 @@ void fwd16_kernel(const FwdArgs a) {
   };
 
   // ---- main loop: ring of ST stages, P = ST-1 tiles in flight ------------------------
+  // Tile t_lo + i lives in stage i % ST.
   typename C::Tile dt;
   dt.init(wid, lane);
-  auto stage_of = [&](int t) { return smem + ((t - t_lo) % ST) * C::kStage; };
-  auto issue = [&](int t) {
-    char* sb = stage_of(t);
+  auto issue = [&](auto J, int t) __attribute__((always_inline)) {
+    char* sb = sptr(J);
     dt.load(K, t * BC, Nk, sb, wid);
     dt.load(V, t * BC, Nk, sb + C::Tile::kBytes, wid);
   };
@@ -698,18 +716,31 @@ void fwd16_kernel(const FwdArgs a) {
     else wait_vmem<0>();
     __builtin_amdgcn_s_barrier();
   };
-#pragma unroll
-  for (int i = 0; i < P; ++i)
-    if (t_lo + i < t_hi) issue(t_lo + i);
-  if (t_lo < t_hi) land(min(P, t_hi - t_lo) - 1);
-  for (int t = t_lo; t < t_hi; ++t) {
+  if (t_lo < t_hi) issue(I0{}, t_lo);
+  if (t_lo + 1 < t_hi) issue(I1{}, t_lo + 1);
+  if constexpr (P >= 2) if (t_lo + 2 < t_hi) issue(I2{}, t_lo + 2);
+  if constexpr (P >= 3) if (t_lo + 3 < t_hi) issue(I3{}, t_lo + 3);
+  // The Q fragments and every prologue tile land. Waiting for all of them (rather than
+  // for the first tile only) leaves no register load outstanding in the loop, so the
+  // compiler puts no full vector-memory wait, which would also wait for the ring's loads
+  // in flight, in front of the loop's MFMAs.
+  wait_vmem<0>();
+  __builtin_amdgcn_s_barrier();
+  auto step = [&](auto J, int t) __attribute__((always_inline)) {
+    constexpr int j = decltype(J)::value;
     // the stage of tile t+P held tile t-1, which every wave finished before the barrier
-    if (t + P < t_hi) issue(t + P);
+    if (t + P < t_hi) issue(std::integral_constant<int, j + P>{}, t + P);
     if (live_tile(t)) {
-      const char* sb = stage_of(t);
+      const char* sb = sptr(J);
       tile(sb, sb + C::Tile::kBytes, t * BC, !full_tile(t));
     }
     if (t + 1 < t_hi) land(min(t + P, t_hi - 1) - (t + 1));
+  };
+  for (int t = t_lo; t < t_hi; t += ST) {
+    step(I0{}, t);
+    if (t + 1 < t_hi) step(I1{}, t + 1);
+    if constexpr (ST > 2) if (t + 2 < t_hi) step(I2{}, t + 2);
+    if constexpr (ST > 3) if (t + 3 < t_hi) step(I3{}, t + 3);
   }
 
   // ---- epilogue -----------------------------------------------------------------------
