@@ -900,15 +900,42 @@ static hipError_t launch16(bool bias, FwdArgs& a, hipStream_t st) {
   return launch_merge<T, D>(a, st);
 }
 
-// 16-bit configurations: d = 128 with 8 waves x 32 rows, 64-key tiles, 4 stages (128 KB);
-// d = 128 split over key ranges with few query rows: 4 waves, 32-key tiles, 4 stages
-// (64 KB: two workgroups, i.e. two computing waves, per compute unit); d = 64: 4 waves,
-// 64-key tiles, 4 stages (64 KB). For N_q <= kFwdFewRows both d = 128 variants hold the
-// whole head in one query block, so the host's split plan does not depend on the choice.
+// Compute units of the current device (cached per device).
+static int device_cus() {
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cus[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cus[dev] = n;
+  }
+  return cus[dev];
+}
+
+// 16-bit configurations.
+//   d = 64: 4 waves x 32 rows, 64-key tiles, 4 stages (64 KB).
+//   d = 128, few query rows split over key ranges: 4 waves, 32-key tiles, 4 stages
+//     (64 KB: two workgroups, i.e. two computing waves, per compute unit).
+//   d = 128 otherwise: 8 waves x 32 rows, 64-key tiles, 4 stages (128 KB). When a head has
+//     more than kFwdFewRows rows and the grid has fewer than four such 256-row units per
+//     compute unit, or rows carry key ranges (whose visible tiles smaller blocks follow
+//     more closely): 4 waves x 32 rows with 2 stages (64 KB, two workgroups per compute
+//     unit), where twice as many, fuller blocks balance the load better than a deeper ring
+//     helps. With few rows (decode-like) the deeper ring of the first form wins.
+// For N_q <= kFwdFewRows every d = 128 variant holds the whole head in one query block.
 template <typename T>
 static hipError_t launch16_for(int d, bool bias, FwdArgs& a, hipStream_t st) {
   if (d == 64) return launch16<T, 64, 64, 4, 4>(bias, a, st);
-  if (a.Nq <= kFwdFewRows && a.n_split > 1) return launch16<T, 128, 32, 4, 4>(bias, a, st);
+  if (a.Nq <= kFwdFewRows) {
+    if (a.n_split > 1) return launch16<T, 128, 32, 4, 4>(bias, a, st);
+    return launch16<T, 128, 64, 8, 4>(bias, a, st);
+  }
+  const long long units256 =
+      (long long)a.B * a.H * ((a.Nq + 255) / 256) * (a.n_split > 1 ? a.n_split : 1);
+  if (a.key_start != nullptr || units256 < 4LL * device_cus())
+    return launch16<T, 128, 64, 4, 2>(bias, a, st);
   return launch16<T, 128, 64, 8, 4>(bias, a, st);
 }
 

@@ -39,8 +39,9 @@ struct FwdArgs {
 // The split-key 16-bit forward uses a smaller workgroup (4 waves, 32-key tiles, 64 KB of
 // LDS, so two workgroups share a compute unit) when a head has at most this many rows.
 constexpr int kFwdFewRows = 64;
-// Query rows one workgroup of the 16-bit forward covers (for N_q <= kFwdFewRows a head is
-// one query block in every configuration).
+// Nominal query rows per work unit of the 16-bit forward, used to plan the automatic
+// split count (for N_q <= kFwdFewRows a head is one query block in every configuration;
+// for d = 128 and more rows the launch picks 256- or 128-row workgroups by grid size).
 inline int fwd16_rows_per_block(int d, int Nq) { return (d == 128 && Nq > kFwdFewRows) ? 256 : 128; }
 // Split ranges are multiples of this many keys (a multiple of every forward tile).
 constexpr int kFwdTileKeys = 64;

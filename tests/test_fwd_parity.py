@@ -156,6 +156,35 @@ def test_mask_summary_bit_exact(block):
 
 
 # ---------------------------------------------------------------------------
+# many heads of ragged length: for d = 128 the library picks the larger workgroup only
+# for grids with several 256-row blocks per compute unit, so small shapes alone would not
+# reach it; whole sampled heads are checked
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("causal,bias,nq,nk", [(True, False, 300, 300), (False, False, 257, 520),
+                                               (True, True, 520, 257), (False, True, 300, 300)])
+def test_many_heads_ragged(causal, bias, nq, nk):
+    B, H, d = 16, 64, 128
+    dtype = torch.bfloat16
+    seed = 4099 + nq + 3 * nk + (7 if causal else 0) + (11 if bias else 0)
+    q = normal((B, H, nq, d), dtype, seed)
+    k = normal((B, H, nk, d), dtype, seed + 1)
+    v = normal((B, H, nk, d), dtype, seed + 2)
+    scale = 1.0 / math.sqrt(d)
+    slopes = [-0.02 - 0.001 * i for i in range(H)] if bias else None
+    kw = dict(scale=scale, causal=causal)
+    if bias:
+        kw.update(bias_slopes=slopes)
+    o, lse = run(q, k, v, **kw)
+    for (b, h) in ((0, 0), (7, 33), (15, 63)):
+        one = lambda t: np64(t[b:b + 1, h:h + 1])  # noqa: E731
+        o_ref, lse_ref = oracle.attention_forward(
+            one(q), one(k), one(v), scale, causal=causal,
+            bias_slopes=None if slopes is None else np.float32([slopes[h]]).astype(np.float64))
+        assert_fwd_close(one(o), np64(lse[b:b + 1, h:h + 1]), o_ref, lse_ref, dtype,
+                         f"many heads b{b} h{h} {nq}x{nk} c{causal} bias{bias}")
+
+
+# ---------------------------------------------------------------------------
 # full-size workloads: sampled rows of sampled heads against the oracle
 # ---------------------------------------------------------------------------
 def _full_config_check(wid, heads, nrows):
