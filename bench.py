@@ -35,9 +35,9 @@ PEAK_HBM_GBS = 8000.0
 # the kernel source they were measured on. A changed source means stale counters -> null.
 TRAFFIC = {
     # kernel: (source hash, bytes read, bytes written) -- profiles/attention_fwd_bwd_bf16_causal_B2H16N8192d128.md
-    "fwd": ("c28a501f06ec9725", 264.8e6, 68.2e6),
-    "bwd_dkdv": ("6f293c039d042386", 270.9e6, 268.4e6),
-    "bwd_dq": ("6f293c039d042386", 393.2e6, 134.2e6),
+    "fwd": ("63005b5724e828ac", 279.2e6, 68.2e6),
+    "bwd_dkdv": ("a2bfad777433b798", 271.0e6, 268.4e6),
+    "bwd_dq": ("a2bfad777433b798", 392.3e6, 134.2e6),
 }
 
 
