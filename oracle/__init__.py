@@ -8,6 +8,7 @@ of the pages it follows.
 
 from .attention import (  # noqa: F401
     visible_mask,
+    block_visible,
     distance_bias,
     scores,
     attention_forward,

@@ -29,7 +29,9 @@ Sources (the pages are cited by title and section):
   FlashAttention" (the abstract on attention with bias): an additive bias matrix
   added to the query-key scores.
 * briefgpt.xyz page for arXiv 2307.08691, FlashAttention abstract (May 2022):
-  the tiled method extends to block-sparse attention (here: a per-row key range).
+  the tiled method extends to block-sparse attention (here: a per-row key range,
+  and a block bitmap); the related abstract (Jun 2023) on a broad class of sparse
+  patterns including key and query dropping.
 
 Readings where the pages are silent (each is also listed in the design notes):
 
@@ -39,6 +41,10 @@ Readings where the pages are silent (each is also listed in the design notes):
   query row, shared by every batch and head); any integers are allowed, the
   interval is intersected with [0, N_k);
 * causal with N_q != N_k is bottom-right aligned: j <= i + N_k - N_q;
+* block-sparse mask: the score matrix of a head is cut into blocks of block_q rows
+  by block_k keys, and entries of a block whose bitmap byte is zero are masked
+  (an entry is visible when every mask in use allows it); the bitmap is given per
+  (batch, head), per head, or once for all;
 * a row with no visible key has O = 0 and LSE = -inf;
 * LSE is the natural log; the backward pass uses the textbook softmax Jacobian
   (the pages only say that P is recomputed from Q, K and the saved statistics).
@@ -82,6 +88,33 @@ def visible_mask(n_q: int, n_k: int, rows: np.ndarray, causal: bool,
     return vis
 
 
+def block_visible(rows: np.ndarray, n_k: int, blocks) -> np.ndarray:
+    """Boolean [len(rows), n_k] of a block-sparse mask for one (b, h).
+
+    ``blocks`` = (bitmap, block_q, block_k) with bitmap [ceil(N_q/block_q),
+    ceil(N_k/block_k)]: entry (i, j) lies in block (i // block_q, j // block_k) and is
+    visible exactly when that block's byte is non-zero.
+    """
+    bm, bq, bk = blocks
+    bm = np.asarray(bm)
+    rows = np.asarray(rows, dtype=np.int64)
+    j = np.arange(n_k, dtype=np.int64)
+    return bm[rows[:, None] // int(bq), j[None, :] // int(bk)] != 0
+
+
+def _blocks_for(block_mask, b: int, h: int):
+    """The (bitmap, block_q, block_k) of head (b, h) from a [B,H,..], [H,..] or [..] bitmap."""
+    if block_mask is None:
+        return None
+    bm, bq, bk = block_mask
+    bm = np.asarray(bm)
+    if bm.ndim == 4:
+        bm = bm[b, h]
+    elif bm.ndim == 3:
+        bm = bm[h]
+    return bm, bq, bk
+
+
 def distance_bias(rows: np.ndarray, n_k: int, slope: float) -> np.ndarray:
     """Additive bias slope * |i - j| for the given query rows, float64 [len(rows), n_k]."""
     rows = np.asarray(rows, dtype=np.int64)
@@ -91,13 +124,15 @@ def distance_bias(rows: np.ndarray, n_k: int, slope: float) -> np.ndarray:
 
 def scores(q_rows: np.ndarray, k: np.ndarray, scale: float, rows: np.ndarray, n_q: int,
            causal: bool = False, bias_slope: Optional[float] = None,
-           key_start=None, key_end=None) -> np.ndarray:
+           key_start=None, key_end=None, blocks=None) -> np.ndarray:
     """S for one (b, h) and a set of query rows: scale * q k^T + bias, masked to -inf."""
     s = float(scale) * (_f64(q_rows) @ _f64(k).T)
     n_k = k.shape[0]
     if bias_slope is not None:
         s = s + distance_bias(rows, n_k, bias_slope)
     vis = visible_mask(n_q, n_k, rows, causal, key_start, key_end)
+    if blocks is not None:
+        vis = vis & block_visible(rows, n_k, blocks)
     s[~vis] = NEG_INF
     return s
 
@@ -131,12 +166,12 @@ def _chunks(n: int, n_k: int, max_elems: int):
 
 def attention_forward_rows(q, k, v, scale: float, rows: Sequence[int], b: int, h: int,
                            causal: bool = False, bias_slopes=None,
-                           key_start=None, key_end=None):
+                           key_start=None, key_end=None, block_mask=None):
     """O and LSE of selected query rows of one (b, h): ([len(rows), d], [len(rows)])."""
     rows = np.asarray(rows, dtype=np.int64)
     n_q = q.shape[2]
     s = scores(_f64(q[b, h][rows]), _f64(k[b, h]), scale, rows, n_q, causal,
-               _slope_for(bias_slopes, h), key_start, key_end)
+               _slope_for(bias_slopes, h), key_start, key_end, _blocks_for(block_mask, b, h))
     p, m, l = _two_pass_softmax(s)
     o = p @ _f64(v[b, h])
     lse = np.where(l > 0, m + np.log(np.where(l > 0, l, 1.0)), NEG_INF)
@@ -144,7 +179,8 @@ def attention_forward_rows(q, k, v, scale: float, rows: Sequence[int], b: int, h
 
 
 def attention_forward(q, k, v, scale: float, causal: bool = False, bias_slopes=None,
-                      key_start=None, key_end=None, max_chunk_elems: int = 1 << 24):
+                      key_start=None, key_end=None, max_chunk_elems: int = 1 << 24,
+                      block_mask=None):
     """Full forward: O [B,H,N_q,d] float64 and LSE [B,H,N_q] float64.
 
     Inputs are [B,H,N,d] arrays (any float dtype; up-cast exactly to float64).
@@ -158,22 +194,25 @@ def attention_forward(q, k, v, scale: float, causal: bool = False, bias_slopes=N
         for h in range(H):
             for rows in _chunks(n_q, n_k, max_chunk_elems):
                 o[b, h, rows], lse[b, h, rows] = attention_forward_rows(
-                    q, k, v, scale, rows, b, h, causal, bias_slopes, key_start, key_end)
+                    q, k, v, scale, rows, b, h, causal, bias_slopes, key_start, key_end,
+                    block_mask)
     return o, lse
 
 
 def attention_probabilities(q, k, scale: float, b: int = 0, h: int = 0, causal: bool = False,
-                            bias_slopes=None, key_start=None, key_end=None) -> np.ndarray:
+                            bias_slopes=None, key_start=None, key_end=None,
+                            block_mask=None) -> np.ndarray:
     """The full probability matrix P [N_q, N_k] of one (b, h) (small inputs only)."""
     n_q = q.shape[2]
     rows = np.arange(n_q, dtype=np.int64)
     s = scores(_f64(q[b, h]), _f64(k[b, h]), scale, rows, n_q, causal,
-               _slope_for(bias_slopes, h), key_start, key_end)
+               _slope_for(bias_slopes, h), key_start, key_end, _blocks_for(block_mask, b, h))
     return _two_pass_softmax(s)[0]
 
 
 def attention_backward(q, k, v, dout, scale: float, causal: bool = False, bias_slopes=None,
-                       key_start=None, key_end=None, max_chunk_elems: int = 1 << 24):
+                       key_start=None, key_end=None, max_chunk_elems: int = 1 << 24,
+                       block_mask=None):
     """Analytic float64 gradients (dQ, dK, dV) of L = sum(O * dO), each [B,H,N,d].
 
     Textbook softmax Jacobian with P recomputed from Q and K:
@@ -192,7 +231,7 @@ def attention_backward(q, k, v, dout, scale: float, causal: bool = False, bias_s
             for rows in _chunks(n_q, n_k, max_chunk_elems):
                 qr, dor = _f64(q[b, h][rows]), _f64(dout[b, h][rows])
                 s = scores(qr, kb, scale, rows, n_q, causal, _slope_for(bias_slopes, h),
-                           key_start, key_end)
+                           key_start, key_end, _blocks_for(block_mask, b, h))
                 p, _, _ = _two_pass_softmax(s)
                 dv[b, h] += p.T @ dor
                 dp = dor @ vb.T
@@ -204,7 +243,7 @@ def attention_backward(q, k, v, dout, scale: float, causal: bool = False, bias_s
 
 
 def tiled_online_forward(q, k, v, scale: float, br: int, bc: int, causal: bool = False,
-                         bias_slopes=None, key_start=None, key_end=None):
+                         bias_slopes=None, key_start=None, key_end=None, block_mask=None):
     """The pages' tiled loop in float64, as a model of the recurrence the GPU runs.
 
     Blog section "Algoritma Flash Attention": Q is cut into ceil(N/B_r) row
@@ -224,6 +263,7 @@ def tiled_online_forward(q, k, v, scale: float, br: int, bc: int, causal: bool =
     for b in range(B):
         for h in range(H):
             slope = _slope_for(bias_slopes, h)
+            blocks = _blocks_for(block_mask, b, h)
             for r0 in range(0, n_q, br):
                 rows = np.arange(r0, min(n_q, r0 + br), dtype=np.int64)
                 qi = _f64(q[b, h][rows])
@@ -235,7 +275,10 @@ def tiled_online_forward(q, k, v, scale: float, br: int, bc: int, causal: bool =
                     s = float(scale) * (qi @ _f64(k[b, h][cols]).T)
                     if slope is not None:
                         s = s + slope * np.abs(rows[:, None] - cols[None, :]).astype(np.float64)
-                    vis = visible_mask(n_q, n_k, rows, causal, key_start, key_end)[:, cols]
+                    vis = visible_mask(n_q, n_k, rows, causal, key_start, key_end)
+                    if blocks is not None:
+                        vis = vis & block_visible(rows, n_k, blocks)
+                    vis = vis[:, cols]
                     if not vis.any():
                         continue  # fully masked tile: never loaded, contributes nothing
                     s[~vis] = NEG_INF
@@ -273,7 +316,7 @@ SKIP, PARTIAL, FULL = 0, 1, 2
 
 
 def tile_classes(n_q: int, n_k: int, br: int, bc: int, causal: bool = False,
-                 key_start=None, key_end=None) -> np.ndarray:
+                 key_start=None, key_end=None, blocks=None) -> np.ndarray:
     """Brute-force class of every (row block, column block) tile of the score matrix.
 
     SKIP = no visible entry, FULL = every entry visible, PARTIAL otherwise.
@@ -284,6 +327,8 @@ def tile_classes(n_q: int, n_k: int, br: int, bc: int, causal: bool = False,
     for r in range(t_r):
         rows = np.arange(r * br, min(n_q, (r + 1) * br), dtype=np.int64)
         vis = visible_mask(n_q, n_k, rows, causal, key_start, key_end)
+        if blocks is not None:
+            vis = vis & block_visible(rows, n_k, blocks)
         for c in range(t_c):
             blk = vis[:, c * bc:min(n_k, (c + 1) * bc)]
             out[r, c] = FULL if blk.all() else (PARTIAL if blk.any() else SKIP)

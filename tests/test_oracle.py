@@ -35,7 +35,7 @@ def rnd(shape, seed, scale=1.0):
 # softmax(scale * q.k + bias) over the visible keys, then the weighted sum of v.
 # --------------------------------------------------------------------------
 
-def mp_forward_row(qi, K, V, scale, i, n_q, causal, slope, ks, ke):
+def mp_forward_row(qi, K, V, scale, i, n_q, causal, slope, ks, ke, blocks=None):
     n_k, d = len(K), len(K[0])
     vis = []
     for j in range(n_k):
@@ -44,6 +44,10 @@ def mp_forward_row(qi, K, V, scale, i, n_q, causal, slope, ks, ke):
             ok = False
         if ks is not None and not (ks[i] <= j < ke[i]):
             ok = False
+        if blocks is not None:
+            bm, bq, bk = blocks
+            if bm[i // bq][j // bk] == 0:
+                ok = False
         if ok:
             vis.append(j)
     if not vis:
@@ -64,12 +68,12 @@ def mp_forward_row(qi, K, V, scale, i, n_q, causal, slope, ks, ke):
     return out, mpmath.log(z)
 
 
-def mp_forward(q, k, v, scale, causal=False, slope=None, ks=None, ke=None):
+def mp_forward(q, k, v, scale, causal=False, slope=None, ks=None, ke=None, blocks=None):
     n_q, n_k = q.shape[0], k.shape[0]
     O, L = [], []
     for i in range(n_q):
         o, l = mp_forward_row(q[i].tolist(), k.tolist(), v.tolist(), scale, i, n_q, causal,
-                              slope, ks, ke)
+                              slope, ks, ke, blocks)
         O.append(o)
         L.append(l)
     return O, L
@@ -424,3 +428,105 @@ def test_half_of_tiles_skipped_for_range_mask_generator():
     cls = oracle.tile_classes(n, n, 128, 128, key_start=s_.numpy(), key_end=e_.numpy())
     frac = (cls == A.SKIP).mean()
     assert 0.45 <= frac <= 0.55
+
+
+# --------------------------------------------------------------------------
+# block-sparse bitmap mask (briefgpt.xyz page for arXiv 2307.08691: the tiled method
+# extends to block-sparse attention; entries of a zero block are masked)
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("causal,slope", [(False, None), (True, 0.2)])
+def test_block_mask_matches_multiprecision_brute_force(causal, slope):
+    n_q, n_k, d, bq, bk = 7, 11, 3, 2, 3
+    bm = np.array([[1, 0, 1, 1], [0, 1, 0, 0], [0, 0, 0, 0], [1, 1, 0, 1]], dtype=np.uint8)
+    q, k, v = rnd((n_q, d), 310), rnd((n_k, d), 311), rnd((n_k, d), 312)
+    O, L = mp_forward(q, k, v, 0.7, causal, slope, blocks=(bm.tolist(), bq, bk))
+    o, lse = oracle.attention_forward(q[None, None], k[None, None], v[None, None], 0.7,
+                                      causal=causal, bias_slopes=slope, block_mask=(bm, bq, bk))
+    for i in range(n_q):
+        if L[i] == -mpmath.inf:
+            assert lse[0, 0, i] == -np.inf and np.all(o[0, 0, i] == 0.0)
+            continue
+        assert abs(float(L[i]) - lse[0, 0, i]) < 1e-12
+        assert max(abs(float(O[i][c]) - o[0, 0, i, c]) for c in range(d)) < 1e-12
+    assert lse[0, 0, 4] == -np.inf and lse[0, 0, 5] == -np.inf  # block row 2 is empty
+
+
+def test_block_permutation_equals_independent_problems():
+    # query block r sees key block pi(r) only, with non-square blocks: each query block is
+    # then an unmasked attention of its own rows over one slice of the keys
+    bq, bk, nb, d = 3, 5, 4, 4
+    pi = [2, 0, 3, 1]
+    bm = np.zeros((nb, nb), dtype=np.uint8)
+    for r, c in enumerate(pi):
+        bm[r, c] = 1
+    n_q, n_k = bq * nb, bk * nb
+    q, k, v, do = (rnd((1, 2, n, d), 320 + i) for i, n in enumerate((n_q, n_k, n_k, n_q)))
+    o, lse = oracle.attention_forward(q, k, v, 0.45, block_mask=(bm, bq, bk))
+    dq, dk, dv = oracle.attention_backward(q, k, v, do, 0.45, block_mask=(bm, bq, bk))
+    for r, c in enumerate(pi):
+        rs, cs = slice(r * bq, (r + 1) * bq), slice(c * bk, (c + 1) * bk)
+        o_r, l_r = oracle.attention_forward(q[:, :, rs], k[:, :, cs], v[:, :, cs], 0.45)
+        g = oracle.attention_backward(q[:, :, rs], k[:, :, cs], v[:, :, cs], do[:, :, rs], 0.45)
+        assert np.allclose(o[:, :, rs], o_r, atol=1e-14, rtol=0)
+        assert np.allclose(lse[:, :, rs], l_r, atol=1e-14, rtol=0)
+        assert np.allclose(dq[:, :, rs], g[0], atol=1e-13, rtol=0)
+        assert np.allclose(dk[:, :, cs], g[1], atol=1e-13, rtol=0)
+        assert np.allclose(dv[:, :, cs], g[2], atol=1e-13, rtol=0)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_block_mask_with_contiguous_rows_equals_key_ranges(causal):
+    # a bitmap whose row r shows key blocks [a_r, b_r) is the key range [a_r bk, b_r bk)
+    bq, bk, n_q, n_k, d = 4, 6, 14, 27, 3
+    spans = [(0, 2), (1, 5), (3, 3), (2, 4)]
+    bm = np.zeros((4, 5), dtype=np.uint8)
+    for r, (lo, hi) in enumerate(spans):
+        bm[r, lo:hi] = 1
+    ks = np.array([spans[i // bq][0] * bk for i in range(n_q)], dtype=np.int32)
+    ke = np.array([min(spans[i // bq][1] * bk, n_k) for i in range(n_q)], dtype=np.int32)
+    q, k, v, do = (rnd((2, 1, n, d), 330 + i) for i, n in enumerate((n_q, n_k, n_k, n_q)))
+    a = oracle.attention_forward(q, k, v, 0.6, causal=causal, block_mask=(bm, bq, bk))
+    b = oracle.attention_forward(q, k, v, 0.6, causal=causal, key_start=ks, key_end=ke)
+    for x, y in zip(a, b):
+        assert np.array_equal(np.isinf(x), np.isinf(y))
+        assert np.allclose(np.nan_to_num(x, neginf=0.0), np.nan_to_num(y, neginf=0.0), atol=1e-14, rtol=0)
+    ga = oracle.attention_backward(q, k, v, do, 0.6, causal=causal, block_mask=(bm, bq, bk))
+    gb = oracle.attention_backward(q, k, v, do, 0.6, causal=causal, key_start=ks, key_end=ke)
+    for x, y in zip(ga, gb):
+        assert np.allclose(x, y, atol=1e-13, rtol=0)
+
+
+def test_block_mask_per_head_selection():
+    # a [B, H, nbq, nbk] bitmap applies head by head; an all-ones bitmap changes nothing
+    bq = bk = 4
+    q, k, v = rnd((2, 3, 8, 3), 340), rnd((2, 3, 12, 3), 341), rnd((2, 3, 12, 3), 342)
+    bm = (np.random.default_rng(343).random((2, 3, 2, 3)) < 0.6).astype(np.uint8)
+    o, lse = oracle.attention_forward(q, k, v, 0.5, block_mask=(bm, bq, bk))
+    for b in range(2):
+        for h in range(3):
+            one = lambda t: t[b:b + 1, h:h + 1]  # noqa: E731
+            o1, l1 = oracle.attention_forward(one(q), one(k), one(v), 0.5, block_mask=(bm[b, h], bq, bk))
+            assert np.array_equal(o[b, h], o1[0, 0]) and np.array_equal(lse[b, h], l1[0, 0])
+    ones = np.ones((2, 3), dtype=np.uint8)
+    o2, l2 = oracle.attention_forward(q, k, v, 0.5, block_mask=(ones, bq, bk))
+    o3, l3 = oracle.attention_forward(q, k, v, 0.5)
+    assert np.array_equal(o2, o3) and np.array_equal(l2, l3)
+
+
+def test_tiled_online_with_block_mask_equals_two_pass():
+    q, k, v = rnd((1, 2, 37, 5), 350), rnd((1, 2, 53, 5), 351), rnd((1, 2, 53, 5), 352)
+    bm = (np.random.default_rng(353).random((2, 10, 11)) < 0.5).astype(np.uint8)
+    o1, l1 = oracle.attention_forward(q, k, v, 0.4, causal=True, block_mask=(bm, 4, 5))
+    o2, l2 = oracle.tiled_online_forward(q, k, v, 0.4, 8, 10, causal=True, block_mask=(bm, 4, 5))
+    assert np.array_equal(np.isinf(l1), np.isinf(l2))
+    assert np.allclose(o1, o2, atol=1e-13, rtol=0)
+    fin = np.isfinite(l1)
+    assert np.allclose(l1[fin], l2[fin], atol=1e-13, rtol=0)
+
+
+def test_tile_classes_of_a_tile_aligned_bitmap():
+    # tiles that coincide with bitmap blocks are SKIP where the byte is 0, else FULL
+    bm = (np.random.default_rng(360).random((5, 7)) < 0.5).astype(np.uint8)
+    cls = oracle.tile_classes(5 * 8, 7 * 16, 8, 16, blocks=(bm, 8, 16))
+    assert np.array_equal(cls, np.where(bm != 0, A.FULL, A.SKIP))

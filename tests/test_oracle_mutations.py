@@ -71,6 +71,27 @@ def mut_softmax_no_normalise(monkeypatch):
     monkeypatch.setattr(A, "_two_pass_softmax", bad)
 
 
+def mut_block_sizes_swapped(monkeypatch):
+    # rows indexed by block_k and keys by block_q (an IndexError also counts as caught)
+    monkeypatch.setattr(A, "block_visible", lambda rows, n_k, blocks: _orig_block_visible(
+        rows, n_k, (blocks[0], blocks[2], blocks[1])))
+
+
+def mut_block_row_off_by_one(monkeypatch):
+    def bad(rows, n_k, blocks):
+        bm, bq, bk = blocks
+        bm = np.asarray(bm)
+        r = np.minimum((np.asarray(rows)[:, None] + 1) // bq, bm.shape[0] - 1)
+        return bm[r, np.arange(n_k)[None, :] // bk] != 0
+    monkeypatch.setattr(A, "block_visible", bad)
+
+
+def mut_block_bitmap_ignored(monkeypatch):
+    monkeypatch.setattr(A, "_blocks_for", lambda bm, b, h: None)
+
+
+_orig_block_visible = A.block_visible
+
 FWD_PINS = [
     lambda: [pins.test_forward_matches_multiprecision_brute_force(i)
              for i in range(len(pins.CASES))],
@@ -92,5 +113,26 @@ def test_planted_mistake_is_caught(monkeypatch, mutation):
         try:
             pin()
         except AssertionError:
+            caught += 1
+    assert caught >= 1, f"no pin caught {mutation.__name__}"
+
+
+BLOCK_PINS = [
+    lambda: pins.test_block_mask_matches_multiprecision_brute_force(False, None),
+    lambda: pins.test_block_permutation_equals_independent_problems(),
+    lambda: pins.test_block_mask_with_contiguous_rows_equals_key_ranges(True),
+]
+
+
+@pytest.mark.parametrize("mutation", [
+    mut_block_sizes_swapped, mut_block_row_off_by_one, mut_block_bitmap_ignored,
+])
+def test_planted_block_mask_mistake_is_caught(monkeypatch, mutation):
+    mutation(monkeypatch)
+    caught = 0
+    for pin in BLOCK_PINS:
+        try:
+            pin()
+        except (AssertionError, IndexError):
             caught += 1
     assert caught >= 1, f"no pin caught {mutation.__name__}"
