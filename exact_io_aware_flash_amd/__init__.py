@@ -52,6 +52,11 @@ class MaskBiasDesc(ctypes.Structure):
         ("slopes", ctypes.POINTER(ctypes.c_float)),
         ("key_start", ctypes.c_void_p),
         ("key_end", ctypes.c_void_p),
+        ("block_mask", ctypes.c_void_p),
+        ("block_q", ctypes.c_int32),
+        ("block_k", ctypes.c_int32),
+        ("mask_stride_b", ctypes.c_int64),
+        ("mask_stride_h", ctypes.c_int64),
     ]
 
 
@@ -138,12 +143,37 @@ def _check_dev(name: str, t: torch.Tensor, dtype=None, shape=None):
         raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
 
 
-def _desc(bias_slopes, key_start, key_end, H, N_q):
-    """Build the mask/bias descriptor; returns (desc or None, keepalive)."""
-    if bias_slopes is None and key_start is None and key_end is None:
+def _desc(bias_slopes, key_start, key_end, H, N_q, block_mask=None, B=1, N_k=1):
+    """Build the mask/bias descriptor; returns (desc or None, keepalive).
+
+    ``block_mask``: (bitmap, block_q, block_k) with bitmap a contiguous uint8 device tensor
+    [nbq, nbk] (shared), [H, nbq, nbk] (per head) or [B, H, nbq, nbk], where
+    nbq = ceil(N_q / block_q) and nbk = ceil(N_k / block_k); a zero byte masks its block.
+    """
+    if bias_slopes is None and key_start is None and key_end is None and block_mask is None:
         return None, None
     d = MaskBiasDesc()
     keep = []
+    if block_mask is not None:
+        bm, bq, bk = block_mask
+        bq, bk = int(bq), int(bk)
+        if bq <= 0 or bk <= 0:
+            raise ValueError("block sizes must be positive")
+        nbq, nbk = (N_q + bq - 1) // bq, (N_k + bk - 1) // bk
+        _check_dev("block_mask", bm, torch.uint8)
+        if tuple(bm.shape[-2:]) != (nbq, nbk):
+            raise ValueError(f"block_mask must end in ({nbq}, {nbk}), got {tuple(bm.shape)}")
+        if bm.dim() == 2:
+            sb, sh = 0, 0
+        elif bm.dim() == 3 and bm.shape[0] == H:
+            sb, sh = 0, nbq * nbk
+        elif bm.dim() == 4 and tuple(bm.shape[:2]) == (B, H):
+            sb, sh = H * nbq * nbk, nbq * nbk
+        else:
+            raise ValueError("block_mask must be [nbq, nbk], [H, nbq, nbk] or [B, H, nbq, nbk]")
+        d.block_mask = bm.data_ptr()
+        d.block_q, d.block_k = bq, bk
+        d.mask_stride_b, d.mask_stride_h = sb, sh
     d.bias_kind = FA_BIAS_NONE
     d.n_slopes = 1
     d.slopes = None
@@ -169,12 +199,14 @@ def fa_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = Fal
            scale: Optional[float] = None, bias_slopes=None,
            key_start: Optional[torch.Tensor] = None, key_end: Optional[torch.Tensor] = None,
            out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
-           stream: Optional[torch.cuda.Stream] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+           stream: Optional[torch.cuda.Stream] = None,
+           block_mask=None) -> Tuple[torch.Tensor, torch.Tensor]:
     """Exact attention forward on the GPU: returns (O [B,H,N_q,d], LSE [B,H,N_q] float32).
 
     q: [B,H,N_q,d], k/v: [B,H,N_k,d], all of one dtype (float32, float16, bfloat16).
     ``bias_slopes``: float or a list of 1 or H floats, bias = slope * |i - j|.
     ``key_start``/``key_end``: int32 [N_q] device tensors, row i sees keys in [start, end).
+    ``block_mask``: (uint8 bitmap, block_q, block_k), see ``_desc``.
     """
     lib = load_library()
     _check_dev("q", q)
@@ -194,7 +226,7 @@ def fa_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = Fal
     if lse is None:
         lse = torch.empty((B, H, N_q), dtype=torch.float32, device=q.device)
     _check_dev("lse", lse, torch.float32, (B, H, N_q))
-    desc, keep = _desc(bias_slopes, key_start, key_end, H, N_q)
+    desc, keep = _desc(bias_slopes, key_start, key_end, H, N_q, block_mask, B, N_k)
     st = lib.fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
                     B, H, N_q, N_k, d, float(scale), 1 if causal else 0,
                     ctypes.byref(desc) if desc is not None else None, _DT[q.dtype],
@@ -211,7 +243,8 @@ def fa_fwd_split(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool
                  key_end: Optional[torch.Tensor] = None, n_split: int = 0,
                  workspace: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
                  lse: Optional[torch.Tensor] = None,
-                 stream: Optional[torch.cuda.Stream] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+                 stream: Optional[torch.cuda.Stream] = None,
+                 block_mask=None) -> Tuple[torch.Tensor, torch.Tensor]:
     """Split-key forward (``fa_fwd_split``): same arguments and result as :func:`fa_fwd`,
     with the keys of every head cut into ``n_split`` ranges (0: automatic) whose partial
     results are merged on the GPU. ``workspace``: optional uint8 device tensor of at least
@@ -239,7 +272,7 @@ def fa_fwd_split(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
     _check_dev("workspace", workspace, torch.uint8)
-    desc, keep = _desc(bias_slopes, key_start, key_end, H, N_q)
+    desc, keep = _desc(bias_slopes, key_start, key_end, H, N_q, block_mask, B, N_k)
     st = lib.fa_fwd_split(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                           lse.data_ptr(), B, H, N_q, N_k, d, float(scale), 1 if causal else 0,
                           ctypes.byref(desc) if desc is not None else None, _DT[q.dtype],
@@ -256,7 +289,8 @@ def fa_bwd(dout: torch.Tensor, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor
            scale: Optional[float] = None, bias_slopes=None,
            key_start: Optional[torch.Tensor] = None, key_end: Optional[torch.Tensor] = None,
            grad_dtype: torch.dtype = torch.float32, workspace: Optional[torch.Tensor] = None,
-           grads=None, phases: int = FA_BWD_ALL, stream: Optional[torch.cuda.Stream] = None):
+           grads=None, phases: int = FA_BWD_ALL, stream: Optional[torch.cuda.Stream] = None,
+           block_mask=None):
     """Backward by recomputation: returns (dQ, dK, dV) in ``grad_dtype``.
 
     ``o`` and ``lse`` are the outputs of :func:`fa_fwd` for the same inputs.
@@ -288,7 +322,7 @@ def fa_bwd(dout: torch.Tensor, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor
     wsb = fa_bwd_workspace_bytes(B, H, N_q, N_k, d)
     if workspace is None:
         workspace = torch.empty(max(wsb, 16), dtype=torch.uint8, device=q.device)
-    desc, keep = _desc(bias_slopes, key_start, key_end, H, N_q)
+    desc, keep = _desc(bias_slopes, key_start, key_end, H, N_q, block_mask, B, N_k)
     st = lib.fa_bwd_phases(int(phases), q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
                     dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
                     _DT[grad_dtype], workspace.data_ptr(), workspace.numel() * workspace.element_size(),

@@ -34,13 +34,31 @@ fa_status check_common(int B, int H, int N_q, int N_k, int d, float scale, fa_dt
 
 // Fills the bias/mask part of an argument block; returns the status.
 template <class Args>
-fa_status read_desc(const fa_mask_bias_desc* mb, int H, bool& bias, Args& a) {
+fa_status read_desc(const fa_mask_bias_desc* mb, int H, int N_q, int N_k, fa_dtype dtype,
+                    bool& bias, Args& a) {
   bias = false;
   a.key_start = nullptr;
   a.key_end = nullptr;
   a.n_slopes = 1;
   for (int i = 0; i < FA_MAX_SLOPES; ++i) a.slope2[i] = 0.f;
+  a.bmask = nullptr;
+  a.bq = a.bk = 64;
+  a.nkb = 0;
+  a.bm_sb = a.bm_sh = 0;
   if (mb == nullptr) return FA_OK;
+  if (mb->block_mask != nullptr) {
+    if (mb->block_q < 64 || mb->block_q % 64 != 0 || mb->block_k < 64 || mb->block_k % 64 != 0)
+      return FA_ERR_MASK;
+    if (mb->mask_stride_b < 0 || mb->mask_stride_h < 0) return FA_ERR_MASK;
+    if (dtype == FA_F32) return FA_ERR_UNSUPPORTED;
+    if (N_q > FA_MAX_SPARSE_N || N_k > FA_MAX_SPARSE_N) return FA_ERR_UNSUPPORTED;
+    a.bmask = mb->block_mask;
+    a.bq = mb->block_q;
+    a.bk = mb->block_k;
+    a.nkb = (N_k + mb->block_k - 1) / mb->block_k;
+    a.bm_sb = mb->mask_stride_b;
+    a.bm_sh = mb->mask_stride_h;
+  }
   if (mb->bias_kind != FA_BIAS_NONE && mb->bias_kind != FA_BIAS_DIST_LINEAR) return FA_ERR_MASK;
   if ((mb->key_start == nullptr) != (mb->key_end == nullptr)) return FA_ERR_MASK;
   if (mb->key_start != nullptr) {
@@ -122,7 +140,7 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
   FwdArgs a;
   std::memset(&a, 0, sizeof(a));
   bool bias = false;
-  st = read_desc(mb, H, bias, a);
+  st = read_desc(mb, H, N_q, N_k, dtype, bias, a);
   if (st != FA_OK) return st;
   a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
   a.B = B; a.H = H; a.Nq = N_q; a.Nk = N_k;
@@ -166,7 +184,7 @@ fa_status fa_fwd_split(const void* q, const void* k, const void* v, void* o, flo
   FwdArgs a;
   std::memset(&a, 0, sizeof(a));
   bool bias = false;
-  st = read_desc(mb, H, bias, a);
+  st = read_desc(mb, H, N_q, N_k, dtype, bias, a);
   if (st != FA_OK) return st;
   a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
   a.B = B; a.H = H; a.Nq = N_q; a.Nk = N_k;
@@ -219,8 +237,9 @@ fa_status fa_bwd_phases(int phases, const void* q, const void* k, const void* v,
   BwdArgs a;
   std::memset(&a, 0, sizeof(a));
   bool bias = false;
-  st = read_desc(mb, H, bias, a);
+  st = read_desc(mb, H, N_q, N_k, dtype, bias, a);
   if (st != FA_OK) return st;
+  if (a.bmask != nullptr) return FA_ERR_UNSUPPORTED;  // block-sparse backward: not built
   a.q = q; a.k = k; a.v = v; a.o = o; a.dout = dout; a.lse = lse;
   a.delta = static_cast<float*>(workspace);
   a.qsum = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + bwd_qsum_offset(B, H, N_q));

@@ -188,6 +188,25 @@ __device__ inline void wait_vmem() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
+// Read-and-wait LDS loads written as inline assembly, for small tables that are filled
+// before a loop and only read inside it. Written through the builtin path, such a read
+// looks to the compiler as if it could alias the ring stages being filled by direct
+// loads, and it puts a wait for every load in flight in front of it. The wait for the
+// read itself is part of the same statement (the whole LDS queue is drained: use where
+// no other LDS read is outstanding).
+__device__ inline uint32_t lds_read_u16_now(const void* p) {
+  const uint32_t a = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) const void*)p);
+  uint32_t v;
+  asm volatile("ds_read_u16 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(a) : "memory");
+  return v;
+}
+__device__ inline uint32_t lds_read_b32_now(const void* p) {
+  const uint32_t a = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) const void*)p);
+  uint32_t v;
+  asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(a) : "memory");
+  return v;
+}
+
 // One wave-wide direct load of 4 bytes per lane: lane i fills bytes [4i, 4i+4) of the
 // 256-byte window at `lds` (wave-uniform).
 __device__ inline void dma4(const void* g, char* lds) {

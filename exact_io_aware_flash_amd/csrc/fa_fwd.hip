@@ -472,7 +472,7 @@ struct Fwd16Cfg {
   static_assert(kST >= 2 && kST * kStage <= 160 * 1024, "LDS budget");
 };
 
-template <typename T, int D, int BC, int NW, int ST, bool BIAS>
+template <typename T, int D, int BC, int NW, int ST, bool BIAS, bool SPARSE>
 __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
                           amdgpu_waves_per_eu(2, 2)))
 void fwd16_kernel(const FwdArgs a) {
@@ -568,6 +568,64 @@ void fwd16_kernel(const FwdArgs a) {
   auto full_tile = [&](int t) {
     const int k0 = t * BC, k1 = k0 + BC;
     return k1 <= Nk && k1 <= w_full_c && (!ranged || (w_max_s <= k0 && w_min_e >= k1));
+  };
+
+  // ---- block-sparse bitmap: the tiles the workgroup loads ---------------------------
+  // Blocks are whole tiles for every wave (block sizes are multiples of 64, tiles and
+  // waves are 64 or 32 aligned), so a tile is either skipped or computed like any other.
+  // Each wave marks the tiles of [t_lo, t_hi) it needs (its window and its bitmap row)
+  // in 64-tile words; wave 0 compacts their union, in order, into the list the ring
+  // walks, so tiles no wave needs are never loaded.
+  constexpr int kMaxT = SPARSE ? kSparseMaxTiles * 32 / BC : 1;
+  constexpr int kWords = SPARSE ? kMaxT / 64 : 1;
+  __shared__ uint32_t need_w[SPARSE ? NW : 1][2 * kWords];  // 64-tile masks as 2 x 32 bits
+  __shared__ uint16_t tlist[kMaxT];
+  __shared__ int n_list_s;
+  int n_pos = t_hi - t_lo;
+  if constexpr (SPARSE) {
+    const uint8_t* brow = nullptr;
+    if (wave_live) {
+      const int bb = bh / a.H, hh = bh - bb * a.H;
+      brow = a.bmask + bb * a.bm_sb + hh * a.bm_sh + (long long)(wq0 / a.bq) * a.nkb;
+    }
+    for (int c = 0; c * 64 < t_hi - t_lo; ++c) {
+      const int t = t_lo + c * 64 + lane;
+      const bool need = brow != nullptr && t < t_hi && live_tile(t) && brow[(t * BC) / a.bk] != 0;
+      const uint64_t m = __builtin_amdgcn_ballot_w64(need);
+      if (lane == 0) {
+        need_w[wid][2 * c] = (uint32_t)m;
+        need_w[wid][2 * c + 1] = (uint32_t)(m >> 32);
+      }
+    }
+    __syncthreads();
+    if (wid == 0) {
+      int cnt = 0;
+      for (int c = 0; c * 64 < t_hi - t_lo; ++c) {
+        uint32_t lo = 0, hi = 0;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) { lo |= need_w[w][2 * c]; hi |= need_w[w][2 * c + 1]; }
+        const uint32_t mine = lane < 32 ? (lo >> lane) & 1u : (hi >> (lane - 32)) & 1u;
+        const int before = (int)__builtin_amdgcn_mbcnt_hi(hi, __builtin_amdgcn_mbcnt_lo(lo, 0u));
+        if (mine) tlist[cnt + before] = (uint16_t)(t_lo + c * 64 + lane);
+        cnt += __builtin_popcount(lo) + __builtin_popcount(hi);
+      }
+      if (lane == 0) n_list_s = cnt;
+    }
+    __syncthreads();
+    n_pos = __builtin_amdgcn_readfirstlane(n_list_s);
+  }
+  // tile at ring position p, and whether this wave computes it
+  auto tile_at = [&](int p) -> int {
+    if constexpr (SPARSE) return __builtin_amdgcn_readfirstlane((int)lds_read_u16_now(&tlist[p]));
+    else return t_lo + p;
+  };
+  auto wave_needs = [&](int t) -> bool {
+    if constexpr (SPARSE) {
+      const int r = t - t_lo;
+      return (__builtin_amdgcn_readfirstlane(lds_read_b32_now(&need_w[wid][r >> 5])) >> (r & 31)) & 1u;
+    } else {
+      return live_tile(t);
+    }
   };
 
   // ---- Q fragments (B operand of S^T = K Q^T) -------------------------------------
@@ -699,7 +757,7 @@ void fwd16_kernel(const FwdArgs a) {
   };
 
   // ---- main loop: ring of ST stages, P = ST-1 tiles in flight ------------------------
-  // Tile t_lo + i lives in stage i % ST.
+  // Ring position p (tile tile_at(p)) lives in stage p % ST.
   typename C::Tile dt;
   dt.init(wid, lane);
   auto issue = [&](auto J, int t) __attribute__((always_inline)) {
@@ -716,31 +774,33 @@ void fwd16_kernel(const FwdArgs a) {
     else wait_vmem<0>();
     __builtin_amdgcn_s_barrier();
   };
-  if (t_lo < t_hi) issue(I0{}, t_lo);
-  if (t_lo + 1 < t_hi) issue(I1{}, t_lo + 1);
-  if constexpr (P >= 2) if (t_lo + 2 < t_hi) issue(I2{}, t_lo + 2);
-  if constexpr (P >= 3) if (t_lo + 3 < t_hi) issue(I3{}, t_lo + 3);
+  if (0 < n_pos) issue(I0{}, tile_at(0));
+  if (1 < n_pos) issue(I1{}, tile_at(1));
+  if constexpr (P >= 2) if (2 < n_pos) issue(I2{}, tile_at(2));
+  if constexpr (P >= 3) if (3 < n_pos) issue(I3{}, tile_at(3));
   // The Q fragments and every prologue tile land. Waiting for all of them (rather than
   // for the first tile only) leaves no register load outstanding in the loop, so the
   // compiler puts no full vector-memory wait, which would also wait for the ring's loads
   // in flight, in front of the loop's MFMAs.
   wait_vmem<0>();
   __builtin_amdgcn_s_barrier();
-  auto step = [&](auto J, int t) __attribute__((always_inline)) {
+  auto step = [&](auto J, int p) __attribute__((always_inline)) {
     constexpr int j = decltype(J)::value;
-    // the stage of tile t+P held tile t-1, which every wave finished before the barrier
-    if (t + P < t_hi) issue(std::integral_constant<int, j + P>{}, t + P);
-    if (live_tile(t)) {
+    const int t = tile_at(p);
+    // the stage of position p+P held position p-1, which every wave finished before the
+    // barrier
+    if (p + P < n_pos) issue(std::integral_constant<int, j + P>{}, tile_at(p + P));
+    if (wave_needs(t)) {
       const char* sb = sptr(J);
       tile(sb, sb + C::Tile::kBytes, t * BC, !full_tile(t));
     }
-    if (t + 1 < t_hi) land(min(t + P, t_hi - 1) - (t + 1));
+    if (p + 1 < n_pos) land(min(p + P, n_pos - 1) - (p + 1));
   };
-  for (int t = t_lo; t < t_hi; t += ST) {
-    step(I0{}, t);
-    if (t + 1 < t_hi) step(I1{}, t + 1);
-    if constexpr (ST > 2) if (t + 2 < t_hi) step(I2{}, t + 2);
-    if constexpr (ST > 3) if (t + 3 < t_hi) step(I3{}, t + 3);
+  for (int p = 0; p < n_pos; p += ST) {
+    step(I0{}, p);
+    if (p + 1 < n_pos) step(I1{}, p + 1);
+    if constexpr (ST > 2) if (p + 2 < n_pos) step(I2{}, p + 2);
+    if constexpr (ST > 3) if (p + 3 < n_pos) step(I3{}, p + 3);
   }
 
   // ---- epilogue -----------------------------------------------------------------------
@@ -891,10 +951,15 @@ static hipError_t launch16(bool bias, FwdArgs& a, hipStream_t st) {
   const int BH = a.B * a.H;
   a.sched = (BH % 8 == 0) ? kSchedXcd : kSchedHeadMajor;
   const dim3 grid((unsigned)(BH * a.nqb * a.n_split)), block(C::kNT);
-  if (bias)
-    hipLaunchKernelGGL((fwd16_kernel<T, D, BC, NW, ST, true>), grid, block, 0, st, a);
+  const bool sparse = a.bmask != nullptr;
+  if (bias && sparse)
+    hipLaunchKernelGGL((fwd16_kernel<T, D, BC, NW, ST, true, true>), grid, block, 0, st, a);
+  else if (bias)
+    hipLaunchKernelGGL((fwd16_kernel<T, D, BC, NW, ST, true, false>), grid, block, 0, st, a);
+  else if (sparse)
+    hipLaunchKernelGGL((fwd16_kernel<T, D, BC, NW, ST, false, true>), grid, block, 0, st, a);
   else
-    hipLaunchKernelGGL((fwd16_kernel<T, D, BC, NW, ST, false>), grid, block, 0, st, a);
+    hipLaunchKernelGGL((fwd16_kernel<T, D, BC, NW, ST, false, false>), grid, block, 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.n_split == 1) return e;
   return launch_merge<T, D>(a, st);

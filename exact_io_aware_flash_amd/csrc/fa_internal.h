@@ -34,6 +34,11 @@ struct FwdArgs {
   int split_keys;   // multiple of the 64-key tile
   float* o_part;    // [n_split][B*H*Nq][d] float32 normalised partial outputs
   float* lse_part;  // [n_split][B*H*Nq] float32 partial LSE (-inf: nothing visible)
+  // block-sparse bitmap (NULL: none): byte (r, c) of head (b, h) at
+  // bmask[b * bm_sb + h * bm_sh + r * nkb + c] for blocks of bq rows x bk keys
+  const uint8_t* bmask;
+  int bq, bk, nkb;
+  long long bm_sb, bm_sh;
 };
 
 // The split-key 16-bit forward uses a smaller workgroup (4 waves, 32-key tiles, 64 KB of
@@ -70,10 +75,16 @@ struct BwdArgs {
   float scale;
   float sl2;
   float slope2[FA_MAX_SLOPES];
+  // block-sparse bitmap, as in FwdArgs
+  const uint8_t* bmask;
+  int bq, bk, nkb;
+  long long bm_sb, bm_sh;
 };
 
 // Launchers (return hipSuccess or the launch error). dtype-specialised in the .hip files.
 hipError_t launch_fwd(fa_dtype dt, int d, bool bias, FwdArgs& a, hipStream_t st);
+// Tiles of the block-sparse forward list per workgroup (keys per tile >= 32).
+constexpr int kSparseMaxTiles = FA_MAX_SPARSE_N / 32;
 hipError_t launch_bwd(fa_dtype dt, int d, bool bias, int phases, BwdArgs& a, hipStream_t st);
 hipError_t launch_mask_summary(const int32_t* ks, const int32_t* ke, int Nq, int Nk, int block,
                                int32_t* out, hipStream_t st);

@@ -88,14 +88,36 @@ typedef enum fa_bias_kind {
  *              key_start[i] <= j < key_end[i] (one interval per row, shared by
  *              every batch and head). Any int32 values are allowed: the interval
  *              is intersected with [0, N_k); an empty interval gives an empty row.
- *  A row with no visible key (after causal and range masking) gets O = 0 and
+ *  block_mask : DEVICE pointer to a block-sparse bitmap of bytes, or NULL (then the
+ *              five fields below are ignored). The score matrix of every (b, h) is cut
+ *              into blocks of block_q query rows by block_k keys; block (r, c) is
+ *              visible when
+ *                block_mask[b * mask_stride_b + h * mask_stride_h + r * n_kb + c] != 0
+ *              with n_kb = ceil(N_k / block_k), r < ceil(N_q / block_q). Entries of an
+ *              invisible block are masked like keys outside a row's key range (the
+ *              method skips such tiles: briefgpt.xyz page for arXiv 2307.08691, its
+ *              FlashAttention abstract on the extension to block-sparse attention, and
+ *              the related abstract on sparsity patterns such as key/query dropping).
+ *  block_q, block_k : block sizes, multiples of 64 (else FA_ERR_MASK).
+ *  mask_stride_b, mask_stride_h : bitmap strides in bytes between batches and heads;
+ *              0 shares one bitmap over that axis (negative: FA_ERR_MASK).
+ *              The bitmap is read during the enqueued work; it must stay valid until the
+ *              stream has passed the call. 16-bit inputs only (float32: FA_ERR_UNSUPPORTED);
+ *              N_q and N_k at most FA_MAX_SPARSE_N (FA_ERR_UNSUPPORTED beyond).
+ *  A row with no visible key (after causal, range and block masking) gets O = 0 and
  *  LSE = -inf. */
+#define FA_MAX_SPARSE_N 65536
 typedef struct fa_mask_bias_desc {
   int32_t bias_kind;
   int32_t n_slopes;
   const float* slopes;
   const int32_t* key_start;
   const int32_t* key_end;
+  const uint8_t* block_mask;
+  int32_t block_q;
+  int32_t block_k;
+  int64_t mask_stride_b;
+  int64_t mask_stride_h;
 } fa_mask_bias_desc;
 
 /* Forward pass.

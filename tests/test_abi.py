@@ -107,6 +107,23 @@ def test_fwd_rejects_malformed_descriptors():
     assert fwd(mb=ctypes.byref(d)) == 6
 
 
+def test_block_mask_descriptor_validation():
+    def desc(bq=64, bk=128, sb=0, sh=0):
+        d = fa.MaskBiasDesc()
+        d.block_mask = P
+        d.block_q, d.block_k = bq, bk
+        d.mask_stride_b, d.mask_stride_h = sb, sh
+        return d
+    for bad in (dict(bq=32), dict(bk=100), dict(bq=0), dict(bk=-64), dict(sb=-1), dict(sh=-5)):
+        d = desc(**bad)
+        assert fwd(mb=ctypes.byref(d)) == 5, bad
+    d = desc()
+    assert fwd(mb=ctypes.byref(d), dtype=fa.FA_F32) == 8  # 16-bit inputs only
+    assert fwd(mb=ctypes.byref(d), Nk=65536 + 64) == 8    # beyond FA_MAX_SPARSE_N
+    assert fwd(mb=ctypes.byref(d), Nq=65536 + 1) == 8
+    assert ctypes.sizeof(fa.MaskBiasDesc) == 64  # the C layout of fa_mask_bias_desc
+
+
 def bwd(**kw):
     lib = fa.load_library()
     a = dict(q=P, k=P, v=P, o=P, lse=P, do=P, dq=P, dk=P, dv=P, gdt=fa.FA_F32, ws=P, wsb=1 << 20,
