@@ -239,7 +239,6 @@ fa_status fa_bwd_phases(int phases, const void* q, const void* k, const void* v,
   bool bias = false;
   st = read_desc(mb, H, N_q, N_k, dtype, bias, a);
   if (st != FA_OK) return st;
-  if (a.bmask != nullptr) return FA_ERR_UNSUPPORTED;  // block-sparse backward: not built
   a.q = q; a.k = k; a.v = v; a.o = o; a.dout = dout; a.lse = lse;
   a.delta = static_cast<float*>(workspace);
   a.qsum = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + bwd_qsum_offset(B, H, N_q));

@@ -92,7 +92,7 @@ struct DkdvLds {
 #define FA_DKDV_STAGES 4
 #endif
 
-template <typename T, int D, int BR, int NW, int WPE, bool BIAS>
+template <typename T, int D, int BR, int NW, int WPE, bool BIAS, bool SPARSE>
 __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
                           amdgpu_waves_per_eu(WPE, WPE)))
 void bwd_dkdv_kernel(const BwdArgs a) {
@@ -157,6 +157,39 @@ void bwd_dkdv_kernel(const BwdArgs a) {
     t_hi = min(t_hi, win[1]);
   }
   if (k0 >= Nk) t_hi = t_lo;
+
+  // block-sparse bitmap: the query tiles the workgroup loads (see build_tile_list); a
+  // 64-row query tile and a wave's 32 keys each lie inside one block
+  constexpr int kMaxT = SPARSE ? FA_MAX_SPARSE_N / BR : 64;
+  __shared__ uint32_t need_w[SPARSE ? NW : 1][2 * (kMaxT / 64)];
+  __shared__ uint16_t tlist[SPARSE ? kMaxT : 1];
+  __shared__ int n_list_s;
+  int n_pos = t_hi - t_lo;
+  if constexpr (SPARSE) {
+    const uint8_t* bcol = nullptr;
+    if (kw0 < Nk) {
+      const int bb = bh / a.H, hh = bh - bb * a.H;
+      bcol = a.bmask + bb * a.bm_sb + hh * a.bm_sh + kw0 / a.bk;
+    }
+    n_pos = build_tile_list(need_w, tlist, &n_list_s, wid_s, lane, t_lo, t_hi, [&](int t) {
+      const int q0t = t * BR;
+      bool skip = bcol == nullptr;
+      if (causal) skip |= q0t + BR - 1 + off < kw0;
+      if (ranged) {
+        const int* sm = a.qsum + 4 * t;
+        skip |= kw1 <= sm[0] || kw0 >= sm[3];
+      }
+      return !skip && bcol[(long long)(q0t / a.bq) * a.nkb] != 0;
+    });
+  }
+  auto tile_at = [&](int p) -> int {
+    if constexpr (SPARSE) return __builtin_amdgcn_readfirstlane((int)lds_read_u16_now(&tlist[p]));
+    else return t_lo + p;
+  };
+  auto wave_needs = [&](int t) -> bool {
+    const int r = t - t_lo;
+    return (__builtin_amdgcn_readfirstlane(lds_read_b32_now(&need_w[wid_s][r >> 5])) >> (r & 31)) & 1u;
+  };
 
   f32x16 dv[DB], dk[DB];
 #pragma unroll
@@ -284,10 +317,11 @@ void bwd_dkdv_kernel(const BwdArgs a) {
              : ranged ? reinterpret_cast<const float*>(wid_s == 2 ? a.key_start : a.key_end) : lse_h;
   }
   const int arr_off = wid_s == 0 ? L::LSE : wid_s == 1 ? L::DLT : wid_s == 2 ? L::KS : L::KE;
-  auto stage_of = [&](int t) { return smem + ((t - t_lo) % ST) * L::STAGE; };
-  auto issue = [&](int t) {
-    char* sb = stage_of(t);
-    const int q0t = t * BR;
+  // ring position p (query tile tile_at(p)) lives in stage p % ST
+  auto stage_of = [&](int p) { return smem + (p % ST) * L::STAGE; };
+  auto issue = [&](int p) {
+    char* sb = stage_of(p);
+    const int q0t = tile_at(p) * BR;
     tile_ld.load(Q, q0t, Nq, sb + L::QT, wid_s);
     tile_ld.load(dO, q0t, Nq, sb + L::DT, wid_s);
     dma4(arr_base + min(q0t + lane, Nq - 1), sb + arr_off);
@@ -301,7 +335,7 @@ void bwd_dkdv_kernel(const BwdArgs a) {
   };
 #pragma unroll
   for (int i = 0; i < P; ++i)
-    if (t_lo + i < t_hi) issue(t_lo + i);
+    if (i < n_pos) issue(i);
   // The K and V fragments and every prologue tile land here. Waiting for all of them
   // (rather than for the first tile only) leaves no register load outstanding once the
   // loop starts, so the compiler has no reason to put a full vector-memory wait, which
@@ -309,15 +343,17 @@ void bwd_dkdv_kernel(const BwdArgs a) {
   wait_vmem<0>();
   __builtin_amdgcn_s_barrier();
 
-  for (int t = t_lo; t < t_hi; ++t) {
+  for (int p = 0; p < n_pos; ++p) {
 #pragma unroll
     for (int db = 0; db < DB; ++db) { pin_agpr(dv[db]); pin_agpr(dk[db]); }
 #pragma unroll
     for (int ks = 0; ks < DK; ++ks) { pin_agpr(kf[ks]); pin_agpr(vf[ks]); }
-    // the stage of tile t+P held tile t-1, which every wave finished before the barrier
-    if (t + P < t_hi) issue(t + P);
+    // the stage of position p+P held position p-1, which every wave finished before the
+    // barrier
+    if (p + P < n_pos) issue(p + P);
+    const int t = tile_at(p);
     const int q0t = t * BR;
-    const char* sb = stage_of(t);
+    const char* sb = stage_of(p);
 
     // classify the tile for this wave's keys [kw0, kw1)
     bool skip = kw0 >= Nk;
@@ -331,6 +367,7 @@ void bwd_dkdv_kernel(const BwdArgs a) {
       skip |= kw1 <= sm[0] || kw0 >= sm[3];
       full &= sm[1] <= kw0 && sm[2] >= kw0 + 32;
     }
+    if constexpr (SPARSE) skip = !wave_needs(t);
     if (!skip) {
       if (full) {
 #pragma unroll
@@ -340,7 +377,7 @@ void bwd_dkdv_kernel(const BwdArgs a) {
         for (int qb = 0; qb < QB; ++qb) qblock(sb, q0t, qb, std::true_type{});
       }
     }
-    if (t + 1 < t_hi) land(min(t + P, t_hi - 1) - (t + 1));
+    if (p + 1 < n_pos) land(min(p + P, n_pos - 1) - (p + 1));
   }
 
   // epilogue: lane holds column d = 32*db + n for keys kw0 + res_row(g, h)
@@ -381,7 +418,7 @@ struct DqLds {
 #define FA_DQ_STAGES 4
 #endif
 
-template <typename T, int D, int BC, int NW, int WPE, bool BIAS>
+template <typename T, int D, int BC, int NW, int WPE, bool BIAS, bool SPARSE>
 __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
                           amdgpu_waves_per_eu(WPE, WPE)))
 void bwd_dq_kernel(const BwdArgs a) {
@@ -455,6 +492,30 @@ void bwd_dq_kernel(const BwdArgs a) {
   for (int w = 0; w < NW; ++w) { g_lo = min(g_lo, wg_win[w][0]); g_hi = max(g_hi, wg_win[w][1]); }
   const int t_lo = g_hi > g_lo ? g_lo / BC : 0;
   const int t_hi = g_hi > g_lo ? (g_hi + BC - 1) / BC : 0;
+
+  // block-sparse bitmap: the key tiles the workgroup loads (see build_tile_list); with
+  // 64-key tiles a tile and a wave's 32 rows each lie inside one block
+  constexpr int kMaxT = SPARSE ? FA_MAX_SPARSE_N / BC : 64;
+  static_assert(!SPARSE || BC == 64, "block-sparse dQ uses 64-key tiles");
+  __shared__ uint32_t need_w[SPARSE ? NW : 1][2 * (kMaxT / 64)];
+  __shared__ uint16_t tlist[SPARSE ? kMaxT : 1];
+  __shared__ int n_list_s;
+  int n_pos = t_hi - t_lo;
+  if constexpr (SPARSE) {
+    const uint8_t* brow = nullptr;
+    if (wave_live) {
+      const int bb = bh / a.H, hh = bh - bb * a.H;
+      brow = a.bmask + bb * a.bm_sb + hh * a.bm_sh + (long long)(wq0 / a.bq) * a.nkb;
+    }
+    n_pos = build_tile_list(need_w, tlist, &n_list_s, wid, lane, t_lo, t_hi, [&](int t) {
+      const int kt0 = t * BC;
+      return brow != nullptr && !(kt0 >= w_hi || kt0 + BC <= w_lo) && brow[kt0 / a.bk] != 0;
+    });
+  }
+  auto tile_at = [&](int p) -> int {
+    if constexpr (SPARSE) return __builtin_amdgcn_readfirstlane((int)lds_read_u16_now(&tlist[p]));
+    else return t_lo + p;
+  };
 
   f32x16 dqa[DB];
 #pragma unroll
@@ -553,9 +614,11 @@ void bwd_dq_kernel(const BwdArgs a) {
 
   Tile tile_ld;
   tile_ld.init(wid, lane);
-  auto stage_of = [&](int t) { return smem + ((t - t_lo) % ST) * L::STAGE; };
-  auto issue = [&](int t) {
-    char* sb = stage_of(t);
+  // ring position p (key tile tile_at(p)) lives in stage p % ST
+  auto stage_of = [&](int p) { return smem + (p % ST) * L::STAGE; };
+  auto issue = [&](int p) {
+    char* sb = stage_of(p);
+    const int t = tile_at(p);
     tile_ld.load(K, t * BC, Nk, sb + L::KT, wid);
     tile_ld.load(V, t * BC, Nk, sb + L::VT, wid);
   };
@@ -568,19 +631,25 @@ void bwd_dq_kernel(const BwdArgs a) {
   };
 #pragma unroll
   for (int i = 0; i < P; ++i)
-    if (t_lo + i < t_hi) issue(t_lo + i);
-  if (t_lo < t_hi) land(min(P, t_hi - t_lo) - 1);
-  for (int t = t_lo; t < t_hi; ++t) {
-    // the stage of tile t+P held tile t-1, which every wave finished before the barrier
-    if (t + P < t_hi) issue(t + P);
+    if (i < n_pos) issue(i);
+  if (0 < n_pos) land(min(P, n_pos) - 1);
+  for (int p = 0; p < n_pos; ++p) {
+    // the stage of position p+P held position p-1, which every wave finished before the
+    // barrier
+    if (p + P < n_pos) issue(p + P);
+    const int t = tile_at(p);
     const int kt0 = t * BC, kt1 = kt0 + BC;
-    const bool skip = kt0 >= w_hi || kt1 <= w_lo;
+    bool skip = kt0 >= w_hi || kt1 <= w_lo;
+    if constexpr (SPARSE) {
+      const int r = t - t_lo;
+      skip = !((__builtin_amdgcn_readfirstlane(lds_read_b32_now(&need_w[wid][r >> 5])) >> (r & 31)) & 1u);
+    }
     if (!skip) {
       const bool full = kt1 <= Nk && kt1 <= w_full_c &&
                         (!ranged || (w_max_s <= kt0 && w_min_e >= kt1));
-      tile(stage_of(t), kt0, !full);
+      tile(stage_of(p), kt0, !full);
     }
-    if (t + 1 < t_hi) land(min(t + P, t_hi - 1) - (t + 1));
+    if (p + 1 < n_pos) land(min(p + P, n_pos - 1) - (p + 1));
   }
 
   // epilogue: lane holds query qrow, registers d = 32*db + res_row(g, h)
@@ -640,10 +709,15 @@ static hipError_t launch_bwd_t(bool bias, int phases, BwdArgs& a, hipStream_t st
     b.nblk = (a.Nk + BK - 1) / BK;
     b.sched = sched;
     const dim3 grid((unsigned)(BH * b.nblk)), block(DKDV_NW * 64);
-    if (bias)
-      hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, kDkdvBR, DKDV_NW, DKDV_WPE, true>), grid, block, 0, st, b);
+    const bool sparse = a.bmask != nullptr;
+    if (bias && sparse)
+      hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, kDkdvBR, DKDV_NW, DKDV_WPE, true, true>), grid, block, 0, st, b);
+    else if (bias)
+      hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, kDkdvBR, DKDV_NW, DKDV_WPE, true, false>), grid, block, 0, st, b);
+    else if (sparse)
+      hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, kDkdvBR, DKDV_NW, DKDV_WPE, false, true>), grid, block, 0, st, b);
     else
-      hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, kDkdvBR, DKDV_NW, DKDV_WPE, false>), grid, block, 0, st, b);
+      hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, kDkdvBR, DKDV_NW, DKDV_WPE, false, false>), grid, block, 0, st, b);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -654,10 +728,15 @@ static hipError_t launch_bwd_t(bool bias, int phases, BwdArgs& a, hipStream_t st
     b.nblk = (a.Nq + BRQ - 1) / BRQ;
     b.sched = sched;
     const dim3 grid((unsigned)(BH * b.nblk)), block(DQ_NW * 64);
-    if (bias)
-      hipLaunchKernelGGL((bwd_dq_kernel<T, D, DQ_BC, DQ_NW, DQ_WPE, true>), grid, block, 0, st, b);
+    // (the block-sparse form always uses 64-key tiles, which lie inside one block)
+    if (a.bmask != nullptr && bias)
+      hipLaunchKernelGGL((bwd_dq_kernel<T, D, 64, DQ_NW, DQ_WPE, true, true>), grid, block, 0, st, b);
+    else if (a.bmask != nullptr)
+      hipLaunchKernelGGL((bwd_dq_kernel<T, D, 64, DQ_NW, DQ_WPE, false, true>), grid, block, 0, st, b);
+    else if (bias)
+      hipLaunchKernelGGL((bwd_dq_kernel<T, D, DQ_BC, DQ_NW, DQ_WPE, true, false>), grid, block, 0, st, b);
     else
-      hipLaunchKernelGGL((bwd_dq_kernel<T, D, DQ_BC, DQ_NW, DQ_WPE, false>), grid, block, 0, st, b);
+      hipLaunchKernelGGL((bwd_dq_kernel<T, D, DQ_BC, DQ_NW, DQ_WPE, false, false>), grid, block, 0, st, b);
     e = hipGetLastError();
   }
   return e;

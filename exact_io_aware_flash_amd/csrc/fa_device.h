@@ -207,6 +207,44 @@ __device__ inline uint32_t lds_read_b32_now(const void* p) {
   return v;
 }
 
+// ---------------------------------------------------------------------------------
+// Block-sparse tile lists. A workgroup walks tiles t_lo .. t_hi-1 along one axis; with a
+// block bitmap some of them are needed by no wave. Each wave marks the tiles it needs in
+// 64-tile words (need[wid][2c], need[wid][2c+1]: tiles t_lo + 64c + 0..31, 32..63); wave
+// 0 then writes the union, in order, to `list` and its length to *n_s. Every thread of
+// the workgroup calls this (two workgroup barriers); need_fn(t) is the calling lane's
+// answer for tile t (only called for t < t_hi). Returns the list length.
+// ---------------------------------------------------------------------------------
+template <int NW, int W2, typename NeedFn>
+__device__ inline int build_tile_list(uint32_t (&need)[NW][W2], uint16_t* list, int* n_s,
+                                      int wid, int lane, int t_lo, int t_hi, NeedFn need_fn) {
+  for (int c = 0; c * 64 < t_hi - t_lo; ++c) {
+    const int t = t_lo + c * 64 + lane;
+    const bool nd = t < t_hi && need_fn(t);
+    const uint64_t m = __builtin_amdgcn_ballot_w64(nd);
+    if (lane == 0) {
+      need[wid][2 * c] = (uint32_t)m;
+      need[wid][2 * c + 1] = (uint32_t)(m >> 32);
+    }
+  }
+  __syncthreads();
+  if (wid == 0) {
+    int cnt = 0;
+    for (int c = 0; c * 64 < t_hi - t_lo; ++c) {
+      uint32_t lo = 0, hi = 0;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) { lo |= need[w][2 * c]; hi |= need[w][2 * c + 1]; }
+      const uint32_t mine = lane < 32 ? (lo >> lane) & 1u : (hi >> (lane - 32)) & 1u;
+      const int before = (int)__builtin_amdgcn_mbcnt_hi(hi, __builtin_amdgcn_mbcnt_lo(lo, 0u));
+      if (mine) list[cnt + before] = (uint16_t)(t_lo + c * 64 + lane);
+      cnt += __builtin_popcount(lo) + __builtin_popcount(hi);
+    }
+    if (lane == 0) *n_s = cnt;
+  }
+  __syncthreads();
+  return __builtin_amdgcn_readfirstlane(*n_s);
+}
+
 // One wave-wide direct load of 4 bytes per lane: lane i fills bytes [4i, 4i+4) of the
 // 256-byte window at `lds` (wave-uniform).
 __device__ inline void dma4(const void* g, char* lds) {

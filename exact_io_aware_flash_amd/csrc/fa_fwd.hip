@@ -576,10 +576,9 @@ void fwd16_kernel(const FwdArgs a) {
   // Each wave marks the tiles of [t_lo, t_hi) it needs (its window and its bitmap row)
   // in 64-tile words; wave 0 compacts their union, in order, into the list the ring
   // walks, so tiles no wave needs are never loaded.
-  constexpr int kMaxT = SPARSE ? kSparseMaxTiles * 32 / BC : 1;
-  constexpr int kWords = SPARSE ? kMaxT / 64 : 1;
-  __shared__ uint32_t need_w[SPARSE ? NW : 1][2 * kWords];  // 64-tile masks as 2 x 32 bits
-  __shared__ uint16_t tlist[kMaxT];
+  constexpr int kMaxT = SPARSE ? kSparseMaxTiles * 32 / BC : 64;
+  __shared__ uint32_t need_w[SPARSE ? NW : 1][2 * (kMaxT / 64)];  // per-wave 64-tile masks
+  __shared__ uint16_t tlist[SPARSE ? kMaxT : 1];
   __shared__ int n_list_s;
   int n_pos = t_hi - t_lo;
   if constexpr (SPARSE) {
@@ -588,31 +587,9 @@ void fwd16_kernel(const FwdArgs a) {
       const int bb = bh / a.H, hh = bh - bb * a.H;
       brow = a.bmask + bb * a.bm_sb + hh * a.bm_sh + (long long)(wq0 / a.bq) * a.nkb;
     }
-    for (int c = 0; c * 64 < t_hi - t_lo; ++c) {
-      const int t = t_lo + c * 64 + lane;
-      const bool need = brow != nullptr && t < t_hi && live_tile(t) && brow[(t * BC) / a.bk] != 0;
-      const uint64_t m = __builtin_amdgcn_ballot_w64(need);
-      if (lane == 0) {
-        need_w[wid][2 * c] = (uint32_t)m;
-        need_w[wid][2 * c + 1] = (uint32_t)(m >> 32);
-      }
-    }
-    __syncthreads();
-    if (wid == 0) {
-      int cnt = 0;
-      for (int c = 0; c * 64 < t_hi - t_lo; ++c) {
-        uint32_t lo = 0, hi = 0;
-#pragma unroll
-        for (int w = 0; w < NW; ++w) { lo |= need_w[w][2 * c]; hi |= need_w[w][2 * c + 1]; }
-        const uint32_t mine = lane < 32 ? (lo >> lane) & 1u : (hi >> (lane - 32)) & 1u;
-        const int before = (int)__builtin_amdgcn_mbcnt_hi(hi, __builtin_amdgcn_mbcnt_lo(lo, 0u));
-        if (mine) tlist[cnt + before] = (uint16_t)(t_lo + c * 64 + lane);
-        cnt += __builtin_popcount(lo) + __builtin_popcount(hi);
-      }
-      if (lane == 0) n_list_s = cnt;
-    }
-    __syncthreads();
-    n_pos = __builtin_amdgcn_readfirstlane(n_list_s);
+    n_pos = build_tile_list(need_w, tlist, &n_list_s, wid, lane, t_lo, t_hi, [&](int t) {
+      return brow != nullptr && live_tile(t) && brow[(t * BC) / a.bk] != 0;
+    });
   }
   // tile at ring position p, and whether this wave computes it
   auto tile_at = [&](int p) -> int {
