@@ -10,7 +10,8 @@ The roofline object describes the dominant kernel, timed with HIP events recorde
 the stream the kernels run on; its achieved rate uses the algorithmic FLOPs of that
 kernel (see ALG_FLOPS below). The CPU baseline times the float64 oracle (fwd + bwd)
 on a bounded sample of whole (b, h) heads of the same workload. A supplementary list
-times the forward on short sequences and decode-like shapes (compulsory-byte GB/s).
+times the forward on short sequences and decode-like shapes (compulsory-byte GB/s), and
+another the forward and backward of the same workload under block-sparse bitmaps.
 """
 
 from __future__ import annotations
@@ -67,6 +68,10 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-hbm-shapes", action="store_true",
                     help="skip the supplementary short-N and decode-like forward timings")
+    ap.add_argument("--no-sparse", action="store_true",
+                    help="skip the supplementary block-sparse fwd/bwd timings")
+    ap.add_argument("--sparse-only", action="store_true",
+                    help="only time the block-sparse shapes and print them as one JSON line")
     ap.add_argument("--hbm-only", action="store_true",
                     help="only time the supplementary shapes and print them as one JSON line")
     ap.add_argument("--hbm-filter", default="",
@@ -115,6 +120,15 @@ def main():
 
     import exact_io_aware_flash_amd as fa
     from synth import CONFIGS, qkv_inputs
+
+    if args.sparse_only:
+        fa.load_library()  # fails loudly if the HIP library is missing
+        if not torch.cuda.is_available():
+            print("no GPU visible", file=sys.stderr)
+            sys.exit(1)
+        print(json.dumps({"block_sparse": block_sparse(fa, torch, CONFIGS[5], qkv_inputs)}),
+              flush=True)
+        return
 
     fa.load_library()  # fails loudly if the HIP library is missing
     if not torch.cuda.is_available():
@@ -204,6 +218,7 @@ def main():
                 "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic}
 
     hbm = None if args.no_hbm_shapes else hbm_shapes(fa, torch)
+    sparse = None if args.no_sparse else block_sparse(fa, torch, w, qkv_inputs)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -235,16 +250,36 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "hbm_shapes": hbm,
+        "block_sparse": sparse,
     }
     print(json.dumps(line), flush=True)
+
+
+def time_us(torch, fn, reps=10, rounds=3):
+    """Average microseconds per call of `fn` over `reps` back-to-back calls, timed with HIP
+    events on the launch stream (torch's current stream); median over `rounds` after 5
+    warm-up calls. Back-to-back calls keep the GPU busy, as in a real pass: a sync between
+    single calls would let the clocks drop and add the host's launch time."""
+    for _ in range(5):
+        fn()
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(rounds):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        e1.synchronize()
+        ts.append(e0.elapsed_time(e1) * 1e3 / reps)
+    return sorted(ts)[len(ts) // 2]
 
 
 def hbm_shapes(fa, torch, only=""):
     """Forward time and compulsory-byte bandwidth on short sequences and decode-like shapes.
 
     Compulsory bytes: Q, K, V read and O written once (bf16) plus the float32 LSE. Inputs
-    are seeded Gaussian bf16 made on the device; each shape is timed with HIP events on
-    the launch stream (10 warm-up calls, median of 20)."""
+    are seeded Gaussian bf16 made on the device; each shape is timed by time_us."""
     dev = torch.device("cuda:0")
     g = torch.Generator(device=dev).manual_seed(1234)
     shapes = [("short-N", 16, 32, n, n, False) for n in (128, 256, 512)]
@@ -270,21 +305,58 @@ def hbm_shapes(fa, torch, only=""):
                           lambda: fa.fa_fwd_split(q, k, v, causal=causal, out=o, lse=lse,
                                                   workspace=ws)))
         for path, fn in paths:
-            for _ in range(10):
-                fn()
-            ts = []
-            for _ in range(20):
-                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                e0.record()
-                fn()
-                e1.record()
-                e1.synchronize()
-                ts.append(e0.elapsed_time(e1) * 1e3)
-            us = sorted(ts)[len(ts) // 2]
+            us = time_us(torch, fn)
             out.append({"shape": name, "path": path, "us": round(us, 2),
                         "GB/s": round(nbytes / (us * 1e-6) / 1e9, 1),
                         "frac_hbm": round(nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)})
         del q, k, v, o, lse
+    return out
+
+
+def block_sparse(fa, torch, w, qkv_inputs):
+    """Forward and backward of the main workload under block bitmaps (one per head).
+
+    Seeded random bitmaps of 128 x 128 blocks at several densities, on top of the causal
+    mask. Each path is timed by time_us; the rate counts only the visible (query, key)
+    pairs, with the same per-pair FLOPs as the dense figures (forward 4d, backward 10d).
+    The dense kernels on the same inputs are timed beside them."""
+    import numpy as np
+
+    dev = torch.device("cuda:0")
+    B, H, N, d = w.B, w.H, w.N_q, w.d
+    q, k, v, do = (t.to(dev) for t in qkv_inputs(w))
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    grads = tuple(torch.empty((B, H, N, d), dtype=torch.float32, device=dev) for _ in range(3))
+    ws = torch.empty(fa.fa_bwd_workspace_bytes(B, H, N, N, d), dtype=torch.uint8, device=dev)
+    blk = 128
+    nb = -(-N // blk)
+    r = np.arange(nb)[:, None]
+    c = np.arange(nb)[None, :]
+    # causal pairs inside block (r, c) of a square N x N head (N a multiple of blk)
+    causal_pairs = np.where(c < r, blk * blk, np.where(c == r, blk * (blk + 1) // 2, 0))
+
+    out = []
+    for density in (None, 1.0, 0.5, 0.25):
+        kw = dict(causal=True, scale=w.scale)
+        if density is None:  # no bitmap: the dense kernels
+            pairs = B * H * N * (N + 1) / 2.0
+        else:
+            bm = (np.random.default_rng(4242).random((H, nb, nb)) < density).astype(np.uint8)
+            pairs = float(B * (bm * causal_pairs[None]).sum())
+            kw["block_mask"] = (torch.from_numpy(bm).to(dev), blk, blk)
+        fwd_us = time_us(torch, lambda: fa.fa_fwd(q, k, v, out=o, lse=lse, **kw))
+        fa.fa_fwd(q, k, v, out=o, lse=lse, **kw)
+        bwd_us = time_us(torch, lambda: fa.fa_bwd(do, q, k, v, o, lse, grads=grads,
+                                                  workspace=ws, **kw))
+        out.append({"shape": f"bf16 causal B{B} H{H} N{N} d{d}" + (
+                        f", per-head {blk}x{blk} bitmap" if density is not None else ", no bitmap"),
+                    "density": density, "visible_frac_of_causal": round(
+                        pairs / (B * H * N * (N + 1) / 2.0), 4),
+                    "fwd_us": round(fwd_us, 1), "bwd_us": round(bwd_us, 1),
+                    "fwd_tflops": round(4.0 * d * pairs / (fwd_us * 1e-6) / 1e12, 1),
+                    "bwd_tflops": round(10.0 * d * pairs / (bwd_us * 1e-6) / 1e12, 1)})
+    del q, k, v, do, o, lse, grads, ws
     return out
 
 

@@ -162,7 +162,7 @@ void bwd_dkdv_kernel(const BwdArgs a) {
   // 64-row query tile and a wave's 32 keys each lie inside one block
   constexpr int kMaxT = SPARSE ? FA_MAX_SPARSE_N / BR : 64;
   __shared__ uint32_t need_w[SPARSE ? NW : 1][2 * (kMaxT / 64)];
-  __shared__ uint16_t tlist[SPARSE ? kMaxT : 1];
+  __shared__ uint32_t tlist[SPARSE ? kMaxT : 1];
   __shared__ int n_list_s;
   int n_pos = t_hi - t_lo;
   if constexpr (SPARSE) {
@@ -182,13 +182,11 @@ void bwd_dkdv_kernel(const BwdArgs a) {
       return !skip && bcol[(long long)(q0t / a.bq) * a.nkb] != 0;
     });
   }
+  ListWindow<kMaxT> lw;
+  if constexpr (SPARSE) lw.init(tlist, lane);
   auto tile_at = [&](int p) -> int {
-    if constexpr (SPARSE) return __builtin_amdgcn_readfirstlane((int)lds_read_u16_now(&tlist[p]));
+    if constexpr (SPARSE) return (int)(lw.at(p) & 0xffffu);
     else return t_lo + p;
-  };
-  auto wave_needs = [&](int t) -> bool {
-    const int r = t - t_lo;
-    return (__builtin_amdgcn_readfirstlane(lds_read_b32_now(&need_w[wid_s][r >> 5])) >> (r & 31)) & 1u;
   };
 
   f32x16 dv[DB], dk[DB];
@@ -350,6 +348,7 @@ void bwd_dkdv_kernel(const BwdArgs a) {
     for (int ks = 0; ks < DK; ++ks) { pin_agpr(kf[ks]); pin_agpr(vf[ks]); }
     // the stage of position p+P held position p-1, which every wave finished before the
     // barrier
+    if constexpr (SPARSE) lw.slide(p);
     if (p + P < n_pos) issue(p + P);
     const int t = tile_at(p);
     const int q0t = t * BR;
@@ -367,7 +366,7 @@ void bwd_dkdv_kernel(const BwdArgs a) {
       skip |= kw1 <= sm[0] || kw0 >= sm[3];
       full &= sm[1] <= kw0 && sm[2] >= kw0 + 32;
     }
-    if constexpr (SPARSE) skip = !wave_needs(t);
+    if constexpr (SPARSE) skip = !((lw.at(p) >> (16 + wid_s)) & 1u);
     if (!skip) {
       if (full) {
 #pragma unroll
@@ -498,7 +497,7 @@ void bwd_dq_kernel(const BwdArgs a) {
   constexpr int kMaxT = SPARSE ? FA_MAX_SPARSE_N / BC : 64;
   static_assert(!SPARSE || BC == 64, "block-sparse dQ uses 64-key tiles");
   __shared__ uint32_t need_w[SPARSE ? NW : 1][2 * (kMaxT / 64)];
-  __shared__ uint16_t tlist[SPARSE ? kMaxT : 1];
+  __shared__ uint32_t tlist[SPARSE ? kMaxT : 1];
   __shared__ int n_list_s;
   int n_pos = t_hi - t_lo;
   if constexpr (SPARSE) {
@@ -512,8 +511,10 @@ void bwd_dq_kernel(const BwdArgs a) {
       return brow != nullptr && !(kt0 >= w_hi || kt0 + BC <= w_lo) && brow[kt0 / a.bk] != 0;
     });
   }
+  ListWindow<kMaxT> lw;
+  if constexpr (SPARSE) lw.init(tlist, lane);
   auto tile_at = [&](int p) -> int {
-    if constexpr (SPARSE) return __builtin_amdgcn_readfirstlane((int)lds_read_u16_now(&tlist[p]));
+    if constexpr (SPARSE) return (int)(lw.at(p) & 0xffffu);
     else return t_lo + p;
   };
 
@@ -636,14 +637,12 @@ void bwd_dq_kernel(const BwdArgs a) {
   for (int p = 0; p < n_pos; ++p) {
     // the stage of position p+P held position p-1, which every wave finished before the
     // barrier
+    if constexpr (SPARSE) lw.slide(p);
     if (p + P < n_pos) issue(p + P);
     const int t = tile_at(p);
     const int kt0 = t * BC, kt1 = kt0 + BC;
     bool skip = kt0 >= w_hi || kt1 <= w_lo;
-    if constexpr (SPARSE) {
-      const int r = t - t_lo;
-      skip = !((__builtin_amdgcn_readfirstlane(lds_read_b32_now(&need_w[wid][r >> 5])) >> (r & 31)) & 1u);
-    }
+    if constexpr (SPARSE) skip = !((lw.at(p) >> (16 + wid)) & 1u);
     if (!skip) {
       const bool full = kt1 <= Nk && kt1 <= w_full_c &&
                         (!ranged || (w_max_s <= kt0 && w_min_e >= kt1));

@@ -188,18 +188,12 @@ __device__ inline void wait_vmem() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
-// Read-and-wait LDS loads written as inline assembly, for small tables that are filled
+// A read-and-wait LDS load written as inline assembly, for small tables that are filled
 // before a loop and only read inside it. Written through the builtin path, such a read
 // looks to the compiler as if it could alias the ring stages being filled by direct
 // loads, and it puts a wait for every load in flight in front of it. The wait for the
 // read itself is part of the same statement (the whole LDS queue is drained: use where
 // no other LDS read is outstanding).
-__device__ inline uint32_t lds_read_u16_now(const void* p) {
-  const uint32_t a = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) const void*)p);
-  uint32_t v;
-  asm volatile("ds_read_u16 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(a) : "memory");
-  return v;
-}
 __device__ inline uint32_t lds_read_b32_now(const void* p) {
   const uint32_t a = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) const void*)p);
   uint32_t v;
@@ -211,13 +205,16 @@ __device__ inline uint32_t lds_read_b32_now(const void* p) {
 // Block-sparse tile lists. A workgroup walks tiles t_lo .. t_hi-1 along one axis; with a
 // block bitmap some of them are needed by no wave. Each wave marks the tiles it needs in
 // 64-tile words (need[wid][2c], need[wid][2c+1]: tiles t_lo + 64c + 0..31, 32..63); wave
-// 0 then writes the union, in order, to `list` and its length to *n_s. Every thread of
-// the workgroup calls this (two workgroup barriers); need_fn(t) is the calling lane's
-// answer for tile t (only called for t < t_hi). Returns the list length.
+// 0 then writes the tiles some wave needs, in order, to `list` as
+//   entry = tile | (bit w set when wave w needs the tile) << 16
+// and the list length to *n_s. Every thread of the workgroup calls this (two workgroup
+// barriers); need_fn(t) is the calling lane's answer for tile t (only called for
+// t < t_hi). Tiles must be below 65536. Returns the list length.
 // ---------------------------------------------------------------------------------
 template <int NW, int W2, typename NeedFn>
-__device__ inline int build_tile_list(uint32_t (&need)[NW][W2], uint16_t* list, int* n_s,
+__device__ inline int build_tile_list(uint32_t (&need)[NW][W2], uint32_t* list, int* n_s,
                                       int wid, int lane, int t_lo, int t_hi, NeedFn need_fn) {
+  static_assert(NW <= 16, "wave masks take the upper 16 bits of an entry");
   for (int c = 0; c * 64 < t_hi - t_lo; ++c) {
     const int t = t_lo + c * 64 + lane;
     const bool nd = t < t_hi && need_fn(t);
@@ -231,12 +228,16 @@ __device__ inline int build_tile_list(uint32_t (&need)[NW][W2], uint16_t* list, 
   if (wid == 0) {
     int cnt = 0;
     for (int c = 0; c * 64 < t_hi - t_lo; ++c) {
-      uint32_t lo = 0, hi = 0;
+      uint32_t lo = 0, hi = 0, waves = 0;
 #pragma unroll
-      for (int w = 0; w < NW; ++w) { lo |= need[w][2 * c]; hi |= need[w][2 * c + 1]; }
-      const uint32_t mine = lane < 32 ? (lo >> lane) & 1u : (hi >> (lane - 32)) & 1u;
+      for (int w = 0; w < NW; ++w) {
+        const uint32_t wl = need[w][2 * c], wh = need[w][2 * c + 1];
+        lo |= wl;
+        hi |= wh;
+        waves |= (lane < 32 ? (wl >> lane) & 1u : (wh >> (lane - 32)) & 1u) << w;
+      }
       const int before = (int)__builtin_amdgcn_mbcnt_hi(hi, __builtin_amdgcn_mbcnt_lo(lo, 0u));
-      if (mine) list[cnt + before] = (uint16_t)(t_lo + c * 64 + lane);
+      if (waves != 0) list[cnt + before] = (uint32_t)(t_lo + c * 64 + lane) | (waves << 16);
       cnt += __builtin_popcount(lo) + __builtin_popcount(hi);
     }
     if (lane == 0) *n_s = cnt;
@@ -244,6 +245,37 @@ __device__ inline int build_tile_list(uint32_t (&need)[NW][W2], uint16_t* list, 
   __syncthreads();
   return __builtin_amdgcn_readfirstlane(*n_s);
 }
+
+// Reads a list built by build_tile_list by position, with no LDS round trip per
+// position: entries base .. base+63 and base+64 .. base+127 sit one per lane in two
+// registers and come out through a lane read. slide(p) moves the window on by 64 once
+// position p has left its first half (one LDS read per 64 positions), so after
+// slide(p), at(q) is valid for p <= q < p + 64. CAP is the list's capacity.
+template <int CAP>
+struct ListWindow {
+  const uint32_t* list;
+  uint32_t w0, w1;
+  int base, lane;
+  __device__ void init(const uint32_t* l, int ln) {
+    list = l;
+    lane = ln;
+    base = 0;
+    w0 = lds_read_b32_now(&l[min(ln, CAP - 1)]);
+    w1 = lds_read_b32_now(&l[min(64 + ln, CAP - 1)]);
+  }
+  __device__ uint32_t at(int p) const {
+    const int r = p - base;
+    return (uint32_t)(r < 64 ? __builtin_amdgcn_readlane((int)w0, r)
+                             : __builtin_amdgcn_readlane((int)w1, r - 64));
+  }
+  __device__ void slide(int p) {
+    if (p - base >= 64) {
+      base += 64;
+      w0 = w1;
+      w1 = lds_read_b32_now(&list[min(base + 64 + lane, CAP - 1)]);
+    }
+  }
+};
 
 // One wave-wide direct load of 4 bytes per lane: lane i fills bytes [4i, 4i+4) of the
 // 256-byte window at `lds` (wave-uniform).

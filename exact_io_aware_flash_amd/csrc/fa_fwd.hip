@@ -578,7 +578,7 @@ void fwd16_kernel(const FwdArgs a) {
   // walks, so tiles no wave needs are never loaded.
   constexpr int kMaxT = SPARSE ? kSparseMaxTiles * 32 / BC : 64;
   __shared__ uint32_t need_w[SPARSE ? NW : 1][2 * (kMaxT / 64)];  // per-wave 64-tile masks
-  __shared__ uint16_t tlist[SPARSE ? kMaxT : 1];
+  __shared__ uint32_t tlist[SPARSE ? kMaxT : 1];
   __shared__ int n_list_s;
   int n_pos = t_hi - t_lo;
   if constexpr (SPARSE) {
@@ -591,18 +591,16 @@ void fwd16_kernel(const FwdArgs a) {
       return brow != nullptr && live_tile(t) && brow[(t * BC) / a.bk] != 0;
     });
   }
+  ListWindow<kMaxT> lw;
+  if constexpr (SPARSE) lw.init(tlist, lane);
   // tile at ring position p, and whether this wave computes it
   auto tile_at = [&](int p) -> int {
-    if constexpr (SPARSE) return __builtin_amdgcn_readfirstlane((int)lds_read_u16_now(&tlist[p]));
+    if constexpr (SPARSE) return (int)(lw.at(p) & 0xffffu);
     else return t_lo + p;
   };
-  auto wave_needs = [&](int t) -> bool {
-    if constexpr (SPARSE) {
-      const int r = t - t_lo;
-      return (__builtin_amdgcn_readfirstlane(lds_read_b32_now(&need_w[wid][r >> 5])) >> (r & 31)) & 1u;
-    } else {
-      return live_tile(t);
-    }
+  auto wave_needs = [&](int p, int t) -> bool {
+    if constexpr (SPARSE) return (lw.at(p) >> (16 + wid)) & 1u;
+    else return live_tile(t);
   };
 
   // ---- Q fragments (B operand of S^T = K Q^T) -------------------------------------
@@ -763,11 +761,12 @@ void fwd16_kernel(const FwdArgs a) {
   __builtin_amdgcn_s_barrier();
   auto step = [&](auto J, int p) __attribute__((always_inline)) {
     constexpr int j = decltype(J)::value;
+    if constexpr (SPARSE) lw.slide(p);
     const int t = tile_at(p);
     // the stage of position p+P held position p-1, which every wave finished before the
     // barrier
     if (p + P < n_pos) issue(std::integral_constant<int, j + P>{}, tile_at(p + P));
-    if (wave_needs(t)) {
+    if (wave_needs(p, t)) {
       const char* sb = sptr(J);
       tile(sb, sb + C::Tile::kBytes, t * BC, !full_tile(t));
     }
