@@ -22,6 +22,8 @@ import torch
 __all__ = [
     "FaError", "fa_fwd", "fa_fwd_split", "fa_fwd_split_count", "fa_fwd_split_workspace_bytes",
     "fa_bwd", "fa_bwd_workspace_bytes", "fa_mask_summary",
+    "fa_fp8_rows", "fa_fp8_quantize", "fa_fwd_fp8", "fa_attention_fp8",
+    "FA_FP8_Q", "FA_FP8_K", "FA_FP8_V",
     "FA_BWD_PREP", "FA_BWD_DKDV", "FA_BWD_DQ", "FA_BWD_ALL",
     "fa_status_string", "fa_version", "lib_path", "load_library",
 ]
@@ -34,6 +36,7 @@ FA_F32, FA_F16, FA_BF16 = 0, 1, 2
 FA_BIAS_NONE, FA_BIAS_DIST_LINEAR = 0, 1
 FA_MAX_SLOPES = 256
 FA_BWD_PREP, FA_BWD_DKDV, FA_BWD_DQ, FA_BWD_ALL = 1, 2, 4, 7
+FA_FP8_Q, FA_FP8_K, FA_FP8_V = 0, 1, 2
 _DT = {torch.float32: FA_F32, torch.float16: FA_F16, torch.bfloat16: FA_BF16}
 
 
@@ -96,6 +99,13 @@ def load_library():
     lib.fa_bwd_phases.restype = i32
     lib.fa_mask_summary.argtypes = [vp, vp, i32, i32, i32, vp, vp]
     lib.fa_mask_summary.restype = i32
+    lib.fa_fp8_rows.argtypes = [i32]
+    lib.fa_fp8_rows.restype = i32
+    lib.fa_fp8_quantize.argtypes = [vp, i32, i32, i32, i32, i32, i32, vp, vp, vp, vp]
+    lib.fa_fp8_quantize.restype = i32
+    lib.fa_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32,
+                               i32, i32, i32, vp]
+    lib.fa_fwd_fp8.restype = i32
     lib.fa_status_string.argtypes = [i32]
     lib.fa_status_string.restype = ctypes.c_char_p
     lib.fa_version.argtypes = []
@@ -349,3 +359,90 @@ def fa_mask_summary(key_start: torch.Tensor, key_end: torch.Tensor, n_k: int, bl
     if st != 0:
         raise FaError(st, "fa_mask_summary")
     return out[:nb]
+
+
+def fa_fp8_rows(n: int) -> int:
+    """Rows of a quantised tensor with n rows (n rounded up to a multiple of 64)."""
+    return int(load_library().fa_fp8_rows(int(n)))
+
+
+def fa_fp8_quantize(x: torch.Tensor, layout: int, signs=None,
+                    stream: Optional[torch.cuda.Stream] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Block-quantise x [B,H,N,d] (bf16 or fp16) to E4M3 (``fa_fp8_quantize``).
+
+    Returns (x8 uint8 [B, H, Np, d] in ``layout``'s byte order, amax float32 [B, H, Np/64]),
+    Np = fa_fp8_rows(N). ``signs``: sequence of d values +-1 to rotate rows by
+    diag(signs) H_d (FA_FP8_Q / FA_FP8_K only).
+    """
+    lib = load_library()
+    _check_dev("x", x)
+    if x.dim() != 4 or x.dtype not in (torch.bfloat16, torch.float16):
+        raise ValueError("x must be a bf16/fp16 [B, H, N, d] tensor")
+    B, H, N, d = x.shape
+    n_p = fa_fp8_rows(N)
+    x8 = torch.empty((B, H, n_p, d), dtype=torch.uint8, device=x.device)
+    amax = torch.empty((B, H, max(n_p // 64, 1)), dtype=torch.float32, device=x.device)
+    keep = None
+    sp = None
+    if signs is not None:
+        sl = [float(v) for v in signs]
+        if len(sl) != d:
+            raise ValueError(f"signs must hold d = {d} values")
+        keep = (ctypes.c_float * d)(*sl)
+        sp = ctypes.cast(keep, ctypes.c_void_p)
+    st = lib.fa_fp8_quantize(x.data_ptr(), B, H, N, d, _DT[x.dtype], int(layout), sp,
+                             x8.data_ptr(), amax.data_ptr(), _stream_ptr(stream))
+    del keep
+    if st != 0:
+        raise FaError(st, "fa_fp8_quantize")
+    return x8, amax
+
+
+def fa_fwd_fp8(q8: torch.Tensor, k8: torch.Tensor, v8: torch.Tensor, q_amax: torch.Tensor,
+               k_amax: torch.Tensor, v_amax: torch.Tensor, n_q: int, n_k: int,
+               causal: bool = False, scale: Optional[float] = None, rotated: bool = False,
+               out_dtype: torch.dtype = torch.bfloat16, out: Optional[torch.Tensor] = None,
+               lse: Optional[torch.Tensor] = None,
+               stream: Optional[torch.cuda.Stream] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """FP8 forward on operands from :func:`fa_fp8_quantize` (``fa_fwd_fp8``):
+    returns (O [B,H,n_q,d] in ``out_dtype``, LSE [B,H,n_q] float32)."""
+    lib = load_library()
+    B, H, nqp, d = q8.shape
+    nkp = fa_fp8_rows(n_k)
+    if nqp != fa_fp8_rows(n_q):
+        raise ValueError("q8 rows do not match n_q")
+    _check_dev("q8", q8, torch.uint8)
+    _check_dev("k8", k8, torch.uint8, (B, H, nkp, d))
+    _check_dev("v8", v8, torch.uint8, (B, H, nkp, d))
+    _check_dev("q_amax", q_amax, torch.float32, (B, H, nqp // 64))
+    _check_dev("k_amax", k_amax, torch.float32, (B, H, nkp // 64))
+    _check_dev("v_amax", v_amax, torch.float32, (B, H, nkp // 64))
+    if out_dtype not in (torch.bfloat16, torch.float16):
+        raise ValueError("out_dtype must be bf16 or fp16")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty((B, H, n_q, d), dtype=out_dtype, device=q8.device)
+    _check_dev("out", out, out_dtype, (B, H, n_q, d))
+    if lse is None:
+        lse = torch.empty((B, H, n_q), dtype=torch.float32, device=q8.device)
+    _check_dev("lse", lse, torch.float32, (B, H, n_q))
+    st = lib.fa_fwd_fp8(q8.data_ptr(), k8.data_ptr(), v8.data_ptr(), q_amax.data_ptr(),
+                        k_amax.data_ptr(), v_amax.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                        B, H, int(n_q), int(n_k), d, float(scale), 1 if causal else 0,
+                        1 if rotated else 0, _DT[out_dtype], _stream_ptr(stream))
+    if st != 0:
+        raise FaError(st, "fa_fwd_fp8")
+    return out, lse
+
+
+def fa_attention_fp8(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
+                     scale: Optional[float] = None, signs=None,
+                     stream: Optional[torch.cuda.Stream] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Quantise q, k (rotated when ``signs`` is given) and v, then run the FP8 forward;
+    O comes back in q's dtype."""
+    q8, qa = fa_fp8_quantize(q, FA_FP8_Q, signs, stream)
+    k8, ka = fa_fp8_quantize(k, FA_FP8_K, signs, stream)
+    v8, va = fa_fp8_quantize(v, FA_FP8_V, None, stream)
+    return fa_fwd_fp8(q8, k8, v8, qa, ka, va, q.shape[2], k.shape[2], causal=causal,
+                      scale=scale, rotated=signs is not None, out_dtype=q.dtype, stream=stream)

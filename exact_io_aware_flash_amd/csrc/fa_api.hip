@@ -129,6 +129,65 @@ const char* fa_status_string(fa_status s) {
 
 const char* fa_version(void) { return "fa 0.1.0 gfx950"; }
 
+int fa_fp8_rows(int N) { return N < 1 ? 0 : ((N + 63) / 64) * 64; }
+
+fa_status fa_fp8_quantize(const void* x, int B, int H, int N, int d, fa_dtype dtype,
+                          fa_fp8_layout layout, const float* signs, void* x8, float* amax,
+                          void* stream) {
+  if (B < 1 || H < 1 || N < 1) return FA_ERR_SHAPE;
+  if (d != 64 && d != 128) return FA_ERR_HEADDIM;
+  if (dtype != FA_BF16 && dtype != FA_F16) return FA_ERR_DTYPE;
+  if (layout != FA_FP8_Q && layout != FA_FP8_K && layout != FA_FP8_V) return FA_ERR_ARG;
+  if (!x || !x8 || !amax) return FA_ERR_NULL;
+  if (!aligned16(x) || !aligned16(x8) || (reinterpret_cast<uintptr_t>(amax) & 3u)) return FA_ERR_ALIGN;
+  if ((long long)N * d > INT_MAX) return FA_ERR_SHAPE;
+  const long long np = fa_fp8_rows(N);
+  if ((long long)B * H * (np / 64) > INT_MAX) return FA_ERR_SHAPE;  // one workgroup per block
+  Fp8QuantArgs a;
+  std::memset(&a, 0, sizeof(a));
+  if (signs != nullptr) {
+    if (layout == FA_FP8_V) return FA_ERR_ARG;
+    for (int e = 0; e < d; ++e) {
+      if (signs[e] == -1.f) a.sign_bits[e >> 5] |= 1u << (e & 31);
+      else if (signs[e] != 1.f) return FA_ERR_ARG;
+    }
+    a.rotate = 1;
+  }
+  a.x = x; a.x8 = static_cast<uint8_t*>(x8); a.amax = amax;
+  a.B = B; a.H = H; a.N = N; a.Np = (int)np;
+  a.layout = layout;
+  const hipError_t e = launch_fp8_quant(dtype, d, a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+fa_status fa_fwd_fp8(const void* q8, const void* k8, const void* v8, const float* q_amax,
+                     const float* k_amax, const float* v_amax, void* o, float* lse, int B, int H,
+                     int N_q, int N_k, int d, float scale, int causal, int rotated,
+                     fa_dtype out_dtype, void* stream) {
+  fa_status st = check_common(B, H, N_q, N_k, d, scale, FA_BF16);
+  if (st != FA_OK) return st;
+  if (out_dtype != FA_BF16 && out_dtype != FA_F16) return FA_ERR_DTYPE;
+  if (!q8 || !k8 || !v8 || !q_amax || !k_amax || !v_amax || !o) return FA_ERR_NULL;
+  if (!aligned16(q8) || !aligned16(k8) || !aligned16(v8) || !aligned16(o)) return FA_ERR_ALIGN;
+  if (((reinterpret_cast<uintptr_t>(q_amax) | reinterpret_cast<uintptr_t>(k_amax) |
+        reinterpret_cast<uintptr_t>(v_amax)) & 3u) ||
+      (lse != nullptr && (reinterpret_cast<uintptr_t>(lse) & 3u)))
+    return FA_ERR_ALIGN;
+  Fp8FwdArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.q8 = static_cast<const uint8_t*>(q8);
+  a.k8 = static_cast<const uint8_t*>(k8);
+  a.v8 = static_cast<const uint8_t*>(v8);
+  a.q_amax = q_amax; a.k_amax = k_amax; a.v_amax = v_amax;
+  a.o = o; a.lse = lse;
+  a.B = B; a.H = H; a.Nq = N_q; a.Nk = N_k;
+  a.Nqp = fa_fp8_rows(N_q); a.Nkp = fa_fp8_rows(N_k);
+  a.causal = causal ? 1 : 0;
+  a.sl2 = scale * 1.4426950408889634f / (rotated ? (float)d : 1.f);
+  const hipError_t e = launch_fwd8(out_dtype, d, a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
 fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
                  int N_q, int N_k, int d, float scale, int causal, const fa_mask_bias_desc* mb,
                  fa_dtype dtype, void* stream) {

@@ -27,6 +27,9 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kNegInf = -__builtin_huge_valf();
+// Lazy rescale of the online softmax: the running max (log2 units) only moves when a
+// row's new scores exceed it by more than kTau, so probabilities stay <= 2^kTau.
+constexpr float kTau = 8.0f;
 
 // Element-type traits: 16-bit types go through the 32x32x16 MFMA, float through 32x32x2.
 template <typename T> struct Elt;
@@ -47,6 +50,8 @@ template <> struct Elt<__bf16> {
     bf16x2 r = {(__bf16)lo, (__bf16)hi};
     return __builtin_bit_cast(uint32_t, r);
   }
+  // the element in the low 16 bits of `bits`, widened exactly
+  __device__ static inline float to_f32(uint32_t bits) { return __builtin_bit_cast(float, bits << 16); }
 };
 
 template <> struct Elt<_Float16> {
@@ -62,6 +67,9 @@ template <> struct Elt<_Float16> {
   __device__ static inline uint32_t pack2(float lo, float hi) {
     f16x2 r = {(_Float16)lo, (_Float16)hi};
     return __builtin_bit_cast(uint32_t, r);
+  }
+  __device__ static inline float to_f32(uint32_t bits) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(bits & 0xffffu));
   }
 };
 
@@ -157,6 +165,10 @@ __device__ inline int wave_min(int v) {
 __device__ inline int wave_max(int v) {
   for (int o = 32; o >= 1; o >>= 1) v = max(v, __shfl_xor(v, o, 64));
   return __builtin_amdgcn_readfirstlane(v);
+}
+__device__ inline float wave_fmax(float v) {
+  for (int o = 32; o >= 1; o >>= 1) v = __builtin_fmaxf(v, __shfl_xor(v, o, 64));
+  return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, v)));
 }
 // Index of the calling wave inside its workgroup, as a wave-uniform (scalar) value.
 __device__ inline int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }

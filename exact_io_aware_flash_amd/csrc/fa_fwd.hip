@@ -31,9 +31,6 @@
 
 namespace fa {
 
-constexpr float kTau = 8.0f;
- // lazy-rescale threshold in log2 units (p <= 2^8)
-
 template <typename T, int D_, int BC_, int QSUB_, int NW_>
 struct FwdCfg {
   static constexpr bool kF32 = std::is_same<T, float>::value;

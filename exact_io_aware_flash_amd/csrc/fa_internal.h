@@ -95,4 +95,35 @@ size_t bwd_qsum_offset(int B, int H, int Nq);
 size_t bwd_lse2_offset(int B, int H, int Nq);
 size_t bwd_workspace_bytes(int B, int H, int Nq);
 
+// FP8 quantiser (fa_fp8_quantize): one launch per tensor (V: an amax pass first)
+struct Fp8QuantArgs {
+  const void* x;       // [B,H,N,d] 16-bit input
+  uint8_t* x8;         // [B,H,Np,d] E4M3 codes in the layout's byte order
+  float* amax;         // [B,H,Np/64] block amax (V: written by the first pass)
+  int B, H, N, Np;     // Np = N rounded up to 64
+  int layout;          // fa_fp8_layout
+  int rotate;          // 1: multiply rows by diag(signs) H_d first (Q, K)
+  uint32_t sign_bits[4];  // bit e set: sign of column e is -1
+};
+
+// FP8 forward (fa_fwd_fp8)
+struct Fp8FwdArgs {
+  const uint8_t* q8;
+  const uint8_t* k8;
+  const uint8_t* v8;
+  const float* q_amax;
+  const float* k_amax;
+  const float* v_amax;
+  void* o;
+  float* lse;
+  int B, H, Nq, Nk, Nqp, Nkp;
+  int causal;
+  int nqb;
+  int sched;
+  float sl2;  // scale * log2(e), divided by d for rotated Q and K
+};
+
+hipError_t launch_fp8_quant(fa_dtype dt, int d, Fp8QuantArgs& a, hipStream_t st);
+hipError_t launch_fwd8(fa_dtype out, int d, Fp8FwdArgs& a, hipStream_t st);
+
 }  // namespace fa

@@ -223,6 +223,67 @@ FA_API fa_status fa_bwd_phases(int phases, const void* q, const void* k, const v
 FA_API fa_status fa_mask_summary(const int32_t* key_start, const int32_t* key_end, int N_q, int N_k,
                           int block_rows, int32_t* out, void* stream);
 
+/* ---------------------------------------------------------------------------------
+ * FP8 forward with block quantisation and incoherent processing.
+ * Source: marketmaker.cc blog on Flash Attention, section "FA3: Mekanika hopper",
+ * item 3 (FP8 at twice the 16-bit matrix rate; plain FP8 attention is spoiled by
+ * outliers; a random rotation of the vectors before block quantisation spreads an
+ * outlier over all coordinates, with a reported 2.6x lower error).
+ *
+ * Format: OCP FP8 E4M3 (1 sign, 4 exponent bits with bias 7, 3 mantissa bits;
+ * largest finite 448; no infinities). A tensor [B,H,N,d] is quantised in blocks of 64
+ * rows of one (b, h): N is padded with zero rows to Np = fa_fp8_rows(N) (a multiple of
+ * 64), block i covers rows 64i .. 64i+63, amax[b,h,i] = max |x| over the block, and a
+ * value x becomes code RNE(clamp(x * (448 / s), -448, 448)) with s the block's amax
+ * (FA_FP8_Q, FA_FP8_K) or the largest block amax of the (b, h) (FA_FP8_V); the stored
+ * value of a code c is decode(c) * s / 448. For Q and K the rows may first be rotated:
+ * x -> x diag(signs) H_d, with H_d the Sylvester Hadamard matrix (entries +-1,
+ * H_d H_d^T = d I) and signs a caller-drawn vector of +-1; Q and K must use the same
+ * signs, and then (Q M)(K M)^T = d Q K^T, which fa_fwd_fp8 divides out.
+ *
+ * Byte layouts of x8 (B*H*Np*d bytes, (b, h) major, then 64-row tiles t of 64*d bytes):
+ *  FA_FP8_Q: row-major, row r of tile t at byte 64*t*d + r*d + column.
+ *  FA_FP8_K: row r (key 64t + r) at r*d inside its tile; the 16-byte chunk c of the
+ *            row (columns 16c .. 16c+15) sits in slot c ^ z(r), z(r) = (r >> 1) & 7 for
+ *            d = 128 and (r >> 2) & 3 for d = 64.
+ *  FA_FP8_V: transposed: column e of the tile is a 64-byte row at e*64; key 64t + k
+ *            sits at position p(k) = 16*(k >> 5) + 32*((k >> 2) & 1) + 4*((k & 31) >> 3)
+ *            + (k & 3) of that row, and the row's 16-byte chunk c sits in slot
+ *            c ^ ((e >> 2) & 3).
+ * (K and V are stored as the forward's LDS tile images, so it copies them linearly.)
+ * --------------------------------------------------------------------------------- */
+typedef enum fa_fp8_layout { FA_FP8_Q = 0, FA_FP8_K = 1, FA_FP8_V = 2 } fa_fp8_layout;
+
+/* Rows of a quantised tensor with N rows: N rounded up to a multiple of 64 (0 if N < 1). */
+FA_API int fa_fp8_rows(int N);
+
+/* Quantise x [B,H,N,d] (device, dtype FA_BF16 or FA_F16, d in {64, 128}) into
+ *  x8:   device, B*H*fa_fp8_rows(N)*d bytes, in `layout`'s byte order;
+ *  amax: device float32 [B, H, fa_fp8_rows(N)/64], the block amaxes (of the rotated
+ *        values when rotating).
+ *  signs: HOST pointer to d floats, each exactly +1 or -1 (read during the call), to
+ *        rotate (FA_FP8_Q and FA_FP8_K only; NULL: no rotation; with FA_FP8_V: FA_ERR_ARG).
+ * The rotation is computed exactly (float64 sums of the 16-bit inputs) and rounded once
+ * to float32; amax, 448/amax and the products are float32. FA_FP8_V takes two launches
+ * (the block amaxes, then the codes with the head-wide scale). */
+FA_API fa_status fa_fp8_quantize(const void* x, int B, int H, int N, int d, fa_dtype dtype,
+                                 fa_fp8_layout layout, const float* signs, void* x8, float* amax,
+                                 void* stream);
+
+/* FP8 forward: O and LSE of attention with scores
+ *   s_ij = scale * <q_i, k_j> (divided by d when rotated != 0),
+ * from operands quantised by fa_fp8_quantize (q8 with FA_FP8_Q, k8 with FA_FP8_K, v8 with
+ * FA_FP8_V; q_amax, k_amax, v_amax their amax arrays; all device). causal as fa_fwd.
+ * o [B,H,N_q,d] device in out_dtype (FA_BF16 or FA_F16), lse [B,H,N_q] float32 or NULL.
+ * Both products run on E4M3 MFMA with float32 accumulation: S^T = K Q^T on the codes,
+ * scaled by the block scales; the probabilities (at most 2^8 with the lazy rescale) are
+ * rounded to E4M3 for O^T += V^T P^T, while the row sum uses them unrounded; O is the
+ * result times V's scale over the row sum. */
+FA_API fa_status fa_fwd_fp8(const void* q8, const void* k8, const void* v8, const float* q_amax,
+                            const float* k_amax, const float* v_amax, void* o, float* lse, int B,
+                            int H, int N_q, int N_k, int d, float scale, int causal, int rotated,
+                            fa_dtype out_dtype, void* stream);
+
 /* Static description of a status code (never NULL). */
 FA_API const char* fa_status_string(fa_status s);
 

@@ -13,4 +13,6 @@ from .inputs import (  # noqa: F401
     qkv_inputs,
     key_ranges,
     seed_for,
+    with_outliers,
+    random_signs,
 )

@@ -115,3 +115,20 @@ def key_ranges(n_q: int, n_k: int, seed: int, block: int = 128,
     start = offs.repeat_interleave(block)[:n_q] + jit
     end = start + width
     return start.to(torch.int32), end.to(torch.int32)
+
+
+def with_outliers(shape, dtype: torch.dtype, seed: int, frac: float = 1e-3,
+                  outlier_std: float = 10.0) -> torch.Tensor:
+    """N(0,1) entries of which a random fraction ``frac`` is redrawn from N(0, outlier_std^2),
+    RNE-rounded to ``dtype`` (a synthetic stand-in for activations with outliers)."""
+    g = torch.Generator("cpu").manual_seed(seed)
+    x = torch.randn(*shape, dtype=torch.float32, generator=g)
+    pick = torch.rand(*shape, generator=g) < frac
+    big = torch.randn(*shape, dtype=torch.float32, generator=g) * outlier_std
+    return torch.where(pick, big, x).to(dtype)
+
+
+def random_signs(d: int, seed: int):
+    """d independent fair draws of +1.0 / -1.0 (a list of floats)."""
+    g = torch.Generator("cpu").manual_seed(seed)
+    return [1.0 if b else -1.0 for b in (torch.rand(d, generator=g) < 0.5).tolist()]

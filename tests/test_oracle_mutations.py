@@ -136,3 +136,60 @@ def test_planted_block_mask_mistake_is_caught(monkeypatch, mutation):
         except (AssertionError, IndexError):
             caught += 1
     assert caught >= 1, f"no pin caught {mutation.__name__}"
+
+
+# ---- FP8 oracle (oracle/fp8.py) -----------------------------------------------------
+from oracle import fp8 as F8  # noqa: E402
+import tests.test_oracle_fp8 as fp8_pins  # noqa: E402
+
+_orig_decode, _orig_round, _orig_hadamard = F8.e4m3_decode, F8.e4m3_round, F8.hadamard
+
+
+def mut_e4m3_bias_8(monkeypatch):
+    monkeypatch.setattr(F8, "e4m3_decode", lambda c: _orig_decode(c) / 2.0)
+
+
+def mut_e4m3_ties_away(monkeypatch):
+    def bad(x):
+        c = _orig_round(x)
+        x = np.clip(np.asarray(x, dtype=np.float64), -448, 448)
+        nxt = np.where(c & 0x80, c + 1, c + 1).astype(np.uint8)  # one step up in magnitude
+        tie = (c & 0x7F) < 0x7E
+        tie &= np.abs(np.abs(x) - np.abs(_orig_decode(c))) == \
+            np.abs(np.abs(_orig_decode(nxt)) - np.abs(x))
+        return np.where(tie, nxt, c).astype(np.uint8)
+    monkeypatch.setattr(F8, "e4m3_round", bad)
+
+
+def mut_hadamard_no_minus(monkeypatch):
+    monkeypatch.setattr(F8, "hadamard", lambda d: np.abs(_orig_hadamard(d)))
+
+
+def mut_rotation_signs_ignored(monkeypatch):
+    monkeypatch.setattr(F8, "rotate", lambda x, s: np.asarray(x, dtype=np.float64) @
+                        _orig_hadamard(np.asarray(x).shape[-1]))
+
+
+FP8_PINS = [
+    lambda: [fp8_pins.test_decode_known_values(c, v) for c, v in
+             [(0x01, 2.0 ** -9), (0x38, 1.0), (0x7E, 448.0)]],
+    lambda: [fp8_pins.test_round_ties_to_even_and_clamp(x, c) for x, c in
+             [(1.0625, 0x38), (1.1875, 0x3A), (432.0, 0x7E)]],
+    lambda: fp8_pins.test_hadamard_is_orthogonal_with_pm1_entries(64),
+    lambda: fp8_pins.test_rotation_of_a_signed_hadamard_row_is_one_hot(),
+    lambda: fp8_pins.test_block_amax_and_codes_by_brute_force(True),
+]
+
+
+@pytest.mark.parametrize("mutation", [
+    mut_e4m3_bias_8, mut_e4m3_ties_away, mut_hadamard_no_minus, mut_rotation_signs_ignored,
+])
+def test_planted_fp8_mistake_is_caught(monkeypatch, mutation):
+    mutation(monkeypatch)
+    caught = 0
+    for pin in FP8_PINS:
+        try:
+            pin()
+        except AssertionError:
+            caught += 1
+    assert caught >= 1, f"no pin caught {mutation.__name__}"
