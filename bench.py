@@ -11,7 +11,8 @@ the stream the kernels run on; its achieved rate uses the algorithmic FLOPs of t
 kernel (see ALG_FLOPS below). The CPU baseline times the float64 oracle (fwd + bwd)
 on a bounded sample of whole (b, h) heads of the same workload. A supplementary list
 times the forward on short sequences and decode-like shapes (compulsory-byte GB/s), and
-another the forward and backward of the same workload under block-sparse bitmaps.
+another the forward and backward of the same workload under block-sparse bitmaps, and
+the FP8 path (quantiser + FP8 forward) on the same inputs.
 """
 
 from __future__ import annotations
@@ -30,6 +31,7 @@ sys.path.insert(0, ROOT)
 METRIC = "attention fwd(+bwd) TFLOP/s and % of MI355X bf16 MFMA peak, B·H·N²·d sweep"
 PEAK_BF16_TFLOPS = 2516.6  # 256 CU x 2.4 GHz x 4096 dense bf16 FLOP/clk/CU (published 2.5 PFLOP/s)
 PEAK_HBM_GBS = 8000.0
+PEAK_FP8_TFLOPS = 2 * PEAK_BF16_TFLOPS  # dense E4M3 MFMA (published 5.0 PFLOP/s)
 
 # HBM traffic of the kernels from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs (bytes per
 # launch, already scaled by the copy-kernel calibration factor), keyed by the sha256 of
@@ -72,6 +74,10 @@ def parse():
                     help="skip the supplementary block-sparse fwd/bwd timings")
     ap.add_argument("--sparse-only", action="store_true",
                     help="only time the block-sparse shapes and print them as one JSON line")
+    ap.add_argument("--no-fp8", action="store_true",
+                    help="skip the supplementary FP8 forward timings")
+    ap.add_argument("--fp8-only", action="store_true",
+                    help="only time the FP8 path and print it as one JSON line")
     ap.add_argument("--hbm-only", action="store_true",
                     help="only time the supplementary shapes and print them as one JSON line")
     ap.add_argument("--hbm-filter", default="",
@@ -121,6 +127,13 @@ def main():
     import exact_io_aware_flash_amd as fa
     from synth import CONFIGS, qkv_inputs
 
+    if args.fp8_only:
+        fa.load_library()  # fails loudly if the HIP library is missing
+        if not torch.cuda.is_available():
+            print("no GPU visible", file=sys.stderr)
+            sys.exit(1)
+        print(json.dumps({"fp8": fp8_forward(fa, torch, CONFIGS[5], qkv_inputs)}), flush=True)
+        return
     if args.sparse_only:
         fa.load_library()  # fails loudly if the HIP library is missing
         if not torch.cuda.is_available():
@@ -219,6 +232,7 @@ def main():
 
     hbm = None if args.no_hbm_shapes else hbm_shapes(fa, torch)
     sparse = None if args.no_sparse else block_sparse(fa, torch, w, qkv_inputs)
+    fp8 = None if args.no_fp8 else fp8_forward(fa, torch, w, qkv_inputs)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -251,6 +265,7 @@ def main():
         "cpu_baseline": cpu,
         "hbm_shapes": hbm,
         "block_sparse": sparse,
+        "fp8": fp8,
     }
     print(json.dumps(line), flush=True)
 
@@ -358,6 +373,41 @@ def block_sparse(fa, torch, w, qkv_inputs):
                     "bwd_tflops": round(10.0 * d * pairs / (bwd_us * 1e-6) / 1e12, 1)})
     del q, k, v, do, o, lse, grads, ws
     return out
+
+
+def fp8_forward(fa, torch, w, qkv_inputs):
+    """The FP8 path on the main workload's forward (rotated Q and K): the three quantiser
+    calls and the FP8 forward, each timed by time_us. The forward's rate uses the same FLOP
+    convention as the bf16 figures, against the dense E4M3 MFMA peak; the quantiser's
+    bytes are the 16-bit input read and the codes written."""
+    from synth import random_signs
+
+    dev = torch.device("cuda:0")
+    B, H, N, d = w.B, w.H, w.N_q, w.d
+    q, k, v, _ = (t.to(dev) if t is not None else None for t in qkv_inputs(w, with_dout=False))
+    signs = random_signs(d, 4243)
+    q8, qa = fa.fa_fp8_quantize(q, fa.FA_FP8_Q, signs)
+    k8, ka = fa.fa_fp8_quantize(k, fa.FA_FP8_K, signs)
+    v8, va = fa.fa_fp8_quantize(v, fa.FA_FP8_V)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    fwd_us = time_us(torch, lambda: fa.fa_fwd_fp8(q8, k8, v8, qa, ka, va, N, N, causal=True,
+                                                  scale=w.scale, rotated=True, out=o, lse=lse))
+    quant = {}
+    for name, x, lay, sg in (("q", q, fa.FA_FP8_Q, signs), ("k", k, fa.FA_FP8_K, signs),
+                             ("v", v, fa.FA_FP8_V, None)):
+        us = time_us(torch, lambda: fa.fa_fp8_quantize(x, lay, sg))
+        nbytes = x.numel() * 3 + (x.numel() * 2 if lay == fa.FA_FP8_V else 0)  # V reads twice
+        quant[name] = {"us": round(us, 1), "GB/s": round(nbytes / (us * 1e-6) / 1e9, 1)}
+    fl = 4.0 * B * H * N * N * d / 2.0
+    bf16_fwd_us = time_us(torch, lambda: fa.fa_fwd(q, k, v, causal=True, scale=w.scale,
+                                                   out=o, lse=lse))
+    return {"shape": f"bf16 causal B{B} H{H} N{N} d{d}, rotated Q/K",
+            "fwd_fp8_us": round(fwd_us, 1),
+            "fwd_fp8_tflops": round(fl / (fwd_us * 1e-6) / 1e12, 1),
+            "fwd_fp8_frac_of_fp8_peak": round(fl / (fwd_us * 1e-6) / 1e12 / PEAK_FP8_TFLOPS, 4),
+            "fwd_bf16_us": round(bf16_fwd_us, 1),
+            "quantise": quant}
 
 
 def cpu_baseline(w, q, k, v, do, seconds):

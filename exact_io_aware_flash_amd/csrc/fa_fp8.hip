@@ -459,7 +459,9 @@ hipError_t launch_fp8_quant(fa_dtype dt, int d, Fp8QuantArgs& a, hipStream_t st)
 
 template <typename T, int D>
 static hipError_t launch_fwd8_t(Fp8FwdArgs& a, hipStream_t st) {
-  constexpr int NW = 4, ST = 4;
+  // 4 waves x 32 rows, one tile in flight (measured on the bf16 causal N = 8192 d = 128
+  // shape: 344 us, against 353 us with 2 or 3 tiles in flight and 370-386 us with 8 waves)
+  constexpr int NW = 4, ST = 2;
   a.nqb = (a.Nq + 32 * NW - 1) / (32 * NW);
   a.sched = ((a.B * a.H) % 8 == 0) ? kSchedXcd : kSchedHeadMajor;
   const dim3 grid((unsigned)(a.B * a.H * a.nqb)), block(NW * 64);
