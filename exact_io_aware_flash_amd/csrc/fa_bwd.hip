@@ -362,7 +362,11 @@ void bwd_dkdv_kernel(const BwdArgs a) {
       full &= q0t + off >= kw0 + 31;
     }
     if (ranged) {
-      const int* sm = a.qsum + 4 * t;
+      // tile t's summary through the constant address space: a scalar load, whose wait
+      // does not cover the ring's loads in flight (a vector load here made every tile wait
+      // for the tile just issued)
+      const __attribute__((address_space(4))) int* sm =
+          (const __attribute__((address_space(4))) int*)a.qsum + 4 * t;
       skip |= kw1 <= sm[0] || kw0 >= sm[3];
       full &= sm[1] <= kw0 && sm[2] >= kw0 + 32;
     }
