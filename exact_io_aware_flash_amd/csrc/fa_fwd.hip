@@ -956,12 +956,14 @@ static int device_cus() {
 //   d = 64: 4 waves x 32 rows, 64-key tiles, 4 stages (64 KB).
 //   d = 128, few query rows split over key ranges: 4 waves, 32-key tiles, 4 stages
 //     (64 KB: two workgroups, i.e. two computing waves, per compute unit).
-//   d = 128 otherwise: 8 waves x 32 rows, 64-key tiles, 4 stages (128 KB). When a head has
-//     more than kFwdFewRows rows and the grid has fewer than four such 256-row units per
-//     compute unit, or rows carry key ranges (whose visible tiles smaller blocks follow
-//     more closely): 4 waves x 32 rows with 2 stages (64 KB, two workgroups per compute
-//     unit), where twice as many, fuller blocks balance the load better than a deeper ring
-//     helps. With few rows (decode-like) the deeper ring of the first form wins.
+//   d = 128 otherwise: 8 waves x 32 rows, 64-key tiles; 4 stages (128 KB) when a head has
+//     at most kFwdFewRows rows (decode-like: the load of every key is compulsory and a
+//     deeper ring hides more of it), else 2 stages (64 KB: one tile in flight measured
+//     3-4 % faster than three on the causal N = 8192 shape). When a head has more than
+//     kFwdFewRows rows and the grid has fewer than four such 256-row units per compute
+//     unit, or rows carry key ranges (whose visible tiles smaller blocks follow more
+//     closely): 4 waves x 32 rows with 2 stages (64 KB, two workgroups per compute unit),
+//     where twice as many, fuller blocks balance the load better.
 // For N_q <= kFwdFewRows every d = 128 variant holds the whole head in one query block.
 template <typename T>
 static hipError_t launch16_for(int d, bool bias, FwdArgs& a, hipStream_t st) {
@@ -974,7 +976,7 @@ static hipError_t launch16_for(int d, bool bias, FwdArgs& a, hipStream_t st) {
       (long long)a.B * a.H * ((a.Nq + 255) / 256) * (a.n_split > 1 ? a.n_split : 1);
   if (a.key_start != nullptr || units256 < 4LL * device_cus())
     return launch16<T, 128, 64, 4, 2>(bias, a, st);
-  return launch16<T, 128, 64, 8, 4>(bias, a, st);
+  return launch16<T, 128, 64, 8, 2>(bias, a, st);
 }
 
 hipError_t launch_fwd(fa_dtype dt, int d, bool bias, FwdArgs& a, hipStream_t st) {
