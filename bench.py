@@ -12,7 +12,8 @@ kernel (see ALG_FLOPS below). The CPU baseline times the float64 oracle (fwd + b
 on a bounded sample of whole (b, h) heads of the same workload. A supplementary list
 times the forward on short sequences and decode-like shapes (compulsory-byte GB/s), and
 another the forward and backward of the same workload under block-sparse bitmaps, and
-the FP8 path (quantiser + FP8 forward) on the same inputs.
+the FP8 path (quantiser + FP8 forward) on the same inputs, and a sweep over the five
+synthetic workloads (forward of each, backward of the last).
 """
 
 from __future__ import annotations
@@ -74,6 +75,8 @@ def parse():
                     help="skip the supplementary block-sparse fwd/bwd timings")
     ap.add_argument("--sparse-only", action="store_true",
                     help="only time the block-sparse shapes and print them as one JSON line")
+    ap.add_argument("--no-sweep", action="store_true",
+                    help="skip the supplementary forward timings of the five workloads")
     ap.add_argument("--no-fp8", action="store_true",
                     help="skip the supplementary FP8 forward timings")
     ap.add_argument("--fp8-only", action="store_true",
@@ -233,6 +236,7 @@ def main():
     hbm = None if args.no_hbm_shapes else hbm_shapes(fa, torch)
     sparse = None if args.no_sparse else block_sparse(fa, torch, w, qkv_inputs)
     fp8 = None if args.no_fp8 else fp8_forward(fa, torch, w, qkv_inputs)
+    sweep = None if args.no_sweep else workload_sweep(fa, torch)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -266,6 +270,7 @@ def main():
         "hbm_shapes": hbm,
         "block_sparse": sparse,
         "fp8": fp8,
+        "sweep": sweep,
     }
     print(json.dumps(line), flush=True)
 
@@ -372,6 +377,56 @@ def block_sparse(fa, torch, w, qkv_inputs):
                     "fwd_tflops": round(4.0 * d * pairs / (fwd_us * 1e-6) / 1e12, 1),
                     "bwd_tflops": round(10.0 * d * pairs / (bwd_us * 1e-6) / 1e12, 1)})
     del q, k, v, do, o, lse, grads, ws
+    return out
+
+
+def workload_sweep(fa, torch):
+    """Forward of each of the five synthetic workloads (fwd + bwd for the last), timed by
+    time_us, in TFLOP/s by the convention (4 B H N_q N_k d, halved for causal; masks and
+    bias otherwise not discounted) and by the visible (query, key) pairs (4 d each), both
+    also as a fraction of the MFMA peak of the input type."""
+    from synth import CONFIGS, key_ranges, qkv_inputs, seed_for
+
+    dev = torch.device("cuda:0")
+    out = []
+    for wid in sorted(CONFIGS):
+        w = CONFIGS[wid]
+        q, k, v, do = (t.to(dev) if t is not None else None for t in qkv_inputs(w))
+        kw = dict(causal=w.causal, scale=w.scale)
+        if w.bias_slope is not None:
+            kw["bias_slopes"] = w.bias_slope
+        if w.key_range:
+            ks, ke = key_ranges(w.N_q, w.N_k, seed_for(w.wid, 9), 128, w.N_k // 2, 64)
+            kw.update(key_start=ks.to(dev), key_end=ke.to(dev))
+        o = torch.empty_like(q)
+        lse = torch.empty((w.B, w.H, w.N_q), dtype=torch.float32, device=dev)
+        fwd_us = time_us(torch, lambda: fa.fa_fwd(q, k, v, out=o, lse=lse, **kw))
+        fl = 4.0 * w.B * w.H * w.N_q * w.N_k * w.d * (0.5 if w.causal else 1.0)
+        # visible (query, key) pairs per head, for the work actually done
+        if w.key_range:
+            pairs = float((ke.clamp(0, w.N_k) - ks.clamp(0, w.N_k)).clamp(min=0).sum())
+        elif w.causal:
+            pairs = w.N_q * (w.N_q + 1) / 2.0 + (w.N_k - w.N_q) * w.N_q
+        else:
+            pairs = float(w.N_q * w.N_k)
+        vis = 4.0 * w.d * pairs * w.B * w.H
+        peak = 157.3 if w.dtype == "f32" else PEAK_BF16_TFLOPS  # fp32 / 16-bit dense MFMA
+        ent = {"workload": w.name, "fwd_us": round(fwd_us, 1),
+               "fwd_tflops": round(fl / (fwd_us * 1e-6) / 1e12, 1),
+               "fwd_frac_of_peak": round(fl / (fwd_us * 1e-6) / 1e12 / peak, 4),
+               "fwd_visible_tflops": round(vis / (fwd_us * 1e-6) / 1e12, 1),
+               "fwd_visible_frac_of_peak": round(vis / (fwd_us * 1e-6) / 1e12 / peak, 4)}
+        if w.backward:
+            grads = tuple(torch.empty(q.shape, dtype=torch.float32, device=dev) for _ in range(3))
+            ws = torch.empty(fa.fa_bwd_workspace_bytes(w.B, w.H, w.N_q, w.N_k, w.d),
+                             dtype=torch.uint8, device=dev)
+            fa.fa_fwd(q, k, v, out=o, lse=lse, **kw)
+            bwd_us = time_us(torch, lambda: fa.fa_bwd(do, q, k, v, o, lse, grads=grads,
+                                                      workspace=ws, **kw))
+            ent.update(bwd_us=round(bwd_us, 1),
+                       bwd_tflops=round(2.5 * fl / (bwd_us * 1e-6) / 1e12, 1))
+        out.append(ent)
+        del q, k, v, do, o, lse
     return out
 
 
