@@ -60,6 +60,7 @@ class MaskBiasDesc(ctypes.Structure):
         ("block_k", ctypes.c_int32),
         ("mask_stride_b", ctypes.c_int64),
         ("mask_stride_h", ctypes.c_int64),
+        ("dslopes", ctypes.c_void_p),
     ]
 
 
@@ -153,14 +154,15 @@ def _check_dev(name: str, t: torch.Tensor, dtype=None, shape=None):
         raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
 
 
-def _desc(bias_slopes, key_start, key_end, H, N_q, block_mask=None, B=1, N_k=1):
+def _desc(bias_slopes, key_start, key_end, H, N_q, block_mask=None, B=1, N_k=1, dslopes=None):
     """Build the mask/bias descriptor; returns (desc or None, keepalive).
 
     ``block_mask``: (bitmap, block_q, block_k) with bitmap a contiguous uint8 device tensor
     [nbq, nbk] (shared), [H, nbq, nbk] (per head) or [B, H, nbq, nbk], where
     nbq = ceil(N_q / block_q) and nbk = ceil(N_k / block_k); a zero byte masks its block.
     """
-    if bias_slopes is None and key_start is None and key_end is None and block_mask is None:
+    if (bias_slopes is None and key_start is None and key_end is None and block_mask is None
+            and dslopes is None):
         return None, None
     d = MaskBiasDesc()
     keep = []
@@ -202,6 +204,9 @@ def _desc(bias_slopes, key_start, key_end, H, N_q, block_mask=None, B=1, N_k=1):
         _check_dev("key_end", key_end, torch.int32, (N_q,))
         d.key_start = key_start.data_ptr()
         d.key_end = key_end.data_ptr()
+    if dslopes is not None:
+        _check_dev("dslopes", dslopes, torch.float32, (d.n_slopes,))
+        d.dslopes = dslopes.data_ptr()
     return d, keep
 
 
@@ -300,10 +305,12 @@ def fa_bwd(dout: torch.Tensor, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor
            key_start: Optional[torch.Tensor] = None, key_end: Optional[torch.Tensor] = None,
            grad_dtype: torch.dtype = torch.float32, workspace: Optional[torch.Tensor] = None,
            grads=None, phases: int = FA_BWD_ALL, stream: Optional[torch.cuda.Stream] = None,
-           block_mask=None):
+           block_mask=None, dslopes: Optional[torch.Tensor] = None):
     """Backward by recomputation: returns (dQ, dK, dV) in ``grad_dtype``.
 
     ``o`` and ``lse`` are the outputs of :func:`fa_fwd` for the same inputs.
+    ``dslopes``: optional float32 device tensor of len(bias_slopes) that receives
+    dL/dslope (``fa_mask_bias_desc.dslopes``).
     ``grads``: optional preallocated (dq, dk, dv); ``phases``: subset of FA_BWD_ALL
     (``fa_bwd_phases``), e.g. to run or time the launches separately with one workspace.
     """
@@ -332,7 +339,7 @@ def fa_bwd(dout: torch.Tensor, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor
     wsb = fa_bwd_workspace_bytes(B, H, N_q, N_k, d)
     if workspace is None:
         workspace = torch.empty(max(wsb, 16), dtype=torch.uint8, device=q.device)
-    desc, keep = _desc(bias_slopes, key_start, key_end, H, N_q, block_mask, B, N_k)
+    desc, keep = _desc(bias_slopes, key_start, key_end, H, N_q, block_mask, B, N_k, dslopes)
     st = lib.fa_bwd_phases(int(phases), q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
                     dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
                     _DT[grad_dtype], workspace.data_ptr(), workspace.numel() * workspace.element_size(),

@@ -259,12 +259,12 @@ fa_status fa_fwd_split(const void* q, const void* k, const void* v, void* o, flo
 }
 
 size_t fa_bwd_workspace_bytes(int B, int H, int N_q, int N_k, int d) {
-  (void)N_k; (void)d;
-  if (B < 1 || H < 1 || N_q < 1) return 0;
+  (void)d;
+  if (B < 1 || H < 1 || N_q < 1 || N_k < 1) return 0;
   // delta = rowsum(dO * O) (one float per query row) + the key-range summary of every
-  // 64-row query tile (4 int32) + LSE * log2(e) (one float per query row), each rounded
-  // up to 256 bytes
-  return bwd_workspace_bytes(B, H, N_q);
+  // 64-row query tile (4 int32) + LSE * log2(e) (one float per query row) + one float
+  // per (b, h, 128-key block) for the slope gradient, each rounded up to 256 bytes
+  return bwd_workspace_bytes(B, H, N_q, N_k);
 }
 
 fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
@@ -302,6 +302,13 @@ fa_status fa_bwd_phases(int phases, const void* q, const void* k, const void* v,
   a.delta = static_cast<float*>(workspace);
   a.qsum = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + bwd_qsum_offset(B, H, N_q));
   a.lse2 = reinterpret_cast<float*>(static_cast<char*>(workspace) + bwd_lse2_offset(B, H, N_q));
+  if (mb != nullptr && mb->dslopes != nullptr) {
+    if (mb->bias_kind != FA_BIAS_DIST_LINEAR) return FA_ERR_MASK;
+    if (reinterpret_cast<uintptr_t>(mb->dslopes) & 3u) return FA_ERR_ALIGN;
+    a.dslopes = mb->dslopes;
+    a.dslope_part =
+        reinterpret_cast<float*>(static_cast<char*>(workspace) + bwd_dslope_offset(B, H, N_q));
+  }
   a.dq = dq; a.dk = dk; a.dv = dv;
   a.B = B; a.H = H; a.Nq = N_q; a.Nk = N_k;
   a.causal = causal ? 1 : 0;

@@ -196,6 +196,7 @@ void bwd_dkdv_kernel(const BwdArgs a) {
   f32x16 dv[DB], dk[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) { dv[db] = f32x16{}; dk[db] = f32x16{}; }
+  float sgrad = 0.f;  // this lane's share of dL/dslope (bias only)
 
   // LDS offsets inside a swizzled tile (see DmaTile): row reads of query row 32qb + n,
   // chunk 2ks + h (A operands of S and dP); transposing gathers of 8 query rows of one
@@ -247,14 +248,15 @@ void bwd_dkdv_kernel(const BwdArgs a) {
       l4[q4] = *reinterpret_cast<const f32x4*>(sb + L::LSE + r0 * 4);
       d4[q4] = *reinterpret_cast<const f32x4*>(sb + L::DLT + r0 * 4);
     }
-    float p[16], ds[16];
+    float p[16], ds[16], adist[BIAS ? 16 : 1];
 #pragma unroll
     for (int g = 0; g < 16; ++g) {
       const float lq = l4[g / 4][g % 4];  // already in log2 units
       float x;
       if constexpr (BIAS) {
         const float dist = (float)(q0t + 32 * qb + 4 * h - key) + (float)(8 * (g / 4) + (g % 4));
-        x = __builtin_fmaf(sc[g], sl2, __builtin_fmaf(slope2, __builtin_fabsf(dist), -lq));
+        adist[g] = __builtin_fabsf(dist);
+        x = __builtin_fmaf(sc[g], sl2, __builtin_fmaf(slope2, adist[g], -lq));
       } else {
         x = __builtin_fmaf(sc[g], sl2, -lq);
       }
@@ -283,6 +285,11 @@ void bwd_dkdv_kernel(const BwdArgs a) {
     }
 #pragma unroll
     for (int g = 0; g < 16; ++g) ds[g] = p[g] * (dp[g] - d4[g / 4][g % 4]);
+    if constexpr (BIAS) {
+      // the slope's gradient: dS |i - j| over the visible entries (masked ones have p = 0)
+#pragma unroll
+      for (int g = 0; g < 16; ++g) sgrad = __builtin_fmaf(ds[g], adist[g], sgrad);
+    }
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
       u32x4 pa, dsa;
@@ -385,6 +392,23 @@ void bwd_dkdv_kernel(const BwdArgs a) {
       }
     }
     if (p + 1 < n_pos) land(min(p + P, n_pos - 1) - (p + 1));
+  }
+
+  // the workgroup's partial of dL/dslope (every workgroup writes one, zero if it saw
+  // nothing, so the reduction reads only values of this call)
+  if constexpr (BIAS) {
+    if (a.dslope_part != nullptr) {
+      __shared__ float sred[NW];
+      const float w = wave_fsum(sgrad);
+      if (lane == 0) sred[wid_s] = w;
+      __syncthreads();
+      if (tid == 0) {
+        float acc = 0.f;
+#pragma unroll
+        for (int i = 0; i < NW; ++i) acc += sred[i];
+        a.dslope_part[(size_t)bh * a.nblk + kb] = acc;
+      }
+    }
   }
 
   // epilogue: lane holds column d = 32*db + n for keys kw0 + res_row(g, h)
@@ -687,8 +711,26 @@ size_t bwd_lse2_offset(int B, int H, int Nq) {
   const size_t nt = (size_t)(Nq + kDkdvBR - 1) / kDkdvBR;
   return bwd_qsum_offset(B, H, Nq) + ((nt * 4 * sizeof(int32_t) + 255) & ~(size_t)255);
 }
-size_t bwd_workspace_bytes(int B, int H, int Nq) {
+size_t bwd_dslope_offset(int B, int H, int Nq) {
   return bwd_lse2_offset(B, H, Nq) + (((size_t)B * H * Nq * sizeof(float) + 255) & ~(size_t)255);
+}
+size_t bwd_workspace_bytes(int B, int H, int Nq, int Nk) {
+  const size_t nblk = (size_t)(Nk + 32 * 4 - 1) / (32 * 4);  // key blocks of the dK/dV pass
+  return bwd_dslope_offset(B, H, Nq) + (((size_t)B * H * nblk * sizeof(float) + 255) & ~(size_t)255);
+}
+
+// dL/dslope from the dK/dV pass's per-workgroup partials, one thread per slope, summed in
+// a fixed order (batch, then key block; all heads for a shared slope)
+__global__ void dslope_reduce_kernel(const float* __restrict__ part, int B, int H, int nblk,
+                                     int n_slopes, float* __restrict__ out) {
+  const int s = threadIdx.x;
+  if (s >= n_slopes) return;
+  const int h0 = n_slopes == 1 ? 0 : s, h1 = n_slopes == 1 ? H : s + 1;
+  float acc = 0.f;
+  for (int b = 0; b < B; ++b)
+    for (int h = h0; h < h1; ++h)
+      for (int k = 0; k < nblk; ++k) acc += part[((size_t)b * H + h) * nblk + k];
+  out[s] = acc;
 }
 
 template <typename T, int D, int DKDV_NW, int DKDV_WPE, int DQ_BC, int DQ_NW, int DQ_WPE>
@@ -727,6 +769,12 @@ static hipError_t launch_bwd_t(bool bias, int phases, BwdArgs& a, hipStream_t st
       hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, kDkdvBR, DKDV_NW, DKDV_WPE, false, false>), grid, block, 0, st, b);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
+    if (bias && a.dslopes != nullptr) {
+      hipLaunchKernelGGL(dslope_reduce_kernel, dim3(1), dim3(FA_MAX_SLOPES), 0, st,
+                         b.dslope_part, a.B, a.H, b.nblk, a.n_slopes, a.dslopes);
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
   }
   // dQ
   if (phases & FA_BWD_DQ) {

@@ -75,6 +75,10 @@ struct BwdArgs {
   float scale;
   float sl2;
   float slope2[FA_MAX_SLOPES];
+  // slope gradient (NULL: not wanted): per-workgroup partial sums of dS |i - j| of the
+  // dK/dV pass [B*H][nblk] in the workspace, reduced into dslopes[n_slopes]
+  float* dslope_part;
+  float* dslopes;
   // block-sparse bitmap, as in FwdArgs
   const uint8_t* bmask;
   int bq, bk, nkb;
@@ -93,7 +97,8 @@ hipError_t launch_mask_summary(const int32_t* ks, const int32_t* ke, int Nq, int
 // LSE * log2(e) at bwd_lse2_offset.
 size_t bwd_qsum_offset(int B, int H, int Nq);
 size_t bwd_lse2_offset(int B, int H, int Nq);
-size_t bwd_workspace_bytes(int B, int H, int Nq);
+size_t bwd_dslope_offset(int B, int H, int Nq);
+size_t bwd_workspace_bytes(int B, int H, int Nq, int Nk);
 
 // FP8 quantiser (fa_fp8_quantize): one launch per tensor (V: an amax pass first)
 struct Fp8QuantArgs {

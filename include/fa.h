@@ -104,6 +104,12 @@ typedef enum fa_bias_kind {
  *              The bitmap is read during the enqueued work; it must stay valid until the
  *              stream has passed the call. 16-bit inputs only (float32: FA_ERR_UNSUPPORTED);
  *              N_q and N_k at most FA_MAX_SPARSE_N (FA_ERR_UNSUPPORTED beyond).
+ *  dslopes : DEVICE pointer to n_slopes floats, or NULL. fa_bwd (and fa_bwd_phases with
+ *              FA_BWD_DKDV) writes there the gradient of the same loss with respect to the
+ *              bias slopes: dL/dslope_h = sum over b, i, j of dS_{b,h,i,j} |i - j| (dS the
+ *              gradient with respect to the scores), or its sum over heads for one shared
+ *              slope; it needs FA_BIAS_DIST_LINEAR (else FA_ERR_MASK). The reduction runs
+ *              in a fixed order, so the result is deterministic. fa_fwd ignores it.
  *  A row with no visible key (after causal, range and block masking) gets O = 0 and
  *  LSE = -inf. */
 #define FA_MAX_SPARSE_N 65536
@@ -118,6 +124,7 @@ typedef struct fa_mask_bias_desc {
   int32_t block_k;
   int64_t mask_stride_b;
   int64_t mask_stride_h;
+  float* dslopes;
 } fa_mask_bias_desc;
 
 /* Forward pass.

@@ -212,19 +212,23 @@ def attention_probabilities(q, k, scale: float, b: int = 0, h: int = 0, causal: 
 
 def attention_backward(q, k, v, dout, scale: float, causal: bool = False, bias_slopes=None,
                        key_start=None, key_end=None, max_chunk_elems: int = 1 << 24,
-                       block_mask=None):
+                       block_mask=None, return_dslopes: bool = False):
     """Analytic float64 gradients (dQ, dK, dV) of L = sum(O * dO), each [B,H,N,d].
 
     Textbook softmax Jacobian with P recomputed from Q and K:
         dV = P^T dO,  dP = dO V^T,  D_i = sum_j P_ij dP_ij,
         dS = P o (dP - D),  dQ = scale * dS K,  dK = scale * dS^T Q.
-    No gradient flows to the bias or the mask.
+    No gradient flows to the mask. With return_dslopes (and bias_slopes given) a fourth
+    result is dL/dslope: the bias slope_h |i - j| enters S additively, so
+        dL/dslope_h = sum_{b, i, j} dS_{b,h,i,j} |i - j|,
+    one value per head, or one in all (summed over heads) for a single shared slope.
     """
     B, H, n_q, d = q.shape
     n_k = k.shape[2]
     dq = np.zeros((B, H, n_q, d), dtype=np.float64)
     dk = np.zeros((B, H, n_k, d), dtype=np.float64)
     dv = np.zeros((B, H, n_k, d), dtype=np.float64)
+    dslope = np.zeros(H, dtype=np.float64)
     for b in range(B):
         for h in range(H):
             kb, vb = _f64(k[b, h]), _f64(v[b, h])
@@ -239,7 +243,14 @@ def attention_backward(q, k, v, dout, scale: float, causal: bool = False, bias_s
                 ds = p * (dp - dsum[:, None])
                 dq[b, h, rows] = float(scale) * (ds @ kb)
                 dk[b, h] += float(scale) * (ds.T @ qr)
-    return dq, dk, dv
+                if return_dslopes:
+                    dslope[h] += float((ds * distance_bias(rows, n_k, 1.0)).sum())
+    if not return_dslopes:
+        return dq, dk, dv
+    if bias_slopes is None:
+        raise ValueError("return_dslopes needs bias_slopes")
+    shared = np.atleast_1d(np.asarray(bias_slopes)).shape[0] == 1
+    return dq, dk, dv, (dslope.sum(keepdims=True) if shared else dslope)
 
 
 def tiled_online_forward(q, k, v, scale: float, br: int, bc: int, causal: bool = False,

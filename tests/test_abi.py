@@ -47,9 +47,11 @@ def test_status_strings_and_version():
 
 def test_workspace_bytes():
     # delta (one float per query row) + key-range summary (4 int32 per 64-row tile) +
-    # LSE * log2(e) (one float per query row), each rounded up to 256 bytes
-    assert fa.fa_bwd_workspace_bytes(2, 16, 8192, 8192, 128) == 2 * (2 * 16 * 8192 * 4) + 2048
-    assert fa.fa_bwd_workspace_bytes(1, 1, 3, 5, 64) == 768
+    # LSE * log2(e) (one float per query row) + one float per (b, h, 128-key block) for
+    # the slope gradient, each rounded up to 256 bytes
+    assert (fa.fa_bwd_workspace_bytes(2, 16, 8192, 8192, 128)
+            == 2 * (2 * 16 * 8192 * 4) + 2048 + 2 * 16 * 64 * 4)
+    assert fa.fa_bwd_workspace_bytes(1, 1, 3, 5, 64) == 1024
     assert fa.fa_bwd_workspace_bytes(0, 1, 3, 5, 64) == 0
 
 
@@ -121,7 +123,7 @@ def test_block_mask_descriptor_validation():
     assert fwd(mb=ctypes.byref(d), dtype=fa.FA_F32) == 8  # 16-bit inputs only
     assert fwd(mb=ctypes.byref(d), Nk=65536 + 64) == 8    # beyond FA_MAX_SPARSE_N
     assert fwd(mb=ctypes.byref(d), Nq=65536 + 1) == 8
-    assert ctypes.sizeof(fa.MaskBiasDesc) == 64  # the C layout of fa_mask_bias_desc
+    assert ctypes.sizeof(fa.MaskBiasDesc) == 72  # the C layout of fa_mask_bias_desc
 
 
 def bwd(**kw):

@@ -115,3 +115,44 @@ def test_fp32_backward_reports_unsupported():
     with pytest.raises(fa.FaError) as e:
         fa.fa_bwd(q, q, q, q, o, lse)
     assert e.value.status == 8
+
+
+@pytest.mark.parametrize("dtype,d", [(torch.bfloat16, 128), (torch.float16, 64)])
+@pytest.mark.parametrize("causal,ranged,per_head", [(True, False, True), (False, True, False),
+                                                    (True, True, True)])
+def test_slope_gradient(dtype, d, causal, ranged, per_head):
+    # dL/dslope = sum dS |i - j| (per head, or over all heads for one shared slope);
+    # tolerance 1e-2 of sum |dS| |i - j|, the scale of the terms being added
+    B, H, nq, nk = 2, 3, 300, 330
+    q, k, v, do = (normal((B, H, n, d), dtype, 8800 + i) for i, n in enumerate((nq, nk, nk, nq)))
+    slopes = [-0.02, 0.01, -0.05] if per_head else [-0.03]
+    kw = dict(causal=causal, scale=1.0 / math.sqrt(d), bias_slopes=slopes)
+    if ranged:
+        ks, ke = key_ranges(nq, nk, seed=8805, block=64, width=nk // 2, jitter=32)
+        kw.update(key_start=ks.to(DEV), key_end=ke.to(DEV))
+    qd, kd, vd, dod = (t.to(DEV) for t in (q, k, v, do))
+    o, lse = fa.fa_fwd(qd, kd, vd, **kw)
+    ds = torch.full((len(slopes),), float("nan"), dtype=torch.float32, device=DEV)
+    got = fa.fa_bwd(dod, qd, kd, vd, o, lse, dslopes=ds, **kw)
+    torch.cuda.synchronize()
+    ref_kw = dict(causal=causal, bias_slopes=np.float32(slopes).astype(np.float64))
+    if ranged:
+        ref_kw.update(key_start=ks.numpy(), key_end=ke.numpy())
+    *want, dref = oracle.attention_backward(np64(q), np64(k), np64(v), np64(do), kw["scale"],
+                                            return_dslopes=True, **ref_kw)
+    check_grads(got, want, "grads with dslopes")
+    # scale of the terms: sum |dS| |i - j| from the oracle's probabilities
+    tot = np.zeros(H)
+    for b in range(B):
+        for h in range(H):
+            p = oracle.attention_probabilities(np64(q), np64(k), kw["scale"], b, h, causal,
+                                               bias_slopes=ref_kw["bias_slopes"],
+                                               key_start=ref_kw.get("key_start"),
+                                               key_end=ref_kw.get("key_end"))
+            dp = np64(do)[b, h] @ np64(v)[b, h].T
+            dsm = p * (dp - (p * dp).sum(axis=1, keepdims=True))
+            dist = np.abs(np.arange(nq)[:, None] - np.arange(nk)[None, :])
+            tot[h] += np.abs(dsm * dist).sum()
+    scale_terms = tot if per_head else tot.sum(keepdims=True)
+    err = np.abs(ds.cpu().numpy() - dref)
+    assert np.all(err <= 1e-2 * scale_terms + 1e-4), (ds.cpu().numpy(), dref, scale_terms)

@@ -161,6 +161,52 @@ def test_backward_matches_multiprecision_finite_differences(ci):
             assert abs(fd - grad[0, 0][idx]) <= 1e-10, (name, idx, fd, grad[0, 0][idx])
 
 
+@pytest.mark.parametrize("ci", [4, 6])
+def test_slope_gradient_matches_multiprecision_finite_differences(ci):
+    # dL/dslope = sum dS |i - j|, against a central difference of the 50-digit forward
+    c = CASES[ci]
+    q, k, v, ks, ke = _case_arrays(c, 500 + ci)
+    do = rnd((c["n_q"], c["d"]), 600 + ci)
+    scale = 0.7
+    slope = c["slope"]
+    ksl = None if ks is None else ks.tolist()
+    kel = None if ke is None else ke.tolist()
+    *_, ds = oracle.attention_backward(q[None, None], k[None, None], v[None, None],
+                                       do[None, None], scale, causal=c["causal"],
+                                       bias_slopes=slope, key_start=ks, key_end=ke,
+                                       return_dslopes=True)
+    hstep = mpmath.mpf("1e-20")
+    fp = _mp_loss(q, k, v, do, scale, c["causal"], mpmath.mpf(slope) + hstep, ksl, kel)
+    fm = _mp_loss(q, k, v, do, scale, c["causal"], mpmath.mpf(slope) - hstep, ksl, kel)
+    fd = float((fp - fm) / (2 * hstep))
+    assert ds.shape == (1,) and abs(fd - ds[0]) <= 1e-10, (fd, ds)
+
+
+def test_slope_gradient_per_head_and_shared_against_torch_autograd():
+    # per-head slopes: one gradient each; one shared slope: the sum over heads
+    B, H, n_q, n_k, d = 2, 3, 19, 23, 8
+    q, k, v, do = (rnd((B, H, n, d), 700 + i) for i, n in enumerate((n_q, n_k, n_k, n_q)))
+    slopes = np.array([-0.2, 0.05, 0.1])
+    ts = torch.tensor(slopes, dtype=torch.float64, requires_grad=True)
+    dist = (torch.arange(n_q)[:, None] - torch.arange(n_k)[None, :]).abs().double()
+    allowed = torch.arange(n_k)[None, :] <= torch.arange(n_q)[:, None] + (n_k - n_q)
+    bias = (ts[:, None, None] * dist).masked_fill(~allowed, float("-inf"))
+    out = torch.nn.functional.scaled_dot_product_attention(
+        torch.tensor(q), torch.tensor(k), torch.tensor(v), attn_mask=bias, scale=0.3)
+    (out * torch.tensor(do)).sum().backward()
+    *_, ds = oracle.attention_backward(q, k, v, do, 0.3, causal=True, bias_slopes=slopes,
+                                       return_dslopes=True)
+    assert np.allclose(ds, ts.grad.numpy(), atol=1e-12, rtol=0)
+    *_, ds1 = oracle.attention_backward(q, k, v, do, 0.3, causal=True, bias_slopes=[0.07],
+                                        return_dslopes=True)
+    t1 = torch.tensor(0.07, dtype=torch.float64, requires_grad=True)
+    out1 = torch.nn.functional.scaled_dot_product_attention(
+        torch.tensor(q), torch.tensor(k), torch.tensor(v),
+        attn_mask=(t1 * dist).masked_fill(~allowed, float("-inf")), scale=0.3)
+    (out1 * torch.tensor(do)).sum().backward()
+    assert ds1.shape == (1,) and abs(ds1[0] - float(t1.grad)) <= 1e-12
+
+
 # --------------------------------------------------------------------------
 # torch's CPU float64 reference routines (an independent library path)
 # --------------------------------------------------------------------------
