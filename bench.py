@@ -39,9 +39,9 @@ PEAK_FP8_TFLOPS = 2 * PEAK_BF16_TFLOPS  # dense E4M3 MFMA (published 5.0 PFLOP/s
 # the kernel source they were measured on. A changed source means stale counters -> null.
 TRAFFIC = {
     # kernel: (source hash, bytes read, bytes written) -- profiles/attention_fwd_bwd_bf16_causal_B2H16N8192d128.md
-    "fwd": ("9846343ec35875c5", 286.7e6, 68.2e6),
-    "bwd_dkdv": ("daa286d9a72eb8c4", 270.9e6, 268.4e6),
-    "bwd_dq": ("daa286d9a72eb8c4", 398.5e6, 138.2e6),
+    "fwd": ("9cd335ca4c02996c", 287.5e6, 68.2e6),
+    "bwd_dkdv": ("4237a51d0f3a8f54", 270.9e6, 268.4e6),
+    "bwd_dq": ("4237a51d0f3a8f54", 398.2e6, 138.2e6),
 }
 
 
