@@ -33,7 +33,7 @@ _LIB_PATH = os.path.join(_HERE, "libfa.so")
 _LIB = None
 
 FA_F32, FA_F16, FA_BF16 = 0, 1, 2
-FA_BIAS_NONE, FA_BIAS_DIST_LINEAR = 0, 1
+FA_BIAS_NONE, FA_BIAS_DIST_LINEAR, FA_BIAS_TENSOR = 0, 1, 2
 FA_MAX_SLOPES = 256
 FA_BWD_PREP, FA_BWD_DKDV, FA_BWD_DQ, FA_BWD_ALL = 1, 2, 4, 7
 FA_FP8_Q, FA_FP8_K, FA_FP8_V = 0, 1, 2
@@ -61,6 +61,11 @@ class MaskBiasDesc(ctypes.Structure):
         ("mask_stride_b", ctypes.c_int64),
         ("mask_stride_h", ctypes.c_int64),
         ("dslopes", ctypes.c_void_p),
+        ("bias", ctypes.c_void_p),
+        ("bias_stride_b", ctypes.c_int64),
+        ("bias_stride_h", ctypes.c_int64),
+        ("bias_stride_i", ctypes.c_int64),
+        ("dbias", ctypes.c_void_p),
     ]
 
 
@@ -154,15 +159,19 @@ def _check_dev(name: str, t: torch.Tensor, dtype=None, shape=None):
         raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
 
 
-def _desc(bias_slopes, key_start, key_end, H, N_q, block_mask=None, B=1, N_k=1, dslopes=None):
+def _desc(bias_slopes, key_start, key_end, H, N_q, block_mask=None, B=1, N_k=1, dslopes=None,
+          bias=None, dbias=None):
     """Build the mask/bias descriptor; returns (desc or None, keepalive).
 
     ``block_mask``: (bitmap, block_q, block_k) with bitmap a contiguous uint8 device tensor
     [nbq, nbk] (shared), [H, nbq, nbk] (per head) or [B, H, nbq, nbk], where
     nbq = ceil(N_q / block_q) and nbk = ceil(N_k / block_k); a zero byte masks its block.
+    ``bias``: float32 device tensor of 4 dimensions that broadcasts to [B, H, N_q, N_k]
+    with key stride 1 after broadcasting (a view with zero strides is fine).
+    ``dbias``: float32 device tensor [B, H, N_q, N_k], contiguous (receives dS).
     """
     if (bias_slopes is None and key_start is None and key_end is None and block_mask is None
-            and dslopes is None):
+            and dslopes is None and bias is None and dbias is None):
         return None, None
     d = MaskBiasDesc()
     keep = []
@@ -207,6 +216,24 @@ def _desc(bias_slopes, key_start, key_end, H, N_q, block_mask=None, B=1, N_k=1, 
     if dslopes is not None:
         _check_dev("dslopes", dslopes, torch.float32, (d.n_slopes,))
         d.dslopes = dslopes.data_ptr()
+    if bias is not None:
+        if bias_slopes is not None:
+            raise ValueError("give either bias_slopes or a bias tensor")
+        if not isinstance(bias, torch.Tensor) or not bias.is_cuda or bias.dtype != torch.float32:
+            raise ValueError("bias must be a float32 device tensor")
+        if bias.dim() != 4:
+            raise ValueError("bias must have 4 dimensions broadcastable to [B, H, N_q, N_k]")
+        view = bias.expand(B, H, N_q, N_k)
+        if N_k > 1 and view.stride(3) != 1:
+            raise ValueError("bias needs stride 1 along the key axis")
+        d.bias_kind = FA_BIAS_TENSOR
+        d.bias = view.data_ptr()
+        d.bias_stride_b, d.bias_stride_h, d.bias_stride_i = (
+            view.stride(0) if B > 1 else 0, view.stride(1) if H > 1 else 0,
+            view.stride(2) if N_q > 1 else 0)
+    if dbias is not None:
+        _check_dev("dbias", dbias, torch.float32, (B, H, N_q, N_k))
+        d.dbias = dbias.data_ptr()
     return d, keep
 
 
@@ -215,11 +242,12 @@ def fa_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = Fal
            key_start: Optional[torch.Tensor] = None, key_end: Optional[torch.Tensor] = None,
            out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
            stream: Optional[torch.cuda.Stream] = None,
-           block_mask=None) -> Tuple[torch.Tensor, torch.Tensor]:
+           block_mask=None, bias: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
     """Exact attention forward on the GPU: returns (O [B,H,N_q,d], LSE [B,H,N_q] float32).
 
     q: [B,H,N_q,d], k/v: [B,H,N_k,d], all of one dtype (float32, float16, bfloat16).
     ``bias_slopes``: float or a list of 1 or H floats, bias = slope * |i - j|.
+    ``bias``: float32 tensor broadcastable to [B,H,N_q,N_k], added after scaling.
     ``key_start``/``key_end``: int32 [N_q] device tensors, row i sees keys in [start, end).
     ``block_mask``: (uint8 bitmap, block_q, block_k), see ``_desc``.
     """
@@ -241,7 +269,7 @@ def fa_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = Fal
     if lse is None:
         lse = torch.empty((B, H, N_q), dtype=torch.float32, device=q.device)
     _check_dev("lse", lse, torch.float32, (B, H, N_q))
-    desc, keep = _desc(bias_slopes, key_start, key_end, H, N_q, block_mask, B, N_k)
+    desc, keep = _desc(bias_slopes, key_start, key_end, H, N_q, block_mask, B, N_k, bias=bias)
     st = lib.fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
                     B, H, N_q, N_k, d, float(scale), 1 if causal else 0,
                     ctypes.byref(desc) if desc is not None else None, _DT[q.dtype],
@@ -259,7 +287,7 @@ def fa_fwd_split(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool
                  workspace: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
                  lse: Optional[torch.Tensor] = None,
                  stream: Optional[torch.cuda.Stream] = None,
-                 block_mask=None) -> Tuple[torch.Tensor, torch.Tensor]:
+                 block_mask=None, bias: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
     """Split-key forward (``fa_fwd_split``): same arguments and result as :func:`fa_fwd`,
     with the keys of every head cut into ``n_split`` ranges (0: automatic) whose partial
     results are merged on the GPU. ``workspace``: optional uint8 device tensor of at least
@@ -287,7 +315,7 @@ def fa_fwd_split(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
     _check_dev("workspace", workspace, torch.uint8)
-    desc, keep = _desc(bias_slopes, key_start, key_end, H, N_q, block_mask, B, N_k)
+    desc, keep = _desc(bias_slopes, key_start, key_end, H, N_q, block_mask, B, N_k, bias=bias)
     st = lib.fa_fwd_split(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                           lse.data_ptr(), B, H, N_q, N_k, d, float(scale), 1 if causal else 0,
                           ctypes.byref(desc) if desc is not None else None, _DT[q.dtype],
@@ -305,12 +333,15 @@ def fa_bwd(dout: torch.Tensor, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor
            key_start: Optional[torch.Tensor] = None, key_end: Optional[torch.Tensor] = None,
            grad_dtype: torch.dtype = torch.float32, workspace: Optional[torch.Tensor] = None,
            grads=None, phases: int = FA_BWD_ALL, stream: Optional[torch.cuda.Stream] = None,
-           block_mask=None, dslopes: Optional[torch.Tensor] = None):
+           block_mask=None, dslopes: Optional[torch.Tensor] = None,
+           bias: Optional[torch.Tensor] = None, dbias: Optional[torch.Tensor] = None):
     """Backward by recomputation: returns (dQ, dK, dV) in ``grad_dtype``.
 
     ``o`` and ``lse`` are the outputs of :func:`fa_fwd` for the same inputs.
     ``dslopes``: optional float32 device tensor of len(bias_slopes) that receives
     dL/dslope (``fa_mask_bias_desc.dslopes``).
+    ``bias``: the forward's bias tensor; ``dbias``: optional float32 device tensor
+    [B,H,N_q,N_k] that receives the gradient of every biased score.
     ``grads``: optional preallocated (dq, dk, dv); ``phases``: subset of FA_BWD_ALL
     (``fa_bwd_phases``), e.g. to run or time the launches separately with one workspace.
     """
@@ -339,7 +370,8 @@ def fa_bwd(dout: torch.Tensor, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor
     wsb = fa_bwd_workspace_bytes(B, H, N_q, N_k, d)
     if workspace is None:
         workspace = torch.empty(max(wsb, 16), dtype=torch.uint8, device=q.device)
-    desc, keep = _desc(bias_slopes, key_start, key_end, H, N_q, block_mask, B, N_k, dslopes)
+    desc, keep = _desc(bias_slopes, key_start, key_end, H, N_q, block_mask, B, N_k, dslopes,
+                       bias=bias, dbias=dbias)
     st = lib.fa_bwd_phases(int(phases), q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
                     dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
                     _DT[grad_dtype], workspace.data_ptr(), workspace.numel() * workspace.element_size(),

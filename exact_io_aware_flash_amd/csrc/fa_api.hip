@@ -35,8 +35,8 @@ fa_status check_common(int B, int H, int N_q, int N_k, int d, float scale, fa_dt
 // Fills the bias/mask part of an argument block; returns the status.
 template <class Args>
 fa_status read_desc(const fa_mask_bias_desc* mb, int H, int N_q, int N_k, fa_dtype dtype,
-                    bool& bias, Args& a) {
-  bias = false;
+                    int& bias, Args& a) {
+  bias = kBiasNone;
   a.key_start = nullptr;
   a.key_end = nullptr;
   a.n_slopes = 1;
@@ -45,6 +45,8 @@ fa_status read_desc(const fa_mask_bias_desc* mb, int H, int N_q, int N_k, fa_dty
   a.bq = a.bk = 64;
   a.nkb = 0;
   a.bm_sb = a.bm_sh = 0;
+  a.tbias = nullptr;
+  a.tb_sb = a.tb_sh = a.tb_si = 0;
   if (mb == nullptr) return FA_OK;
   if (mb->block_mask != nullptr) {
     if (mb->block_q < 64 || mb->block_q % 64 != 0 || mb->block_k < 64 || mb->block_k % 64 != 0)
@@ -59,7 +61,9 @@ fa_status read_desc(const fa_mask_bias_desc* mb, int H, int N_q, int N_k, fa_dty
     a.bm_sb = mb->mask_stride_b;
     a.bm_sh = mb->mask_stride_h;
   }
-  if (mb->bias_kind != FA_BIAS_NONE && mb->bias_kind != FA_BIAS_DIST_LINEAR) return FA_ERR_MASK;
+  if (mb->bias_kind != FA_BIAS_NONE && mb->bias_kind != FA_BIAS_DIST_LINEAR &&
+      mb->bias_kind != FA_BIAS_TENSOR)
+    return FA_ERR_MASK;
   if ((mb->key_start == nullptr) != (mb->key_end == nullptr)) return FA_ERR_MASK;
   if (mb->key_start != nullptr) {
     if (!aligned16(mb->key_start) || !aligned16(mb->key_end)) return FA_ERR_ALIGN;
@@ -75,7 +79,18 @@ fa_status read_desc(const fa_mask_bias_desc* mb, int H, int N_q, int N_k, fa_dty
       a.slope2[i] = mb->slopes[i] * 1.4426950408889634f;
     }
     a.n_slopes = mb->n_slopes;
-    bias = true;
+    bias = kBiasSlope;
+  }
+  if (mb->bias_kind == FA_BIAS_TENSOR) {
+    if (mb->bias == nullptr) return FA_ERR_NULL;
+    if (reinterpret_cast<uintptr_t>(mb->bias) & 3u) return FA_ERR_ALIGN;
+    if (mb->bias_stride_b < 0 || mb->bias_stride_h < 0 || mb->bias_stride_i < 0) return FA_ERR_MASK;
+    if (mb->block_mask != nullptr) return FA_ERR_UNSUPPORTED;
+    a.tbias = mb->bias;
+    a.tb_sb = mb->bias_stride_b;
+    a.tb_sh = mb->bias_stride_h;
+    a.tb_si = mb->bias_stride_i;
+    bias = kBiasTensor;
   }
   return FA_OK;
 }
@@ -198,7 +213,7 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
   if (lse != nullptr && (reinterpret_cast<uintptr_t>(lse) & 3u)) return FA_ERR_ALIGN;
   FwdArgs a;
   std::memset(&a, 0, sizeof(a));
-  bool bias = false;
+  int bias = kBiasNone;
   st = read_desc(mb, H, N_q, N_k, dtype, bias, a);
   if (st != FA_OK) return st;
   a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
@@ -242,7 +257,7 @@ fa_status fa_fwd_split(const void* q, const void* k, const void* v, void* o, flo
   if (!aligned16(workspace)) return FA_ERR_ALIGN;
   FwdArgs a;
   std::memset(&a, 0, sizeof(a));
-  bool bias = false;
+  int bias = kBiasNone;
   st = read_desc(mb, H, N_q, N_k, dtype, bias, a);
   if (st != FA_OK) return st;
   a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
@@ -295,7 +310,7 @@ fa_status fa_bwd_phases(int phases, const void* q, const void* k, const void* v,
   if (!aligned16(workspace)) return FA_ERR_ALIGN;
   BwdArgs a;
   std::memset(&a, 0, sizeof(a));
-  bool bias = false;
+  int bias = kBiasNone;
   st = read_desc(mb, H, N_q, N_k, dtype, bias, a);
   if (st != FA_OK) return st;
   a.q = q; a.k = k; a.v = v; a.o = o; a.dout = dout; a.lse = lse;
@@ -308,6 +323,11 @@ fa_status fa_bwd_phases(int phases, const void* q, const void* k, const void* v,
     a.dslopes = mb->dslopes;
     a.dslope_part =
         reinterpret_cast<float*>(static_cast<char*>(workspace) + bwd_dslope_offset(B, H, N_q));
+  }
+  if (mb != nullptr && mb->dbias != nullptr) {
+    if (mb->bias_kind != FA_BIAS_TENSOR) return FA_ERR_MASK;
+    if (reinterpret_cast<uintptr_t>(mb->dbias) & 3u) return FA_ERR_ALIGN;
+    a.dbias = mb->dbias;
   }
   a.dq = dq; a.dk = dk; a.dv = dv;
   a.B = B; a.H = H; a.Nq = N_q; a.Nk = N_k;

@@ -20,6 +20,7 @@
 //            transposed) and V tiles are double-buffered in LDS; dQ^T += K^T dS^T.
 // The dq pass recomputes S and dP a second time (7 matrix products instead of 5) in
 // exchange for no float32 atomics on dQ.
+#include <algorithm>
 #include <type_traits>
 
 #include "fa_device.h"
@@ -96,19 +97,28 @@ struct DkdvLds {
 #define FA_DKDV_STAGES 2
 #endif
 
-template <typename T, int D, int BR, int NW, int WPE, bool BIAS, bool SPARSE>
+template <typename T, int D, int BR, int NW, int WPE, int BM, bool SPARSE>
 __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
                           amdgpu_waves_per_eu(WPE, WPE)))
 void bwd_dkdv_kernel(const BwdArgs a) {
   using E = Elt<T>;
   using L = DkdvLds<D, BR>;
   using Tile = DmaTile<BR, D, NW>;
+  using BT = BiasColTile;
+  constexpr bool BIAS = BM == kBiasSlope, TENSOR = BM == kBiasTensor;
   constexpr int BK = 32 * NW, QB = BR / 32, DK = D / 16, DB = D / 32, RB = L::RB;
   constexpr int ST = FA_DKDV_STAGES, P = ST - 1;
-  constexpr int kOpsPerTile = 2 * Tile::kOpsPerWave + 1;  // Q, dO windows + one row array
+  // Q, dO windows + one row array (+ the wave's bias windows)
+  constexpr int kOpsPerTile = 2 * Tile::kOpsPerWave + 1 + (TENSOR ? BT::kOps : 0);
+  // a stage: Q, dO, row arrays (+ each wave's bias windows)
+  constexpr int kStage = L::STAGE + (TENSOR ? NW * BT::kWaveBytes : 0);
   static_assert(BR == 64 && NW == 4, "one row array (64 entries) per wave");
-  static_assert(ST * L::STAGE <= 160 * 1024, "LDS budget");
-  __shared__ __attribute__((aligned(1024))) char smem[ST * L::STAGE];
+  // with the bias tensor the loop's only wait is the full one (the dbias stores count
+  // in the same counter as the direct loads)
+  static_assert(!TENSOR || ST == 2, "bias tensor: one tile in flight");
+  static_assert(P * kOpsPerTile < 64, "vmcnt range");
+  static_assert(ST * kStage <= 160 * 1024, "LDS budget");
+  __shared__ __attribute__((aligned(1024))) char smem[ST * kStage];
   __shared__ int win[2];
 
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6, n = lane & 31, h = lane >> 5;
@@ -124,6 +134,9 @@ void bwd_dkdv_kernel(const BwdArgs a) {
   const T* dO = static_cast<const T*>(a.dout) + (size_t)bh * Nq * D;
   const float sl2 = a.sl2;
   const float slope2 = BIAS ? a.slope2[a.n_slopes == 1 ? 0 : head] : 0.f;
+  const float* TB = TENSOR ? a.tbias + (long long)(bh / a.H) * a.tb_sb + (long long)head * a.tb_sh
+                           : nullptr;
+  float* dB = TENSOR ? a.dbias : nullptr;  // NULL: dbias not wanted
 
   const int k0 = kb * BK, k1 = min(k0 + BK, Nk);
   const int kw0 = k0 + 32 * wid, kw1 = min(kw0 + 32, Nk);
@@ -249,11 +262,14 @@ void bwd_dkdv_kernel(const BwdArgs a) {
       d4[q4] = *reinterpret_cast<const f32x4*>(sb + L::DLT + r0 * 4);
     }
     float p[16], ds[16], adist[BIAS ? 16 : 1];
+    const char* bs = sb + L::STAGE + wid_s * BT::kWaveBytes;  // this wave's bias windows
 #pragma unroll
     for (int g = 0; g < 16; ++g) {
       const float lq = l4[g / 4][g % 4];  // already in log2 units
       float x;
-      if constexpr (BIAS) {
+      if constexpr (TENSOR) {
+        x = __builtin_fmaf(sc[g], sl2, __builtin_fmaf(BT::read(bs, qb, g, lane), kLog2e, -lq));
+      } else if constexpr (BIAS) {
         const float dist = (float)(q0t + 32 * qb + 4 * h - key) + (float)(8 * (g / 4) + (g % 4));
         adist[g] = __builtin_fabsf(dist);
         x = __builtin_fmaf(sc[g], sl2, __builtin_fmaf(slope2, adist[g], -lq));
@@ -285,6 +301,17 @@ void bwd_dkdv_kernel(const BwdArgs a) {
     }
 #pragma unroll
     for (int g = 0; g < 16; ++g) ds[g] = p[g] * (dp[g] - d4[g / 4][g % 4]);
+    if constexpr (TENSOR) {
+      // dbias = dS (zero where masked: p = 0 there); lanes 0-31 and 32-63 each store 128
+      // contiguous bytes of one row
+      if (dB != nullptr && key < Nk) {
+#pragma unroll
+        for (int g = 0; g < 16; ++g) {
+          const int qi = q0t + 32 * qb + res_row(g, h);
+          if (qi < Nq) dB[((size_t)bh * Nq + qi) * Nk + key] = ds[g];
+        }
+      }
+    }
     if constexpr (BIAS) {
       // the slope's gradient: dS |i - j| over the visible entries (masked ones have p = 0)
 #pragma unroll
@@ -327,13 +354,15 @@ void bwd_dkdv_kernel(const BwdArgs a) {
   }
   const int arr_off = wid_s == 0 ? L::LSE : wid_s == 1 ? L::DLT : wid_s == 2 ? L::KS : L::KE;
   // ring position p (query tile tile_at(p)) lives in stage p % ST
-  auto stage_of = [&](int p) { return smem + (p % ST) * L::STAGE; };
+  auto stage_of = [&](int p) { return smem + (p % ST) * kStage; };
   auto issue = [&](int p) {
     char* sb = stage_of(p);
     const int q0t = tile_at(p) * BR;
     tile_ld.load(Q, q0t, Nq, sb + L::QT, wid_s);
     tile_ld.load(dO, q0t, Nq, sb + L::DT, wid_s);
     dma4(arr_base + min(q0t + lane, Nq - 1), sb + arr_off);
+    if constexpr (TENSOR)
+      BT::load(TB, a.tb_si, q0t, Nq, kw0, Nk, sb + L::STAGE + wid_s * BT::kWaveBytes, lane);
   };
   auto land = [&](int later) {
     if (P >= 3 && later >= 3) wait_vmem<(P >= 3 ? 3 : 0) * kOpsPerTile>();
@@ -449,18 +478,23 @@ struct DqLds {
 #define FA_DQ_STAGES 4
 #endif
 
-template <typename T, int D, int BC, int NW, int WPE, bool BIAS, bool SPARSE>
+template <typename T, int D, int BC, int NW, int WPE, int BM, bool SPARSE>
 __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
                           amdgpu_waves_per_eu(WPE, WPE)))
 void bwd_dq_kernel(const BwdArgs a) {
   using E = Elt<T>;
   using L = DqLds<D, BC>;
   using Tile = DmaTile<BC, D, NW>;
+  constexpr bool BIAS = BM == kBiasSlope, TENSOR = BM == kBiasTensor;
+  using BT = BiasRowTile<TENSOR ? BC : 64>;
   constexpr int BRQ = 32 * NW, KB = BC / 32, DK = D / 16, DB = D / 32, RB = L::RB;
-  constexpr int ST = FA_DQ_STAGES, P = ST - 1;
-  constexpr int kOpsPerTile = 2 * Tile::kOpsPerWave;
-  static_assert(ST * L::STAGE <= 160 * 1024, "LDS budget");
-  __shared__ __attribute__((aligned(1024))) char smem[ST * L::STAGE];
+  // the bias tensor's tile (32 rows x BC float32 per wave) leaves room for two stages
+  constexpr int ST = TENSOR ? 2 : FA_DQ_STAGES, P = ST - 1;
+  constexpr int kOpsPerTile = 2 * Tile::kOpsPerWave + (TENSOR ? BT::kOps : 0);
+  constexpr int kStage = L::STAGE + (TENSOR ? NW * BT::kWaveBytes : 0);
+  static_assert(P * kOpsPerTile < 64, "vmcnt range");
+  static_assert(ST * kStage <= 160 * 1024, "LDS budget");
+  __shared__ __attribute__((aligned(1024))) char smem[ST * kStage];
   __shared__ int wg_win[NW][2];
 
   const int tid = threadIdx.x, lane = tid & 63, wid = wave_id(), n = lane & 31, h = lane >> 5;
@@ -475,6 +509,8 @@ void bwd_dq_kernel(const BwdArgs a) {
   const T* dO = static_cast<const T*>(a.dout) + (size_t)bh * Nq * D;
   const float sl2 = a.sl2;
   const float slope2 = BIAS ? a.slope2[a.n_slopes == 1 ? 0 : head] : 0.f;
+  const float* TB = TENSOR ? a.tbias + (long long)(bh / a.H) * a.tb_sb + (long long)head * a.tb_sh
+                           : nullptr;
 
   const int q0 = qb * BRQ, wq0 = q0 + 32 * wid;
   const int qrow = wq0 + n;
@@ -604,12 +640,20 @@ void bwd_dq_kernel(const BwdArgs a) {
         for (int ks = 0; ks < DK; ++ks) dp[kb] = E::mma(va[ks], dof[ks], dp[kb]);
       }
     }
+    const char* Bs = sb + L::STAGE + wid * BT::kWaveBytes;  // this wave's bias rows
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
+      f32x4 bv[TENSOR ? 4 : 1];
+      if constexpr (TENSOR) {
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) bv[g4] = BT::read(Bs, n, kb * 32 + 8 * g4 + 4 * h);
+      }
 #pragma unroll
       for (int g = 0; g < 16; ++g) {
         float x;
-        if constexpr (BIAS) {
+        if constexpr (TENSOR) {
+          x = __builtin_fmaf(sc[kb][g], sl2, __builtin_fmaf(bv[g / 4][g % 4], kLog2e, -lq));
+        } else if constexpr (BIAS) {
           const float dist = (float)(qrow - kt0 - 4 * h) - (float)(kb * 32 + 8 * (g / 4) + (g % 4));
           x = __builtin_fmaf(sc[kb][g], sl2, __builtin_fmaf(slope2, __builtin_fabsf(dist), -lq));
         } else {
@@ -648,12 +692,14 @@ void bwd_dq_kernel(const BwdArgs a) {
   Tile tile_ld;
   tile_ld.init(wid, lane);
   // ring position p (key tile tile_at(p)) lives in stage p % ST
-  auto stage_of = [&](int p) { return smem + (p % ST) * L::STAGE; };
+  auto stage_of = [&](int p) { return smem + (p % ST) * kStage; };
   auto issue = [&](int p) {
     char* sb = stage_of(p);
     const int t = tile_at(p);
     tile_ld.load(K, t * BC, Nk, sb + L::KT, wid);
     tile_ld.load(V, t * BC, Nk, sb + L::VT, wid);
+    if constexpr (TENSOR)
+      BT::load(TB, a.tb_si, wq0, Nq, t * BC, Nk, sb + L::STAGE + wid * BT::kWaveBytes, lane);
   };
   auto land = [&](int later) {
     if (P >= 3 && later >= 3) wait_vmem<(P >= 3 ? 3 : 0) * kOpsPerTile>();
@@ -733,8 +779,16 @@ __global__ void dslope_reduce_kernel(const float* __restrict__ part, int B, int 
   out[s] = acc;
 }
 
+// dbias starts at zero: the dK/dV pass writes only the tiles it visits (every (i, j) of
+// those exactly once); masked-out tiles keep the zero. A kernel rather than a memset, so
+// that the clear stays correct inside a captured graph.
+__global__ __launch_bounds__(256) void zero_f32_kernel(float* __restrict__ p, size_t n) {
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) p[i] = 0.f;
+}
+
 template <typename T, int D, int DKDV_NW, int DKDV_WPE, int DQ_BC, int DQ_NW, int DQ_WPE>
-static hipError_t launch_bwd_t(bool bias, int phases, BwdArgs& a, hipStream_t st) {
+static hipError_t launch_bwd_t(int bias, int phases, BwdArgs& a, hipStream_t st) {
   const int BH = a.B * a.H;
   const int rows = BH * a.Nq;
   constexpr int RPB = 256 / (D / 8);
@@ -759,17 +813,26 @@ static hipError_t launch_bwd_t(bool bias, int phases, BwdArgs& a, hipStream_t st
     b.sched = sched;
     const dim3 grid((unsigned)(BH * b.nblk)), block(DKDV_NW * 64);
     const bool sparse = a.bmask != nullptr;
-    if (bias && sparse)
-      hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, kDkdvBR, DKDV_NW, DKDV_WPE, true, true>), grid, block, 0, st, b);
+    if (bias == kBiasTensor && a.dbias != nullptr) {
+      const size_t nel = (size_t)BH * a.Nq * a.Nk;
+      const size_t blocks = std::min<size_t>((nel + 255) / 256, 8192);
+      hipLaunchKernelGGL(zero_f32_kernel, dim3((unsigned)blocks), dim3(256), 0, st, a.dbias, nel);
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+    if (bias == kBiasTensor)
+      hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, kDkdvBR, DKDV_NW, DKDV_WPE, kBiasTensor, false>), grid, block, 0, st, b);
+    else if (bias && sparse)
+      hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, kDkdvBR, DKDV_NW, DKDV_WPE, kBiasSlope, true>), grid, block, 0, st, b);
     else if (bias)
-      hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, kDkdvBR, DKDV_NW, DKDV_WPE, true, false>), grid, block, 0, st, b);
+      hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, kDkdvBR, DKDV_NW, DKDV_WPE, kBiasSlope, false>), grid, block, 0, st, b);
     else if (sparse)
-      hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, kDkdvBR, DKDV_NW, DKDV_WPE, false, true>), grid, block, 0, st, b);
+      hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, kDkdvBR, DKDV_NW, DKDV_WPE, kBiasNone, true>), grid, block, 0, st, b);
     else
-      hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, kDkdvBR, DKDV_NW, DKDV_WPE, false, false>), grid, block, 0, st, b);
+      hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, kDkdvBR, DKDV_NW, DKDV_WPE, kBiasNone, false>), grid, block, 0, st, b);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    if (bias && a.dslopes != nullptr) {
+    if (bias == kBiasSlope && a.dslopes != nullptr) {
       hipLaunchKernelGGL(dslope_reduce_kernel, dim3(1), dim3(FA_MAX_SLOPES), 0, st,
                          b.dslope_part, a.B, a.H, b.nblk, a.n_slopes, a.dslopes);
       e = hipGetLastError();
@@ -778,26 +841,30 @@ static hipError_t launch_bwd_t(bool bias, int phases, BwdArgs& a, hipStream_t st
   }
   // dQ
   if (phases & FA_BWD_DQ) {
-    constexpr int BRQ = 32 * DQ_NW;
+    // the bias tensor's form: 4 waves, 64-key tiles, two stages (its tile shares them)
+    const int nw = bias == kBiasTensor ? 4 : DQ_NW;
+    const int brq = 32 * nw;
     BwdArgs b = a;
-    b.nblk = (a.Nq + BRQ - 1) / BRQ;
+    b.nblk = (a.Nq + brq - 1) / brq;
     b.sched = sched;
-    const dim3 grid((unsigned)(BH * b.nblk)), block(DQ_NW * 64);
+    const dim3 grid((unsigned)(BH * b.nblk)), block(nw * 64);
     // (the block-sparse form always uses 64-key tiles, which lie inside one block)
-    if (a.bmask != nullptr && bias)
-      hipLaunchKernelGGL((bwd_dq_kernel<T, D, 64, DQ_NW, DQ_WPE, true, true>), grid, block, 0, st, b);
+    if (bias == kBiasTensor)
+      hipLaunchKernelGGL((bwd_dq_kernel<T, D, 64, 4, DQ_WPE, kBiasTensor, false>), grid, block, 0, st, b);
+    else if (a.bmask != nullptr && bias)
+      hipLaunchKernelGGL((bwd_dq_kernel<T, D, 64, DQ_NW, DQ_WPE, kBiasSlope, true>), grid, block, 0, st, b);
     else if (a.bmask != nullptr)
-      hipLaunchKernelGGL((bwd_dq_kernel<T, D, 64, DQ_NW, DQ_WPE, false, true>), grid, block, 0, st, b);
+      hipLaunchKernelGGL((bwd_dq_kernel<T, D, 64, DQ_NW, DQ_WPE, kBiasNone, true>), grid, block, 0, st, b);
     else if (bias)
-      hipLaunchKernelGGL((bwd_dq_kernel<T, D, DQ_BC, DQ_NW, DQ_WPE, true, false>), grid, block, 0, st, b);
+      hipLaunchKernelGGL((bwd_dq_kernel<T, D, DQ_BC, DQ_NW, DQ_WPE, kBiasSlope, false>), grid, block, 0, st, b);
     else
-      hipLaunchKernelGGL((bwd_dq_kernel<T, D, DQ_BC, DQ_NW, DQ_WPE, false, false>), grid, block, 0, st, b);
+      hipLaunchKernelGGL((bwd_dq_kernel<T, D, DQ_BC, DQ_NW, DQ_WPE, kBiasNone, false>), grid, block, 0, st, b);
     e = hipGetLastError();
   }
   return e;
 }
 
-hipError_t launch_bwd(fa_dtype dt, int d, bool bias, int phases, BwdArgs& a, hipStream_t st) {
+hipError_t launch_bwd(fa_dtype dt, int d, int bias, int phases, BwdArgs& a, hipStream_t st) {
   switch (dt) {
     case FA_BF16:
       return d == 128 ? launch_bwd_t<__bf16, 128, 4, 1, 64, 8, 2>(bias, phases, a, st)

@@ -337,6 +337,63 @@ struct DmaTile {
   }
 };
 
+// float32 bias tiles carried by the same direct-load rings as K and V (4-byte loads, so
+// any row stride, broadcast stride and ragged key count works: every lane's element index
+// is clamped into the matrix, and clamped entries are masked by the kernel).
+//
+// Query-on-lane kernels (scores S^T: lane = query row n of the wave, registers = keys):
+// the wave's 32 rows x BC keys, row-major; one direct load fills a 64-float window of
+// 64/BC rows, and windows are 272 bytes apart, so that the 16-byte reads of 4 keys by
+// lanes of consecutive rows fall into distinct bank groups.
+template <int BC>
+struct BiasRowTile {
+  static_assert(BC == 32 || BC == 64, "key tile");
+  static constexpr int kRW = 64 / BC;        // rows per window
+  static constexpr int kWin = 272;           // bytes between windows
+  static constexpr int kOps = 32 / kRW;      // direct loads per wave per tile
+  static constexpr int kWaveBytes = kOps * kWin;
+  // rows [wq0, wq0 + 32) (clamped to nq - 1), keys [kt0, kt0 + BC) (clamped to nk - 1) of
+  // the (b, h) matrix at `base` with row stride si, into this wave's region `lds`
+  __device__ static inline void load(const float* base, long long si, int wq0, int nq, int kt0,
+                                     int nk, char* lds, int lane) {
+    const int j = min(kt0 + lane % BC, nk - 1);
+#pragma unroll
+    for (int w = 0; w < kOps; ++w) {
+      const int i = min(wq0 + w * kRW + lane / BC, nq - 1);
+      dma4(base + (long long)i * si + j, lds + w * kWin);
+    }
+  }
+  // keys c0 .. c0 + 3 (c0 a multiple of 4) of wave row r
+  __device__ static inline f32x4 read(const char* lds, int r, int c0) {
+    return *reinterpret_cast<const f32x4*>(lds + (r / kRW) * kWin + ((r % kRW) * BC + c0) * 4);
+  }
+};
+
+// Key-on-lane kernel (dK/dV: scores S; lane l holds key l % 32 of the wave's 32 keys, and
+// the 16 registers of a 32-query block rows res_row(g, l / 32)): the 64-row query tile x the
+// wave's 32 keys, stored in the order the lanes read it: window (qb, g) holds at lane l
+// the entry of row 32 qb + res_row(g, l / 32) and key l % 32, so a read is one 4-byte
+// access per lane with no bank conflict, and each direct load reads two 128-byte row
+// segments.
+struct BiasColTile {
+  static constexpr int kOps = 32;            // windows (2 query blocks x 16 registers)
+  static constexpr int kWaveBytes = kOps * 256;
+  __device__ static inline void load(const float* base, long long si, int q0t, int nq, int kw0,
+                                     int nk, char* lds, int lane) {
+    const int j = min(kw0 + (lane & 31), nk - 1);
+    const int hh = lane >> 5;
+#pragma unroll
+    for (int w = 0; w < kOps; ++w) {
+      const int qb = w >> 4, g = w & 15;
+      const int i = min(q0t + 32 * qb + 8 * (g >> 2) + 4 * hh + (g & 3), nq - 1);
+      dma4(base + (long long)i * si + j, lds + w * 256);
+    }
+  }
+  __device__ static inline float read(const char* lds, int qb, int g, int lane) {
+    return *reinterpret_cast<const float*>(lds + (qb * 16 + g) * 256 + lane * 4);
+  }
+};
+
 // A [ROWS x D] tile of 16-bit elements copied global -> registers -> LDS by NT threads.
 // Thread b owns KQ consecutive rows of one 16-byte column chunk, so the same registers
 // can be written row-major ("natural": row stride NSTRIDE bytes) and transposed

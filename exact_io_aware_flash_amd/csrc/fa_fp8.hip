@@ -400,10 +400,10 @@ void fwd8_kernel(const Fp8FwdArgs a) {
     else wait_vmem<0>();
     __builtin_amdgcn_s_barrier();
   };
+  // prologue: tiles 0 .. P-1 (step t issues tile t + P)
   if (0 < n_t) issue(I0{}, 0);
-  if (1 < n_t) issue(I1{}, 1);
-  if constexpr (P >= 2) if (2 < n_t) issue(I2{}, 2);
-  if constexpr (P >= 3) if (3 < n_t) issue(I3{}, 3);
+  if constexpr (P >= 2) if (1 < n_t) issue(I1{}, 1);
+  if constexpr (P >= 3) if (2 < n_t) issue(I2{}, 2);
   wait_vmem<0>();
   __builtin_amdgcn_s_barrier();
   auto step = [&](auto J, int t) __attribute__((always_inline)) {

@@ -73,13 +73,15 @@ __device__ inline int vt_off(int row, int chunk) {
   return row * C::kVStride + 16 * (chunk ^ ((row >> 4) & (C::kVChunksSwz - 1)));
 }
 
-template <typename T, int D, int BC, int QSUB, int NW, int WPE, bool BIAS>
+template <typename T, int D, int BC, int QSUB, int NW, int WPE, int BM>
 __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
                           amdgpu_waves_per_eu(WPE, WPE)))
 void fwd_kernel(const FwdArgs a) {
   using C = FwdCfg<T, D, BC, QSUB, NW>;
   using E = Elt<T>;
   constexpr bool F32 = C::kF32;
+  constexpr bool SLOPE = BM == kBiasSlope, TENSOR = BM == kBiasTensor;
+  constexpr bool PRE = BM != kBiasNone;  // scores scaled to log2 units before the row max
   __shared__ __attribute__((aligned(16))) char smem[2 * C::kStage];
   __shared__ int wg_win[NW][2];
 
@@ -100,7 +102,9 @@ void fwd_kernel(const FwdArgs a) {
   const T* __restrict__ V = static_cast<const T*>(a.v) + (size_t)bh * Nk * D;
   T* __restrict__ O = static_cast<T*>(a.o) + (size_t)bh * Nq * D;
   const float sl2 = a.sl2;
-  const float slope2 = BIAS ? a.slope2[a.n_slopes == 1 ? 0 : head] : 0.f;
+  const float slope2 = SLOPE ? a.slope2[a.n_slopes == 1 ? 0 : head] : 0.f;
+  const float* TB = TENSOR ? a.tbias + (long long)(bh / a.H) * a.tb_sb + (long long)head * a.tb_sh
+                           : nullptr;
 
   // ---- this lane's query rows and key intervals ----------------------------------
   const int wq0 = q0 + wid * C::kQW;
@@ -307,7 +311,23 @@ void fwd_kernel(const FwdArgs a) {
       }
 
       // ---- bias and masking (masking only on partially visible tiles) ----------
-      if constexpr (BIAS) {
+      if constexpr (TENSOR) {
+        // the bias entries of this lane's row and keys, read straight from memory (this
+        // kernel stages K and V through registers, so plain loads need no extra wait);
+        // indices clamped into the matrix, clamped entries are masked below
+#pragma unroll
+        for (int qs = 0; qs < QSUB; ++qs) {
+          const float* brow = TB + (long long)min(qrow[qs], Nq - 1) * a.tb_si;
+#pragma unroll
+          for (int kb = 0; kb < C::kKB; ++kb)
+#pragma unroll
+            for (int g = 0; g < 16; ++g) {
+              const int j = min(kt0 + kb * 32 + res_row(g, h), Nk - 1);
+              s[qs][kb][g] = __builtin_fmaf(s[qs][kb][g], sl2, brow[j] * kLog2e);
+            }
+        }
+      }
+      if constexpr (SLOPE) {
 #pragma unroll
         for (int qs = 0; qs < QSUB; ++qs) {
           const float base = (float)(qrow[qs] - kt0 - 4 * h);
@@ -347,7 +367,7 @@ void fwd_kernel(const FwdArgs a) {
 #pragma unroll
           for (int g = 0; g < 16; ++g) mx = __builtin_fmaxf(mx, s[qs][kb][g]);
         mx = __builtin_fmaxf(mx, xhalf(mx));
-        tmax[qs] = BIAS ? mx : mx * sl2;
+        tmax[qs] = PRE ? mx : mx * sl2;
         need |= tmax[qs] > m2[qs] + kTau;
       }
       if (wave_any(need)) {
@@ -369,7 +389,7 @@ void fwd_kernel(const FwdArgs a) {
         for (int kb = 0; kb < C::kKB; ++kb)
 #pragma unroll
           for (int g = 0; g < 16; ++g) {
-            const float x = BIAS ? s[qs][kb][g] + nb : __builtin_fmaf(s[qs][kb][g], sl2, nb);
+            const float x = PRE ? s[qs][kb][g] + nb : __builtin_fmaf(s[qs][kb][g], sl2, nb);
             const float p = fast_exp2(x);
             s[qs][kb][g] = p;
             rs += p;
@@ -469,23 +489,31 @@ struct Fwd16Cfg {
   static_assert(kST >= 2 && kST * kStage <= 160 * 1024, "LDS budget");
 };
 
-template <typename T, int D, int BC, int NW, int ST, bool BIAS, bool SPARSE>
+template <typename T, int D, int BC, int NW, int ST, int BM, bool SPARSE>
 __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
                           amdgpu_waves_per_eu(2, 2)))
 void fwd16_kernel(const FwdArgs a) {
   using C = Fwd16Cfg<D, BC, NW, ST>;
   using E = Elt<T>;
+  using BT = BiasRowTile<BC>;
+  constexpr bool SLOPE = BM == kBiasSlope, TENSOR = BM == kBiasTensor;
+  constexpr bool PRE = BM != kBiasNone;  // scores scaled to log2 units before the row max
   constexpr int KB = C::kKB, DB = C::kDB, DK = C::kDK, RB = C::kRB;
   constexpr int P = ST - 1;                                  // tiles in flight ahead
-  constexpr int kOpsPerTile = 2 * C::Tile::kOpsPerWave;      // direct loads per wave per tile
+  // direct loads per wave per tile: K and V windows (+ the bias tile's rows)
+  constexpr int kOpsPerTile = 2 * C::Tile::kOpsPerWave + (TENSOR ? BT::kOps : 0);
+  // a stage: K tile, V tile (+ each wave's bias rows)
+  constexpr int kStage = C::kStage + (TENSOR ? NW * BT::kWaveBytes : 0);
+  static_assert(!TENSOR || ST == 2, "bias tensor: one tile in flight");
+  static_assert(ST * kStage <= 160 * 1024, "LDS budget");
   // One LDS array per ring stage, and a loop unrolled over the stages so that every
   // access names its array: the compiler can then tell the stage being read from the
   // stages the direct loads are filling, and adds no wait on those loads.
   static_assert(ST >= 2 && ST <= 4, "two to four ring stages");
-  __shared__ __attribute__((aligned(1024))) char stg0[C::kStage];
-  __shared__ __attribute__((aligned(1024))) char stg1[C::kStage];
-  __shared__ __attribute__((aligned(1024))) char stg2[ST > 2 ? C::kStage : 1];
-  __shared__ __attribute__((aligned(1024))) char stg3[ST > 3 ? C::kStage : 1];
+  __shared__ __attribute__((aligned(1024))) char stg0[kStage];
+  __shared__ __attribute__((aligned(1024))) char stg1[kStage];
+  __shared__ __attribute__((aligned(1024))) char stg2[ST > 2 ? kStage : 1];
+  __shared__ __attribute__((aligned(1024))) char stg3[ST > 3 ? kStage : 1];
   __shared__ int wg_win[NW][2];
   auto sptr = [&](auto J) -> char* {
     constexpr int j = decltype(J)::value % ST;
@@ -517,7 +545,9 @@ void fwd16_kernel(const FwdArgs a) {
   const T* __restrict__ V = static_cast<const T*>(a.v) + (size_t)bh * Nk * D;
   T* __restrict__ O = static_cast<T*>(a.o) + (size_t)bh * Nq * D;
   const float sl2 = a.sl2;
-  const float slope2 = BIAS ? a.slope2[a.n_slopes == 1 ? 0 : head] : 0.f;
+  const float slope2 = SLOPE ? a.slope2[a.n_slopes == 1 ? 0 : head] : 0.f;
+  const float* TB = TENSOR ? a.tbias + (long long)(bh / a.H) * a.tb_sb + (long long)head * a.tb_sh
+                           : nullptr;
 
   // ---- rows, key intervals, windows -----------------------------------------------
   const int wq0 = qb * C::kBR + wid * 32;
@@ -642,7 +672,8 @@ void fwd16_kernel(const FwdArgs a) {
 
   // One key tile: S^T = K Q^T, (bias), (mask: a small branch of its own, so both outcomes
   // share the rest), running max, exponentials, O^T += V^T P^T.
-  auto tile = [&](const char* Ks, const char* Vs, int kt0, bool masked) __attribute__((always_inline)) {
+  auto tile = [&](const char* Ks, const char* Vs, const char* Bs, int kt0, bool masked)
+                  __attribute__((always_inline)) {
     f32x16 sc[KB];
     {
       // Every K operand of the tile is requested before the first MFMA: the scheduler
@@ -661,7 +692,7 @@ void fwd16_kernel(const FwdArgs a) {
         for (int ks = 0; ks < DK; ++ks) sc[kb] = E::mma(kf[kb][ks], qf[ks], sc[kb]);
       }
     }
-    if constexpr (BIAS) {
+    if constexpr (SLOPE) {
       const float base = (float)(qrow - kt0 - 4 * h);
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
@@ -669,6 +700,18 @@ void fwd16_kernel(const FwdArgs a) {
         for (int g = 0; g < 16; ++g) {
           const float dist = base - (float)(kb * 32 + 8 * (g / 4) + (g % 4));
           sc[kb][g] = __builtin_fmaf(sc[kb][g], sl2, slope2 * __builtin_fabsf(dist));
+        }
+    }
+    if constexpr (TENSOR) {
+      // keys kb*32 + 8 g4 + 4h .. +3 of row n, from this wave's bias rows in the stage
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const f32x4 bv = BT::read(Bs, n, kb * 32 + 8 * g4 + 4 * h);
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            sc[kb][4 * g4 + e] = __builtin_fmaf(sc[kb][4 * g4 + e], sl2, bv[e] * kLog2e);
         }
     }
     if (masked) {
@@ -691,7 +734,7 @@ void fwd16_kernel(const FwdArgs a) {
     for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
       for (int g = 0; g < 16; ++g) mx = __builtin_fmaxf(mx, sc[kb][g]);
-    const float hmax = BIAS ? mx : mx * sl2;
+    const float hmax = PRE ? mx : mx * sl2;
     if (__builtin_expect(wave_any(hmax > m2 + kTau), 0)) {  // rare after the first tiles
       const float tmax = xhalf_max(hmax);  // the whole row
       const float mnew = __builtin_fmaxf(m2, tmax);
@@ -710,8 +753,8 @@ void fwd16_kernel(const FwdArgs a) {
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
           const int g = 8 * st + 2 * w;
-          const float x0 = BIAS ? sc[kb][g] + nb : __builtin_fmaf(sc[kb][g], sl2, nb);
-          const float x1 = BIAS ? sc[kb][g + 1] + nb : __builtin_fmaf(sc[kb][g + 1], sl2, nb);
+          const float x0 = PRE ? sc[kb][g] + nb : __builtin_fmaf(sc[kb][g], sl2, nb);
+          const float x1 = PRE ? sc[kb][g + 1] + nb : __builtin_fmaf(sc[kb][g + 1], sl2, nb);
           const float p0 = fast_exp2(x0), p1 = fast_exp2(x1);
           pb[kb][st][w] = E::pack2(p0, p1);
           l += p0 + p1;  // float32 row sum (the LSE needs the unrounded probabilities)
@@ -736,6 +779,8 @@ void fwd16_kernel(const FwdArgs a) {
     char* sb = sptr(J);
     dt.load(K, t * BC, Nk, sb, wid);
     dt.load(V, t * BC, Nk, sb + C::Tile::kBytes, wid);
+    if constexpr (TENSOR)
+      BT::load(TB, a.tb_si, wq0, Nq, t * BC, Nk, sb + C::kStage + wid * BT::kWaveBytes, lane);
   };
   // wait until the oldest tile in flight has landed while `later` younger tiles may stay
   // in flight, then make every wave's part visible
@@ -746,10 +791,10 @@ void fwd16_kernel(const FwdArgs a) {
     else wait_vmem<0>();
     __builtin_amdgcn_s_barrier();
   };
+  // prologue: ring positions 0 .. P-1 (step p issues position p + P)
   if (0 < n_pos) issue(I0{}, tile_at(0));
-  if (1 < n_pos) issue(I1{}, tile_at(1));
-  if constexpr (P >= 2) if (2 < n_pos) issue(I2{}, tile_at(2));
-  if constexpr (P >= 3) if (3 < n_pos) issue(I3{}, tile_at(3));
+  if constexpr (P >= 2) if (1 < n_pos) issue(I1{}, tile_at(1));
+  if constexpr (P >= 3) if (2 < n_pos) issue(I2{}, tile_at(2));
   // The Q fragments and every prologue tile land. Waiting for all of them (rather than
   // for the first tile only) leaves no register load outstanding in the loop, so the
   // compiler puts no full vector-memory wait, which would also wait for the ring's loads
@@ -765,7 +810,7 @@ void fwd16_kernel(const FwdArgs a) {
     if (p + P < n_pos) issue(std::integral_constant<int, j + P>{}, tile_at(p + P));
     if (wave_needs(p, t)) {
       const char* sb = sptr(J);
-      tile(sb, sb + C::Tile::kBytes, t * BC, !full_tile(t));
+      tile(sb, sb + C::Tile::kBytes, sb + C::kStage + wid * BT::kWaveBytes, t * BC, !full_tile(t));
     }
     if (p + 1 < n_pos) land(min(p + P, n_pos - 1) - (p + 1));
   };
@@ -852,16 +897,18 @@ hipError_t launch_mask_summary(const int32_t* ks, const int32_t* ke, int Nq, int
 // tile configurations per (dtype, d) and the launcher
 // ---------------------------------------------------------------------------------
 template <typename T, int D, int BC, int QSUB, int NW, int WPE>
-static hipError_t launch_cfg(bool bias, FwdArgs& a, hipStream_t st) {
+static hipError_t launch_cfg(int bias, FwdArgs& a, hipStream_t st) {
   using C = FwdCfg<T, D, BC, QSUB, NW>;
   a.nqb = (a.Nq + C::kBR - 1) / C::kBR;
   const int BH = a.B * a.H;
   a.sched = (BH % 8 == 0) ? kSchedXcd : kSchedHeadMajor;
   const dim3 grid((unsigned)(BH * a.nqb)), block(C::kNT);
-  if (bias)
-    hipLaunchKernelGGL((fwd_kernel<T, D, BC, QSUB, NW, WPE, true>), grid, block, 0, st, a);
+  if (bias == kBiasTensor)
+    hipLaunchKernelGGL((fwd_kernel<T, D, BC, QSUB, NW, WPE, kBiasTensor>), grid, block, 0, st, a);
+  else if (bias)
+    hipLaunchKernelGGL((fwd_kernel<T, D, BC, QSUB, NW, WPE, kBiasSlope>), grid, block, 0, st, a);
   else
-    hipLaunchKernelGGL((fwd_kernel<T, D, BC, QSUB, NW, WPE, false>), grid, block, 0, st, a);
+    hipLaunchKernelGGL((fwd_kernel<T, D, BC, QSUB, NW, WPE, kBiasNone>), grid, block, 0, st, a);
   return hipGetLastError();
 }
 
@@ -916,7 +963,7 @@ static hipError_t launch_merge(const FwdArgs& a, hipStream_t st) {
 
 
 template <typename T, int D, int BC, int NW, int ST>
-static hipError_t launch16(bool bias, FwdArgs& a, hipStream_t st) {
+static hipError_t launch16(int bias, FwdArgs& a, hipStream_t st) {
   using C = Fwd16Cfg<D, BC, NW, ST>;
   static_assert(kFwdTileKeys % BC == 0, "split ranges are whole tiles");
   a.nqb = (a.Nq + C::kBR - 1) / C::kBR;
@@ -925,14 +972,20 @@ static hipError_t launch16(bool bias, FwdArgs& a, hipStream_t st) {
   a.sched = (BH % 8 == 0) ? kSchedXcd : kSchedHeadMajor;
   const dim3 grid((unsigned)(BH * a.nqb * a.n_split)), block(C::kNT);
   const bool sparse = a.bmask != nullptr;
-  if (bias && sparse)
-    hipLaunchKernelGGL((fwd16_kernel<T, D, BC, NW, ST, true, true>), grid, block, 0, st, a);
+  if (bias == kBiasTensor) {
+    // (a bias tensor comes without a bitmap; its tile rides in a two-stage ring)
+    if constexpr (ST == 2 && NW == 4)
+      hipLaunchKernelGGL((fwd16_kernel<T, D, BC, NW, ST, kBiasTensor, false>), grid, block, 0, st, a);
+    else
+      return hipErrorNotSupported;
+  } else if (bias && sparse)
+    hipLaunchKernelGGL((fwd16_kernel<T, D, BC, NW, ST, kBiasSlope, true>), grid, block, 0, st, a);
   else if (bias)
-    hipLaunchKernelGGL((fwd16_kernel<T, D, BC, NW, ST, true, false>), grid, block, 0, st, a);
+    hipLaunchKernelGGL((fwd16_kernel<T, D, BC, NW, ST, kBiasSlope, false>), grid, block, 0, st, a);
   else if (sparse)
-    hipLaunchKernelGGL((fwd16_kernel<T, D, BC, NW, ST, false, true>), grid, block, 0, st, a);
+    hipLaunchKernelGGL((fwd16_kernel<T, D, BC, NW, ST, kBiasNone, true>), grid, block, 0, st, a);
   else
-    hipLaunchKernelGGL((fwd16_kernel<T, D, BC, NW, ST, false, false>), grid, block, 0, st, a);
+    hipLaunchKernelGGL((fwd16_kernel<T, D, BC, NW, ST, kBiasNone, false>), grid, block, 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.n_split == 1) return e;
   return launch_merge<T, D>(a, st);
@@ -965,8 +1018,16 @@ static int device_cus() {
 //     closely): 4 waves x 32 rows with 2 stages (64 KB, two workgroups per compute unit),
 //     where twice as many, fuller blocks balance the load better.
 // For N_q <= kFwdFewRows every d = 128 variant holds the whole head in one query block.
+// With a bias tensor, whose tile (4 waves x 32 rows x the tile's keys, float32) shares
+// each stage with K and V: 4 waves, two stages (d = 128: 64-key tiles, 134 KB, or
+// 32-key tiles when split; d = 64: 64-key tiles, 102 KB).
 template <typename T>
-static hipError_t launch16_for(int d, bool bias, FwdArgs& a, hipStream_t st) {
+static hipError_t launch16_for(int d, int bias, FwdArgs& a, hipStream_t st) {
+  if (bias == kBiasTensor) {
+    if (d == 64) return launch16<T, 64, 64, 4, 2>(bias, a, st);
+    if (a.Nq <= kFwdFewRows && a.n_split > 1) return launch16<T, 128, 32, 4, 2>(bias, a, st);
+    return launch16<T, 128, 64, 4, 2>(bias, a, st);
+  }
   if (d == 64) return launch16<T, 64, 64, 4, 4>(bias, a, st);
   if (a.Nq <= kFwdFewRows) {
     if (a.n_split > 1) return launch16<T, 128, 32, 4, 4>(bias, a, st);
@@ -979,7 +1040,7 @@ static hipError_t launch16_for(int d, bool bias, FwdArgs& a, hipStream_t st) {
   return launch16<T, 128, 64, 8, 2>(bias, a, st);
 }
 
-hipError_t launch_fwd(fa_dtype dt, int d, bool bias, FwdArgs& a, hipStream_t st) {
+hipError_t launch_fwd(fa_dtype dt, int d, int bias, FwdArgs& a, hipStream_t st) {
   switch (dt) {
     case FA_BF16:
       return launch16_for<__bf16>(d, bias, a, st);

@@ -39,6 +39,10 @@ struct FwdArgs {
   const uint8_t* bmask;
   int bq, bk, nkb;
   long long bm_sb, bm_sh;
+  // float32 bias tensor (bias mode 2): element (b, h, i, j) at
+  // tbias[b * tb_sb + h * tb_sh + i * tb_si + j]
+  const float* tbias;
+  long long tb_sb, tb_sh, tb_si;
 };
 
 // The split-key 16-bit forward uses a smaller workgroup (4 waves, 32-key tiles, 64 KB of
@@ -83,13 +87,20 @@ struct BwdArgs {
   const uint8_t* bmask;
   int bq, bk, nkb;
   long long bm_sb, bm_sh;
+  // bias tensor, as in FwdArgs; dbias (NULL: not wanted) dense [B,H,Nq,Nk] float32
+  const float* tbias;
+  long long tb_sb, tb_sh, tb_si;
+  float* dbias;
 };
 
+// Bias modes of the kernels: none, slope * |i - j| generated on the fly, float32 tensor.
+enum BiasMode : int { kBiasNone = 0, kBiasSlope = 1, kBiasTensor = 2 };
+
 // Launchers (return hipSuccess or the launch error). dtype-specialised in the .hip files.
-hipError_t launch_fwd(fa_dtype dt, int d, bool bias, FwdArgs& a, hipStream_t st);
+hipError_t launch_fwd(fa_dtype dt, int d, int bias_mode, FwdArgs& a, hipStream_t st);
 // Tiles of the block-sparse forward list per workgroup (keys per tile >= 32).
 constexpr int kSparseMaxTiles = FA_MAX_SPARSE_N / 32;
-hipError_t launch_bwd(fa_dtype dt, int d, bool bias, int phases, BwdArgs& a, hipStream_t st);
+hipError_t launch_bwd(fa_dtype dt, int d, int bias_mode, int phases, BwdArgs& a, hipStream_t st);
 hipError_t launch_mask_summary(const int32_t* ks, const int32_t* ke, int Nq, int Nk, int block,
                                int32_t* out, hipStream_t st);
 

@@ -73,7 +73,10 @@ typedef enum fa_bias_kind {
   FA_BIAS_NONE = 0,
   /* bias(h, i, j) = slopes[h] * |i - j|, i and j absolute row/column indices,
      generated on the fly (never stored); added after scaling (see fa_fwd). */
-  FA_BIAS_DIST_LINEAR = 1
+  FA_BIAS_DIST_LINEAR = 1,
+  /* bias(b, h, i, j) = bias[b * bias_stride_b + h * bias_stride_h + i * bias_stride_i + j],
+     a float32 tensor in device memory (see the descriptor); added after scaling. */
+  FA_BIAS_TENSOR = 2
 } fa_bias_kind;
 
 #define FA_MAX_SLOPES 256
@@ -110,6 +113,23 @@ typedef enum fa_bias_kind {
  *              gradient with respect to the scores), or its sum over heads for one shared
  *              slope; it needs FA_BIAS_DIST_LINEAR (else FA_ERR_MASK). The reduction runs
  *              in a fixed order, so the result is deterministic. fa_fwd ignores it.
+ *  bias :      FA_BIAS_TENSOR only: DEVICE pointer to float32 values, 4-byte aligned
+ *              (NULL: FA_ERR_NULL; misaligned: FA_ERR_ALIGN). Element (b, h, i, j) is read
+ *              at the offset given for FA_BIAS_TENSOR; the key index j has stride 1.
+ *              Any array the caller can index that way works: a dense [B, H, N_q, N_k]
+ *              tensor, or one broadcast over batches, heads or query rows by a zero
+ *              stride. Attention with an additive bias matrix on the query-key scores
+ *              (scifaro.com related-papers page for FlashMask, arXiv 2410.01359: the
+ *              abstract on attention with bias); -inf entries act as a mask; +inf or NaN
+ *              entries give undefined results. Read during the enqueued work. With a
+ *              block bitmap: FA_ERR_UNSUPPORTED.
+ *  bias_stride_b, bias_stride_h, bias_stride_i : element strides, >= 0 (else FA_ERR_MASK).
+ *  dbias :     DEVICE pointer to a dense float32 [B, H, N_q, N_k] array (4-byte aligned),
+ *              or NULL. fa_bwd (and fa_bwd_phases with FA_BWD_DKDV) writes there the
+ *              gradient of the loss with respect to every biased score, dS_{b,h,i,j}
+ *              (zero where masked); for a bias broadcast over an axis the gradient of the
+ *              shared values is the sum of dbias over that axis, left to the caller. Needs
+ *              FA_BIAS_TENSOR (else FA_ERR_MASK). fa_fwd ignores it.
  *  A row with no visible key (after causal, range and block masking) gets O = 0 and
  *  LSE = -inf. */
 #define FA_MAX_SPARSE_N 65536
@@ -125,6 +145,11 @@ typedef struct fa_mask_bias_desc {
   int64_t mask_stride_b;
   int64_t mask_stride_h;
   float* dslopes;
+  const float* bias;
+  int64_t bias_stride_b;
+  int64_t bias_stride_h;
+  int64_t bias_stride_i;
+  float* dbias;
 } fa_mask_bias_desc;
 
 /* Forward pass.

@@ -27,7 +27,8 @@ Sources (the pages are cited by title and section):
   section "Causal masking ...": keys in the future of a query are never used.
 * scifaro.com "related papers: FlashMask: Efficient and Rich Mask Extension of
   FlashAttention" (the abstract on attention with bias): an additive bias matrix
-  added to the query-key scores.
+  added to the query-key scores (here either generated, slope * |i - j|, or given
+  as a tensor broadcastable to [B, H, N_q, N_k]).
 * briefgpt.xyz page for arXiv 2307.08691, FlashAttention abstract (May 2022):
   the tiled method extends to block-sparse attention (here: a per-row key range,
   and a block bitmap); the related abstract (Jun 2023) on a broad class of sparse
@@ -37,6 +38,9 @@ Readings where the pages are silent (each is also listed in the design notes):
 
 * bias is added after scaling and is not multiplied by ``scale``;
   bias(h, i, j) = slopes[h] * |i - j| with absolute row/column indices;
+* a bias tensor's -inf entries mask like any other mask (a row whose every
+  visible entry is -inf is empty); its gradient is dS, the gradient with respect
+  to the biased score, zero where masked;
 * a row attends exactly to keys j with start_i <= j < end_i (one interval per
   query row, shared by every batch and head); any integers are allowed, the
   interval is intersected with [0, N_k);
@@ -122,14 +126,29 @@ def distance_bias(rows: np.ndarray, n_k: int, slope: float) -> np.ndarray:
     return float(slope) * np.abs(rows[:, None] - j[None, :]).astype(np.float64)
 
 
+def bias_rows(bias, B: int, H: int, n_q: int, n_k: int, b: int, h: int,
+              rows: np.ndarray) -> Optional[np.ndarray]:
+    """Rows of head (b, h) of a bias tensor broadcastable to [B, H, N_q, N_k], float64."""
+    if bias is None:
+        return None
+    full = np.broadcast_to(np.asarray(bias), (B, H, n_q, n_k))
+    return _f64(full[b, h][np.asarray(rows, dtype=np.int64)])
+
+
 def scores(q_rows: np.ndarray, k: np.ndarray, scale: float, rows: np.ndarray, n_q: int,
            causal: bool = False, bias_slope: Optional[float] = None,
-           key_start=None, key_end=None, blocks=None) -> np.ndarray:
-    """S for one (b, h) and a set of query rows: scale * q k^T + bias, masked to -inf."""
+           key_start=None, key_end=None, blocks=None,
+           bias: Optional[np.ndarray] = None) -> np.ndarray:
+    """S for one (b, h) and a set of query rows: scale * q k^T + bias, masked to -inf.
+
+    ``bias``: the rows' entries of a bias tensor, [len(rows), n_k] (see ``bias_rows``).
+    """
     s = float(scale) * (_f64(q_rows) @ _f64(k).T)
     n_k = k.shape[0]
     if bias_slope is not None:
         s = s + distance_bias(rows, n_k, bias_slope)
+    if bias is not None:
+        s = s + bias
     vis = visible_mask(n_q, n_k, rows, causal, key_start, key_end)
     if blocks is not None:
         vis = vis & block_visible(rows, n_k, blocks)
@@ -166,12 +185,14 @@ def _chunks(n: int, n_k: int, max_elems: int):
 
 def attention_forward_rows(q, k, v, scale: float, rows: Sequence[int], b: int, h: int,
                            causal: bool = False, bias_slopes=None,
-                           key_start=None, key_end=None, block_mask=None):
+                           key_start=None, key_end=None, block_mask=None, bias=None):
     """O and LSE of selected query rows of one (b, h): ([len(rows), d], [len(rows)])."""
     rows = np.asarray(rows, dtype=np.int64)
-    n_q = q.shape[2]
+    B, H, n_q = q.shape[:3]
+    n_k = k.shape[2]
     s = scores(_f64(q[b, h][rows]), _f64(k[b, h]), scale, rows, n_q, causal,
-               _slope_for(bias_slopes, h), key_start, key_end, _blocks_for(block_mask, b, h))
+               _slope_for(bias_slopes, h), key_start, key_end, _blocks_for(block_mask, b, h),
+               bias_rows(bias, B, H, n_q, n_k, b, h, rows))
     p, m, l = _two_pass_softmax(s)
     o = p @ _f64(v[b, h])
     lse = np.where(l > 0, m + np.log(np.where(l > 0, l, 1.0)), NEG_INF)
@@ -180,10 +201,11 @@ def attention_forward_rows(q, k, v, scale: float, rows: Sequence[int], b: int, h
 
 def attention_forward(q, k, v, scale: float, causal: bool = False, bias_slopes=None,
                       key_start=None, key_end=None, max_chunk_elems: int = 1 << 24,
-                      block_mask=None):
+                      block_mask=None, bias=None):
     """Full forward: O [B,H,N_q,d] float64 and LSE [B,H,N_q] float64.
 
     Inputs are [B,H,N,d] arrays (any float dtype; up-cast exactly to float64).
+    ``bias``: optional array broadcastable to [B,H,N_q,N_k], added after scaling.
     Memory stays bounded by processing one (b, h, row-chunk) at a time.
     """
     B, H, n_q, d = q.shape
@@ -195,24 +217,26 @@ def attention_forward(q, k, v, scale: float, causal: bool = False, bias_slopes=N
             for rows in _chunks(n_q, n_k, max_chunk_elems):
                 o[b, h, rows], lse[b, h, rows] = attention_forward_rows(
                     q, k, v, scale, rows, b, h, causal, bias_slopes, key_start, key_end,
-                    block_mask)
+                    block_mask, bias)
     return o, lse
 
 
 def attention_probabilities(q, k, scale: float, b: int = 0, h: int = 0, causal: bool = False,
                             bias_slopes=None, key_start=None, key_end=None,
-                            block_mask=None) -> np.ndarray:
+                            block_mask=None, bias=None) -> np.ndarray:
     """The full probability matrix P [N_q, N_k] of one (b, h) (small inputs only)."""
-    n_q = q.shape[2]
+    B, H, n_q = q.shape[:3]
     rows = np.arange(n_q, dtype=np.int64)
     s = scores(_f64(q[b, h]), _f64(k[b, h]), scale, rows, n_q, causal,
-               _slope_for(bias_slopes, h), key_start, key_end, _blocks_for(block_mask, b, h))
+               _slope_for(bias_slopes, h), key_start, key_end, _blocks_for(block_mask, b, h),
+               bias_rows(bias, B, H, n_q, k.shape[2], b, h, rows))
     return _two_pass_softmax(s)[0]
 
 
 def attention_backward(q, k, v, dout, scale: float, causal: bool = False, bias_slopes=None,
                        key_start=None, key_end=None, max_chunk_elems: int = 1 << 24,
-                       block_mask=None, return_dslopes: bool = False):
+                       block_mask=None, return_dslopes: bool = False, bias=None,
+                       return_dbias: bool = False):
     """Analytic float64 gradients (dQ, dK, dV) of L = sum(O * dO), each [B,H,N,d].
 
     Textbook softmax Jacobian with P recomputed from Q and K:
@@ -222,6 +246,8 @@ def attention_backward(q, k, v, dout, scale: float, causal: bool = False, bias_s
     result is dL/dslope: the bias slope_h |i - j| enters S additively, so
         dL/dslope_h = sum_{b, i, j} dS_{b,h,i,j} |i - j|,
     one value per head, or one in all (summed over heads) for a single shared slope.
+    With return_dbias (a bias tensor enters S additively, entry by entry) the last result
+    is dS itself, [B, H, N_q, N_k] (zero where masked).
     """
     B, H, n_q, d = q.shape
     n_k = k.shape[2]
@@ -229,13 +255,15 @@ def attention_backward(q, k, v, dout, scale: float, causal: bool = False, bias_s
     dk = np.zeros((B, H, n_k, d), dtype=np.float64)
     dv = np.zeros((B, H, n_k, d), dtype=np.float64)
     dslope = np.zeros(H, dtype=np.float64)
+    dbias = np.zeros((B, H, n_q, n_k), dtype=np.float64) if return_dbias else None
     for b in range(B):
         for h in range(H):
             kb, vb = _f64(k[b, h]), _f64(v[b, h])
             for rows in _chunks(n_q, n_k, max_chunk_elems):
                 qr, dor = _f64(q[b, h][rows]), _f64(dout[b, h][rows])
                 s = scores(qr, kb, scale, rows, n_q, causal, _slope_for(bias_slopes, h),
-                           key_start, key_end, _blocks_for(block_mask, b, h))
+                           key_start, key_end, _blocks_for(block_mask, b, h),
+                           bias_rows(bias, B, H, n_q, n_k, b, h, rows))
                 p, _, _ = _two_pass_softmax(s)
                 dv[b, h] += p.T @ dor
                 dp = dor @ vb.T
@@ -245,16 +273,22 @@ def attention_backward(q, k, v, dout, scale: float, causal: bool = False, bias_s
                 dk[b, h] += float(scale) * (ds.T @ qr)
                 if return_dslopes:
                     dslope[h] += float((ds * distance_bias(rows, n_k, 1.0)).sum())
-    if not return_dslopes:
-        return dq, dk, dv
-    if bias_slopes is None:
-        raise ValueError("return_dslopes needs bias_slopes")
-    shared = np.atleast_1d(np.asarray(bias_slopes)).shape[0] == 1
-    return dq, dk, dv, (dslope.sum(keepdims=True) if shared else dslope)
+                if return_dbias:
+                    dbias[b, h, rows] = ds
+    out = [dq, dk, dv]
+    if return_dslopes:
+        if bias_slopes is None:
+            raise ValueError("return_dslopes needs bias_slopes")
+        shared = np.atleast_1d(np.asarray(bias_slopes)).shape[0] == 1
+        out.append(dslope.sum(keepdims=True) if shared else dslope)
+    if return_dbias:
+        out.append(dbias)
+    return tuple(out)
 
 
 def tiled_online_forward(q, k, v, scale: float, br: int, bc: int, causal: bool = False,
-                         bias_slopes=None, key_start=None, key_end=None, block_mask=None):
+                         bias_slopes=None, key_start=None, key_end=None, block_mask=None,
+                         bias=None):
     """The pages' tiled loop in float64, as a model of the recurrence the GPU runs.
 
     Blog section "Algoritma Flash Attention": Q is cut into ceil(N/B_r) row
@@ -286,6 +320,8 @@ def tiled_online_forward(q, k, v, scale: float, br: int, bc: int, causal: bool =
                     s = float(scale) * (qi @ _f64(k[b, h][cols]).T)
                     if slope is not None:
                         s = s + slope * np.abs(rows[:, None] - cols[None, :]).astype(np.float64)
+                    if bias is not None:
+                        s = s + bias_rows(bias, B, H, n_q, n_k, b, h, rows)[:, cols]
                     vis = visible_mask(n_q, n_k, rows, causal, key_start, key_end)
                     if blocks is not None:
                         vis = vis & block_visible(rows, n_k, blocks)

@@ -15,4 +15,5 @@ from .inputs import (  # noqa: F401
     seed_for,
     with_outliers,
     random_signs,
+    bias_tensor,
 )

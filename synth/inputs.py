@@ -13,7 +13,9 @@ Recipe (shared by tests and bench):
   ``[start_i, end_i)``: rows are grouped in blocks of ``block`` rows; each block
   draws one offset uniformly, each row adds a jitter in ``[0, jitter)``, and
   every interval has the same width.  With width ``N/2`` and 128-row blocks about
-  half of the 128x128 tiles of the score matrix are fully masked.
+  half of the 128x128 tiles of the score matrix are fully masked;
+* a bias tensor is float32 N(0, std) of its own (possibly broadcast) shape, with an
+  optional seeded fraction of entries set to -inf.
 """
 
 from __future__ import annotations
@@ -132,3 +134,13 @@ def random_signs(d: int, seed: int):
     """d independent fair draws of +1.0 / -1.0 (a list of floats)."""
     g = torch.Generator("cpu").manual_seed(seed)
     return [1.0 if b else -1.0 for b in (torch.rand(d, generator=g) < 0.5).tolist()]
+
+
+def bias_tensor(shape, seed: int, std: float = 1.0, neg_inf_frac: float = 0.0) -> torch.Tensor:
+    """float32 N(0, std) of ``shape`` from a seeded CPU generator; a fraction
+    ``neg_inf_frac`` of the entries (drawn from the same generator) is -inf."""
+    g = torch.Generator("cpu").manual_seed(seed)
+    x = torch.randn(*shape, dtype=torch.float32, generator=g) * std
+    if neg_inf_frac > 0:
+        x[torch.rand(*shape, generator=g) < neg_inf_frac] = float("-inf")
+    return x

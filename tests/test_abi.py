@@ -123,7 +123,35 @@ def test_block_mask_descriptor_validation():
     assert fwd(mb=ctypes.byref(d), dtype=fa.FA_F32) == 8  # 16-bit inputs only
     assert fwd(mb=ctypes.byref(d), Nk=65536 + 64) == 8    # beyond FA_MAX_SPARSE_N
     assert fwd(mb=ctypes.byref(d), Nq=65536 + 1) == 8
-    assert ctypes.sizeof(fa.MaskBiasDesc) == 72  # the C layout of fa_mask_bias_desc
+    assert ctypes.sizeof(fa.MaskBiasDesc) == 112  # the C layout of fa_mask_bias_desc
+
+
+def test_bias_tensor_descriptor_validation():
+    def desc(bias=P, sb=0, sh=0, si=16):
+        d = fa.MaskBiasDesc()
+        d.bias_kind = fa.FA_BIAS_TENSOR
+        d.bias = bias
+        d.bias_stride_b, d.bias_stride_h, d.bias_stride_i = sb, sh, si
+        return d
+    assert fwd(mb=ctypes.byref(desc(bias=None))) == 1
+    assert fwd(mb=ctypes.byref(desc(bias=P + 2))) == 6   # float32: 4-byte alignment
+    for bad in (dict(sb=-1), dict(sh=-16), dict(si=-1)):
+        assert fwd(mb=ctypes.byref(desc(**bad))) == 5, bad
+    d = desc()
+    d.block_mask, d.block_q, d.block_k = P, 64, 64
+    assert fwd(mb=ctypes.byref(d)) == 8  # no bitmap together with a bias tensor
+    # dbias needs the bias tensor, 4-byte aligned; misaligned bias rejected in the backward
+    d = desc()
+    d.dbias = P + 2
+    assert bwd(mb=ctypes.byref(d)) == 6
+    d = fa.MaskBiasDesc()
+    d.dbias = P
+    assert bwd(mb=ctypes.byref(d)) == 5
+    arr = (ctypes.c_float * 1)(0.5)
+    d.bias_kind, d.n_slopes = fa.FA_BIAS_DIST_LINEAR, 1
+    d.slopes = ctypes.cast(arr, ctypes.POINTER(ctypes.c_float))
+    assert bwd(mb=ctypes.byref(d)) == 5
+    assert bwd(mb=ctypes.byref(desc(bias=P + 1))) == 6
 
 
 def bwd(**kw):

@@ -1,0 +1,231 @@
+"""GPU parity of the float32 bias-tensor path (FA_BIAS_TENSOR): forward, split forward and
+backward with dbias, against the float64 oracle on the same seeded inputs.
+
+Source: scifaro.com related-papers page for FlashMask (arXiv 2410.01359), the abstract on
+attention with an additive bias matrix. Tolerances as for the other parity tests: O within
+1e-5 (float32 inputs) or 2e-2 (bf16/fp16), LSE within 1e-3 relative, dQ, dK, dV within
+2e-2 absolute (float32 gradients of 16-bit inputs).
+
+dbias = dS = P o (dP - D) has a bound of its own, derived from the arithmetic: the
+backward takes D_i = sum_c dO_ic O_ic from the stored 16-bit O, whose entries differ from
+the exact ones by the rounding of the probabilities before P V (2^-9 relative each) and of
+the stored value (2^-9), so |dO_i| . |dO - O| <= 2^-8 sum_c |dO_ic| (P |V|)_ic =: 2^-8 A_i.
+Every other step is float32 (relative 1e-6 scale), so per element
+    |d dbias_ij| <= P_ij (2^-8 A_i + 1e-3) + 1e-6,
+with P the oracle's probabilities (large where a bias makes the softmax peaky, which is
+where this term exceeds a flat 2e-2).
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from synth import CONFIGS, bias_tensor, key_ranges, normal, qkv_inputs, seed_for
+from tests.util import GRAD_TOL, assert_fwd_close, np64, sample_rows
+
+pytestmark = pytest.mark.gpu
+
+fa = pytest.importorskip("exact_io_aware_flash_amd")
+DEV = "cuda:0"
+
+
+def bias_shape(kind, B, H, nq, nk):
+    return {"full": (B, H, nq, nk), "head": (1, H, nq, nk), "key": (B, 1, 1, nk),
+            "rows": (1, 1, nq, nk)}[kind]
+
+
+def strided(b):
+    """The same values in a buffer whose rows are 3 floats longer (row stride nk + 3)."""
+    big = torch.full(b.shape[:-1] + (b.shape[-1] + 3,), 7.0, dtype=b.dtype, device=b.device)
+    big[..., :b.shape[-1]] = b
+    return big[..., :b.shape[-1]]
+
+
+FWD_CASES = [
+    # dtype, d, causal, nq, nk, bias kind, -inf fraction, key ranges, row-strided buffer
+    (torch.bfloat16, 128, True, 300, 300, "full", 0.0, False, False),
+    (torch.bfloat16, 128, False, 200, 333, "head", 0.1, False, True),
+    (torch.float16, 64, True, 257, 513, "key", 0.0, False, False),
+    (torch.float16, 64, False, 129, 70, "full", 0.05, True, True),
+    (torch.bfloat16, 128, True, 1000, 1000, "rows", 0.0, True, False),
+    (torch.bfloat16, 64, True, 64, 64, "full", 0.0, False, False),
+    (torch.float16, 128, False, 1, 1, "full", 0.0, False, False),
+    (torch.float32, 128, True, 200, 250, "full", 0.1, False, True),
+    (torch.float32, 64, False, 100, 77, "key", 0.0, True, False),
+]
+
+
+@pytest.mark.parametrize("dtype,d,causal,nq,nk,kind,ninf,ranged,stride", FWD_CASES)
+def test_forward_matches_oracle(dtype, d, causal, nq, nk, kind, ninf, ranged, stride):
+    B, H = 2, 3
+    seed = 900 + nq + 7 * nk + d
+    q, k, v = (normal((B, H, n, d), dtype, seed + i) for i, n in enumerate((nq, nk, nk)))
+    bias = bias_tensor(bias_shape(kind, B, H, nq, nk), seed + 5, 2.0, ninf)
+    if kind == "full" and nq > 2:
+        bias[0, 1, 2] = float("-inf")  # a row whose every entry is masked by the bias
+    kw = {}
+    ks = ke = None
+    if ranged:
+        ks, ke = key_ranges(nq, nk, seed=seed + 6, block=64, width=max(nk // 2, 1), jitter=16)
+        kw = dict(key_start=ks.to(DEV), key_end=ke.to(DEV))
+    bd = bias.to(DEV)
+    if stride:
+        bd = strided(bd)
+    scale = 1.0 / math.sqrt(d)
+    o, lse = fa.fa_fwd(q.to(DEV), k.to(DEV), v.to(DEV), causal=causal, scale=scale, bias=bd, **kw)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.attention_forward(
+        np64(q), np64(k), np64(v), scale, causal=causal, bias=bias.double().numpy(),
+        key_start=None if ks is None else ks.numpy(), key_end=None if ke is None else ke.numpy())
+    assert_fwd_close(np64(o), np64(lse), o_ref, lse_ref, dtype,
+                     f"bias {kind} {dtype} d{d} c{causal} {nq}x{nk}")
+
+
+@pytest.mark.parametrize("nq,nk,n_split", [(1, 2000, 4), (16, 4100, 0), (64, 777, 3)])
+def test_split_forward_matches_oracle(nq, nk, n_split):
+    B, H, d = 2, 4, 128
+    dtype = torch.bfloat16
+    q, k, v = (normal((B, H, n, d), dtype, 950 + i) for i, n in enumerate((nq, nk, nk)))
+    bias = bias_tensor((B, H, nq, nk), 955, 1.5, 0.02)
+    assert fa.fa_fwd_split_count(B, H, nq, nk, d, n_split) > 1
+    o, lse = fa.fa_fwd_split(q.to(DEV), k.to(DEV), v.to(DEV), causal=True, bias=bias.to(DEV),
+                             n_split=n_split)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.attention_forward(np64(q), np64(k), np64(v), 1 / math.sqrt(d),
+                                              causal=True, bias=bias.double().numpy())
+    assert_fwd_close(np64(o), np64(lse), o_ref, lse_ref, dtype, f"split bias {nq}x{nk}")
+
+
+def check(got, want, names, what):
+    for name, g, w in zip(names, got, want):
+        g = np64(g)
+        assert np.isfinite(g).all(), f"{what}: non-finite {name}"
+        err = float(np.abs(g - w).max()) if g.size else 0.0
+        assert err <= GRAD_TOL, f"{what}: {name} max err {err:.3e} > {GRAD_TOL}"
+
+
+def dbias_tol(q, k, v, do, scale, causal, bias, ks, ke):
+    """Per-element bound on |dbias - dS| (module docstring), [B, H, N_q, N_k], and the
+    entries the oracle masks (probability exactly 0)."""
+    B, H, nq, _ = q.shape
+    nk = k.shape[2]
+    tol = np.empty((B, H, nq, nk))
+    masked = np.empty((B, H, nq, nk), dtype=bool)
+    for b in range(B):
+        for h in range(H):
+            p = oracle.attention_probabilities(q, k, scale, b, h, causal, key_start=ks,
+                                               key_end=ke, bias=bias)
+            a = (np.abs(do[b, h]) * (p @ np.abs(v[b, h]))).sum(axis=1)
+            tol[b, h] = p * (2.0 ** -8 * a[:, None] + 1e-3) + 1e-6
+            masked[b, h] = p == 0
+    return tol, masked
+
+
+def check_dbias(got, want, tol_masked, what):
+    tol, masked = tol_masked
+    g = np64(got)
+    assert np.isfinite(g).all(), f"{what}: non-finite dbias"
+    err = np.abs(g - want)
+    worst = np.unravel_index(np.argmax(err - tol), err.shape)
+    assert np.all(err <= tol), (f"{what}: |d dbias| {err[worst]:.3e} > {tol[worst]:.3e} "
+                                f"at {tuple(int(x) for x in worst)}")
+    # masked entries are exactly zero (the library clears what it skips)
+    assert np.all(g[masked] == 0), f"{what}: {int((g[masked] != 0).sum())} masked entries != 0"
+
+
+BWD_CASES = [
+    # dtype, d, causal, nq, nk, bias kind, -inf fraction, key ranges
+    (torch.bfloat16, 128, True, 300, 300, "full", 0.0, False),
+    (torch.float16, 64, False, 200, 333, "head", 0.1, False),
+    (torch.bfloat16, 64, True, 257, 513, "key", 0.0, True),
+    (torch.float16, 128, True, 130, 70, "full", 0.05, False),
+    (torch.bfloat16, 128, False, 3, 1, "rows", 0.0, False),
+]
+
+
+@pytest.mark.parametrize("dtype,d,causal,nq,nk,kind,ninf,ranged", BWD_CASES)
+def test_backward_and_dbias_match_oracle(dtype, d, causal, nq, nk, kind, ninf, ranged):
+    B, H = 2, 2
+    seed = 970 + nq + 3 * nk + d
+    q, k, v, do = (normal((B, H, n, d), dtype, seed + i) for i, n in enumerate((nq, nk, nk, nq)))
+    bias = bias_tensor(bias_shape(kind, B, H, nq, nk), seed + 5, 2.0, ninf)
+    kw = {}
+    ks = ke = None
+    if ranged:
+        ks, ke = key_ranges(nq, nk, seed=seed + 6, block=64, width=max(nk // 2, 1), jitter=16)
+        kw = dict(key_start=ks.to(DEV), key_end=ke.to(DEV))
+    scale = 1.0 / math.sqrt(d)
+    qd, kd, vd, dod, bd = (t.to(DEV) for t in (q, k, v, do, bias))
+    o, lse = fa.fa_fwd(qd, kd, vd, causal=causal, scale=scale, bias=bd, **kw)
+    dbias = torch.full((B, H, nq, nk), float("nan"), dtype=torch.float32, device=DEV)
+    dq, dk, dv = fa.fa_bwd(dod, qd, kd, vd, o, lse, causal=causal, scale=scale, bias=bd,
+                           dbias=dbias, **kw)
+    torch.cuda.synchronize()
+    want = oracle.attention_backward(
+        np64(q), np64(k), np64(v), np64(do), scale, causal=causal, bias=bias.double().numpy(),
+        key_start=None if ks is None else ks.numpy(), key_end=None if ke is None else ke.numpy(),
+        return_dbias=True)
+    what = f"bias {kind} {dtype} d{d} c{causal} {nq}x{nk}"
+    check((dq, dk, dv), want[:3], ("dQ", "dK", "dV"), what)
+    ksn = None if ks is None else ks.numpy()
+    ken = None if ke is None else ke.numpy()
+    check_dbias(dbias, want[3], dbias_tol(np64(q), np64(k), np64(v), np64(do), scale, causal,
+                                          bias.double().numpy(), ksn, ken), what)
+    # without dbias the gradients are the same bits
+    dq2, dk2, dv2 = fa.fa_bwd(dod, qd, kd, vd, o, lse, causal=causal, scale=scale, bias=bd, **kw)
+    torch.cuda.synchronize()
+    for a, b in ((dq, dq2), (dk, dk2), (dv, dv2)):
+        assert torch.equal(a, b), what
+
+
+def test_zero_bias_agrees_with_no_bias():
+    # an all-zero bias tensor gives the unbiased result (the two paths round the scores
+    # differently: scaled before the row max here, after it without a bias)
+    B, H, n, d = 1, 2, 384, 128
+    q, k, v = (normal((B, H, n, d), torch.bfloat16, 990 + i) for i in range(3))
+    zero = torch.zeros((1, 1, n, n), dtype=torch.float32, device=DEV)
+    o1, l1 = fa.fa_fwd(q.to(DEV), k.to(DEV), v.to(DEV), causal=True, bias=zero)
+    o0, l0 = fa.fa_fwd(q.to(DEV), k.to(DEV), v.to(DEV), causal=True)
+    torch.cuda.synchronize()
+    assert float((o1.float() - o0.float()).abs().max()) <= 2e-2
+    assert float((l1 - l0).abs().max()) <= 1e-4
+
+
+def test_full_size_shared_bias_sampled():
+    # the bf16 B2 H8 N8192 d128 workload with key ranges and a per-head bias shared over
+    # the batch ([1, H, N, N], 2.1 GB): sampled rows of the forward, and one whole head of
+    # the backward (dQ, dK, dV, dbias) against the oracle
+    w = CONFIGS[4]
+    q, k, v, do = qkv_inputs(w, with_dout=True)
+    ks, ke = key_ranges(w.N_q, w.N_k, seed_for(w.wid, 9), block=128, width=w.N_k // 2, jitter=64)
+    bias = bias_tensor((1, w.H, w.N_q, w.N_k), seed_for(w.wid, 10), 1.0)
+    qd, kd, vd, dod, bd = (t.to(DEV) for t in (q, k, v, do, bias))
+    ksd, ked = ks.to(DEV), ke.to(DEV)
+    o, lse = fa.fa_fwd(qd, kd, vd, causal=w.causal, scale=w.scale, bias=bd, key_start=ksd,
+                       key_end=ked)
+    torch.cuda.synchronize()
+    rows = sample_rows(w.N_q, 16, 4011)
+    bnp = bias.numpy()
+    for (b, h) in ((0, 0), (1, 5)):
+        o_ref, l_ref = oracle.attention_forward_rows(
+            np64(q), np64(k), np64(v), w.scale, rows, b, h, causal=w.causal,
+            key_start=ks.numpy(), key_end=ke.numpy(), bias=bnp)
+        assert_fwd_close(np64(o[b, h][rows]), np64(lse[b, h][rows]), o_ref, l_ref, w.torch_dtype,
+                         f"full-size bias b{b} h{h}")
+    dbias = torch.empty((w.B, w.H, w.N_q, w.N_k), dtype=torch.float32, device=DEV)
+    dq, dk, dv = fa.fa_bwd(dod, qd, kd, vd, o, lse, causal=w.causal, scale=w.scale, bias=bd,
+                           dbias=dbias, key_start=ksd, key_end=ked)
+    torch.cuda.synchronize()
+    b, h = 1, 3
+    one = lambda t: t[b:b + 1, h:h + 1]  # noqa: E731
+    want = oracle.attention_backward(
+        np64(one(q)), np64(one(k)), np64(one(v)), np64(one(do)), w.scale, causal=w.causal,
+        bias=bnp[:, h:h + 1], key_start=ks.numpy(), key_end=ke.numpy(), return_dbias=True)
+    check((one(dq), one(dk), one(dv)), want[:3], ("dQ", "dK", "dV"), "full-size bias backward")
+    check_dbias(one(dbias), want[3],
+                dbias_tol(np64(one(q)), np64(one(k)), np64(one(v)), np64(one(do)), w.scale,
+                          w.causal, bnp[:, h:h + 1], ks.numpy(), ke.numpy()),
+                "full-size bias backward")

@@ -193,3 +193,54 @@ def test_planted_fp8_mistake_is_caught(monkeypatch, mutation):
         except AssertionError:
             caught += 1
     assert caught >= 1, f"no pin caught {mutation.__name__}"
+
+
+# ---- bias tensor (oracle/attention.py bias_rows, scores) ------------------------------
+import tests.test_oracle_bias as bias_pins  # noqa: E402
+
+_orig_bias_rows, _orig_scores = A.bias_rows, A.scores
+
+
+def mut_tensor_bias_sign(monkeypatch):
+    def bad(*a, **kw):
+        r = _orig_bias_rows(*a, **kw)
+        return None if r is None else -r
+    monkeypatch.setattr(A, "bias_rows", bad)
+
+
+def mut_tensor_bias_scaled(monkeypatch):
+    # scores(q_rows, k, scale, rows, n_q, causal, slope, key_start, key_end, blocks, bias)
+    def bad(q_rows, k, scale, *a):
+        a = list(a)
+        if len(a) > 7 and a[7] is not None:
+            a[7] = scale * a[7]
+        return _orig_scores(q_rows, k, scale, *a)
+    monkeypatch.setattr(A, "scores", bad)
+
+
+def mut_tensor_bias_rows_reversed(monkeypatch):
+    def bad(bias, B, H, n_q, n_k, b, h, rows):
+        return _orig_bias_rows(bias, B, H, n_q, n_k, b, h, n_q - 1 - np.asarray(rows))
+    monkeypatch.setattr(A, "bias_rows", bad)
+
+
+BIAS_PINS = [
+    lambda: bias_pins.test_forward_with_bias_matches_multiprecision_brute_force(False, 5, 7, 0.0),
+    lambda: bias_pins.test_row_constant_bias_shifts_lse_only(),
+    lambda: bias_pins.test_log2_bias_equals_the_key_taken_twice(),
+    lambda: bias_pins.test_dbias_against_torch_autograd_with_broadcast_bias(),
+]
+
+
+@pytest.mark.parametrize("mutation", [
+    mut_tensor_bias_sign, mut_tensor_bias_scaled, mut_tensor_bias_rows_reversed,
+])
+def test_planted_bias_tensor_mistake_is_caught(monkeypatch, mutation):
+    mutation(monkeypatch)
+    caught = 0
+    for pin in BIAS_PINS:
+        try:
+            pin()
+        except AssertionError:
+            caught += 1
+    assert caught >= 1, f"no pin caught {mutation.__name__}"
