@@ -39,9 +39,9 @@ PEAK_FP8_TFLOPS = 2 * PEAK_BF16_TFLOPS  # dense E4M3 MFMA (published 5.0 PFLOP/s
 # the kernel source they were measured on. A changed source means stale counters -> null.
 TRAFFIC = {
     # kernel: (source hash, bytes read, bytes written) -- profiles/attention_fwd_bwd_bf16_causal_B2H16N8192d128.md
-    "fwd": ("9cd335ca4c02996c", 287.5e6, 68.2e6),
-    "bwd_dkdv": ("4237a51d0f3a8f54", 270.9e6, 268.4e6),
-    "bwd_dq": ("4237a51d0f3a8f54", 398.2e6, 138.2e6),
+    "fwd": ("8826a0dbdaf728a5", 288.4e6, 68.2e6),
+    "bwd_dkdv": ("c0ac0fc4af42aacd", 270.9e6, 268.4e6),
+    "bwd_dq": ("c0ac0fc4af42aacd", 398.6e6, 138.2e6),
 }
 
 
@@ -81,6 +81,10 @@ def parse():
                     help="skip the supplementary FP8 forward timings")
     ap.add_argument("--fp8-only", action="store_true",
                     help="only time the FP8 path and print it as one JSON line")
+    ap.add_argument("--no-bias-tensor", action="store_true",
+                    help="skip the supplementary bias-tensor fwd/bwd timings")
+    ap.add_argument("--bias-only", action="store_true",
+                    help="only time the bias-tensor shapes and print them as one JSON line")
     ap.add_argument("--hbm-only", action="store_true",
                     help="only time the supplementary shapes and print them as one JSON line")
     ap.add_argument("--hbm-filter", default="",
@@ -136,6 +140,13 @@ def main():
             print("no GPU visible", file=sys.stderr)
             sys.exit(1)
         print(json.dumps({"fp8": fp8_forward(fa, torch, CONFIGS[5], qkv_inputs)}), flush=True)
+        return
+    if args.bias_only:
+        fa.load_library()  # fails loudly if the HIP library is missing
+        if not torch.cuda.is_available():
+            print("no GPU visible", file=sys.stderr)
+            sys.exit(1)
+        print(json.dumps({"bias_tensor": bias_tensor_bench(fa, torch)}), flush=True)
         return
     if args.sparse_only:
         fa.load_library()  # fails loudly if the HIP library is missing
@@ -237,6 +248,7 @@ def main():
     sparse = None if args.no_sparse else block_sparse(fa, torch, w, qkv_inputs)
     fp8 = None if args.no_fp8 else fp8_forward(fa, torch, w, qkv_inputs)
     sweep = None if args.no_sweep else workload_sweep(fa, torch)
+    btensor = None if args.no_bias_tensor else bias_tensor_bench(fa, torch)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -271,6 +283,7 @@ def main():
         "block_sparse": sparse,
         "fp8": fp8,
         "sweep": sweep,
+        "bias_tensor": btensor,
     }
     print(json.dumps(line), flush=True)
 
@@ -378,6 +391,51 @@ def block_sparse(fa, torch, w, qkv_inputs):
                     "bwd_tflops": round(10.0 * d * pairs / (bwd_us * 1e-6) / 1e12, 1)})
     del q, k, v, do, o, lse, grads, ws
     return out
+
+
+def bias_tensor_bench(fa, torch):
+    """The ALiBi-like workload (bf16 B2 H8 N8192 d128, key ranges) with its bias given as
+    a float32 tensor [1, H, N, N] (one matrix per head, shared over the batch) instead of
+    generated from the slope: forward, backward, and backward writing dbias [B, H, N, N],
+    each timed by time_us, beside the generated-slope forward and backward. Rates count
+    the visible (query, key) pairs (forward 4d, backward 10d FLOPs each); the bias bytes
+    are 4 per visible pair and (b, h), the dbias bytes the clear of the whole array plus
+    4 per visible pair and (b, h)."""
+    from synth import CONFIGS, bias_tensor, key_ranges, qkv_inputs, seed_for
+
+    dev = torch.device("cuda:0")
+    w = CONFIGS[4]
+    B, H, N, d = w.B, w.H, w.N_q, w.d
+    q, k, v, do = (t.to(dev) for t in qkv_inputs(w, with_dout=True))
+    ks, ke = key_ranges(N, N, seed_for(w.wid, 9), 128, N // 2, 64)
+    pairs = B * H * float((ke.clamp(0, N) - ks.clamp(0, N)).clamp(min=0).sum())
+    rng = dict(key_start=ks.to(dev), key_end=ke.to(dev), scale=w.scale)
+    bias = bias_tensor((1, H, N, N), seed_for(w.wid, 10), 1.0).to(dev)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    grads = tuple(torch.empty((B, H, N, d), dtype=torch.float32, device=dev) for _ in range(3))
+    ws = torch.empty(fa.fa_bwd_workspace_bytes(B, H, N, N, d), dtype=torch.uint8, device=dev)
+    dbias = torch.empty((B, H, N, N), dtype=torch.float32, device=dev)
+    res = {"shape": f"bf16 B{B} H{H} N{N} d{d}, key ranges (visible {pairs / (B * H * N * N):.3f} "
+                    "of the pairs)"}
+    for name, kw in (("slope", dict(bias_slopes=w.bias_slope)), ("tensor", dict(bias=bias))):
+        fwd_us = time_us(torch, lambda: fa.fa_fwd(q, k, v, out=o, lse=lse, **rng, **kw))
+        fa.fa_fwd(q, k, v, out=o, lse=lse, **rng, **kw)
+        bwd_us = time_us(torch, lambda: fa.fa_bwd(do, q, k, v, o, lse, grads=grads, workspace=ws,
+                                                  **rng, **kw))
+        ent = {"fwd_us": round(fwd_us, 1), "bwd_us": round(bwd_us, 1),
+               "fwd_visible_tflops": round(4.0 * d * pairs / (fwd_us * 1e-6) / 1e12, 1),
+               "bwd_visible_tflops": round(10.0 * d * pairs / (bwd_us * 1e-6) / 1e12, 1)}
+        if name == "tensor":
+            ent["fwd_bias_gbs"] = round(4.0 * pairs / (fwd_us * 1e-6) / 1e9, 1)
+            db_us = time_us(torch, lambda: fa.fa_bwd(do, q, k, v, o, lse, grads=grads,
+                                                     workspace=ws, dbias=dbias, **rng, **kw))
+            ent["bwd_dbias_us"] = round(db_us, 1)
+            ent["dbias_write_gbs"] = round((4.0 * B * H * N * N + 4.0 * pairs)
+                                           / (db_us * 1e-6) / 1e9, 1)
+        res[name] = ent
+    del q, k, v, do, o, lse, grads, ws, dbias, bias
+    return res
 
 
 def workload_sweep(fa, torch):
