@@ -1019,14 +1019,16 @@ static int device_cus() {
 //     where twice as many, fuller blocks balance the load better.
 // For N_q <= kFwdFewRows every d = 128 variant holds the whole head in one query block.
 // With a bias tensor, whose tile (4 waves x 32 rows x the tile's keys, float32) shares
-// each stage with K and V: 4 waves, two stages (d = 128: 64-key tiles, 134 KB, or
-// 32-key tiles when split; d = 64: 64-key tiles, 102 KB).
+// each stage with K and V: 4 waves, two stages, 32-key tiles (d = 128: 67 KB, two
+// workgroups per compute unit; d = 64: 51 KB). The bias makes the kernel wait on HBM;
+// a second workgroup per compute unit hides it better than 64-key tiles at one
+// workgroup (134 KB): 503-510 against 649-667 us on the bf16 B2 H8 N8192 d128
+// key-range workload with a [1, H, N, N] bias.
 template <typename T>
 static hipError_t launch16_for(int d, int bias, FwdArgs& a, hipStream_t st) {
   if (bias == kBiasTensor) {
-    if (d == 64) return launch16<T, 64, 64, 4, 2>(bias, a, st);
-    if (a.Nq <= kFwdFewRows && a.n_split > 1) return launch16<T, 128, 32, 4, 2>(bias, a, st);
-    return launch16<T, 128, 64, 4, 2>(bias, a, st);
+    if (d == 64) return launch16<T, 64, 32, 4, 2>(bias, a, st);
+    return launch16<T, 128, 32, 4, 2>(bias, a, st);
   }
   if (d == 64) return launch16<T, 64, 64, 4, 4>(bias, a, st);
   if (a.Nq <= kFwdFewRows) {
