@@ -229,3 +229,27 @@ def test_full_size_shared_bias_sampled():
                 dbias_tol(np64(one(q)), np64(one(k)), np64(one(v)), np64(one(do)), w.scale,
                           w.causal, bnp[:, h:h + 1], ks.numpy(), ke.numpy()),
                 "full-size bias backward")
+
+
+def test_dbias_by_phases_equals_one_call():
+    # the dK/dV phase alone writes dbias; the dQ phase leaves it untouched
+    B, H, n, d = 1, 2, 200, 64
+    q, k, v, do = (normal((B, H, n, d), torch.float16, 1990 + i) for i in range(4))
+    bias = bias_tensor((B, 1, n, n), 1995, 1.0, 0.05).to(DEV)
+    qd, kd, vd, dod = (t.to(DEV) for t in (q, k, v, do))
+    o, lse = fa.fa_fwd(qd, kd, vd, causal=True, bias=bias)
+    db1 = torch.full((B, H, n, n), float("nan"), dtype=torch.float32, device=DEV)
+    g1 = fa.fa_bwd(dod, qd, kd, vd, o, lse, causal=True, bias=bias, dbias=db1)
+    ws = torch.empty(fa.fa_bwd_workspace_bytes(B, H, n, n, d), dtype=torch.uint8, device=DEV)
+    db2 = torch.full((B, H, n, n), float("nan"), dtype=torch.float32, device=DEV)
+    grads = tuple(torch.empty((B, H, n, d), dtype=torch.float32, device=DEV) for _ in range(3))
+    fa.fa_bwd(dod, qd, kd, vd, o, lse, causal=True, bias=bias, dbias=db2, grads=grads,
+              workspace=ws, phases=fa.FA_BWD_PREP | fa.FA_BWD_DQ)
+    torch.cuda.synchronize()
+    assert torch.isnan(db2).all()  # no dK/dV phase: dbias not touched
+    fa.fa_bwd(dod, qd, kd, vd, o, lse, causal=True, bias=bias, dbias=db2, grads=grads,
+              workspace=ws, phases=fa.FA_BWD_DKDV)
+    torch.cuda.synchronize()
+    assert torch.equal(db1, db2)
+    for a, b in zip(g1, grads):
+        assert torch.equal(a, b)
