@@ -253,3 +253,26 @@ def test_dbias_by_phases_equals_one_call():
     assert torch.equal(db1, db2)
     for a, b in zip(g1, grads):
         assert torch.equal(a, b)
+
+
+def test_dbias_beyond_2_31_elements_matches_the_head_alone():
+    # B2 H16 N8192: dbias holds 2^31 + 2^27 elements (8.6 GB), so the last heads' entries
+    # sit past 32-bit offsets; head (1, 15) must equal the same head computed alone (a
+    # call with small offsets, whose parity the oracle tests above establish)
+    B, H, n, d = 2, 16, 8192, 64
+    q, k, v, do = (normal((B, H, n, d), torch.bfloat16, 2990 + i).to(DEV) for i in range(4))
+    bias = bias_tensor((1, 1, n, n), 2995, 1.0).to(DEV)
+    o, lse = fa.fa_fwd(q, k, v, causal=True, bias=bias)
+    dbias = torch.empty((B, H, n, n), dtype=torch.float32, device=DEV)
+    dq, dk, dv = fa.fa_bwd(do, q, k, v, o, lse, causal=True, bias=bias, dbias=dbias)
+    torch.cuda.synchronize()
+    one = lambda t: t[1:2, 15:16].contiguous()  # noqa: E731
+    o1, lse1 = fa.fa_fwd(one(q), one(k), one(v), causal=True, bias=bias)
+    db1 = torch.empty((1, 1, n, n), dtype=torch.float32, device=DEV)
+    g1 = fa.fa_bwd(one(do), one(q), one(k), one(v), o1, lse1, causal=True, bias=bias, dbias=db1)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, one(o)) and torch.equal(lse1, one(lse))
+    assert torch.equal(db1, dbias[1:2, 15:16])
+    for a, b in zip(g1, (dq, dk, dv)):
+        assert torch.equal(a, one(b))
+    del dbias
