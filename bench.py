@@ -132,14 +132,14 @@ def main():
     import torch
 
     import exact_io_aware_flash_amd as fa
-    from synth import CONFIGS, qkv_inputs
+    from synth import WORKLOADS, qkv_inputs
 
     if args.fp8_only:
         fa.load_library()  # fails loudly if the HIP library is missing
         if not torch.cuda.is_available():
             print("no GPU visible", file=sys.stderr)
             sys.exit(1)
-        print(json.dumps({"fp8": fp8_forward(fa, torch, CONFIGS[5], qkv_inputs)}), flush=True)
+        print(json.dumps({"fp8": fp8_forward(fa, torch, WORKLOADS[5], qkv_inputs)}), flush=True)
         return
     if args.bias_only:
         fa.load_library()  # fails loudly if the HIP library is missing
@@ -153,7 +153,7 @@ def main():
         if not torch.cuda.is_available():
             print("no GPU visible", file=sys.stderr)
             sys.exit(1)
-        print(json.dumps({"block_sparse": block_sparse(fa, torch, CONFIGS[5], qkv_inputs)}),
+        print(json.dumps({"block_sparse": block_sparse(fa, torch, WORKLOADS[5], qkv_inputs)}),
               flush=True)
         return
 
@@ -163,7 +163,7 @@ def main():
         sys.exit(1)
     dev = torch.device("cuda:0")
 
-    w = CONFIGS[5]
+    w = WORKLOADS[5]
     B, H, N, d = w.B, w.H, w.N_q, w.d
     q, k, v, do = (t.to(dev) for t in qkv_inputs(w))
     o = torch.empty_like(q)
@@ -401,10 +401,10 @@ def bias_tensor_bench(fa, torch):
     the visible (query, key) pairs (forward 4d, backward 10d FLOPs each); the bias bytes
     are 4 per visible pair and (b, h), the dbias bytes the clear of the whole array plus
     4 per visible pair and (b, h)."""
-    from synth import CONFIGS, bias_tensor, key_ranges, qkv_inputs, seed_for
+    from synth import WORKLOADS, bias_tensor, key_ranges, qkv_inputs, seed_for
 
     dev = torch.device("cuda:0")
-    w = CONFIGS[4]
+    w = WORKLOADS[4]
     B, H, N, d = w.B, w.H, w.N_q, w.d
     q, k, v, do = (t.to(dev) for t in qkv_inputs(w, with_dout=True))
     ks, ke = key_ranges(N, N, seed_for(w.wid, 9), 128, N // 2, 64)
@@ -443,12 +443,12 @@ def workload_sweep(fa, torch):
     time_us, in TFLOP/s by the convention (4 B H N_q N_k d, halved for causal; masks and
     bias otherwise not discounted) and by the visible (query, key) pairs (4 d each), both
     also as a fraction of the MFMA peak of the input type."""
-    from synth import CONFIGS, key_ranges, qkv_inputs, seed_for
+    from synth import WORKLOADS, key_ranges, qkv_inputs, seed_for
 
     dev = torch.device("cuda:0")
     out = []
-    for wid in sorted(CONFIGS):
-        w = CONFIGS[wid]
+    for wid in sorted(WORKLOADS):
+        w = WORKLOADS[wid]
         q, k, v, do = (t.to(dev) if t is not None else None for t in qkv_inputs(w))
         kw = dict(causal=w.causal, scale=w.scale)
         if w.bias_slope is not None:

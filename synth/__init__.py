@@ -7,7 +7,7 @@ scores, softmax, masks applied to scores or gradients. Both the CPU oracle side
 """
 
 from .inputs import (  # noqa: F401
-    CONFIGS,
+    WORKLOADS,
     Workload,
     normal,
     qkv_inputs,

@@ -63,7 +63,7 @@ class Workload:
 
 # The five workloads: shapes, dtypes and recipes follow the exact-attention
 # configurations this library is measured on.
-CONFIGS = {
+WORKLOADS = {
     1: Workload(1, "fp32 single head B1 H1 N256 d64", "f32", 1, 1, 256, 256, 64),
     2: Workload(2, "bf16 causal fwd B4 H16 N2048 d128", "bf16", 4, 16, 2048, 2048, 128,
                 causal=True, factor=0.5),

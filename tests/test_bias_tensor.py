@@ -23,7 +23,7 @@ import pytest
 import torch
 
 import oracle
-from synth import CONFIGS, bias_tensor, key_ranges, normal, qkv_inputs, seed_for
+from synth import WORKLOADS, bias_tensor, key_ranges, normal, qkv_inputs, seed_for
 from tests.util import GRAD_TOL, assert_fwd_close, np64, sample_rows
 
 pytestmark = pytest.mark.gpu
@@ -198,7 +198,7 @@ def test_full_size_shared_bias_sampled():
     # the bf16 B2 H8 N8192 d128 workload with key ranges and a per-head bias shared over
     # the batch ([1, H, N, N], 2.1 GB): sampled rows of the forward, and one whole head of
     # the backward (dQ, dK, dV, dbias) against the oracle
-    w = CONFIGS[4]
+    w = WORKLOADS[4]
     q, k, v, do = qkv_inputs(w, with_dout=True)
     ks, ke = key_ranges(w.N_q, w.N_k, seed_for(w.wid, 9), block=128, width=w.N_k // 2, jitter=64)
     bias = bias_tensor((1, w.H, w.N_q, w.N_k), seed_for(w.wid, 10), 1.0)

@@ -14,7 +14,7 @@ import pytest
 import torch
 
 import oracle
-from synth import CONFIGS, key_ranges, normal, qkv_inputs
+from synth import WORKLOADS, key_ranges, normal, qkv_inputs
 from tests.util import GRAD_TOL, np64
 
 pytestmark = pytest.mark.gpu
@@ -141,7 +141,7 @@ def test_block_sparse_many_heads():
 def test_block_sparse_full_size_backward():
     # the bf16 causal N = 8192 d = 128 workload with half of its 128 x 128 blocks masked;
     # the oracle checks one whole (b, h) head
-    w = CONFIGS[5]
+    w = WORKLOADS[5]
     q, k, v, do = qkv_inputs(w)
     nb = -(-w.N_q // 128)
     bm = bitmap((w.H, nb, nb), 0.5, 19605)

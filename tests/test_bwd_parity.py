@@ -7,7 +7,7 @@ import pytest
 import torch
 
 import oracle
-from synth import CONFIGS, key_ranges, normal, qkv_inputs
+from synth import WORKLOADS, key_ranges, normal, qkv_inputs
 from tests.util import GRAD_TOL, np64
 
 pytestmark = pytest.mark.gpu
@@ -96,7 +96,7 @@ def test_backward_is_deterministic():
 
 def test_full_causal_bf16_n8192_backward():
     # the full fwd+bwd workload; the oracle checks two whole (b, h) heads
-    w = CONFIGS[5]
+    w = WORKLOADS[5]
     q, k, v, do = qkv_inputs(w)
     dq, dk, dv = fwd_bwd(q, k, v, do, scale=w.scale, causal=True)
     for g in (dq, dk, dv):

@@ -25,7 +25,7 @@ import torch
 
 import oracle
 from oracle import fp8 as F
-from synth import normal, random_signs, with_outliers, CONFIGS, qkv_inputs
+from synth import normal, random_signs, with_outliers, WORKLOADS, qkv_inputs
 from tests.util import np64, sample_rows
 
 pytestmark = pytest.mark.gpu
@@ -202,7 +202,7 @@ def test_fp8_rotation_lowers_error_against_exact_attention():
 def test_fp8_full_size_sampled_rows():
     # the bf16 causal B2 H16 N8192 d128 workload, rotated; two whole heads' operands
     # quantised by the oracle, sampled rows compared
-    w = CONFIGS[5]
+    w = WORKLOADS[5]
     q, k, v, _ = qkv_inputs(w, with_dout=False)
     s = random_signs(w.d, 705)
     o, lse = fa.fa_attention_fp8(q.to(DEV), k.to(DEV), v.to(DEV), causal=True, scale=w.scale,

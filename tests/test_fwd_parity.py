@@ -7,7 +7,7 @@ import pytest
 import torch
 
 import oracle
-from synth import CONFIGS, key_ranges, normal, qkv_inputs, seed_for
+from synth import WORKLOADS, key_ranges, normal, qkv_inputs, seed_for
 from tests.util import assert_fwd_close, np64, sample_rows
 
 pytestmark = pytest.mark.gpu
@@ -30,7 +30,7 @@ def ranges_dev(ks, ke):
 # the single-head fp32 workload, full oracle
 # ---------------------------------------------------------------------------
 def test_fp32_single_head_full():
-    w = CONFIGS[1]
+    w = WORKLOADS[1]
     q, k, v, _ = qkv_inputs(w)
     o, lse = run(q, k, v, scale=w.scale)
     o_ref, lse_ref = oracle.attention_forward(np64(q), np64(k), np64(v), w.scale)
@@ -133,7 +133,7 @@ def test_large_magnitude_scores_stay_finite():
 
 
 def test_forward_is_deterministic():
-    w = CONFIGS[2].scaled(B=1, H=4, N_q=1000, N_k=1000)
+    w = WORKLOADS[2].scaled(B=1, H=4, N_q=1000, N_k=1000)
     q, k, v, _ = qkv_inputs(w)
     o1, l1 = run(q, k, v, causal=True)
     o2, l2 = run(q, k, v, causal=True)
@@ -188,7 +188,7 @@ def test_many_heads_ragged(causal, bias, nq, nk):
 # full-size workloads: sampled rows of sampled heads against the oracle
 # ---------------------------------------------------------------------------
 def _full_config_check(wid, heads, nrows):
-    w = CONFIGS[wid]
+    w = WORKLOADS[wid]
     q, k, v, _ = qkv_inputs(w, with_dout=False)
     kw = dict(scale=w.scale, causal=w.causal)
     ks = ke = None
@@ -231,7 +231,7 @@ def test_full_causal_bf16_n8192_forward():
 def test_long_sequence_memory_stays_linear():
     # the fp16 score matrix of this workload would be ~13 GB; the kernel must only
     # need its inputs and outputs
-    w = CONFIGS[3]
+    w = WORKLOADS[3]
     q, k, v, _ = qkv_inputs(w, with_dout=False)
     q, k, v = q.to(DEV), k.to(DEV), v.to(DEV)
     o = torch.empty_like(q)
