@@ -133,7 +133,7 @@ const char* fa_status_string(fa_status s) {
     case FA_ERR_DTYPE: return "unknown dtype";
     case FA_ERR_HEADDIM: return "head dimension must be 64 or 128";
     case FA_ERR_MASK: return "malformed mask/bias descriptor";
-    case FA_ERR_ALIGN: return "device pointer not 16-byte aligned";
+    case FA_ERR_ALIGN: return "device pointer misaligned (16 bytes; 4 for float32 arrays)";
     case FA_ERR_WORKSPACE: return "workspace missing or too small";
     case FA_ERR_UNSUPPORTED: return "combination not implemented";
     case FA_ERR_HIP: return "HIP launch error";

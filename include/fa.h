@@ -60,7 +60,8 @@ typedef enum fa_status {
   FA_ERR_DTYPE = 3,       /* unknown dtype or gradient dtype */
   FA_ERR_HEADDIM = 4,     /* d not in {64, 128} */
   FA_ERR_MASK = 5,        /* malformed mask/bias descriptor */
-  FA_ERR_ALIGN = 6,       /* a device pointer is not 16-byte aligned */
+  FA_ERR_ALIGN = 6,       /* a device pointer is misaligned (16 bytes; 4 for float32 arrays
+                             such as lse, the bias tensor, dbias and dslopes) */
   FA_ERR_WORKSPACE = 7,   /* workspace NULL or smaller than fa_bwd_workspace_bytes() */
   FA_ERR_UNSUPPORTED = 8, /* a valid combination this build does not implement */
   FA_ERR_HIP = 9,         /* the HIP runtime reported an error at launch */
