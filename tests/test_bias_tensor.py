@@ -84,9 +84,11 @@ def test_forward_matches_oracle(dtype, d, causal, nq, nk, kind, ninf, ranged, st
                      f"bias {kind} {dtype} d{d} c{causal} {nq}x{nk}")
 
 
-@pytest.mark.parametrize("nq,nk,n_split", [(1, 2000, 4), (16, 4100, 0), (64, 777, 3)])
-def test_split_forward_matches_oracle(nq, nk, n_split):
-    B, H, d = 2, 4, 128
+@pytest.mark.parametrize("d,nq,nk,n_split", [(128, 1, 2000, 4), (128, 16, 4100, 0),
+                                              (128, 64, 777, 3), (64, 5, 1500, 0),
+                                              (64, 64, 1000, 2)])
+def test_split_forward_matches_oracle(d, nq, nk, n_split):
+    B, H = 2, 4
     dtype = torch.bfloat16
     q, k, v = (normal((B, H, n, d), dtype, 950 + i) for i, n in enumerate((nq, nk, nk)))
     bias = bias_tensor((B, H, nq, nk), 955, 1.5, 0.02)
