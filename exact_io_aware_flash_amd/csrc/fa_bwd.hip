@@ -371,6 +371,14 @@ void bwd_dkdv_kernel(const BwdArgs a) {
     else wait_vmem<0>();
     __builtin_amdgcn_s_barrier();
   };
+  // zero dbias of query tile t for this wave's keys (lanes 0-31 and 32-63: alternate rows)
+  auto zero_dbias_tile = [&](int t) {
+    if (dB == nullptr || key >= Nk) return;
+    for (int i = 0; i < BR / 2; ++i) {
+      const int qi = t * BR + 2 * i + h;
+      if (qi < Nq) dB[((size_t)bh * Nq + qi) * Nk + key] = 0.f;
+    }
+  };
 #pragma unroll
   for (int i = 0; i < P; ++i)
     if (i < n_pos) issue(i);
@@ -419,8 +427,18 @@ void bwd_dkdv_kernel(const BwdArgs a) {
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) qblock(sb, q0t, qb, std::true_type{});
       }
+    } else if constexpr (TENSOR) {
+      zero_dbias_tile(t);
     }
     if (p + 1 < n_pos) land(min(p + P, n_pos - 1) - (p + 1));
+  }
+  // dbias of the query tiles outside the workgroup's window is zero (every (i, j) of this
+  // wave's keys is then written exactly once: computed, or zero where nothing is visible)
+  if constexpr (TENSOR) {
+    if (dB != nullptr) {
+      for (int t = 0; t < t_lo; ++t) zero_dbias_tile(t);
+      for (int t = max(t_hi, t_lo); t < nqt; ++t) zero_dbias_tile(t);
+    }
   }
 
   // the workgroup's partial of dL/dslope (every workgroup writes one, zero if it saw
@@ -779,14 +797,6 @@ __global__ void dslope_reduce_kernel(const float* __restrict__ part, int B, int 
   out[s] = acc;
 }
 
-// dbias starts at zero: the dK/dV pass writes only the tiles it visits (every (i, j) of
-// those exactly once); masked-out tiles keep the zero. A kernel rather than a memset, so
-// that the clear stays correct inside a captured graph.
-__global__ __launch_bounds__(256) void zero_f32_kernel(float* __restrict__ p, size_t n) {
-  const size_t stride = (size_t)gridDim.x * blockDim.x;
-  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) p[i] = 0.f;
-}
-
 template <typename T, int D, int DKDV_NW, int DKDV_WPE, int DQ_BC, int DQ_NW, int DQ_WPE>
 static hipError_t launch_bwd_t(int bias, int phases, BwdArgs& a, hipStream_t st) {
   const int BH = a.B * a.H;
@@ -813,13 +823,6 @@ static hipError_t launch_bwd_t(int bias, int phases, BwdArgs& a, hipStream_t st)
     b.sched = sched;
     const dim3 grid((unsigned)(BH * b.nblk)), block(DKDV_NW * 64);
     const bool sparse = a.bmask != nullptr;
-    if (bias == kBiasTensor && a.dbias != nullptr) {
-      const size_t nel = (size_t)BH * a.Nq * a.Nk;
-      const size_t blocks = std::min<size_t>((nel + 255) / 256, 8192);
-      hipLaunchKernelGGL(zero_f32_kernel, dim3((unsigned)blocks), dim3(256), 0, st, a.dbias, nel);
-      e = hipGetLastError();
-      if (e != hipSuccess) return e;
-    }
     if (bias == kBiasTensor)
       hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, kDkdvBR, DKDV_NW, DKDV_WPE, kBiasTensor, false>), grid, block, 0, st, b);
     else if (bias && sparse)
