@@ -39,9 +39,9 @@ PEAK_FP8_TFLOPS = 2 * PEAK_BF16_TFLOPS  # dense E4M3 MFMA (published 5.0 PFLOP/s
 # the kernel source they were measured on. A changed source means stale counters -> null.
 TRAFFIC = {
     # kernel: (source hash, bytes read, bytes written) -- profiles/attention_fwd_bwd_bf16_causal_B2H16N8192d128.md
-    "fwd": ("7fdf4bb51cebec1c", 288.6e6, 68.2e6),
-    "bwd_dkdv": ("c0ac0fc4af42aacd", 270.9e6, 268.4e6),
-    "bwd_dq": ("c0ac0fc4af42aacd", 398.7e6, 138.2e6),
+    "fwd": ("7fdf4bb51cebec1c", 287.6e6, 68.2e6),
+    "bwd_dkdv": ("687f94f7376ce93f", 270.9e6, 268.4e6),
+    "bwd_dq": ("687f94f7376ce93f", 398.6e6, 138.2e6),
 }
 
 
