@@ -31,7 +31,14 @@ namespace fa {
 // ---------------------------------------------------------------------------------
 // 1. D = rowsum(dO * O)
 // ---------------------------------------------------------------------------------
-// Also writes LSE * log2(e) per row (the exponent offset the dK/dV pass uses).
+// Exponent offset of a row in the recomputed probabilities, p = exp2(s * scale * log2(e)
+// + bias * log2(e) - offset). A row with no visible key has LSE = -inf (its output is 0);
+// its offset is +inf, so every probability of the row is exactly 0 whatever the bias
+// (-inf - (-inf) would be NaN, and a finite score minus -inf would be +inf).
+__device__ inline float lse_offset2(float lse) { return lse == kNegInf ? -kNegInf : lse * kLog2e; }
+
+// Also writes the exponent offset per row (lse_offset2: LSE * log2(e)), which the dK/dV
+// pass reads.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void bwd_prep_kernel(const T* __restrict__ o,
                                                        const T* __restrict__ dout,
@@ -61,7 +68,7 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const T* __restrict__ o,
   for (int s = TPR / 2; s >= 1; s >>= 1) acc += __shfl_xor(acc, s, 64);
   if (row < rows && c == 0) {
     delta[row] = acc;
-    lse2[row] = lse[row] * kLog2e;
+    lse2[row] = lse_offset2(lse[row]);
   }
 }
 
@@ -539,7 +546,7 @@ void bwd_dq_kernel(const BwdArgs a) {
     qf[ks] = ldg16(Q + qr * D + 16 * ks + 8 * h);
     dof[ks] = ldg16(dO + qr * D + 16 * ks + 8 * h);
   }
-  const float lq = a.lse[(size_t)bh * Nq + qr] * kLog2e;
+  const float lq = lse_offset2(a.lse[(size_t)bh * Nq + qr]);
   const float dq_d = a.delta[(size_t)bh * Nq + qr];
 
   // key window of this wave / workgroup (same rules as the forward pass)

@@ -138,22 +138,45 @@ def check_dbias(got, want, tol_masked, what):
     assert np.all(g[masked] == 0), f"{what}: {int((g[masked] != 0).sum())} masked entries != 0"
 
 
+def plant_empty_rows(bias, kind):
+    """Set -inf over whole rows of the bias, so that those query rows see no key (their
+    forward gives O = 0 and LSE = -inf; their probabilities, gradients and dbias are 0).
+    "full" / "head": rows 0, 5, 64 and 130 of head 1 (inside fully visible tiles when
+    nothing else masks them); "key" ([B, 1, 1, N_k]): every row of batch 1."""
+    if kind in ("full", "head"):
+        for r in (0, 5, 64, 130):
+            if r < bias.shape[2]:
+                bias[:, 1, r] = float("-inf")
+    elif kind == "key":
+        bias[1] = float("-inf")
+    else:
+        raise ValueError(kind)
+
+
 BWD_CASES = [
-    # dtype, d, causal, nq, nk, bias kind, -inf fraction, key ranges
-    (torch.bfloat16, 128, True, 300, 300, "full", 0.0, False),
-    (torch.float16, 64, False, 200, 333, "head", 0.1, False),
-    (torch.bfloat16, 64, True, 257, 513, "key", 0.0, True),
-    (torch.float16, 128, True, 130, 70, "full", 0.05, False),
-    (torch.bfloat16, 128, False, 3, 1, "rows", 0.0, False),
+    # dtype, d, causal, nq, nk, bias kind, -inf fraction, key ranges, rows emptied by the bias
+    (torch.bfloat16, 128, True, 300, 300, "full", 0.0, False, False),
+    (torch.float16, 64, False, 200, 333, "head", 0.1, False, False),
+    (torch.bfloat16, 64, True, 257, 513, "key", 0.0, True, False),
+    (torch.float16, 128, True, 130, 70, "full", 0.05, False, False),
+    (torch.bfloat16, 128, False, 3, 1, "rows", 0.0, False, False),
+    # rows whose every entry is -inf: in fully visible tiles (non-causal, no ranges) ...
+    (torch.bfloat16, 128, False, 300, 300, "full", 0.0, False, True),
+    (torch.float16, 64, False, 200, 333, "head", 0.02, False, True),
+    # ... under key ranges, and a whole batch masked (causal, partial tiles)
+    (torch.bfloat16, 128, False, 257, 300, "head", 0.0, True, True),
+    (torch.float16, 128, True, 130, 200, "key", 0.0, False, True),
 ]
 
 
-@pytest.mark.parametrize("dtype,d,causal,nq,nk,kind,ninf,ranged", BWD_CASES)
-def test_backward_and_dbias_match_oracle(dtype, d, causal, nq, nk, kind, ninf, ranged):
+@pytest.mark.parametrize("dtype,d,causal,nq,nk,kind,ninf,ranged,empty", BWD_CASES)
+def test_backward_and_dbias_match_oracle(dtype, d, causal, nq, nk, kind, ninf, ranged, empty):
     B, H = 2, 2
     seed = 970 + nq + 3 * nk + d
     q, k, v, do = (normal((B, H, n, d), dtype, seed + i) for i, n in enumerate((nq, nk, nk, nq)))
     bias = bias_tensor(bias_shape(kind, B, H, nq, nk), seed + 5, 2.0, ninf)
+    if empty:
+        plant_empty_rows(bias, kind)
     kw = {}
     ks = ke = None
     if ranged:
@@ -170,7 +193,18 @@ def test_backward_and_dbias_match_oracle(dtype, d, causal, nq, nk, kind, ninf, r
         np64(q), np64(k), np64(v), np64(do), scale, causal=causal, bias=bias.double().numpy(),
         key_start=None if ks is None else ks.numpy(), key_end=None if ke is None else ke.numpy(),
         return_dbias=True)
-    what = f"bias {kind} {dtype} d{d} c{causal} {nq}x{nk}"
+    what = f"bias {kind} {dtype} d{d} c{causal} {nq}x{nk}" + (" empty rows" if empty else "")
+    if empty:
+        # the planted rows are empty in the forward and give exact zeros in the backward
+        lse_np = np64(lse)
+        ref_empty = ~np.isfinite(oracle.attention_forward(
+            np64(q), np64(k), np64(v), scale, causal=causal, bias=bias.double().numpy(),
+            key_start=None if ks is None else ks.numpy(),
+            key_end=None if ke is None else ke.numpy())[1])
+        assert ref_empty.any(), what
+        assert np.all(np.isneginf(lse_np[ref_empty])), what
+        assert np.all(np64(dq)[ref_empty] == 0), what
+        assert np.all(np64(dbias)[ref_empty] == 0), what
     check((dq, dk, dv), want[:3], ("dQ", "dK", "dV"), what)
     ksn = None if ks is None else ks.numpy()
     ken = None if ke is None else ke.numpy()
