@@ -7,6 +7,9 @@ gradients max abs error <= 2e-2 (bf16 inputs, float32 gradients).
 
 from __future__ import annotations
 
+import concurrent.futures as cf
+import os
+
 import numpy as np
 import torch
 
@@ -52,3 +55,22 @@ def sample_rows(n: int, count: int, seed: int) -> np.ndarray:
     rows = set(int(r) for r in fixed if 0 <= r < n)
     rows.update(int(x) for x in rng.integers(0, n, size=count))
     return np.array(sorted(rows), dtype=np.int64)
+
+
+def oracle_workers() -> int:
+    """Worker threads for oracle jobs: the host cores this process may run on, at most 16."""
+    return max(1, min(16, len(os.sched_getaffinity(0))))
+
+
+def run_oracle_jobs(fn, jobs):
+    """``[fn(j) for j in jobs]`` on a thread pool, BLAS limited to one thread per call.
+
+    NumPy releases the interpreter lock inside BLAS and inside elementwise loops over
+    large arrays, so independent oracle calls (one head, or one chunk of rows of a head)
+    run side by side on the host cores; the oracle itself is unchanged.
+    """
+    from threadpoolctl import threadpool_limits
+
+    with threadpool_limits(1):
+        with cf.ThreadPoolExecutor(oracle_workers()) as ex:
+            return list(ex.map(fn, jobs))
