@@ -21,7 +21,8 @@ import torch
 
 __all__ = [
     "FaError", "fa_fwd", "fa_fwd_split", "fa_fwd_split_count", "fa_fwd_split_workspace_bytes",
-    "fa_bwd", "fa_bwd_workspace_bytes", "fa_mask_summary",
+    "fa_bwd", "fa_bwd_noalloc", "fa_bwd_workspace_bytes", "fa_mask_summary",
+    "FA_NOALLOC_SCRATCH_BYTES",
     "fa_fp8_rows", "fa_fp8_quantize", "fa_fwd_fp8", "fa_attention_fp8",
     "FA_FP8_Q", "FA_FP8_K", "FA_FP8_V",
     "FA_BWD_PREP", "FA_BWD_DKDV", "FA_BWD_DQ", "FA_BWD_ALL",
@@ -37,6 +38,7 @@ FA_BIAS_NONE, FA_BIAS_DIST_LINEAR, FA_BIAS_TENSOR = 0, 1, 2
 FA_MAX_SLOPES = 256
 FA_BWD_PREP, FA_BWD_DKDV, FA_BWD_DQ, FA_BWD_ALL = 1, 2, 4, 7
 FA_FP8_Q, FA_FP8_K, FA_FP8_V = 0, 1, 2
+FA_NOALLOC_SCRATCH_BYTES = 16 << 20  # include/fa.h
 _DT = {torch.float32: FA_F32, torch.float16: FA_F16, torch.bfloat16: FA_BF16}
 
 
@@ -103,6 +105,9 @@ def load_library():
                                   ctypes.c_size_t, i32, i32, i32, i32, i32, f32, i32, desc_p,
                                   i32, vp]
     lib.fa_bwd_phases.restype = i32
+    lib.fa_bwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
+                                   i32, f32, i32, desc_p, i32, vp]
+    lib.fa_bwd_noalloc.restype = i32
     lib.fa_mask_summary.argtypes = [vp, vp, i32, i32, i32, vp, vp]
     lib.fa_mask_summary.restype = i32
     lib.fa_fp8_rows.argtypes = [i32]
@@ -381,6 +386,49 @@ def fa_bwd(dout: torch.Tensor, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor
     del keep
     if st != 0:
         raise FaError(st, "fa_bwd_phases")
+    return dq, dk, dv
+
+
+def fa_bwd_noalloc(dout: torch.Tensor, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                   o: torch.Tensor, lse: torch.Tensor, grads, causal: bool = False,
+                   scale: Optional[float] = None, bias_slopes=None,
+                   key_start: Optional[torch.Tensor] = None,
+                   key_end: Optional[torch.Tensor] = None,
+                   stream: Optional[torch.cuda.Stream] = None, block_mask=None,
+                   dslopes: Optional[torch.Tensor] = None, bias: Optional[torch.Tensor] = None,
+                   dbias: Optional[torch.Tensor] = None):
+    """The allocation-free backward (``fa_bwd_noalloc``): what :func:`fa_bwd` computes, into
+    the caller's preallocated ``grads`` = (dq, dk, dv) (float32 or the input dtype), with
+    the library's fixed device scratch in place of a workspace. Neither this wrapper nor
+    the library allocates device memory. Calls that overlap on one GPU race."""
+    lib = load_library()
+    _check_dev("q", q)
+    B, H, N_q, d = q.shape
+    N_k = k.shape[2]
+    _check_dev("k", k, q.dtype, (B, H, N_k, d))
+    _check_dev("v", v, q.dtype, (B, H, N_k, d))
+    _check_dev("o", o, q.dtype, (B, H, N_q, d))
+    _check_dev("dout", dout, q.dtype, (B, H, N_q, d))
+    _check_dev("lse", lse, torch.float32, (B, H, N_q))
+    dq, dk, dv = grads
+    grad_dtype = dq.dtype
+    if grad_dtype not in (torch.float32, q.dtype):
+        raise ValueError("grad dtype must be float32 or the input dtype")
+    _check_dev("dq", dq, grad_dtype, (B, H, N_q, d))
+    _check_dev("dk", dk, grad_dtype, (B, H, N_k, d))
+    _check_dev("dv", dv, grad_dtype, (B, H, N_k, d))
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    desc, keep = _desc(bias_slopes, key_start, key_end, H, N_q, block_mask, B, N_k, dslopes,
+                       bias=bias, dbias=dbias)
+    st = lib.fa_bwd_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                            lse.data_ptr(), dout.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                            dv.data_ptr(), _DT[grad_dtype], B, H, N_q, N_k, d, float(scale),
+                            1 if causal else 0, ctypes.byref(desc) if desc is not None else None,
+                            _DT[q.dtype], _stream_ptr(stream))
+    del keep
+    if st != 0:
+        raise FaError(st, "fa_bwd_noalloc")
     return dq, dk, dv
 
 

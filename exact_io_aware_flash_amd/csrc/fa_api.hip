@@ -10,11 +10,19 @@
 #include <climits>
 #include <cmath>
 #include <cstring>
+#include <mutex>
 
 #include "fa.h"
 #include "fa_internal.h"
 
 using namespace fa;
+
+// Scratch of the allocation-free backward (fa_bwd_noalloc): a fixed device array of the
+// library, one per GPU, holding what fa_bwd keeps in the caller's workspace. Host code
+// never uses the name below as an address (on the host it is only a stand-in for the
+// symbol); it uses the device address from hipGetSymbolAddress, taken once per device
+// on the first call there, with that device current.
+static __device__ __align__(256) unsigned char scratch[FA_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -117,6 +125,23 @@ int split_plan(int B, int H, int N_q, int N_k, int d, int n_split, int& split_ke
 
 size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];  // device address of `scratch` per device id, or NULL
+
+// The current device's scratch address (looked up on first use); NULL on a HIP error.
+void* scratch_for_current_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
+
 size_t split_part_bytes(int B, int H, int N_q, int d, int n) {
   return round256((size_t)n * B * H * N_q * d * sizeof(float));
 }
@@ -138,6 +163,8 @@ const char* fa_status_string(fa_status s) {
     case FA_ERR_UNSUPPORTED: return "combination not implemented";
     case FA_ERR_HIP: return "HIP launch error";
     case FA_ERR_ARG: return "invalid scalar argument (scale must be finite and > 0)";
+    case FA_ERR_SCRATCH:
+      return "problem too large for the fixed scratch of fa_bwd_noalloc (FA_NOALLOC_SCRATCH_BYTES)";
   }
   return "unknown status";
 }
@@ -291,11 +318,16 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, con
                        workspace_bytes, B, H, N_q, N_k, d, scale, causal, mb, dtype, stream);
 }
 
-fa_status fa_bwd_phases(int phases, const void* q, const void* k, const void* v, const void* o,
-                        const float* lse, const void* dout, void* dq, void* dk, void* dv,
-                        fa_dtype grad_dtype, void* workspace, size_t workspace_bytes, int B,
-                        int H, int N_q, int N_k, int d, float scale, int causal,
-                        const fa_mask_bias_desc* mb, fa_dtype dtype, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Validation of a backward call, everything except the workspace (shared by fa_bwd_phases
+// and fa_bwd_noalloc); fills the argument block's descriptor part.
+fa_status bwd_check(int phases, const void* q, const void* k, const void* v, const void* o,
+                    const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                    fa_dtype grad_dtype, int B, int H, int N_q, int N_k, int d, float scale,
+                    const fa_mask_bias_desc* mb, fa_dtype dtype, int& bias, BwdArgs& a) {
   if (phases < 1 || (phases & ~FA_BWD_ALL) != 0) return FA_ERR_ARG;
   fa_status st = check_common(B, H, N_q, N_k, d, scale, dtype);
   if (st != FA_OK) return st;
@@ -305,30 +337,37 @@ fa_status fa_bwd_phases(int phases, const void* q, const void* k, const void* v,
   for (const void* p : dev)
     if (!aligned16(p)) return FA_ERR_ALIGN;
   if (reinterpret_cast<uintptr_t>(lse) & 3u) return FA_ERR_ALIGN;
-  if (workspace == nullptr || workspace_bytes < fa_bwd_workspace_bytes(B, H, N_q, N_k, d))
-    return FA_ERR_WORKSPACE;
-  if (!aligned16(workspace)) return FA_ERR_ALIGN;
-  BwdArgs a;
   std::memset(&a, 0, sizeof(a));
-  int bias = kBiasNone;
+  bias = kBiasNone;
   st = read_desc(mb, H, N_q, N_k, dtype, bias, a);
   if (st != FA_OK) return st;
+  if (mb != nullptr && mb->dslopes != nullptr) {
+    if (mb->bias_kind != FA_BIAS_DIST_LINEAR) return FA_ERR_MASK;
+    if (reinterpret_cast<uintptr_t>(mb->dslopes) & 3u) return FA_ERR_ALIGN;
+  }
+  if (mb != nullptr && mb->dbias != nullptr) {
+    if (mb->bias_kind != FA_BIAS_TENSOR) return FA_ERR_MASK;
+    if (reinterpret_cast<uintptr_t>(mb->dbias) & 3u) return FA_ERR_ALIGN;
+  }
+  return FA_OK;
+}
+
+// Launches of a validated backward call with `workspace` (fa_bwd_workspace_bytes bytes).
+fa_status bwd_launch(int phases, const void* q, const void* k, const void* v, const void* o,
+                     const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                     fa_dtype grad_dtype, void* workspace, int B, int H, int N_q, int N_k, int d,
+                     float scale, int causal, const fa_mask_bias_desc* mb, fa_dtype dtype,
+                     int bias, BwdArgs& a, void* stream) {
   a.q = q; a.k = k; a.v = v; a.o = o; a.dout = dout; a.lse = lse;
   a.delta = static_cast<float*>(workspace);
   a.qsum = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + bwd_qsum_offset(B, H, N_q));
   a.lse2 = reinterpret_cast<float*>(static_cast<char*>(workspace) + bwd_lse2_offset(B, H, N_q));
   if (mb != nullptr && mb->dslopes != nullptr) {
-    if (mb->bias_kind != FA_BIAS_DIST_LINEAR) return FA_ERR_MASK;
-    if (reinterpret_cast<uintptr_t>(mb->dslopes) & 3u) return FA_ERR_ALIGN;
     a.dslopes = mb->dslopes;
     a.dslope_part =
         reinterpret_cast<float*>(static_cast<char*>(workspace) + bwd_dslope_offset(B, H, N_q));
   }
-  if (mb != nullptr && mb->dbias != nullptr) {
-    if (mb->bias_kind != FA_BIAS_TENSOR) return FA_ERR_MASK;
-    if (reinterpret_cast<uintptr_t>(mb->dbias) & 3u) return FA_ERR_ALIGN;
-    a.dbias = mb->dbias;
-  }
+  if (mb != nullptr && mb->dbias != nullptr) a.dbias = mb->dbias;
   a.dq = dq; a.dk = dk; a.dv = dv;
   a.B = B; a.H = H; a.Nq = N_q; a.Nk = N_k;
   a.causal = causal ? 1 : 0;
@@ -338,6 +377,47 @@ fa_status fa_bwd_phases(int phases, const void* q, const void* k, const void* v,
   hipError_t e = launch_bwd(dtype, d, bias, phases, a, static_cast<hipStream_t>(stream));
   if (e == hipErrorNotSupported) return FA_ERR_UNSUPPORTED;
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+fa_status fa_bwd_phases(int phases, const void* q, const void* k, const void* v, const void* o,
+                        const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                        fa_dtype grad_dtype, void* workspace, size_t workspace_bytes, int B,
+                        int H, int N_q, int N_k, int d, float scale, int causal,
+                        const fa_mask_bias_desc* mb, fa_dtype dtype, void* stream) {
+  BwdArgs a;
+  int bias = kBiasNone;
+  fa_status st = bwd_check(phases, q, k, v, o, lse, dout, dq, dk, dv, grad_dtype, B, H, N_q, N_k,
+                           d, scale, mb, dtype, bias, a);
+  if (st != FA_OK) return st;
+  if (workspace == nullptr || workspace_bytes < fa_bwd_workspace_bytes(B, H, N_q, N_k, d))
+    return FA_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return FA_ERR_ALIGN;
+  return bwd_launch(phases, q, k, v, o, lse, dout, dq, dk, dv, grad_dtype, workspace, B, H, N_q,
+                    N_k, d, scale, causal, mb, dtype, bias, a, stream);
+}
+
+fa_status fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
+                         const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                         fa_dtype grad_dtype, int B, int H, int N_q, int N_k, int d, float scale,
+                         int causal, const fa_mask_bias_desc* mb, fa_dtype dtype, void* stream) {
+  BwdArgs a;
+  int bias = kBiasNone;
+  fa_status st = bwd_check(FA_BWD_ALL, q, k, v, o, lse, dout, dq, dk, dv, grad_dtype, B, H, N_q,
+                           N_k, d, scale, mb, dtype, bias, a);
+  if (st != FA_OK) return st;
+  if (fa_bwd_workspace_bytes(B, H, N_q, N_k, d) > (size_t)FA_NOALLOC_SCRATCH_BYTES)
+    return FA_ERR_SCRATCH;
+  void* ws = scratch_for_current_device();
+  if (ws == nullptr) return FA_ERR_HIP;
+  // Everything the launches read from the scratch is written earlier in the same call
+  // (prep: D and the exponent offsets; key-range summary; every dK/dV workgroup writes
+  // its slope-gradient partial), so the previous call's contents need no clearing.
+  return bwd_launch(FA_BWD_ALL, q, k, v, o, lse, dout, dq, dk, dv, grad_dtype, ws, B, H, N_q,
+                    N_k, d, scale, causal, mb, dtype, bias, a, stream);
 }
 
 fa_status fa_mask_summary(const int32_t* key_start, const int32_t* key_end, int N_q, int N_k,

@@ -32,7 +32,8 @@
  *    (b,h,n,c) at ((b*H + h)*N + n)*d + c). LSE is [B, H, N_q] float32.
  *  - Pointers named "device" must be device memory of the current HIP device,
  *    16-byte aligned. The caller owns every buffer; the library allocates and
- *    frees nothing and keeps no state between calls.
+ *    frees nothing and keeps no state between calls (one exception: the fixed
+ *    scratch array that fa_bwd_noalloc uses in place of a workspace).
  *  - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and
  *    the calls return without synchronising. Inputs must stay valid until the
  *    stream has passed the call.
@@ -65,7 +66,8 @@ typedef enum fa_status {
   FA_ERR_WORKSPACE = 7,   /* workspace NULL or smaller than fa_bwd_workspace_bytes() */
   FA_ERR_UNSUPPORTED = 8, /* a valid combination this build does not implement */
   FA_ERR_HIP = 9,         /* the HIP runtime reported an error at launch */
-  FA_ERR_ARG = 10         /* scale not finite or not positive; a slope not finite; bad phase set */
+  FA_ERR_ARG = 10,        /* scale not finite or not positive; a slope not finite; bad phase set */
+  FA_ERR_SCRATCH = 11     /* fa_bwd_noalloc: the sizes need more than FA_NOALLOC_SCRATCH_BYTES */
 } fa_status;
 
 typedef enum fa_dtype { FA_F32 = 0, FA_F16 = 1, FA_BF16 = 2 } fa_dtype;
@@ -245,6 +247,29 @@ FA_API fa_status fa_bwd_phases(int phases, const void* q, const void* k, const v
                                size_t workspace_bytes, int B, int H, int N_q, int N_k, int d,
                                float scale, int causal, const fa_mask_bias_desc* mb,
                                fa_dtype dtype, void* stream);
+
+/* Allocation-free backward, for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving or training loops, harnesses that forbid hipMalloc.
+ * Computes exactly what fa_bwd computes (the same kernels, bit for bit), with the same
+ * arguments except the workspace: the library keeps a fixed device array of
+ * FA_NOALLOC_SCRATCH_BYTES bytes per GPU (allocated when the library is loaded, held until
+ * the process ends) and uses it in place of the caller's workspace. The call itself
+ * allocates and frees nothing; the caller still provides every input and output.
+ *  Limit: fa_bwd_workspace_bytes(B, H, N_q, N_k, d) <= FA_NOALLOC_SCRATCH_BYTES, i.e. about
+ *         2 * 4 bytes per (b, h, query row): B * H * N_q up to about 2 million rows;
+ *         larger problems return FA_ERR_SCRATCH (checked before anything is enqueued).
+ *  Concurrency: every call on one GPU uses that GPU's one array; calls whose work can
+ *         overlap on the device (different streams, or other host threads) race and give
+ *         undefined gradients. Calls in order on one stream are safe: each call writes
+ *         everything it reads from the array before reading it.
+ *  Errors: as fa_bwd (FA_ERR_WORKSPACE never), plus FA_ERR_SCRATCH, and FA_ERR_HIP if the
+ *         array's device address cannot be obtained. */
+#define FA_NOALLOC_SCRATCH_BYTES (16u << 20)
+FA_API fa_status fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
+                                const float* lse, const void* dout, void* dq, void* dk,
+                                void* dv, fa_dtype grad_dtype, int B, int H, int N_q, int N_k,
+                                int d, float scale, int causal, const fa_mask_bias_desc* mb,
+                                fa_dtype dtype, void* stream);
 
 /* Key-range summary of consecutive blocks of `block_rows` query rows.
  *  key_start, key_end: device int32 [N_q] (same meaning as in fa_mask_bias_desc).

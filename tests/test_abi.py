@@ -37,7 +37,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_status_strings_and_version():
     lib = fa.load_library()
-    for code in range(0, 11):
+    for code in range(0, 12):
         s = fa.fa_status_string(code)
         assert isinstance(s, str) and s
     assert fa.fa_status_string(0) == "ok"
@@ -244,3 +244,35 @@ def fwd_split(**kw):
 ])
 def test_fwd_split_rejects_invalid_arguments(kw, status):
     assert fwd_split(**kw) == status
+
+
+# ---- allocation-free backward: validation before any HIP call --------------------------
+
+def bwd_noalloc(**kw):
+    lib = fa.load_library()
+    a = dict(q=P, k=P, v=P, o=P, lse=P, do=P, dq=P, dk=P, dv=P, gdt=fa.FA_F32,
+             B=1, H=1, Nq=16, Nk=16, d=128, scale=0.1, causal=1, mb=None, dtype=fa.FA_BF16,
+             stream=None)
+    a.update(kw)
+    return lib.fa_bwd_noalloc(a["q"], a["k"], a["v"], a["o"], a["lse"], a["do"], a["dq"],
+                              a["dk"], a["dv"], a["gdt"], a["B"], a["H"], a["Nq"], a["Nk"],
+                              a["d"], a["scale"], a["causal"], a["mb"], a["dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(do=None), 1), (dict(lse=None), 1), (dict(dq=None), 1),
+    (dict(gdt=fa.FA_F16), 3), (dict(d=32), 4), (dict(Nk=0), 2),
+    (dict(dv=MIS), 6), (dict(scale=0.0), 10),
+    # the workspace these sizes need exceeds the fixed scratch: rejected, nothing launched
+    (dict(B=64, H=64, Nq=8192, Nk=8192), 11),
+    (dict(B=1, H=1, Nq=2_200_000, Nk=64, d=64), 11),
+])
+def test_bwd_noalloc_rejects_invalid_arguments(kw, status):
+    assert bwd_noalloc(**kw) == status
+
+
+def test_bwd_noalloc_scratch_limit_is_the_workspace_size():
+    # a problem fits exactly when fa_bwd's workspace for it fits the scratch
+    assert fa.fa_bwd_workspace_bytes(2, 16, 8192, 8192, 128) <= fa.FA_NOALLOC_SCRATCH_BYTES
+    assert fa.fa_bwd_workspace_bytes(64, 64, 8192, 8192, 128) > fa.FA_NOALLOC_SCRATCH_BYTES
+    assert "scratch" in fa.fa_status_string(11)
