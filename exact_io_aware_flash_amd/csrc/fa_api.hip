@@ -94,6 +94,8 @@ fa_status read_desc(const fa_mask_bias_desc* mb, int H, int N_q, int N_k, fa_dty
     if (reinterpret_cast<uintptr_t>(mb->bias) & 3u) return FA_ERR_ALIGN;
     if (mb->bias_stride_b < 0 || mb->bias_stride_h < 0 || mb->bias_stride_i < 0) return FA_ERR_MASK;
     if (mb->block_mask != nullptr) return FA_ERR_UNSUPPORTED;
+    // a bias tile (up to 64 rows) is addressed by 32-bit byte offsets from its first row
+    if (mb->bias_stride_i * 64 + N_k >= (1LL << 30)) return FA_ERR_UNSUPPORTED;
     a.tbias = mb->bias;
     a.tb_sb = mb->bias_stride_b;
     a.tb_sh = mb->bias_stride_h;

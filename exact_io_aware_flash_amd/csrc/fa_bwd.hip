@@ -365,9 +365,9 @@ void bwd_dkdv_kernel(const BwdArgs a) {
   auto issue = [&](int p) {
     char* sb = stage_of(p);
     const int q0t = tile_at(p) * BR;
-    tile_ld.load(Q, q0t, Nq, sb + L::QT, wid_s);
-    tile_ld.load(dO, q0t, Nq, sb + L::DT, wid_s);
-    dma4(arr_base + min(q0t + lane, Nq - 1), sb + arr_off);
+    tile_ld.template load<false>(Q, q0t, Nq, sb + L::QT, wid_s);
+    tile_ld.template load<false>(dO, q0t, Nq, sb + L::DT, wid_s);
+    dma4<false>(arr_base, (uint32_t)min(q0t + lane, Nq - 1), sb + arr_off);
     if constexpr (TENSOR)
       BT::load(TB, a.tb_si, q0t, Nq, kw0, Nk, sb + L::STAGE + wid_s * BT::kWaveBytes, lane);
   };

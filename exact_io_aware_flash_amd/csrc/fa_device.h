@@ -293,10 +293,55 @@ struct ListWindow {
   }
 };
 
-// One wave-wide direct load of 4 bytes per lane: lane i fills bytes [4i, 4i+4) of the
-// 256-byte window at `lds` (wave-uniform).
-__device__ inline void dma4(const void* g, char* lds) {
-  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds, 4, 0, 0);
+// ---------------------------------------------------------------------------------
+// Direct global -> LDS loads, in two forms.
+//  * buffer form (buffer_load_dword{,x4} ... lds): a resource covers the bytes from a
+//    wave-uniform base; per-lane offsets are 32-bit (every caller keeps them inside one
+//    matrix of fewer than 2^32 bytes), the range check is off (num_records = 0xffffffff)
+//    and word 3 selects 32-bit raw data. The compiler tracks it with the vector-memory
+//    counter only.
+//  * global form (global_load_lds_dword{,x4}): a FLAT-encoded instruction that writes
+//    LDS. While one is in flight the compiler counts LDS reads as possibly out of order
+//    and waits for every one of them (lgkmcnt(0)) before using any.
+// The forward and dQ passes use the buffer form (their MFMAs then wait only for their own
+// operands: 512 -> 520 us and 734 -> 742 us measured the other way on the bf16 causal
+// B2 H16 N8192 d128 shape); the dK/dV pass measured faster with the global form (1187
+// against 1229 us), so each kernel picks its form (BUF).
+// ---------------------------------------------------------------------------------
+template <bool BUF>
+struct DmaBase;
+template <>
+struct DmaBase<true> {
+  __amdgpu_buffer_rsrc_t r;
+  __device__ explicit DmaBase(const void* base)
+      : r(__builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)0xffffffffu,
+                                            0x00020000)) {}
+  // one wave-wide direct load of SIZE (4 or 16) bytes per lane from byte offset `voff`:
+  // lane i fills bytes [SIZE*i, SIZE*i + SIZE) of the window at `lds` (wave-uniform)
+  template <int SIZE>
+  __device__ void load(uint32_t voff, char* lds) const {
+    static_assert(SIZE == 4 || SIZE == 16, "4 or 16 bytes per lane");
+    auto* l = (__attribute__((address_space(3))) void*)lds;
+    if constexpr (SIZE == 16) __builtin_amdgcn_raw_ptr_buffer_load_lds(r, l, 16, voff, 0, 0, 0);
+    else __builtin_amdgcn_raw_ptr_buffer_load_lds(r, l, 4, voff, 0, 0, 0);
+  }
+};
+template <>
+struct DmaBase<false> {
+  const char* p;
+  __device__ explicit DmaBase(const void* base) : p(static_cast<const char*>(base)) {}
+  template <int SIZE>
+  __device__ void load(uint32_t voff, char* lds) const {
+    static_assert(SIZE == 4 || SIZE == 16, "4 or 16 bytes per lane");
+    auto* l = (__attribute__((address_space(3))) void*)lds;
+    if constexpr (SIZE == 16) __builtin_amdgcn_global_load_lds(p + voff, l, 16, 0, 0);
+    else __builtin_amdgcn_global_load_lds(p + voff, l, 4, 0, 0);
+  }
+};
+// 4 bytes per lane from element `idx` of the float array at the wave-uniform `base`
+template <bool BUF>
+__device__ inline void dma4(const float* base, uint32_t idx, char* lds) {
+  DmaBase<BUF>(base).template load<4>(idx * 4u, lds);
 }
 
 // One wave-wide direct load moves 1 KB: lane i fills bytes [16i, 16i+16) of the window
@@ -324,15 +369,18 @@ struct DmaTile {
     }
   }
   // this wave's share of rows [row0, row0 + ROWS) of a row-major (nrows x D) matrix;
-  // rows past the end repeat the last row (their scores are masked)
-  template <typename T>
+  // rows past the end repeat the last row (their scores are masked). The byte offset
+  // inside the matrix is formed in 32 bits (a matrix of one (b, h) holds fewer than 2^32
+  // bytes: N * d <= INT_MAX elements of 2 bytes), so the load takes the wave-uniform base
+  // plus a 32-bit per-lane offset and no 64-bit address per lane stays live in a loop.
+  template <bool BUF = true, typename T>
   __device__ inline void load(const T* base, int row0, int nrows, char* lds, int wid) const {
+    const DmaBase<BUF> rs(base);
 #pragma unroll
     for (int j = 0; j < kOpsPerWave; ++j) {
-      const int r = min(row0 + row[j], nrows - 1);
-      const char* g = reinterpret_cast<const char*>(base) + (size_t)r * kRowBytes + col[j];
-      __builtin_amdgcn_global_load_lds(
-          g, (__attribute__((address_space(3))) void*)(lds + (wid * kOpsPerWave + j) * 1024), 16, 0, 0);
+      const uint32_t r = (uint32_t)min(row0 + row[j], nrows - 1);
+      const uint32_t off = r * (uint32_t)kRowBytes + (uint32_t)col[j];
+      rs.template load<16>(off, lds + (wid * kOpsPerWave + j) * 1024);
     }
   }
 };
@@ -356,11 +404,14 @@ struct BiasRowTile {
   // the (b, h) matrix at `base` with row stride si, into this wave's region `lds`
   __device__ static inline void load(const float* base, long long si, int wq0, int nq, int kt0,
                                      int nk, char* lds, int lane) {
-    const int j = min(kt0 + lane % BC, nk - 1);
+    // the resource starts at the tile's first row, so offsets stay within 32 rows
+    const int r0 = min(wq0, nq - 1);
+    const DmaBase<true> rs(base + (long long)r0 * si);
+    const uint32_t j = (uint32_t)min(kt0 + lane % BC, nk - 1);
 #pragma unroll
     for (int w = 0; w < kOps; ++w) {
-      const int i = min(wq0 + w * kRW + lane / BC, nq - 1);
-      dma4(base + (long long)i * si + j, lds + w * kWin);
+      const uint32_t i = (uint32_t)(min(wq0 + w * kRW + lane / BC, nq - 1) - r0);
+      rs.load<4>((i * (uint32_t)si + j) * 4u, lds + w * kWin);
     }
   }
   // keys c0 .. c0 + 3 (c0 a multiple of 4) of wave row r
@@ -380,13 +431,17 @@ struct BiasColTile {
   static constexpr int kWaveBytes = kOps * 256;
   __device__ static inline void load(const float* base, long long si, int q0t, int nq, int kw0,
                                      int nk, char* lds, int lane) {
-    const int j = min(kw0 + (lane & 31), nk - 1);
+    // the resource starts at the tile's first row, so offsets stay within 64 rows
+    const int r0 = min(q0t, nq - 1);
+    const DmaBase<false> rs(base + (long long)r0 * si);  // (dK/dV pass: global form)
+    const uint32_t j = (uint32_t)min(kw0 + (lane & 31), nk - 1);
     const int hh = lane >> 5;
 #pragma unroll
     for (int w = 0; w < kOps; ++w) {
       const int qb = w >> 4, g = w & 15;
-      const int i = min(q0t + 32 * qb + 8 * (g >> 2) + 4 * hh + (g & 3), nq - 1);
-      dma4(base + (long long)i * si + j, lds + w * 256);
+      const uint32_t i =
+          (uint32_t)(min(q0t + 32 * qb + 8 * (g >> 2) + 4 * hh + (g & 3), nq - 1) - r0);
+      rs.load<4>((i * (uint32_t)si + j) * 4u, lds + w * 256);
     }
   }
   __device__ static inline float read(const char* lds, int qb, int g, int lane) {

@@ -386,11 +386,10 @@ void fwd8_kernel(const Fp8FwdArgs a) {
     char* sb = sptr(J);
 #pragma unroll
     for (int j = 0; j < kOpsPerWave; ++j) {
-      const int u = wid * kOpsPerWave + j;  // 1 KB window of the stage
-      const uint8_t* g = (u * 1024 < TB ? K8 + (size_t)t * TB + u * 1024
-                                        : V8 + (size_t)t * TB + (u * 1024 - TB)) + 16 * lane;
-      __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)(sb + u * 1024),
-                                       16, 0, 0);
+      const int u = wid * kOpsPerWave + j;  // 1 KB window of the stage (wave-uniform)
+      const uint8_t* g = u * 1024 < TB ? K8 + (size_t)t * TB + u * 1024
+                                       : V8 + (size_t)t * TB + (u * 1024 - TB);
+      DmaBase<true>(g).load<16>(16u * (uint32_t)lane, sb + u * 1024);
     }
   };
   auto land = [&](int later) {

@@ -126,7 +126,8 @@ typedef enum fa_bias_kind {
  *              abstract on attention with bias); -inf entries act as a mask; +inf or NaN
  *              entries give undefined results. Read during the enqueued work. With a
  *              block bitmap: FA_ERR_UNSUPPORTED.
- *  bias_stride_b, bias_stride_h, bias_stride_i : element strides, >= 0 (else FA_ERR_MASK).
+ *  bias_stride_b, bias_stride_h, bias_stride_i : element strides, >= 0 (else FA_ERR_MASK);
+ *              64 * bias_stride_i + N_k must stay below 2^30 (else FA_ERR_UNSUPPORTED).
  *  dbias :     DEVICE pointer to a dense float32 [B, H, N_q, N_k] array (4-byte aligned),
  *              or NULL. fa_bwd (and fa_bwd_phases with FA_BWD_DKDV) writes there the
  *              gradient of the loss with respect to every biased score, dS_{b,h,i,j}

@@ -137,6 +137,7 @@ def test_bias_tensor_descriptor_validation():
     assert fwd(mb=ctypes.byref(desc(bias=P + 2))) == 6   # float32: 4-byte alignment
     for bad in (dict(sb=-1), dict(sh=-16), dict(si=-1)):
         assert fwd(mb=ctypes.byref(desc(**bad))) == 5, bad
+    assert fwd(mb=ctypes.byref(desc(si=1 << 24))) == 8  # tile offsets would pass 32 bits
     d = desc()
     d.block_mask, d.block_q, d.block_k = P, 64, 64
     assert fwd(mb=ctypes.byref(d)) == 8  # no bitmap together with a bias tensor
