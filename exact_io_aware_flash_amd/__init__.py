@@ -22,6 +22,7 @@ import torch
 __all__ = [
     "FaError", "fa_fwd", "fa_fwd_split", "fa_fwd_split_count", "fa_fwd_split_workspace_bytes",
     "fa_bwd", "fa_bwd_noalloc", "fa_bwd_workspace_bytes", "fa_mask_summary",
+    "fa_fwd_tile_counts",
     "FA_NOALLOC_SCRATCH_BYTES",
     "fa_fp8_rows", "fa_fp8_quantize", "fa_fwd_fp8", "fa_attention_fp8",
     "FA_FP8_Q", "FA_FP8_K", "FA_FP8_V",
@@ -105,6 +106,9 @@ def load_library():
                                   ctypes.c_size_t, i32, i32, i32, i32, i32, f32, i32, desc_p,
                                   i32, vp]
     lib.fa_bwd_phases.restype = i32
+    lib.fa_fwd_tile_counts.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32,
+                                       desc_p, i32, vp, vp, ctypes.POINTER(ctypes.c_int)]
+    lib.fa_fwd_tile_counts.restype = i32
     lib.fa_bwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
                                    i32, f32, i32, desc_p, i32, vp]
     lib.fa_bwd_noalloc.restype = i32
@@ -283,6 +287,41 @@ def fa_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = Fal
     if st != 0:
         raise FaError(st, "fa_fwd")
     return out, lse
+
+
+def fa_fwd_tile_counts(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
+                       scale: Optional[float] = None, bias_slopes=None,
+                       key_start: Optional[torch.Tensor] = None,
+                       key_end: Optional[torch.Tensor] = None, block_mask=None,
+                       bias: Optional[torch.Tensor] = None,
+                       stream: Optional[torch.cuda.Stream] = None):
+    """The forward with tile counters (``fa_fwd_tile_counts``): returns (O, LSE, counts,
+    config) with counts = [key tiles loaded, summed over workgroups; (wave, tile) score
+    blocks computed] and config = (query rows per workgroup, per wave, keys per tile)."""
+    lib = load_library()
+    _check_dev("q", q)
+    B, H, N_q, d = q.shape
+    N_k = k.shape[2]
+    if q.dtype not in _DT:
+        raise ValueError(f"unsupported dtype {q.dtype}")
+    _check_dev("k", k, q.dtype, (B, H, N_k, d))
+    _check_dev("v", v, q.dtype, (B, H, N_k, d))
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    out = torch.empty_like(q)
+    lse = torch.empty((B, H, N_q), dtype=torch.float32, device=q.device)
+    counts = torch.zeros(2, dtype=torch.int64, device=q.device)
+    config = (ctypes.c_int * 3)()
+    desc, keep = _desc(bias_slopes, key_start, key_end, H, N_q, block_mask, B, N_k, bias=bias)
+    st = lib.fa_fwd_tile_counts(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                lse.data_ptr(), B, H, N_q, N_k, d, float(scale),
+                                1 if causal else 0,
+                                ctypes.byref(desc) if desc is not None else None,
+                                _DT[q.dtype], _stream_ptr(stream), counts.data_ptr(), config)
+    del keep
+    if st != 0:
+        raise FaError(st, "fa_fwd_tile_counts")
+    return out, lse, counts, tuple(config)
 
 
 def fa_fwd_split(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,

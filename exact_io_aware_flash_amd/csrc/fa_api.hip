@@ -253,6 +253,35 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
+fa_status fa_fwd_tile_counts(const void* q, const void* k, const void* v, void* o, float* lse,
+                             int B, int H, int N_q, int N_k, int d, float scale, int causal,
+                             const fa_mask_bias_desc* mb, fa_dtype dtype, void* stream,
+                             unsigned long long* counts, int* config) {
+  fa_status st = check_common(B, H, N_q, N_k, d, scale, dtype);
+  if (st != FA_OK) return st;
+  if (!q || !k || !v || !o || !counts || !config) return FA_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return FA_ERR_ALIGN;
+  if (lse != nullptr && (reinterpret_cast<uintptr_t>(lse) & 3u)) return FA_ERR_ALIGN;
+  if (reinterpret_cast<uintptr_t>(counts) & 7u) return FA_ERR_ALIGN;
+  if (dtype == FA_F32) return FA_ERR_UNSUPPORTED;  // counted in the 16-bit kernels only
+  FwdArgs a;
+  std::memset(&a, 0, sizeof(a));
+  int bias = kBiasNone;
+  st = read_desc(mb, H, N_q, N_k, dtype, bias, a);
+  if (st != FA_OK) return st;
+  a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
+  a.B = B; a.H = H; a.Nq = N_q; a.Nk = N_k;
+  a.causal = causal ? 1 : 0;
+  a.sl2 = scale * 1.4426950408889634f;
+  a.counts = counts;
+  hipError_t e = launch_fwd(dtype, d, bias, a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return FA_ERR_HIP;
+  config[0] = a.rows_wg;
+  config[1] = 32;  // query rows per wave
+  config[2] = a.keys_tile;
+  return FA_OK;
+}
+
 int fa_fwd_split_count(int B, int H, int N_q, int N_k, int d, int n_split) {
   if (n_split < 0 || check_common(B, H, N_q, N_k, d, 1.f, FA_BF16) != FA_OK) return 0;
   int sk = 0;

@@ -801,6 +801,7 @@ void fwd16_kernel(const FwdArgs a) {
   // in flight, in front of the loop's MFMAs.
   wait_vmem<0>();
   __builtin_amdgcn_s_barrier();
+  int n_comp = 0;  // tiles this wave computes (wave-uniform; reported with a.counts)
   auto step = [&](auto J, int p) __attribute__((always_inline)) {
     constexpr int j = decltype(J)::value;
     if constexpr (SPARSE) lw.slide(p);
@@ -809,6 +810,7 @@ void fwd16_kernel(const FwdArgs a) {
     // barrier
     if (p + P < n_pos) issue(std::integral_constant<int, j + P>{}, tile_at(p + P));
     if (wave_needs(p, t)) {
+      ++n_comp;
       const char* sb = sptr(J);
       tile(sb, sb + C::Tile::kBytes, sb + C::kStage + wid * BT::kWaveBytes, t * BC, !full_tile(t));
     }
@@ -822,6 +824,10 @@ void fwd16_kernel(const FwdArgs a) {
   }
 
   // ---- epilogue -----------------------------------------------------------------------
+  if (a.counts != nullptr && lane == 0) {
+    atomicAdd(&a.counts[1], (unsigned long long)n_comp);
+    if (wid == 0) atomicAdd(&a.counts[0], (unsigned long long)n_pos);
+  }
   const float lt = xhalf_sum(l);
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
   if (a.n_split > 1) {
@@ -967,6 +973,8 @@ static hipError_t launch16(int bias, FwdArgs& a, hipStream_t st) {
   using C = Fwd16Cfg<D, BC, NW, ST>;
   static_assert(kFwdTileKeys % BC == 0, "split ranges are whole tiles");
   a.nqb = (a.Nq + C::kBR - 1) / C::kBR;
+  a.rows_wg = C::kBR;
+  a.keys_tile = BC;
   if (a.n_split < 1) a.n_split = 1;
   const int BH = a.B * a.H;
   a.sched = (BH % 8 == 0) ? kSchedXcd : kSchedHeadMajor;

@@ -43,6 +43,10 @@ struct FwdArgs {
   // tbias[b * tb_sb + h * tb_sh + i * tb_si + j]
   const float* tbias;
   long long tb_sb, tb_sh, tb_si;
+  // tile counters (NULL: off): [0] += key tiles each workgroup loads, [1] += (wave, tile)
+  // score blocks computed; the 16-bit launcher reports its workgroup rows and tile keys
+  unsigned long long* counts;
+  int rows_wg, keys_tile;
 };
 
 // The split-key 16-bit forward uses a smaller workgroup (4 waves, 32-key tiles, 64 KB of

@@ -174,6 +174,32 @@ FA_API fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, fl
                  int B, int H, int N_q, int N_k, int d, float scale, int causal,
                  const fa_mask_bias_desc* mb, fa_dtype dtype, void* stream);
 
+/* Forward with tile counters, to verify that tiles no row can see are neither loaded nor
+ * computed (blog "Apakah Konteks Sehari Penuh...", section "Causal masking adalah
+ * tempat perdagangan mendapat diskon": key tiles in the future of every query of a block
+ * are never loaded or computed, about half of the work for causal attention; the same
+ * holds for key ranges and block bitmaps).
+ * Computes exactly what fa_fwd computes, with the same launches, and in addition adds
+ *  counts[0]: the number of key tiles loaded into on-chip memory, summed over workgroups,
+ *  counts[1]: the number of (wave, key tile) score blocks computed, summed over waves,
+ * (device, two 8-byte-aligned uint64 the caller has zeroed; atomically added, so calls
+ * may accumulate) and writes to the HOST array config the launch's geometry:
+ *  config[0] = query rows per workgroup, config[1] = query rows per wave,
+ *  config[2] = keys per tile.
+ * Without a bitmap a workgroup loads the tiles from the one holding the first key any of
+ * its rows can see to the one holding the last, and a wave computes the tiles of that
+ * span for its own 32 rows; with a bitmap only tiles whose block byte is set for some
+ * wave (workgroup) or for the wave (wave count) are counted. So tiles that no row of the
+ * workgroup (wave) can see are never loaded (computed) when the visible keys of its rows
+ * form one span, as for causal masks and key ranges of overlapping rows.
+ * Errors: as fa_fwd; FA_ERR_NULL without counts or config; FA_ERR_ALIGN for misaligned
+ * counts; FA_ERR_UNSUPPORTED for float32 inputs (counted in the 16-bit kernels only). */
+FA_API fa_status fa_fwd_tile_counts(const void* q, const void* k, const void* v, void* o,
+                                    float* lse, int B, int H, int N_q, int N_k, int d,
+                                    float scale, int causal, const fa_mask_bias_desc* mb,
+                                    fa_dtype dtype, void* stream, unsigned long long* counts,
+                                    int* config);
+
 /* Split-key forward, for shapes with few query rows per head (decode-like: N_q small,
  * N_k long), where one workgroup per (b, h, query block) leaves most compute units idle.
  * The keys of every head are cut into n_split consecutive ranges (multiples of 64 keys);

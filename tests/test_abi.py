@@ -277,3 +277,20 @@ def test_bwd_noalloc_scratch_limit_is_the_workspace_size():
     assert fa.fa_bwd_workspace_bytes(2, 16, 8192, 8192, 128) <= fa.FA_NOALLOC_SCRATCH_BYTES
     assert fa.fa_bwd_workspace_bytes(64, 64, 8192, 8192, 128) > fa.FA_NOALLOC_SCRATCH_BYTES
     assert "scratch" in fa.fa_status_string(11)
+
+
+# ---- forward with tile counters: validation before any HIP call -------------------------
+
+def test_fwd_tile_counts_validation():
+    lib = fa.load_library()
+    cfg = (ctypes.c_int * 3)()
+
+    def call(counts=P, config=cfg, dtype=fa.FA_BF16, d=128, q=P):
+        return lib.fa_fwd_tile_counts(q, P, P, P, P, 1, 1, 64, 64, d, 0.1, 1, None, dtype, None,
+                                      counts, config)
+    assert call(counts=None) == 1
+    assert call(config=None) == 1
+    assert call(q=None) == 1
+    assert call(counts=P + 4) == 6
+    assert call(dtype=fa.FA_F32) == 8  # counted in the 16-bit kernels only
+    assert call(d=96) == 4
