@@ -31,7 +31,8 @@ __all__ = [
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(_HERE, "libfa.so")
+# FA_LIBRARY names another build of the library (e.g. one with host-side sanitizers)
+_LIB_PATH = os.environ.get("FA_LIBRARY") or os.path.join(_HERE, "libfa.so")
 _LIB = None
 
 FA_F32, FA_F16, FA_BF16 = 0, 1, 2

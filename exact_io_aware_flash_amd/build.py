@@ -32,8 +32,8 @@ COMMON = [
 SOURCES = ["fa_api.hip", "fa_fwd.hip", "fa_bwd.hip", "fa_fp8.hip"]
 
 
-def _compile(src: str, obj: str) -> str:
-    cmd = [HIPCC, *COMMON, "-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(src: str, obj: str, extra=()) -> str:
+    cmd = [HIPCC, *COMMON, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     out = "\n".join(l for l in (r.stdout + r.stderr).splitlines()
                     if "packed-fp32-ops' is not a recognized feature" not in l)
@@ -42,25 +42,44 @@ def _compile(src: str, obj: str) -> str:
     return out
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every HIP source for gfx950 and link ``libfa.so``; returns its path."""
-    bdir = os.path.join(PKG, "_build")
+# Host-side sanitizers (AddressSanitizer, UndefinedBehaviorSanitizer) for the argument
+# validation and launch code; device code is compiled as usual. Load the result with
+# FA_LIBRARY=<path> and the clang ASan runtime preloaded (see sanitizer_runtime()).
+SANITIZE = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+            "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host",
+            "-fno-omit-frame-pointer"]
+
+
+def sanitizer_runtime() -> str:
+    """Path of the clang AddressSanitizer runtime that a sanitized build needs preloaded."""
+    import glob
+    found = sorted(glob.glob("/opt/rocm/lib/llvm/lib/clang/*/lib/linux/libclang_rt.asan-x86_64.so"))
+    if not found:
+        raise RuntimeError("clang AddressSanitizer runtime not found under /opt/rocm/lib/llvm")
+    return found[-1]
+
+
+def build(verbose: bool = False, sanitize: bool = False, out: str = LIB) -> str:
+    """Compile every HIP source for gfx950 and link ``libfa.so`` (or ``out``); returns its
+    path. ``sanitize``: host code built with AddressSanitizer and UBSan (SANITIZE)."""
+    extra = SANITIZE if sanitize else []
+    bdir = os.path.join(PKG, "_build_san" if sanitize else "_build")
     os.makedirs(bdir, exist_ok=True)
     objs = [os.path.join(bdir, s.replace(".hip", ".o")) for s in SOURCES]
     with cf.ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 1)) as ex:
-        futs = [ex.submit(_compile, s, o) for s, o in zip(SOURCES, objs)]
+        futs = [ex.submit(_compile, s, o, extra) for s, o in zip(SOURCES, objs)]
         for s, f in zip(SOURCES, futs):
             msg = f.result()
             if verbose and msg.strip():
                 print(f"[{s}]\n{msg}", file=sys.stderr)
-    tmp = LIB + ".tmp"
-    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
+    tmp = out + ".tmp"
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *extra, "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{r.stdout}{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
     shutil.rmtree(bdir, ignore_errors=True)
-    return LIB
+    return out
 
 
 if __name__ == "__main__":

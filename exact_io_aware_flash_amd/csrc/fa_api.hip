@@ -28,7 +28,19 @@ namespace {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-fa_status check_common(int B, int H, int N_q, int N_k, int d, float scale, fa_dtype dtype) {
+// The bits of an enum argument as an int. The C caller may pass any int where the header
+// says fa_dtype, fa_status or fa_fp8_layout; in C++ using such an enum object with a value
+// outside its enumerators' range is undefined, so arguments are validated on these
+// copies and used as enums only once valid.
+template <typename E>
+int raw(const E& e) {
+  static_assert(sizeof(E) == sizeof(int), "C enums are int-sized");
+  int v;
+  std::memcpy(&v, &e, sizeof v);
+  return v;
+}
+
+fa_status check_common(int B, int H, int N_q, int N_k, int d, float scale, int dtype) {
   if (dtype != FA_F32 && dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_DTYPE;
   if (B < 1 || H < 1 || N_q < 1 || N_k < 1) return FA_ERR_SHAPE;
   if (d != 64 && d != 128) return FA_ERR_HEADDIM;
@@ -153,7 +165,7 @@ size_t split_part_bytes(int B, int H, int N_q, int d, int n) {
 extern "C" {
 
 const char* fa_status_string(fa_status s) {
-  switch (s) {
+  switch (raw(s)) {
     case FA_OK: return "ok";
     case FA_ERR_NULL: return "a required pointer is NULL";
     case FA_ERR_SHAPE: return "invalid shape (B, H, N_q, N_k must be >= 1 and fit 32-bit indexing)";
@@ -180,8 +192,8 @@ fa_status fa_fp8_quantize(const void* x, int B, int H, int N, int d, fa_dtype dt
                           void* stream) {
   if (B < 1 || H < 1 || N < 1) return FA_ERR_SHAPE;
   if (d != 64 && d != 128) return FA_ERR_HEADDIM;
-  if (dtype != FA_BF16 && dtype != FA_F16) return FA_ERR_DTYPE;
-  if (layout != FA_FP8_Q && layout != FA_FP8_K && layout != FA_FP8_V) return FA_ERR_ARG;
+  if (raw(dtype) != FA_BF16 && raw(dtype) != FA_F16) return FA_ERR_DTYPE;
+  if (raw(layout) != FA_FP8_Q && raw(layout) != FA_FP8_K && raw(layout) != FA_FP8_V) return FA_ERR_ARG;
   if (!x || !x8 || !amax) return FA_ERR_NULL;
   if (!aligned16(x) || !aligned16(x8) || (reinterpret_cast<uintptr_t>(amax) & 3u)) return FA_ERR_ALIGN;
   if ((long long)N * d > INT_MAX) return FA_ERR_SHAPE;
@@ -210,7 +222,7 @@ fa_status fa_fwd_fp8(const void* q8, const void* k8, const void* v8, const float
                      fa_dtype out_dtype, void* stream) {
   fa_status st = check_common(B, H, N_q, N_k, d, scale, FA_BF16);
   if (st != FA_OK) return st;
-  if (out_dtype != FA_BF16 && out_dtype != FA_F16) return FA_ERR_DTYPE;
+  if (raw(out_dtype) != FA_BF16 && raw(out_dtype) != FA_F16) return FA_ERR_DTYPE;
   if (!q8 || !k8 || !v8 || !q_amax || !k_amax || !v_amax || !o) return FA_ERR_NULL;
   if (!aligned16(q8) || !aligned16(k8) || !aligned16(v8) || !aligned16(o)) return FA_ERR_ALIGN;
   if (((reinterpret_cast<uintptr_t>(q_amax) | reinterpret_cast<uintptr_t>(k_amax) |
@@ -235,7 +247,7 @@ fa_status fa_fwd_fp8(const void* q8, const void* k8, const void* v8, const float
 fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
                  int N_q, int N_k, int d, float scale, int causal, const fa_mask_bias_desc* mb,
                  fa_dtype dtype, void* stream) {
-  fa_status st = check_common(B, H, N_q, N_k, d, scale, dtype);
+  fa_status st = check_common(B, H, N_q, N_k, d, scale, raw(dtype));
   if (st != FA_OK) return st;
   if (!q || !k || !v || !o) return FA_ERR_NULL;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return FA_ERR_ALIGN;
@@ -257,7 +269,7 @@ fa_status fa_fwd_tile_counts(const void* q, const void* k, const void* v, void* 
                              int B, int H, int N_q, int N_k, int d, float scale, int causal,
                              const fa_mask_bias_desc* mb, fa_dtype dtype, void* stream,
                              unsigned long long* counts, int* config) {
-  fa_status st = check_common(B, H, N_q, N_k, d, scale, dtype);
+  fa_status st = check_common(B, H, N_q, N_k, d, scale, raw(dtype));
   if (st != FA_OK) return st;
   if (!q || !k || !v || !o || !counts || !config) return FA_ERR_NULL;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return FA_ERR_ALIGN;
@@ -299,7 +311,7 @@ fa_status fa_fwd_split(const void* q, const void* k, const void* v, void* o, flo
                        const fa_mask_bias_desc* mb, fa_dtype dtype, int n_split, void* workspace,
                        size_t workspace_bytes, void* stream) {
   if (n_split < 0) return FA_ERR_ARG;
-  fa_status st = check_common(B, H, N_q, N_k, d, scale, dtype);
+  fa_status st = check_common(B, H, N_q, N_k, d, scale, raw(dtype));
   if (st != FA_OK) return st;
   int split_keys = 0;
   const int n = split_plan(B, H, N_q, N_k, d, n_split, split_keys);
@@ -360,9 +372,9 @@ fa_status bwd_check(int phases, const void* q, const void* k, const void* v, con
                     fa_dtype grad_dtype, int B, int H, int N_q, int N_k, int d, float scale,
                     const fa_mask_bias_desc* mb, fa_dtype dtype, int& bias, BwdArgs& a) {
   if (phases < 1 || (phases & ~FA_BWD_ALL) != 0) return FA_ERR_ARG;
-  fa_status st = check_common(B, H, N_q, N_k, d, scale, dtype);
+  fa_status st = check_common(B, H, N_q, N_k, d, scale, raw(dtype));
   if (st != FA_OK) return st;
-  if (grad_dtype != FA_F32 && grad_dtype != dtype) return FA_ERR_DTYPE;
+  if (raw(grad_dtype) != FA_F32 && raw(grad_dtype) != raw(dtype)) return FA_ERR_DTYPE;
   if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return FA_ERR_NULL;
   const void* dev[] = {q, k, v, o, dout, dq, dk, dv};
   for (const void* p : dev)
