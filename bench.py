@@ -23,6 +23,7 @@ import hashlib
 import json
 import math
 import os
+import platform
 import sys
 import time
 
@@ -39,9 +40,10 @@ PEAK_FP8_TFLOPS = 2 * PEAK_BF16_TFLOPS  # dense E4M3 MFMA (published 5.0 PFLOP/s
 # the kernel source they were measured on. A changed source means stale counters -> null.
 TRAFFIC = {
     # kernel: (source hash, bytes read, bytes written) -- profiles/attention_fwd_bwd_bf16_causal_B2H16N8192d128.md
-    "fwd": ("7fdf4bb51cebec1c", 287.6e6, 68.2e6),
-    "bwd_dkdv": ("687f94f7376ce93f", 270.9e6, 268.4e6),
-    "bwd_dq": ("687f94f7376ce93f", 398.6e6, 138.2e6),
+    "fwd": ("95f972e2f93c5058", 292.7e6, 68.2e6),
+    "bwd_prep": ("e457124e31a2aaa3", 136.3e6, 2.1e6),
+    "bwd_dkdv": ("e457124e31a2aaa3", 270.9e6, 268.4e6),
+    "bwd_dq": ("e457124e31a2aaa3", 411.5e6, 138.2e6),
 }
 
 
@@ -317,6 +319,8 @@ def hbm_shapes(fa, torch, only=""):
     g = torch.Generator(device=dev).manual_seed(1234)
     shapes = [("short-N", 16, 32, n, n, False) for n in (128, 256, 512)]
     shapes += [("decode", 8, 32, nq, nk, True) for nq in (1, 16) for nk in (8192, 32768)]
+    # one sequence, few heads: B H = 8 work-groups for the plain forward on 256 CUs
+    shapes += [("decode", 1, 8, 1, 131072, True)]
     out = []
     for kind, B, H, nq, nk, causal in shapes:
         d = 128
@@ -396,8 +400,9 @@ def block_sparse(fa, torch, w, qkv_inputs):
 def bias_tensor_bench(fa, torch):
     """The ALiBi-like workload (bf16 B2 H8 N8192 d128, key ranges) with its bias given as
     a float32 tensor [1, H, N, N] (one matrix per head, shared over the batch) instead of
-    generated from the slope: forward, backward, and backward writing dbias [B, H, N, N],
-    each timed by time_us, beside the generated-slope forward and backward. Rates count
+    generated from the slope: forward, backward, backward writing dbias [B, H, N, N], and
+    backward writing dbias [1, H, N, N] summed over the batch, each timed by time_us,
+    beside the generated-slope forward and backward. Rates count
     the visible (query, key) pairs (forward 4d, backward 10d FLOPs each); the bias bytes
     are 4 per visible pair and (b, h), the dbias bytes the clear of the whole array plus
     4 per visible pair and (b, h)."""
@@ -433,6 +438,12 @@ def bias_tensor_bench(fa, torch):
             ent["bwd_dbias_us"] = round(db_us, 1)
             ent["dbias_write_gbs"] = round((4.0 * B * H * N * N + 4.0 * pairs)
                                            / (db_us * 1e-6) / 1e9, 1)
+            # the shared bias's own gradient: dbias [1, H, N, N] summed over the batch
+            del dbias
+            dbias = torch.empty((1, H, N, N), dtype=torch.float32, device=dev)
+            ds_us = time_us(torch, lambda: fa.fa_bwd(do, q, k, v, o, lse, grads=grads,
+                                                     workspace=ws, dbias=dbias, **rng, **kw))
+            ent["bwd_dbias_summed_over_batch_us"] = round(ds_us, 1)
         res[name] = ent
     del q, k, v, do, o, lse, grads, ws, dbias, bias
     return res
@@ -534,6 +545,12 @@ def cpu_baseline(w, q, k, v, do, seconds):
                        if p.get("internal_api") in ("openblas", "mkl", "blis")), default=1)
     except Exception:  # pragma: no cover - threadpoolctl missing
         threads = len(os.sched_getaffinity(0))
+    model = platform.processor() or "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next(l.split(":", 1)[1].strip() for l in f if l.startswith("model name"))
+    except (OSError, StopIteration):
+        pass
     heads = [(b, h) for b in range(w.B) for h in range(w.H)]
     done = 0
     el = 0.0
@@ -549,7 +566,7 @@ def cpu_baseline(w, q, k, v, do, seconds):
             break
     per_head = 4.0 * w.N_q * w.N_k * w.d / 2.0 * 3.5  # fwd + bwd, same convention
     return {"value": round(done * per_head / el / 1e12, 5), "unit": "TFLOP/s",
-            "cores": int(threads), "kind": "oracle",
+            "cores": int(threads), "kind": "oracle", "cpu": model,
             "sample": f"float64 numpy oracle fwd+bwd of {done} of {len(heads)} (b,h) heads "
                       f"at full N={w.N_q} ({el:.1f} s of oracle wall time)"}
 

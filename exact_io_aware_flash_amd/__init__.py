@@ -27,6 +27,7 @@ __all__ = [
     "fa_fp8_rows", "fa_fp8_quantize", "fa_fwd_fp8", "fa_attention_fp8",
     "FA_FP8_Q", "FA_FP8_K", "FA_FP8_V",
     "FA_BWD_PREP", "FA_BWD_DKDV", "FA_BWD_DQ", "FA_BWD_ALL",
+    "FA_DBIAS_SUM_BATCH", "FA_DBIAS_SUM_HEADS", "FA_DBIAS_SUM_ROWS",
     "fa_status_string", "fa_version", "lib_path", "load_library",
 ]
 
@@ -39,6 +40,7 @@ FA_F32, FA_F16, FA_BF16 = 0, 1, 2
 FA_BIAS_NONE, FA_BIAS_DIST_LINEAR, FA_BIAS_TENSOR = 0, 1, 2
 FA_MAX_SLOPES = 256
 FA_BWD_PREP, FA_BWD_DKDV, FA_BWD_DQ, FA_BWD_ALL = 1, 2, 4, 7
+FA_DBIAS_SUM_BATCH, FA_DBIAS_SUM_HEADS, FA_DBIAS_SUM_ROWS = 1, 2, 4
 FA_FP8_Q, FA_FP8_K, FA_FP8_V = 0, 1, 2
 FA_NOALLOC_SCRATCH_BYTES = 16 << 20  # include/fa.h
 _DT = {torch.float32: FA_F32, torch.float16: FA_F16, torch.bfloat16: FA_BF16}
@@ -70,6 +72,7 @@ class MaskBiasDesc(ctypes.Structure):
         ("bias_stride_h", ctypes.c_int64),
         ("bias_stride_i", ctypes.c_int64),
         ("dbias", ctypes.c_void_p),
+        ("dbias_reduce", ctypes.c_int32),
     ]
 
 
@@ -178,7 +181,8 @@ def _desc(bias_slopes, key_start, key_end, H, N_q, block_mask=None, B=1, N_k=1, 
     nbq = ceil(N_q / block_q) and nbk = ceil(N_k / block_k); a zero byte masks its block.
     ``bias``: float32 device tensor of 4 dimensions that broadcasts to [B, H, N_q, N_k]
     with key stride 1 after broadcasting (a view with zero strides is fine).
-    ``dbias``: float32 device tensor [B, H, N_q, N_k], contiguous (receives dS).
+    ``dbias``: contiguous float32 device tensor [B or 1, H or 1, N_q or 1, N_k]: receives
+    dS summed over each axis of size 1 (the gradient of a bias broadcast over it).
     """
     if (bias_slopes is None and key_start is None and key_end is None and block_mask is None
             and dslopes is None and bias is None and dbias is None):
@@ -242,8 +246,16 @@ def _desc(bias_slopes, key_start, key_end, H, N_q, block_mask=None, B=1, N_k=1, 
             view.stride(0) if B > 1 else 0, view.stride(1) if H > 1 else 0,
             view.stride(2) if N_q > 1 else 0)
     if dbias is not None:
-        _check_dev("dbias", dbias, torch.float32, (B, H, N_q, N_k))
+        _check_dev("dbias", dbias, torch.float32)
+        shp = tuple(dbias.shape)
+        if (len(shp) != 4 or shp[0] not in (1, B) or shp[1] not in (1, H)
+                or shp[2] not in (1, N_q) or shp[3] != N_k):
+            raise ValueError(f"dbias has shape {shp}, expected [B or 1, H or 1, N_q or 1, N_k] "
+                             f"with B={B}, H={H}, N_q={N_q}, N_k={N_k}")
         d.dbias = dbias.data_ptr()
+        d.dbias_reduce = ((FA_DBIAS_SUM_BATCH if shp[0] < B else 0)
+                          | (FA_DBIAS_SUM_HEADS if shp[1] < H else 0)
+                          | (FA_DBIAS_SUM_ROWS if shp[2] < N_q else 0))
     return d, keep
 
 
@@ -386,7 +398,9 @@ def fa_bwd(dout: torch.Tensor, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor
     ``dslopes``: optional float32 device tensor of len(bias_slopes) that receives
     dL/dslope (``fa_mask_bias_desc.dslopes``).
     ``bias``: the forward's bias tensor; ``dbias``: optional float32 device tensor
-    [B,H,N_q,N_k] that receives the gradient of every biased score.
+    [B,H,N_q,N_k] that receives the gradient of every biased score, or with size 1 on any
+    of the first three axes (e.g. [1,H,N_q,N_k] for a bias shared over the batch,
+    [B,1,1,N_k] for a per-key bias), which receives those gradients summed over that axis.
     ``grads``: optional preallocated (dq, dk, dv); ``phases``: subset of FA_BWD_ALL
     (``fa_bwd_phases``), e.g. to run or time the launches separately with one workspace.
     """

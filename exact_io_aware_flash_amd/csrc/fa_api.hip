@@ -392,6 +392,10 @@ fa_status bwd_check(int phases, const void* q, const void* k, const void* v, con
     if (mb->bias_kind != FA_BIAS_TENSOR) return FA_ERR_MASK;
     if (reinterpret_cast<uintptr_t>(mb->dbias) & 3u) return FA_ERR_ALIGN;
   }
+  if (mb != nullptr && mb->dbias_reduce != 0) {
+    const int all = FA_DBIAS_SUM_BATCH | FA_DBIAS_SUM_HEADS | FA_DBIAS_SUM_ROWS;
+    if (mb->dbias == nullptr || (mb->dbias_reduce & ~all) != 0) return FA_ERR_MASK;
+  }
   return FA_OK;
 }
 
@@ -410,7 +414,10 @@ fa_status bwd_launch(int phases, const void* q, const void* k, const void* v, co
     a.dslope_part =
         reinterpret_cast<float*>(static_cast<char*>(workspace) + bwd_dslope_offset(B, H, N_q));
   }
-  if (mb != nullptr && mb->dbias != nullptr) a.dbias = mb->dbias;
+  if (mb != nullptr && mb->dbias != nullptr) {
+    a.dbias = mb->dbias;
+    a.db_red = mb->dbias_reduce;
+  }
   a.dq = dq; a.dk = dk; a.dv = dv;
   a.B = B; a.H = H; a.Nq = N_q; a.Nk = N_k;
   a.causal = causal ? 1 : 0;

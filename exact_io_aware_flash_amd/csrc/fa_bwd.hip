@@ -104,7 +104,8 @@ struct DkdvLds {
 #define FA_DKDV_STAGES 2
 #endif
 
-template <typename T, int D, int BR, int NW, int WPE, int BM, bool SPARSE>
+// MEM: dbias summed over batches and/or heads (bias tensor only): the member loop below
+template <typename T, int D, int BR, int NW, int WPE, int BM, bool SPARSE, bool MEM = false>
 __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
                           amdgpu_waves_per_eu(WPE, WPE)))
 void bwd_dkdv_kernel(const BwdArgs a) {
@@ -132,358 +133,409 @@ void bwd_dkdv_kernel(const BwdArgs a) {
   const int wid_s = wave_id();  // the same index as a scalar, for LDS window bases
   const int Nq = a.Nq, Nk = a.Nk, off = Nk - Nq;
   const bool causal = a.causal != 0, ranged = a.key_start != nullptr;
-  int bh, kb;
-  map_block(blockIdx.x, a.B * a.H, a.nblk, a.sched, false, bh, kb);
-  const int head = bh % a.H;
-  const T* Q = static_cast<const T*>(a.q) + (size_t)bh * Nq * D;
-  const T* K = static_cast<const T*>(a.k) + (size_t)bh * Nk * D;
-  const T* V = static_cast<const T*>(a.v) + (size_t)bh * Nk * D;
-  const T* dO = static_cast<const T*>(a.dout) + (size_t)bh * Nq * D;
-  const float sl2 = a.sl2;
-  const float slope2 = BIAS ? a.slope2[a.n_slopes == 1 ? 0 : head] : 0.f;
-  const float* TB = TENSOR ? a.tbias + (long long)(bh / a.H) * a.tb_sb + (long long)head * a.tb_sh
-                           : nullptr;
-  float* dB = TENSOR ? a.dbias : nullptr;  // NULL: dbias not wanted
+  // dbias summed over batches and/or heads: the workgroup owns one dbias slice (slot) and
+  // computes, one after the other, every (b, h) that shares it (its members), so each
+  // element is summed by one thread in a fixed order; otherwise a slot is one (b, h)
+  static_assert(!MEM || TENSOR, "member loop: bias tensor only");
+  const int rb = MEM ? (a.db_red & FA_DBIAS_SUM_BATCH) : 0;
+  const int rh = MEM ? (a.db_red & FA_DBIAS_SUM_HEADS) : 0;
+  const bool rrows = TENSOR && (a.db_red & FA_DBIAS_SUM_ROWS) != 0;
+  const int slot_h = rh ? 1 : a.H;                    // heads of the dbias array
+  const int n_slots = (rb ? 1 : a.B) * slot_h;
+  const int mem_h = rh ? a.H : 1, n_mem = (rb ? a.B : 1) * mem_h;
+  int slot, kb;
+  map_block(blockIdx.x, n_slots, a.nblk, a.sched, false, slot, kb);
+  float* dB = nullptr;  // the slot's dbias [Nq' rows][Nk] (NULL: dbias not wanted)
+  if constexpr (TENSOR)
+    if (a.dbias != nullptr) dB = a.dbias + (size_t)slot * (rrows ? 1 : Nq) * Nk;
+  float dbr = 0.f;  // rows summed: this lane's share of its key's dbias, over all members
 
-  const int k0 = kb * BK, k1 = min(k0 + BK, Nk);
-  const int kw0 = k0 + 32 * wid, kw1 = min(kw0 + 32, Nk);
-  const int key = kw0 + n;  // this lane's key (column of S)
+  for (int m = 0; m < n_mem; ++m) {
+    if (m > 0) __syncthreads();  // every wave is done with the ring and the tile list
+    const bool first = m == 0;   // the first member writes dbias, later ones add to it
+    const int bh = (rb | rh) ? (rb ? m / mem_h : slot / slot_h) * a.H
+                                   + (rh ? m % mem_h : slot % slot_h)
+                             : slot;
+    const int head = bh % a.H;
+    const T* Q = static_cast<const T*>(a.q) + (size_t)bh * Nq * D;
+    const T* K = static_cast<const T*>(a.k) + (size_t)bh * Nk * D;
+    const T* V = static_cast<const T*>(a.v) + (size_t)bh * Nk * D;
+    const T* dO = static_cast<const T*>(a.dout) + (size_t)bh * Nq * D;
+    const float sl2 = a.sl2;
+    const float slope2 = BIAS ? a.slope2[a.n_slopes == 1 ? 0 : head] : 0.f;
+    const float* TB = TENSOR ? a.tbias + (long long)(bh / a.H) * a.tb_sb + (long long)head * a.tb_sh
+                             : nullptr;
 
-  // K and V rows of the wave's keys: B operands of S = Q K^T and dP = dO V^T
-  u32x4 kf[DK], vf[DK];
-  {
-    const size_t r = (size_t)min(key, Nk - 1);
-#pragma unroll
-    for (int ks = 0; ks < DK; ++ks) {
-      kf[ks] = ldg16(K + r * D + 16 * ks + 8 * h);
-      vf[ks] = ldg16(V + r * D + 16 * ks + 8 * h);
-    }
-  }
+    const int k0 = kb * BK, k1 = min(k0 + BK, Nk);
+    const int kw0 = k0 + 32 * wid, kw1 = min(kw0 + 32, Nk);
+    const int key = kw0 + n;  // this lane's key (column of S)
 
-  // query tiles that can see a key of this block
-  const int nqt = (Nq + BR - 1) / BR;
-  int t_lo = 0, t_hi = nqt;
-  if (causal) t_lo = max(0, k0 - off) / BR;
-  if (causal && k0 - off >= Nq) t_hi = 0;
-  if (ranged) {
-    if (tid < 64) {
-      int lo = nqt, hi = -1;
-      for (int t = lane; t < nqt; t += 64) {
-        const int* sm = a.qsum + 4 * t;  // {min start, max start, min end, max end}
-        if (!(k1 <= sm[0] || k0 >= sm[3])) { lo = min(lo, t); hi = max(hi, t); }
-      }
-      lo = wave_min(lo);
-      hi = wave_max(hi);
-      if (lane == 0) { win[0] = lo; win[1] = hi + 1; }
-    }
-    __syncthreads();
-    t_lo = max(t_lo, win[0]);
-    t_hi = min(t_hi, win[1]);
-  }
-  if (k0 >= Nk) t_hi = t_lo;
-
-  // block-sparse bitmap: the query tiles the workgroup loads (see build_tile_list); a
-  // 64-row query tile and a wave's 32 keys each lie inside one block
-  constexpr int kMaxT = SPARSE ? FA_MAX_SPARSE_N / BR : 64;
-  __shared__ uint32_t need_w[SPARSE ? NW : 1][2 * (kMaxT / 64)];
-  __shared__ uint32_t tlist[SPARSE ? kMaxT : 1];
-  __shared__ int n_list_s;
-  int n_pos = t_hi - t_lo;
-  if constexpr (SPARSE) {
-    const uint8_t* bcol = nullptr;
-    if (kw0 < Nk) {
-      const int bb = bh / a.H, hh = bh - bb * a.H;
-      bcol = a.bmask + bb * a.bm_sb + hh * a.bm_sh + kw0 / a.bk;
-    }
-    n_pos = build_tile_list(need_w, tlist, &n_list_s, wid_s, lane, t_lo, t_hi, [&](int t) {
-      const int q0t = t * BR;
-      bool skip = bcol == nullptr;
-      if (causal) skip |= q0t + BR - 1 + off < kw0;
-      if (ranged) {
-        const int* sm = a.qsum + 4 * t;
-        skip |= kw1 <= sm[0] || kw0 >= sm[3];
-      }
-      return !skip && bcol[(long long)(q0t / a.bq) * a.nkb] != 0;
-    });
-  }
-  ListWindow<kMaxT> lw;
-  if constexpr (SPARSE) lw.init(tlist, lane);
-  auto tile_at = [&](int p) -> int {
-    if constexpr (SPARSE) return (int)(lw.at(p) & 0xffffu);
-    else return t_lo + p;
-  };
-
-  f32x16 dv[DB], dk[DB];
-#pragma unroll
-  for (int db = 0; db < DB; ++db) { dv[db] = f32x16{}; dk[db] = f32x16{}; }
-  float sgrad = 0.f;  // this lane's share of dL/dslope (bias only)
-
-  // LDS offsets inside a swizzled tile (see DmaTile): row reads of query row 32qb + n,
-  // chunk 2ks + h (A operands of S and dP); transposing gathers of 8 query rows of one
-  // d column (B operands of dV += P^T dO and dK += dS^T Q).
-  int ra[DK];
-#pragma unroll
-  for (int ks = 0; ks < DK; ++ks) ra[ks] = n * RB + 16 * ((2 * ks + h) ^ swz<D>(n));
-  int ta[DB][2];
-  {
-    const int q = (lane >> 2) & 3, g16 = (lane >> 4) & 1, lo2 = lane & 3;
-#pragma unroll
-    for (int p = 0; p < 2; ++p) {
-      const int r = 8 * p + 4 * h + q;
-#pragma unroll
-      for (int db = 0; db < DB; ++db)
-        ta[db][p] = r * RB + 16 * ((4 * db + 2 * g16 + (lo2 >> 1)) ^ swz<D>(r)) + 8 * (lo2 & 1);
-    }
-  }
-  auto cfrag = [&](const char* base, int qb, int st, int db) {
-    const int rows = (32 * qb + 16 * st) * RB;
-    const u32x2 lo = lds_ld8_tr(base, rows + ta[db][0]);
-    const u32x2 hi = lds_ld8_tr(base, rows + ta[db][1]);
-    return u32x4{lo[0], lo[1], hi[0], hi[1]};
-  };
-
-  // one 32-query block of a tile; MASK: per-element visibility
-  auto qblock = [&](const char* sb, int q0t, int qb, auto mask_tag) {
-    constexpr bool MASK = decltype(mask_tag)::value;
-    f32x16 sc = f32x16{}, dp = f32x16{};
+    // K and V rows of the wave's keys: B operands of S = Q K^T and dP = dO V^T
+    u32x4 kf[DK], vf[DK];
     {
-      u32x4 qa[DK], da[DK];
+      const size_t r = (size_t)min(key, Nk - 1);
 #pragma unroll
       for (int ks = 0; ks < DK; ++ks) {
-        qa[ks] = lds_ld16(sb + L::QT, 32 * qb * RB + ra[ks]);
-        da[ks] = lds_ld16(sb + L::DT, 32 * qb * RB + ra[ks]);
-      }
-      sched_fence();  // all Q and dO operands in flight before the first MFMA
-#pragma unroll
-      for (int ks = 0; ks < DK; ++ks) {
-        sc = E::mma(qa[ks], kf[ks], sc);
-        dp = E::mma(da[ks], vf[ks], dp);
+        kf[ks] = ldg16(K + r * D + 16 * ks + 8 * h);
+        vf[ks] = ldg16(V + r * D + 16 * ks + 8 * h);
       }
     }
-    // statistics of the 16 queries this lane holds (rows res_row(g, h) of the block)
-    f32x4 l4[4], d4[4];
-#pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      const int r0 = 32 * qb + 8 * q4 + 4 * h;
-      l4[q4] = *reinterpret_cast<const f32x4*>(sb + L::LSE + r0 * 4);
-      d4[q4] = *reinterpret_cast<const f32x4*>(sb + L::DLT + r0 * 4);
-    }
-    float p[16], ds[16], adist[BIAS ? 16 : 1];
-    const char* bs = sb + L::STAGE + wid_s * BT::kWaveBytes;  // this wave's bias windows
-#pragma unroll
-    for (int g = 0; g < 16; ++g) {
-      const float lq = l4[g / 4][g % 4];  // already in log2 units
-      float x;
-      if constexpr (TENSOR) {
-        x = __builtin_fmaf(sc[g], sl2, __builtin_fmaf(BT::read(bs, qb, g, lane), kLog2e, -lq));
-      } else if constexpr (BIAS) {
-        const float dist = (float)(q0t + 32 * qb + 4 * h - key) + (float)(8 * (g / 4) + (g % 4));
-        adist[g] = __builtin_fabsf(dist);
-        x = __builtin_fmaf(sc[g], sl2, __builtin_fmaf(slope2, adist[g], -lq));
-      } else {
-        x = __builtin_fmaf(sc[g], sl2, -lq);
+
+    // query tiles that can see a key of this block
+    const int nqt = (Nq + BR - 1) / BR;
+    int t_lo = 0, t_hi = nqt;
+    if (causal) t_lo = max(0, k0 - off) / BR;
+    if (causal && k0 - off >= Nq) t_hi = 0;
+    if (ranged) {
+      if (tid < 64) {
+        int lo = nqt, hi = -1;
+        for (int t = lane; t < nqt; t += 64) {
+          const int* sm = a.qsum + 4 * t;  // {min start, max start, min end, max end}
+          if (!(k1 <= sm[0] || k0 >= sm[3])) { lo = min(lo, t); hi = max(hi, t); }
+        }
+        lo = wave_min(lo);
+        hi = wave_max(hi);
+        if (lane == 0) { win[0] = lo; win[1] = hi + 1; }
       }
-      p[g] = fast_exp2(x);
+      __syncthreads();
+      t_lo = max(t_lo, win[0]);
+      t_hi = min(t_hi, win[1]);
     }
-    if constexpr (MASK) {
-      int4 st4[4], en4[4];
-      if (ranged) {
+    if (k0 >= Nk) t_hi = t_lo;
+
+    // block-sparse bitmap: the query tiles the workgroup loads (see build_tile_list); a
+    // 64-row query tile and a wave's 32 keys each lie inside one block
+    constexpr int kMaxT = SPARSE ? FA_MAX_SPARSE_N / BR : 64;
+    __shared__ uint32_t need_w[SPARSE ? NW : 1][2 * (kMaxT / 64)];
+    __shared__ uint32_t tlist[SPARSE ? kMaxT : 1];
+    __shared__ int n_list_s;
+    int n_pos = t_hi - t_lo;
+    if constexpr (SPARSE) {
+      const uint8_t* bcol = nullptr;
+      if (kw0 < Nk) {
+        const int bb = bh / a.H, hh = bh - bb * a.H;
+        bcol = a.bmask + bb * a.bm_sb + hh * a.bm_sh + kw0 / a.bk;
+      }
+      n_pos = build_tile_list(need_w, tlist, &n_list_s, wid_s, lane, t_lo, t_hi, [&](int t) {
+        const int q0t = t * BR;
+        bool skip = bcol == nullptr;
+        if (causal) skip |= q0t + BR - 1 + off < kw0;
+        if (ranged) {
+          const int* sm = a.qsum + 4 * t;
+          skip |= kw1 <= sm[0] || kw0 >= sm[3];
+        }
+        return !skip && bcol[(long long)(q0t / a.bq) * a.nkb] != 0;
+      });
+    }
+    ListWindow<kMaxT> lw;
+    if constexpr (SPARSE) lw.init(tlist, lane);
+    auto tile_at = [&](int p) -> int {
+      if constexpr (SPARSE) return (int)(lw.at(p) & 0xffffu);
+      else return t_lo + p;
+    };
+
+    f32x16 dv[DB], dk[DB];
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          const int r0 = 32 * qb + 8 * q4 + 4 * h;
-          st4[q4] = *reinterpret_cast<const int4*>(sb + L::KS + r0 * 4);
-          en4[q4] = *reinterpret_cast<const int4*>(sb + L::KE + r0 * 4);
+    for (int db = 0; db < DB; ++db) { dv[db] = f32x16{}; dk[db] = f32x16{}; }
+    float sgrad = 0.f;  // this lane's share of dL/dslope (bias only)
+
+    // LDS offsets inside a swizzled tile (see DmaTile): row reads of query row 32qb + n,
+    // chunk 2ks + h (A operands of S and dP); transposing gathers of 8 query rows of one
+    // d column (B operands of dV += P^T dO and dK += dS^T Q).
+    int ra[DK];
+#pragma unroll
+    for (int ks = 0; ks < DK; ++ks) ra[ks] = n * RB + 16 * ((2 * ks + h) ^ swz<D>(n));
+    int ta[DB][2];
+    {
+      const int q = (lane >> 2) & 3, g16 = (lane >> 4) & 1, lo2 = lane & 3;
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        const int r = 8 * p + 4 * h + q;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+          ta[db][p] = r * RB + 16 * ((4 * db + 2 * g16 + (lo2 >> 1)) ^ swz<D>(r)) + 8 * (lo2 & 1);
+      }
+    }
+    auto cfrag = [&](const char* base, int qb, int st, int db) {
+      const int rows = (32 * qb + 16 * st) * RB;
+      const u32x2 lo = lds_ld8_tr(base, rows + ta[db][0]);
+      const u32x2 hi = lds_ld8_tr(base, rows + ta[db][1]);
+      return u32x4{lo[0], lo[1], hi[0], hi[1]};
+    };
+
+    // one 32-query block of a tile; MASK: per-element visibility
+    float pre[TENSOR ? QB : 1][16];  // dbias values a later member adds to (see below)
+    auto qblock = [&](const char* sb, int q0t, int qb, auto mask_tag) {
+      constexpr bool MASK = decltype(mask_tag)::value;
+      f32x16 sc = f32x16{}, dp = f32x16{};
+      {
+        u32x4 qa[DK], da[DK];
+#pragma unroll
+        for (int ks = 0; ks < DK; ++ks) {
+          qa[ks] = lds_ld16(sb + L::QT, 32 * qb * RB + ra[ks]);
+          da[ks] = lds_ld16(sb + L::DT, 32 * qb * RB + ra[ks]);
+        }
+        sched_fence();  // all Q and dO operands in flight before the first MFMA
+#pragma unroll
+        for (int ks = 0; ks < DK; ++ks) {
+          sc = E::mma(qa[ks], kf[ks], sc);
+          dp = E::mma(da[ks], vf[ks], dp);
         }
       }
-      const int kvis = key < Nk ? 1 : 0;
+      // statistics of the 16 queries this lane holds (rows res_row(g, h) of the block)
+      f32x4 l4[4], d4[4];
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int r0 = 32 * qb + 8 * q4 + 4 * h;
+        l4[q4] = *reinterpret_cast<const f32x4*>(sb + L::LSE + r0 * 4);
+        d4[q4] = *reinterpret_cast<const f32x4*>(sb + L::DLT + r0 * 4);
+      }
+      float p[16], ds[16], adist[BIAS ? 16 : 1];
+      const char* bs = sb + L::STAGE + wid_s * BT::kWaveBytes;  // this wave's bias windows
 #pragma unroll
       for (int g = 0; g < 16; ++g) {
-        const int qi = q0t + 32 * qb + res_row(g, h);
-        const int lo = ranged ? min(max((&st4[g / 4].x)[g % 4], 0), Nk) : 0;
-        const int hi = ranged ? min(max((&en4[g / 4].x)[g % 4], 0), Nk) : Nk;
-        const int cmin = causal ? qi + off : Nk;
-        const bool vis = kvis && qi < Nq && key >= lo && key < hi && key <= cmin;
-        p[g] = vis ? p[g] : 0.f;
+        const float lq = l4[g / 4][g % 4];  // already in log2 units
+        float x;
+        if constexpr (TENSOR) {
+          x = __builtin_fmaf(sc[g], sl2, __builtin_fmaf(BT::read(bs, qb, g, lane), kLog2e, -lq));
+        } else if constexpr (BIAS) {
+          const float dist = (float)(q0t + 32 * qb + 4 * h - key) + (float)(8 * (g / 4) + (g % 4));
+          adist[g] = __builtin_fabsf(dist);
+          x = __builtin_fmaf(sc[g], sl2, __builtin_fmaf(slope2, adist[g], -lq));
+        } else {
+          x = __builtin_fmaf(sc[g], sl2, -lq);
+        }
+        p[g] = fast_exp2(x);
       }
-    }
+      if constexpr (MASK) {
+        int4 st4[4], en4[4];
+        if (ranged) {
 #pragma unroll
-    for (int g = 0; g < 16; ++g) ds[g] = p[g] * (dp[g] - d4[g / 4][g % 4]);
-    if constexpr (TENSOR) {
-      // dbias = dS (zero where masked: p = 0 there); lanes 0-31 and 32-63 each store 128
-      // contiguous bytes of one row
-      if (dB != nullptr && key < Nk) {
+          for (int q4 = 0; q4 < 4; ++q4) {
+            const int r0 = 32 * qb + 8 * q4 + 4 * h;
+            st4[q4] = *reinterpret_cast<const int4*>(sb + L::KS + r0 * 4);
+            en4[q4] = *reinterpret_cast<const int4*>(sb + L::KE + r0 * 4);
+          }
+        }
+        const int kvis = key < Nk ? 1 : 0;
 #pragma unroll
         for (int g = 0; g < 16; ++g) {
           const int qi = q0t + 32 * qb + res_row(g, h);
-          if (qi < Nq) dB[((size_t)bh * Nq + qi) * Nk + key] = ds[g];
+          const int lo = ranged ? min(max((&st4[g / 4].x)[g % 4], 0), Nk) : 0;
+          const int hi = ranged ? min(max((&en4[g / 4].x)[g % 4], 0), Nk) : Nk;
+          const int cmin = causal ? qi + off : Nk;
+          const bool vis = kvis && qi < Nq && key >= lo && key < hi && key <= cmin;
+          p[g] = vis ? p[g] : 0.f;
         }
       }
-    }
-    if constexpr (BIAS) {
-      // the slope's gradient: dS |i - j| over the visible entries (masked ones have p = 0)
 #pragma unroll
-      for (int g = 0; g < 16; ++g) sgrad = __builtin_fmaf(ds[g], adist[g], sgrad);
-    }
+      for (int g = 0; g < 16; ++g) ds[g] = p[g] * (dp[g] - d4[g / 4][g % 4]);
+      if constexpr (TENSOR) {
+        // dbias = dS (zero where masked: p = 0 there); lanes 0-31 and 32-63 each store 128
+        // contiguous bytes of one row. Rows summed: the lane adds its 16 rows.
+        if (dB != nullptr && key < Nk) {
+          if (rrows) {
 #pragma unroll
-    for (int st = 0; st < 2; ++st) {
-      u32x4 pa, dsa;
+            for (int g = 0; g < 16; ++g) dbr += ds[g];
+          } else {
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        pa[w] = E::pack2(p[8 * st + 2 * w], p[8 * st + 2 * w + 1]);
-        dsa[w] = E::pack2(ds[8 * st + 2 * w], ds[8 * st + 2 * w + 1]);
+            for (int g = 0; g < 16; ++g) {
+              const int qi = q0t + 32 * qb + res_row(g, h);
+              if (qi < Nq) {
+                float* pd = dB + (size_t)qi * Nk + key;
+                *pd = first ? ds[g] : pre[qb][g] + ds[g];
+              }
+            }
+          }
+        }
       }
-      u32x4 ob[DB], qbf[DB];
+      if constexpr (BIAS) {
+        // the slope's gradient: dS |i - j| over the visible entries (masked ones have p = 0)
 #pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        ob[db] = cfrag(sb + L::DT, qb, st, db);
-        qbf[db] = cfrag(sb + L::QT, qb, st, db);
+        for (int g = 0; g < 16; ++g) sgrad = __builtin_fmaf(ds[g], adist[g], sgrad);
       }
 #pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        dv[db] = E::mma(pa, ob[db], dv[db]);
-        dk[db] = E::mma(dsa, qbf[db], dk[db]);
+      for (int st = 0; st < 2; ++st) {
+        u32x4 pa, dsa;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          pa[w] = E::pack2(p[8 * st + 2 * w], p[8 * st + 2 * w + 1]);
+          dsa[w] = E::pack2(ds[8 * st + 2 * w], ds[8 * st + 2 * w + 1]);
+        }
+        u32x4 ob[DB], qbf[DB];
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          ob[db] = cfrag(sb + L::DT, qb, st, db);
+          qbf[db] = cfrag(sb + L::QT, qb, st, db);
+        }
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          dv[db] = E::mma(pa, ob[db], dv[db]);
+          dk[db] = E::mma(dsa, qbf[db], dk[db]);
+        }
       }
-    }
-  };
+    };
 
-  // ---- ring of ST stages, P = ST-1 query tiles in flight -------------------------------
-  Tile tile_ld;
-  tile_ld.init(wid_s, lane);
-  // wave w brings the tile's row array w: 0 LSE*log2(e), 1 D, 2 key_start, 3 key_end
-  // (without a range mask waves 2 and 3 load the first array again, so that every wave
-  // issues the same count)
-  const float* arr_base;
-  {
-    const float* lse_h = a.lse2 + (size_t)bh * Nq;  // LSE * log2(e), from the prep pass
-    const float* dlt_h = a.delta + (size_t)bh * Nq;
-    arr_base = wid_s == 0 ? lse_h : wid_s == 1 ? dlt_h
-             : ranged ? reinterpret_cast<const float*>(wid_s == 2 ? a.key_start : a.key_end) : lse_h;
-  }
-  const int arr_off = wid_s == 0 ? L::LSE : wid_s == 1 ? L::DLT : wid_s == 2 ? L::KS : L::KE;
-  // ring position p (query tile tile_at(p)) lives in stage p % ST
-  auto stage_of = [&](int p) { return smem + (p % ST) * kStage; };
-  auto issue = [&](int p) {
-    char* sb = stage_of(p);
-    const int q0t = tile_at(p) * BR;
-    tile_ld.template load<false>(Q, q0t, Nq, sb + L::QT, wid_s);
-    tile_ld.template load<false>(dO, q0t, Nq, sb + L::DT, wid_s);
-    dma4<false>(arr_base, (uint32_t)min(q0t + lane, Nq - 1), sb + arr_off);
-    if constexpr (TENSOR)
-      BT::load(TB, a.tb_si, q0t, Nq, kw0, Nk, sb + L::STAGE + wid_s * BT::kWaveBytes, lane);
-  };
-  auto land = [&](int later) {
-    if (P >= 3 && later >= 3) wait_vmem<(P >= 3 ? 3 : 0) * kOpsPerTile>();
-    else if (P >= 2 && later == 2) wait_vmem<(P >= 2 ? 2 : 0) * kOpsPerTile>();
-    else if (later == 1) wait_vmem<kOpsPerTile>();
-    else wait_vmem<0>();
+    // ---- ring of ST stages, P = ST-1 query tiles in flight -------------------------------
+    Tile tile_ld;
+    tile_ld.init(wid_s, lane);
+    // wave w brings the tile's row array w: 0 LSE*log2(e), 1 D, 2 key_start, 3 key_end
+    // (without a range mask waves 2 and 3 load the first array again, so that every wave
+    // issues the same count)
+    const float* arr_base;
+    {
+      const float* lse_h = a.lse2 + (size_t)bh * Nq;  // LSE * log2(e), from the prep pass
+      const float* dlt_h = a.delta + (size_t)bh * Nq;
+      arr_base = wid_s == 0 ? lse_h : wid_s == 1 ? dlt_h
+               : ranged ? reinterpret_cast<const float*>(wid_s == 2 ? a.key_start : a.key_end) : lse_h;
+    }
+    const int arr_off = wid_s == 0 ? L::LSE : wid_s == 1 ? L::DLT : wid_s == 2 ? L::KS : L::KE;
+    // ring position p (query tile tile_at(p)) lives in stage p % ST
+    auto stage_of = [&](int p) { return smem + (p % ST) * kStage; };
+    auto issue = [&](int p) {
+      char* sb = stage_of(p);
+      const int q0t = tile_at(p) * BR;
+      tile_ld.template load<false>(Q, q0t, Nq, sb + L::QT, wid_s);
+      tile_ld.template load<false>(dO, q0t, Nq, sb + L::DT, wid_s);
+      dma4<false>(arr_base, (uint32_t)min(q0t + lane, Nq - 1), sb + arr_off);
+      if constexpr (TENSOR)
+        BT::load(TB, a.tb_si, q0t, Nq, kw0, Nk, sb + L::STAGE + wid_s * BT::kWaveBytes, lane);
+    };
+    auto land = [&](int later) {
+      if (P >= 3 && later >= 3) wait_vmem<(P >= 3 ? 3 : 0) * kOpsPerTile>();
+      else if (P >= 2 && later == 2) wait_vmem<(P >= 2 ? 2 : 0) * kOpsPerTile>();
+      else if (later == 1) wait_vmem<kOpsPerTile>();
+      else wait_vmem<0>();
+      __builtin_amdgcn_s_barrier();
+    };
+    // zero dbias of query tile t for this wave's keys (lanes 0-31 and 32-63: alternate rows)
+    // (only the first member: later ones add nothing there; rows summed: written at the end)
+    auto zero_dbias_tile = [&](int t) {
+      if (dB == nullptr || rrows || !first || key >= Nk) return;
+      for (int i = 0; i < BR / 2; ++i) {
+        const int qi = t * BR + 2 * i + h;
+        if (qi < Nq) dB[(size_t)qi * Nk + key] = 0.f;
+      }
+    };
+#pragma unroll
+    for (int i = 0; i < P; ++i)
+      if (i < n_pos) issue(i);
+    // The K and V fragments and every prologue tile land here. Waiting for all of them
+    // (rather than for the first tile only) leaves no register load outstanding once the
+    // loop starts, so the compiler has no reason to put a full vector-memory wait, which
+    // would also wait for the ring's loads in flight, in front of the loop's MFMAs.
+    wait_vmem<0>();
     __builtin_amdgcn_s_barrier();
-  };
-  // zero dbias of query tile t for this wave's keys (lanes 0-31 and 32-63: alternate rows)
-  auto zero_dbias_tile = [&](int t) {
-    if (dB == nullptr || key >= Nk) return;
-    for (int i = 0; i < BR / 2; ++i) {
-      const int qi = t * BR + 2 * i + h;
-      if (qi < Nq) dB[((size_t)bh * Nq + qi) * Nk + key] = 0.f;
-    }
-  };
-#pragma unroll
-  for (int i = 0; i < P; ++i)
-    if (i < n_pos) issue(i);
-  // The K and V fragments and every prologue tile land here. Waiting for all of them
-  // (rather than for the first tile only) leaves no register load outstanding once the
-  // loop starts, so the compiler has no reason to put a full vector-memory wait, which
-  // would also wait for the ring's loads in flight, in front of the loop's MFMAs.
-  wait_vmem<0>();
-  __builtin_amdgcn_s_barrier();
 
-  for (int p = 0; p < n_pos; ++p) {
+    for (int p = 0; p < n_pos; ++p) {
 #pragma unroll
-    for (int db = 0; db < DB; ++db) { pin_agpr(dv[db]); pin_agpr(dk[db]); }
+      for (int db = 0; db < DB; ++db) { pin_agpr(dv[db]); pin_agpr(dk[db]); }
 #pragma unroll
-    for (int ks = 0; ks < DK; ++ks) { pin_agpr(kf[ks]); pin_agpr(vf[ks]); }
-    // the stage of position p+P held position p-1, which every wave finished before the
-    // barrier
-    if constexpr (SPARSE) lw.slide(p);
-    if (p + P < n_pos) issue(p + P);
-    const int t = tile_at(p);
-    const int q0t = t * BR;
-    const char* sb = stage_of(p);
+      for (int ks = 0; ks < DK; ++ks) { pin_agpr(kf[ks]); pin_agpr(vf[ks]); }
+      // the stage of position p+P held position p-1, which every wave finished before the
+      // barrier
+      if constexpr (SPARSE) lw.slide(p);
+      if (p + P < n_pos) issue(p + P);
+      const int t = tile_at(p);
+      const int q0t = t * BR;
+      const char* sb = stage_of(p);
 
-    // classify the tile for this wave's keys [kw0, kw1)
-    bool skip = kw0 >= Nk;
-    bool full = q0t + BR <= Nq && kw0 + 32 <= Nk;
-    if (causal) {
-      skip |= q0t + BR - 1 + off < kw0;
-      full &= q0t + off >= kw0 + 31;
-    }
-    if (ranged) {
-      // tile t's summary through the constant address space: a scalar load, whose wait
-      // does not cover the ring's loads in flight (a vector load here made every tile wait
-      // for the tile just issued)
-      const __attribute__((address_space(4))) int* sm =
-          (const __attribute__((address_space(4))) int*)a.qsum + 4 * t;
-      skip |= kw1 <= sm[0] || kw0 >= sm[3];
-      full &= sm[1] <= kw0 && sm[2] >= kw0 + 32;
-    }
-    if constexpr (SPARSE) skip = !((lw.at(p) >> (16 + wid_s)) & 1u);
-    if (!skip) {
-      if (full) {
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) qblock(sb, q0t, qb, std::false_type{});
-      } else {
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) qblock(sb, q0t, qb, std::true_type{});
+      // classify the tile for this wave's keys [kw0, kw1)
+      bool skip = kw0 >= Nk;
+      bool full = q0t + BR <= Nq && kw0 + 32 <= Nk;
+      if (causal) {
+        skip |= q0t + BR - 1 + off < kw0;
+        full &= q0t + off >= kw0 + 31;
       }
-    } else if constexpr (TENSOR) {
-      zero_dbias_tile(t);
-    }
-    if (p + 1 < n_pos) land(min(p + P, n_pos - 1) - (p + 1));
-  }
-  // dbias of the query tiles outside the workgroup's window is zero (every (i, j) of this
-  // wave's keys is then written exactly once: computed, or zero where nothing is visible)
-  if constexpr (TENSOR) {
-    if (dB != nullptr) {
-      for (int t = 0; t < t_lo; ++t) zero_dbias_tile(t);
-      for (int t = max(t_hi, t_lo); t < nqt; ++t) zero_dbias_tile(t);
-    }
-  }
-
-  // the workgroup's partial of dL/dslope (every workgroup writes one, zero if it saw
-  // nothing, so the reduction reads only values of this call)
-  if constexpr (BIAS) {
-    if (a.dslope_part != nullptr) {
-      __shared__ float sred[NW];
-      const float w = wave_fsum(sgrad);
-      if (lane == 0) sred[wid_s] = w;
-      __syncthreads();
-      if (tid == 0) {
-        float acc = 0.f;
-#pragma unroll
-        for (int i = 0; i < NW; ++i) acc += sred[i];
-        a.dslope_part[(size_t)bh * a.nblk + kb] = acc;
+      if (ranged) {
+        // tile t's summary through the constant address space: a scalar load, whose wait
+        // does not cover the ring's loads in flight (a vector load here made every tile wait
+        // for the tile just issued)
+        const __attribute__((address_space(4))) int* sm =
+            (const __attribute__((address_space(4))) int*)a.qsum + 4 * t;
+        skip |= kw1 <= sm[0] || kw0 >= sm[3];
+        full &= sm[1] <= kw0 && sm[2] >= kw0 + 32;
       }
-    }
-  }
-
-  // epilogue: lane holds column d = 32*db + n for keys kw0 + res_row(g, h)
-  const float scale = a.scale;
+      if constexpr (SPARSE) skip = !((lw.at(p) >> (16 + wid_s)) & 1u);
+      if constexpr (TENSOR) {
+        // later members add to dbias: read the values this lane adds to before the tile's
+        // products, so the loads' latency hides behind them
+        if (!skip && !first && !rrows && dB != nullptr && key < Nk) {
 #pragma unroll
-  for (int db = 0; db < DB; ++db) {
+          for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
-    for (int g = 0; g < 16; ++g) {
-      const int kr = kw0 + res_row(g, h);
-      if (kr < Nk) {
-        const size_t idx = ((size_t)bh * Nk + kr) * D + 32 * db + n;
-        if (a.grad_f32) {
-          static_cast<float*>(a.dk)[idx] = dk[db][g] * scale;
-          static_cast<float*>(a.dv)[idx] = dv[db][g];
+            for (int g = 0; g < 16; ++g) {
+              const int qi = min(q0t + 32 * qb + res_row(g, h), Nq - 1);
+              pre[qb][g] = dB[(size_t)qi * Nk + key];
+            }
+        }
+      }
+      if (!skip) {
+        if (full) {
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb) qblock(sb, q0t, qb, std::false_type{});
         } else {
-          static_cast<T*>(a.dk)[idx] = (T)(dk[db][g] * scale);
-          static_cast<T*>(a.dv)[idx] = (T)dv[db][g];
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb) qblock(sb, q0t, qb, std::true_type{});
+        }
+      } else if constexpr (TENSOR) {
+        zero_dbias_tile(t);
+      }
+      if (p + 1 < n_pos) land(min(p + P, n_pos - 1) - (p + 1));
+    }
+    // dbias of the query tiles outside the workgroup's window is zero (every (i, j) of this
+    // wave's keys is then written exactly once: computed, or zero where nothing is visible)
+    if constexpr (TENSOR) {
+      if (dB != nullptr) {
+        for (int t = 0; t < t_lo; ++t) zero_dbias_tile(t);
+        for (int t = max(t_hi, t_lo); t < nqt; ++t) zero_dbias_tile(t);
+      }
+    }
+
+    // the workgroup's partial of dL/dslope (every workgroup writes one, zero if it saw
+    // nothing, so the reduction reads only values of this call)
+    if constexpr (BIAS) {
+      if (a.dslope_part != nullptr) {
+        __shared__ float sred[NW];
+        const float w = wave_fsum(sgrad);
+        if (lane == 0) sred[wid_s] = w;
+        __syncthreads();
+        if (tid == 0) {
+          float acc = 0.f;
+#pragma unroll
+          for (int i = 0; i < NW; ++i) acc += sred[i];
+          a.dslope_part[(size_t)bh * a.nblk + kb] = acc;
         }
       }
     }
-  }
+
+    // epilogue: lane holds column d = 32*db + n for keys kw0 + res_row(g, h)
+    const float scale = a.scale;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+#pragma unroll
+      for (int g = 0; g < 16; ++g) {
+        const int kr = kw0 + res_row(g, h);
+        if (kr < Nk) {
+          const size_t idx = ((size_t)bh * Nk + kr) * D + 32 * db + n;
+          if (a.grad_f32) {
+            static_cast<float*>(a.dk)[idx] = dk[db][g] * scale;
+            static_cast<float*>(a.dv)[idx] = dv[db][g];
+          } else {
+            static_cast<T*>(a.dk)[idx] = (T)(dk[db][g] * scale);
+            static_cast<T*>(a.dv)[idx] = (T)dv[db][g];
+          }
+        }
+      }
+    }
+    // rows summed: the two lanes of a key hold the sums of alternate row groups
+    if constexpr (TENSOR) {
+      if (rrows && dB != nullptr && m == n_mem - 1) {
+        const float tot = dbr + __shfl_xor(dbr, 32, 64);
+        if (h == 0 && key < Nk) dB[key] = tot;
+      }
+    }
+  }  // members
 }
 
 // ---------------------------------------------------------------------------------
@@ -827,10 +879,20 @@ static hipError_t launch_bwd_t(int bias, int phases, BwdArgs& a, hipStream_t st)
     constexpr int BK = 32 * DKDV_NW;
     BwdArgs b = a;
     b.nblk = (a.Nk + BK - 1) / BK;
-    b.sched = sched;
-    const dim3 grid((unsigned)(BH * b.nblk)), block(DKDV_NW * 64);
+    // a workgroup per dbias slice and key block: dbias summed over batches or heads
+    // makes one workgroup compute every (b, h) of its slice
+    int slots = BH;
+    if (bias == kBiasTensor && a.dbias != nullptr)
+      slots = ((a.db_red & FA_DBIAS_SUM_BATCH) ? 1 : a.B) *
+              ((a.db_red & FA_DBIAS_SUM_HEADS) ? 1 : a.H);
+    else
+      b.db_red = 0;
+    b.sched = (slots % 8 == 0) ? 1 : 0;
+    const dim3 grid((unsigned)(slots * b.nblk)), block(DKDV_NW * 64);
     const bool sparse = a.bmask != nullptr;
-    if (bias == kBiasTensor)
+    if (bias == kBiasTensor && slots != BH)
+      hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, kDkdvBR, DKDV_NW, DKDV_WPE, kBiasTensor, false, true>), grid, block, 0, st, b);
+    else if (bias == kBiasTensor)
       hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, kDkdvBR, DKDV_NW, DKDV_WPE, kBiasTensor, false>), grid, block, 0, st, b);
     else if (bias && sparse)
       hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, kDkdvBR, DKDV_NW, DKDV_WPE, kBiasSlope, true>), grid, block, 0, st, b);

@@ -953,9 +953,67 @@ __global__ __launch_bounds__(256) void fwd_merge_kernel(const float* __restrict_
     lse[r] = den > 0.f ? m + __builtin_amdgcn_logf(den) * kLn2 : kNegInf;
 }
 
+// The same merge with one workgroup per row, for many ranges: D/4 threads per group, G
+// groups; group g takes ranges g, g + G, ... (their loads are independent, so they
+// overlap), and the G partial sums are added in group order through LDS. With one
+// thread per float4 of a row and 64 ranges, the loop above waits for 64 loads one
+// after the other, which is most of a decode step with few heads.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void fwd_merge_wide_kernel(const float* __restrict__ o_part,
+                                                             const float* __restrict__ lse_part,
+                                                             T* __restrict__ o,
+                                                             float* __restrict__ lse, int rows,
+                                                             int n_split) {
+  constexpr int TPR = D / 4, G = 256 / TPR;
+  __shared__ float wmax[4];
+  __shared__ f32x4 acc_s[G][TPR];
+  __shared__ float den_s[G];
+  const int r = blockIdx.x, tid = threadIdx.x, g = tid / TPR, t = tid % TPR, c = 4 * t;
+  float m = kNegInf;
+  for (int s = tid; s < n_split; s += 256) m = __builtin_fmaxf(m, lse_part[(size_t)s * rows + r]);
+  m = wave_fmax(m);
+  if ((tid & 63) == 0) wmax[tid >> 6] = m;
+  __syncthreads();
+  m = __builtin_fmaxf(__builtin_fmaxf(wmax[0], wmax[1]), __builtin_fmaxf(wmax[2], wmax[3]));
+  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+  float den = 0.f;
+  if (m != kNegInf) {
+    for (int s = g; s < n_split; s += G) {
+      const float ls = lse_part[(size_t)s * rows + r];
+      if (ls == kNegInf) continue;  // nothing visible in that range
+      const float w = fast_exp2((ls - m) * kLog2e);
+      den += w;
+      const f32x4 x = *reinterpret_cast<const f32x4*>(o_part + ((size_t)s * rows + r) * D + c);
+      acc += w * x;
+    }
+  }
+  acc_s[g][t] = acc;
+  if (t == 0) den_s[g] = den;
+  __syncthreads();
+  if (g != 0) return;
+  for (int j = 1; j < G; ++j) {
+    acc += acc_s[j][t];
+    den += den_s[j];
+  }
+  const float inv = den > 0.f ? 1.f / den : 0.f;
+  using E = Elt<T>;
+  stg8(o + (size_t)r * D + c, u32x2{E::pack2(acc[0] * inv, acc[1] * inv),
+                                    E::pack2(acc[2] * inv, acc[3] * inv)});
+  if (t == 0 && lse != nullptr)
+    lse[r] = den > 0.f ? m + __builtin_amdgcn_logf(den) * kLn2 : kNegInf;
+}
+
+// Up to kMergeRowsSplit ranges: one thread per float4 of a row; more: a workgroup per row.
+constexpr int kMergeRowsSplit = 4;
+
 template <typename T, int D>
 static hipError_t launch_merge(const FwdArgs& a, hipStream_t st) {
   const int rows = a.B * a.H * a.Nq;
+  if (a.n_split > kMergeRowsSplit) {
+    hipLaunchKernelGGL((fwd_merge_wide_kernel<T, D>), dim3((unsigned)rows), dim3(256), 0, st,
+                       a.o_part, a.lse_part, static_cast<T*>(a.o), a.lse, rows, a.n_split);
+    return hipGetLastError();
+  }
   constexpr int RPB = 256 / (D / 4);
   hipLaunchKernelGGL((fwd_merge_kernel<T, D>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256),
                      0, st, a.o_part, a.lse_part, static_cast<T*>(a.o), a.lse, rows, a.n_split);

@@ -91,10 +91,12 @@ struct BwdArgs {
   const uint8_t* bmask;
   int bq, bk, nkb;
   long long bm_sb, bm_sh;
-  // bias tensor, as in FwdArgs; dbias (NULL: not wanted) dense [B,H,Nq,Nk] float32
+  // bias tensor, as in FwdArgs; dbias (NULL: not wanted) dense [B',H',Nq',Nk] float32,
+  // summed over the axes of db_red (FA_DBIAS_SUM_* bits)
   const float* tbias;
   long long tb_sb, tb_sh, tb_si;
   float* dbias;
+  int db_red;
 };
 
 // Bias modes of the kernels: none, slope * |i - j| generated on the fly, float32 tensor.

@@ -128,12 +128,22 @@ typedef enum fa_bias_kind {
  *              block bitmap: FA_ERR_UNSUPPORTED.
  *  bias_stride_b, bias_stride_h, bias_stride_i : element strides, >= 0 (else FA_ERR_MASK);
  *              64 * bias_stride_i + N_k must stay below 2^30 (else FA_ERR_UNSUPPORTED).
- *  dbias :     DEVICE pointer to a dense float32 [B, H, N_q, N_k] array (4-byte aligned),
- *              or NULL. fa_bwd (and fa_bwd_phases with FA_BWD_DKDV) writes there the
- *              gradient of the loss with respect to every biased score, dS_{b,h,i,j}
- *              (zero where masked); for a bias broadcast over an axis the gradient of the
- *              shared values is the sum of dbias over that axis, left to the caller. Needs
- *              FA_BIAS_TENSOR (else FA_ERR_MASK). fa_fwd ignores it.
+ *  dbias :     DEVICE pointer to a dense float32 array (4-byte aligned), or NULL. fa_bwd
+ *              (and fa_bwd_phases with FA_BWD_DKDV) writes there the gradient of the loss
+ *              with respect to the bias: dS_{b,h,i,j}, the gradient with respect to each
+ *              biased score (zero where masked), summed over the axes that dbias_reduce
+ *              names. Needs FA_BIAS_TENSOR (else FA_ERR_MASK). fa_fwd ignores it.
+ *  dbias_reduce : 0, or an OR of FA_DBIAS_SUM_BATCH, FA_DBIAS_SUM_HEADS, FA_DBIAS_SUM_ROWS
+ *              (other bits, or nonzero without dbias: FA_ERR_MASK). dbias is dense
+ *              [B', H', N_q', N_k] with B' = 1 when batches are summed (else B), H' = 1
+ *              when heads are summed (else H), N_q' = 1 when query rows are summed (else
+ *              N_q): the gradient of a bias broadcast over those axes, e.g. [1, H, N_q, N_k]
+ *              for one bias matrix per head shared over the batch, [B, 1, 1, N_k] for a
+ *              per-key bias. Every element is written (zero where nothing is visible).
+ *              The sums run in a fixed order (batches, then heads, then rows), so the
+ *              result is deterministic. Summing batches or heads makes one workgroup
+ *              compute every (b, h) that shares a dbias slice, one after the other: the
+ *              dK/dV launch then has B' H' (not B H) times ceil(N_k / 128) workgroups.
  *  A row with no visible key (after causal, range and block masking) gets O = 0 and
  *  LSE = -inf. */
 #define FA_MAX_SPARSE_N 65536
@@ -154,7 +164,11 @@ typedef struct fa_mask_bias_desc {
   int64_t bias_stride_h;
   int64_t bias_stride_i;
   float* dbias;
+  int32_t dbias_reduce;
 } fa_mask_bias_desc;
+#define FA_DBIAS_SUM_BATCH 1
+#define FA_DBIAS_SUM_HEADS 2
+#define FA_DBIAS_SUM_ROWS 4
 
 /* Forward pass.
  *  q [B,H,N_q,d], k and v [B,H,N_k,d]: device, element type `dtype`.

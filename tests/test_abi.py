@@ -123,7 +123,7 @@ def test_block_mask_descriptor_validation():
     assert fwd(mb=ctypes.byref(d), dtype=fa.FA_F32) == 8  # 16-bit inputs only
     assert fwd(mb=ctypes.byref(d), Nk=65536 + 64) == 8    # beyond FA_MAX_SPARSE_N
     assert fwd(mb=ctypes.byref(d), Nq=65536 + 1) == 8
-    assert ctypes.sizeof(fa.MaskBiasDesc) == 112  # the C layout of fa_mask_bias_desc
+    assert ctypes.sizeof(fa.MaskBiasDesc) == 120  # the C layout of fa_mask_bias_desc
 
 
 def test_bias_tensor_descriptor_validation():
@@ -153,6 +153,16 @@ def test_bias_tensor_descriptor_validation():
     d.slopes = ctypes.cast(arr, ctypes.POINTER(ctypes.c_float))
     assert bwd(mb=ctypes.byref(d)) == 5
     assert bwd(mb=ctypes.byref(desc(bias=P + 1))) == 6
+    # dbias_reduce: known bits only, and only together with dbias (a valid descriptor
+    # passes on to the workspace check, which a 16-byte workspace fails: nothing launches)
+    for bits, status in ((fa.FA_DBIAS_SUM_BATCH | fa.FA_DBIAS_SUM_ROWS, 7), (7, 7), (8, 5),
+                         (-1, 5)):
+        d = desc()
+        d.dbias, d.dbias_reduce = P, bits
+        assert bwd(mb=ctypes.byref(d), wsb=16) == status, bits
+    d = desc()
+    d.dbias_reduce = fa.FA_DBIAS_SUM_HEADS
+    assert bwd(mb=ctypes.byref(d)) == 5
 
 
 def bwd(**kw):

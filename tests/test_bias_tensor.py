@@ -217,6 +217,110 @@ def test_backward_and_dbias_match_oracle(dtype, d, causal, nq, nk, kind, ninf, r
         assert torch.equal(a, b), what
 
 
+RED_CASES = [
+    # dtype, d, causal, nq, nk, summed axes (b batches, h heads, i query rows), -inf
+    # fraction, key ranges
+    (torch.bfloat16, 128, True, 300, 300, "b", 0.0, False),
+    (torch.float16, 64, False, 200, 333, "h", 0.05, False),
+    (torch.bfloat16, 128, False, 257, 300, "bh", 0.0, True),
+    (torch.bfloat16, 64, True, 257, 513, "i", 0.0, False),
+    (torch.float16, 128, True, 130, 200, "bhi", 0.0, True),
+    (torch.bfloat16, 128, False, 3, 1, "hi", 0.0, False),
+    (torch.float16, 64, True, 200, 70, "bi", 0.1, False),
+]
+
+
+@pytest.mark.parametrize("dtype,d,causal,nq,nk,axes,ninf,ranged", RED_CASES)
+def test_dbias_summed_over_broadcast_axes(dtype, d, causal, nq, nk, axes, ninf, ranged):
+    # a bias broadcast over some axes (size 1 there): a dbias of the bias's own shape
+    # receives dS summed over those axes. Bound: the sum of the per-element bounds plus
+    # the float32 rounding of a sum of n terms (n 2^-23 times the sum of |dS|).
+    B, H = 2, 3
+    seed = 4100 + nq + 7 * nk + d
+    q, k, v, do = (normal((B, H, n, d), dtype, seed + i) for i, n in enumerate((nq, nk, nk, nq)))
+    shape = (1 if "b" in axes else B, 1 if "h" in axes else H, 1 if "i" in axes else nq, nk)
+    bias = bias_tensor(shape, seed + 5, 2.0, ninf)
+    kw = {}
+    ks = ke = None
+    if ranged:
+        ks, ke = key_ranges(nq, nk, seed=seed + 6, block=64, width=max(nk // 2, 1), jitter=16)
+        kw = dict(key_start=ks.to(DEV), key_end=ke.to(DEV))
+    scale = 1.0 / math.sqrt(d)
+    qd, kd, vd, dod, bd = (t.to(DEV) for t in (q, k, v, do, bias))
+    o, lse = fa.fa_fwd(qd, kd, vd, causal=causal, scale=scale, bias=bd, **kw)
+    dbias = torch.full(shape, float("nan"), dtype=torch.float32, device=DEV)
+    dq, dk, dv = fa.fa_bwd(dod, qd, kd, vd, o, lse, causal=causal, scale=scale, bias=bd,
+                           dbias=dbias, **kw)
+    torch.cuda.synchronize()
+    ksn = None if ks is None else ks.numpy()
+    ken = None if ke is None else ke.numpy()
+    want = oracle.attention_backward(np64(q), np64(k), np64(v), np64(do), scale, causal=causal,
+                                     bias=bias.double().numpy(), key_start=ksn, key_end=ken,
+                                     return_dbias=True)
+    what = f"dbias summed over {axes}: {dtype} d{d} c{causal} {nq}x{nk}"
+    check((dq, dk, dv), want[:3], ("dQ", "dK", "dV"), what)
+    red = tuple(ax for ax, c in enumerate("bhi") if c in axes)
+    n_terms = int(np.prod([(B, H, nq)[ax] for ax in red]))
+    tol, masked = dbias_tol(np64(q), np64(k), np64(v), np64(do), scale, causal,
+                            bias.double().numpy(), ksn, ken)
+    ref = want[3].sum(axis=red, keepdims=True)
+    bound = (tol.sum(axis=red, keepdims=True)
+             + n_terms * 2.0 ** -23 * np.abs(want[3]).sum(axis=red, keepdims=True))
+    g = np64(dbias)
+    assert g.shape == ref.shape and np.isfinite(g).all(), what
+    err = np.abs(g - ref)
+    worst = np.unravel_index(np.argmax(err - bound), err.shape)
+    assert np.all(err <= bound), (f"{what}: {err[worst]:.3e} > {bound[worst]:.3e} at "
+                                  f"{tuple(int(x) for x in worst)}")
+    # an element whose every summand is masked is exactly zero
+    assert np.all(g[masked.all(axis=red, keepdims=True)] == 0), what
+    # deterministic, and the gradients are the same bits as without dbias
+    dbias2 = torch.full(shape, float("nan"), dtype=torch.float32, device=DEV)
+    g2 = fa.fa_bwd(dod, qd, kd, vd, o, lse, causal=causal, scale=scale, bias=bd, dbias=dbias2,
+                   **kw)
+    g3 = fa.fa_bwd(dod, qd, kd, vd, o, lse, causal=causal, scale=scale, bias=bd, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(dbias, dbias2), what
+    for a, b2, b3 in zip((dq, dk, dv), g2, g3):
+        assert torch.equal(a, b2) and torch.equal(a, b3), what
+
+
+def test_dbias_shape_is_checked():
+    q = torch.zeros((2, 3, 64, 64), dtype=torch.bfloat16, device=DEV)
+    o, lse = fa.fa_fwd(q, q, q)
+    bias = torch.zeros((1, 3, 64, 64), dtype=torch.float32, device=DEV)
+    for shape in ((2, 2, 64, 64), (1, 3, 64, 63), (3, 64, 64)):
+        with pytest.raises(ValueError):
+            fa.fa_bwd(q, q, q, q, o, lse, bias=bias,
+                      dbias=torch.zeros(shape, dtype=torch.float32, device=DEV))
+
+
+def test_full_size_dbias_summed_over_batch_equals_dense_sum():
+    # the bf16 B2 H8 N8192 d128 workload with key ranges and a bias shared over the batch
+    # ([1, H, N, N]): dbias of that shape equals the dense [B, H, N, N] dbias (whose parity
+    # the tests above establish) summed over the batch, up to one float32 rounding
+    w = WORKLOADS[4]
+    q, k, v, do = (t.to(DEV) for t in qkv_inputs(w, with_dout=True))
+    ks, ke = key_ranges(w.N_q, w.N_k, seed_for(w.wid, 9), block=128, width=w.N_k // 2, jitter=64)
+    bias = bias_tensor((1, w.H, w.N_q, w.N_k), seed_for(w.wid, 10), 1.0).to(DEV)
+    kw = dict(causal=w.causal, scale=w.scale, bias=bias, key_start=ks.to(DEV),
+              key_end=ke.to(DEV))
+    o, lse = fa.fa_fwd(q, k, v, **kw)
+    dense = torch.empty((w.B, w.H, w.N_q, w.N_k), dtype=torch.float32, device=DEV)
+    g1 = fa.fa_bwd(do, q, k, v, o, lse, dbias=dense, **kw)
+    summed = torch.full((1, w.H, w.N_q, w.N_k), float("nan"), dtype=torch.float32, device=DEV)
+    g2 = fa.fa_bwd(do, q, k, v, o, lse, dbias=summed, **kw)
+    torch.cuda.synchronize()
+    for a, b in zip(g1, g2):
+        assert torch.equal(a, b)
+    for h in range(w.H):
+        ref = dense[0, h].double() + dense[1, h].double()
+        err = (summed[0, h].double() - ref).abs()
+        bound = 2.0 ** -23 * (dense[0, h].double().abs() + dense[1, h].double().abs())
+        assert bool((err <= bound).all()), f"head {h}: {float((err - bound).max()):.3e}"
+    del dense, summed
+
+
 def test_zero_bias_agrees_with_no_bias():
     # an all-zero bias tensor gives the unbiased result (the two paths round the scores
     # differently: scaled before the row max here, after it without a bias)

@@ -117,3 +117,22 @@ def test_decode_shape_full_size(B, nq, nk):
         o_ref, lse_ref = oracle.attention_forward(one(q), one(k), one(v), scale, causal=True)
         assert_fwd_close(one(o), np64(lse[b:b + 1, h:h + 1]), o_ref, lse_ref, dtype,
                          f"decode {nq}x{nk} b{b} h{h}")
+
+
+def test_decode_few_heads_long_cache():
+    # one sequence, eight heads, one query row against 131072 keys: the automatic count
+    # cuts each head into many ranges, merged by one workgroup per row; the oracle checks
+    # every head
+    B, H, nq, nk, d = 1, 8, 1, 131072, 128
+    dtype = torch.bfloat16
+    assert fa.fa_fwd_split_count(B, H, nq, nk, d, 0) > 4
+    q = normal((B, H, nq, d), dtype, 90)
+    k = normal((B, H, nk, d), dtype, 91)
+    v = normal((B, H, nk, d), dtype, 92)
+    o, lse = run_split(q, k, v, 0, causal=True)
+    scale = 1.0 / math.sqrt(d)
+    for h in range(H):
+        one = lambda t: np64(t[:, h:h + 1])  # noqa: E731
+        o_ref, lse_ref = oracle.attention_forward(one(q), one(k), one(v), scale, causal=True)
+        assert_fwd_close(one(o), np64(lse[:, h:h + 1]), o_ref, lse_ref, dtype,
+                         f"decode B1 H8 1x{nk} h{h}")
