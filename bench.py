@@ -246,6 +246,7 @@ def main():
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic}
 
+    forms = backward_forms(fa, torch, q, k, v, do, o, lse, grads, ws, kw, bwd_flops)
     hbm = None if args.no_hbm_shapes else hbm_shapes(fa, torch)
     sparse = None if args.no_sparse else block_sparse(fa, torch, w, qkv_inputs)
     fp8 = None if args.no_fp8 else fp8_forward(fa, torch, w, qkv_inputs)
@@ -279,6 +280,7 @@ def main():
         "fwd_frac_of_bf16_peak": round(fwd_tflops / PEAK_BF16_TFLOPS, 4),
         "bwd_tflops": round(bwd_flops / (bwd_ms * 1e-3) / 1e12, 1),
         "kernels": kernels,
+        "backward_forms": forms,
         "roofline": roofline,
         "cpu_baseline": cpu,
         "hbm_shapes": hbm,
@@ -308,6 +310,21 @@ def time_us(torch, fn, reps=10, rounds=3):
         e1.synchronize()
         ts.append(e0.elapsed_time(e1) * 1e3 / reps)
     return sorted(ts)[len(ts) // 2]
+
+
+def backward_forms(fa, torch, q, k, v, do, o, lse, grads, ws, kw, bwd_flops):
+    """The whole backward of the main workload in its two forms, each timed by time_us:
+    dQ in a separate query-outer pass (deterministic; the timed step above), and dQ added
+    with float32 atomics inside the dK/dV pass (FA_BWD_DQ_ATOMIC)."""
+    fa.fa_fwd(q, k, v, out=o, lse=lse, **kw)
+    out = {}
+    for name, ph in (("separate_dq_pass", fa.FA_BWD_ALL),
+                     ("dq_atomics_in_dkdv_pass",
+                      fa.FA_BWD_PREP | fa.FA_BWD_DKDV | fa.FA_BWD_DQ_ATOMIC)):
+        us = time_us(torch, lambda: fa.fa_bwd(do, q, k, v, o, lse, grads=grads, workspace=ws,
+                                              phases=ph, **kw))
+        out[name] = {"bwd_us": round(us, 1), "bwd_tflops": round(bwd_flops / (us * 1e-6) / 1e12, 1)}
+    return out
 
 
 def hbm_shapes(fa, torch, only=""):

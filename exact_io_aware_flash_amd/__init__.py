@@ -26,7 +26,7 @@ __all__ = [
     "FA_NOALLOC_SCRATCH_BYTES",
     "fa_fp8_rows", "fa_fp8_quantize", "fa_fwd_fp8", "fa_attention_fp8",
     "FA_FP8_Q", "FA_FP8_K", "FA_FP8_V",
-    "FA_BWD_PREP", "FA_BWD_DKDV", "FA_BWD_DQ", "FA_BWD_ALL",
+    "FA_BWD_PREP", "FA_BWD_DKDV", "FA_BWD_DQ", "FA_BWD_ALL", "FA_BWD_DQ_ATOMIC",
     "FA_DBIAS_SUM_BATCH", "FA_DBIAS_SUM_HEADS", "FA_DBIAS_SUM_ROWS",
     "fa_status_string", "fa_version", "lib_path", "load_library",
 ]
@@ -40,6 +40,7 @@ FA_F32, FA_F16, FA_BF16 = 0, 1, 2
 FA_BIAS_NONE, FA_BIAS_DIST_LINEAR, FA_BIAS_TENSOR = 0, 1, 2
 FA_MAX_SLOPES = 256
 FA_BWD_PREP, FA_BWD_DKDV, FA_BWD_DQ, FA_BWD_ALL = 1, 2, 4, 7
+FA_BWD_DQ_ATOMIC = 8  # dQ by float32 atomics inside the dK/dV launch (see include/fa.h)
 FA_DBIAS_SUM_BATCH, FA_DBIAS_SUM_HEADS, FA_DBIAS_SUM_ROWS = 1, 2, 4
 FA_FP8_Q, FA_FP8_K, FA_FP8_V = 0, 1, 2
 FA_NOALLOC_SCRATCH_BYTES = 16 << 20  # include/fa.h

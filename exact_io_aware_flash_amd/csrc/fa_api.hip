@@ -371,7 +371,9 @@ fa_status bwd_check(int phases, const void* q, const void* k, const void* v, con
                     const float* lse, const void* dout, void* dq, void* dk, void* dv,
                     fa_dtype grad_dtype, int B, int H, int N_q, int N_k, int d, float scale,
                     const fa_mask_bias_desc* mb, fa_dtype dtype, int& bias, BwdArgs& a) {
-  if (phases < 1 || (phases & ~FA_BWD_ALL) != 0) return FA_ERR_ARG;
+  if (phases < 1 || (phases & ~(FA_BWD_ALL | FA_BWD_DQ_ATOMIC)) != 0) return FA_ERR_ARG;
+  const bool dqa = (phases & FA_BWD_DQ_ATOMIC) != 0;
+  if (dqa && ((phases & FA_BWD_DKDV) == 0 || (phases & FA_BWD_DQ) != 0)) return FA_ERR_ARG;
   fa_status st = check_common(B, H, N_q, N_k, d, scale, raw(dtype));
   if (st != FA_OK) return st;
   if (raw(grad_dtype) != FA_F32 && raw(grad_dtype) != raw(dtype)) return FA_ERR_DTYPE;
@@ -396,6 +398,9 @@ fa_status bwd_check(int phases, const void* q, const void* k, const void* v, con
     const int all = FA_DBIAS_SUM_BATCH | FA_DBIAS_SUM_HEADS | FA_DBIAS_SUM_ROWS;
     if (mb->dbias == nullptr || (mb->dbias_reduce & ~all) != 0) return FA_ERR_MASK;
   }
+  if (dqa && (raw(grad_dtype) != FA_F32 || raw(dtype) == FA_F32 || a.bmask != nullptr ||
+              bias == kBiasTensor))
+    return FA_ERR_UNSUPPORTED;
   return FA_OK;
 }
 

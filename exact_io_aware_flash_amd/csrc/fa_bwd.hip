@@ -104,8 +104,11 @@ struct DkdvLds {
 #define FA_DKDV_STAGES 2
 #endif
 
-// MEM: dbias summed over batches and/or heads (bias tensor only): the member loop below
-template <typename T, int D, int BR, int NW, int WPE, int BM, bool SPARSE, bool MEM = false>
+// MEM: dbias summed over batches and/or heads (bias tensor only): the member loop below.
+// DQA: the pass also forms dQ = scale dS K for its keys and adds it into the float32 dq
+// with atomics (no bias tensor, no bitmap).
+template <typename T, int D, int BR, int NW, int WPE, int BM, bool SPARSE, bool MEM = false,
+          bool DQA = false>
 __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
                           amdgpu_waves_per_eu(WPE, WPE)))
 void bwd_dkdv_kernel(const BwdArgs a) {
@@ -124,10 +127,17 @@ void bwd_dkdv_kernel(const BwdArgs a) {
   // with the bias tensor the loop's only wait is the full one (the dbias stores count
   // in the same counter as the direct loads)
   static_assert(!TENSOR || ST == 2, "bias tensor: one tile in flight");
+  // dQ by atomics: one tile in flight (its waits are full ones: the atomics count in the
+  // same counter as the direct loads)
+  static_assert(!DQA || (!TENSOR && !SPARSE && ST == 2), "dQ atomics: plain or slope bias");
   static_assert(P * kOpsPerTile < 64, "vmcnt range");
   static_assert(ST * kStage <= 160 * 1024, "LDS budget");
   __shared__ __attribute__((aligned(1024))) char smem[ST * kStage];
   __shared__ int win[2];
+  // dQ by atomics: dS^T of a query tile (BK keys x BR queries, 16-bit, rows of 2 BR bytes
+  // swizzled like 64-column tiles), two buffers used by alternate tiles
+  constexpr int kDsBuf = BK * BR * 2;
+  __shared__ __attribute__((aligned(1024))) char dst_s[DQA ? 2 * kDsBuf : 16];
 
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6, n = lane & 31, h = lane >> 5;
   const int wid_s = wave_id();  // the same index as a scalar, for LDS window bases
@@ -180,6 +190,37 @@ void bwd_dkdv_kernel(const BwdArgs a) {
         vf[ks] = ldg16(V + r * D + 16 * ks + 8 * h);
       }
     }
+
+    // dQ by atomics: wave w forms the d columns 32 dbw .. 32 dbw + 31 of dQ (both 32-row
+    // blocks of a tile for d = 128; block w / 2 for d = 64) over the workgroup's BK keys.
+    // kt[s]: its B operands K^T (keys 16s + 8p + 4h + i, i < 4, p < 2, as the transposing
+    // reads deliver them), gathered once from the block's K rows staged in ring stage 0,
+    // which the prologue below has not yet filled.
+    constexpr int NS = DQA ? BK / 16 : 1;
+    const int dbw = wid_s % DB;
+    const int q4 = (lane >> 2) & 3, g16 = (lane >> 4) & 1, lo2 = lane & 3;
+    u32x4 kt[NS];
+    if constexpr (DQA) {
+      wait_vmem<0>();
+      const int rr = 32 * wid + n;
+#pragma unroll
+      for (int ks = 0; ks < DK; ++ks) lds_st16(smem, rr * RB + 16 * ((2 * ks + h) ^ swz<D>(rr)), kf[ks]);
+      __syncthreads();
+      int o2[2];
+#pragma unroll
+      for (int pp = 0; pp < 2; ++pp) {
+        const int r = 8 * pp + 4 * h + q4;
+        o2[pp] = r * RB + 16 * ((4 * dbw + 2 * g16 + (lo2 >> 1)) ^ swz<D>(r)) + 8 * (lo2 & 1);
+      }
+#pragma unroll
+      for (int s2 = 0; s2 < NS; ++s2) {
+        const u32x2 lo = lds_ld8_tr(smem, 16 * s2 * RB + o2[0]);
+        const u32x2 hi = lds_ld8_tr(smem, 16 * s2 * RB + o2[1]);
+        kt[s2] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+      }
+      __syncthreads();  // every wave holds its fragments before the ring reuses the stage
+    }
+    char* dsw = dst_s;  // dS^T buffer the current tile writes
 
     // query tiles that can see a key of this block
     const int nqt = (Nq + BR - 1) / BR;
@@ -330,6 +371,15 @@ void bwd_dkdv_kernel(const BwdArgs a) {
       }
 #pragma unroll
       for (int g = 0; g < 16; ++g) ds[g] = p[g] * (dp[g] - d4[g / 4][g % 4]);
+      if constexpr (DQA) {
+        // dS^T row 32 w + n (this lane's key), queries 32 qb + 8 t4 + 4 h + (0..3)
+        const int rr = 32 * wid_s + n;
+#pragma unroll
+        for (int t4 = 0; t4 < 4; ++t4)
+          lds_st8(dsw, rr * (2 * BR) + 16 * ((4 * qb + t4) ^ swz<64>(rr)) + 8 * h,
+                  u32x2{E::pack2(ds[4 * t4], ds[4 * t4 + 1]),
+                        E::pack2(ds[4 * t4 + 2], ds[4 * t4 + 3])});
+      }
       if constexpr (TENSOR) {
         // dbias = dS (zero where masked: p = 0 there); lanes 0-31 and 32-63 each store 128
         // contiguous bytes of one row. Rows summed: the lane adds its 16 rows.
@@ -406,7 +456,43 @@ void bwd_dkdv_kernel(const BwdArgs a) {
       else if (P >= 2 && later == 2) wait_vmem<(P >= 2 ? 2 : 0) * kOpsPerTile>();
       else if (later == 1) wait_vmem<kOpsPerTile>();
       else wait_vmem<0>();
-      __builtin_amdgcn_s_barrier();
+      if constexpr (DQA) __syncthreads();  // the dS^T stores too
+      else __builtin_amdgcn_s_barrier();
+    };
+    // dQ of ring position pp from its dS^T (written by every wave before the barrier that
+    // ended that position): 8 products over 16 keys each per 32-row block, then one
+    // float32 atomic add per element into dq
+    auto dq_tile = [&](int pp) {
+      const char* dsr = dst_s + (pp & 1) * kDsBuf;
+      const int q0p = tile_at(pp) * BR;
+      float* dqp = static_cast<float*>(a.dq) + (size_t)bh * Nq * D + 32 * dbw + n;
+      for (int u = wid_s; u < DB * QB; u += NW) {
+        const int qb = u / DB;
+        int oa[2];
+#pragma unroll
+        for (int pp2 = 0; pp2 < 2; ++pp2) {
+          const int r = 8 * pp2 + 4 * h + q4;
+          oa[pp2] = r * (2 * BR) + 16 * ((4 * qb + 2 * g16 + (lo2 >> 1)) ^ swz<64>(r)) +
+                    8 * (lo2 & 1);
+        }
+        u32x4 af[NS];
+#pragma unroll
+        for (int s2 = 0; s2 < NS; ++s2) {
+          const u32x2 lo = lds_ld8_tr(dsr, 16 * s2 * (2 * BR) + oa[0]);
+          const u32x2 hi = lds_ld8_tr(dsr, 16 * s2 * (2 * BR) + oa[1]);
+          af[s2] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+        }
+        sched_fence();
+        f32x16 acc = f32x16{};
+#pragma unroll
+        for (int s2 = 0; s2 < NS; ++s2) acc = E::mma(af[s2], kt[s2], acc);
+        const float scale = a.scale;
+#pragma unroll
+        for (int g = 0; g < 16; ++g) {
+          const int qi = q0p + 32 * qb + res_row(g, h);
+          if (qi < Nq) unsafeAtomicAdd(dqp + (size_t)qi * D, acc[g] * scale);
+        }
+      }
     };
     // zero dbias of query tile t for this wave's keys (lanes 0-31 and 32-63: alternate rows)
     // (only the first member: later ones add nothing there; rows summed: written at the end)
@@ -436,6 +522,10 @@ void bwd_dkdv_kernel(const BwdArgs a) {
       // barrier
       if constexpr (SPARSE) lw.slide(p);
       if (p + P < n_pos) issue(p + P);
+      if constexpr (DQA) {
+        if (p > 0) dq_tile(p - 1);
+        dsw = dst_s + (p & 1) * kDsBuf;
+      }
       const int t = tile_at(p);
       const int q0t = t * BR;
       const char* sb = stage_of(p);
@@ -481,7 +571,20 @@ void bwd_dkdv_kernel(const BwdArgs a) {
       } else if constexpr (TENSOR) {
         zero_dbias_tile(t);
       }
+      if constexpr (DQA) {
+        if (skip) {  // no key of this wave visible: its dS^T rows are zero
+          const int rr = 32 * wid_s + (lane >> 1);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) lds_st16(dsw, rr * (2 * BR) + 64 * (lane & 1) + 16 * j, u32x4{});
+        }
+      }
       if (p + 1 < n_pos) land(min(p + P, n_pos - 1) - (p + 1));
+    }
+    if constexpr (DQA) {
+      if (n_pos > 0) {
+        __syncthreads();
+        dq_tile(n_pos - 1);
+      }
     }
     // dbias of the query tiles outside the workgroup's window is zero (every (i, j) of this
     // wave's keys is then written exactly once: computed, or zero where nothing is visible)
@@ -856,6 +959,13 @@ __global__ void dslope_reduce_kernel(const float* __restrict__ part, int B, int 
   out[s] = acc;
 }
 
+// Clears n4 float4 (dq before the dK/dV pass adds into it with atomics; a kernel rather
+// than a memset node, so that a captured graph replays it correctly).
+__global__ __launch_bounds__(256) void zero_f32x4_kernel(f32x4* __restrict__ p, size_t n4) {
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += (size_t)gridDim.x * 256)
+    p[i] = f32x4{};
+}
+
 template <typename T, int D, int DKDV_NW, int DKDV_WPE, int DQ_BC, int DQ_NW, int DQ_WPE>
 static hipError_t launch_bwd_t(int bias, int phases, BwdArgs& a, hipStream_t st) {
   const int BH = a.B * a.H;
@@ -890,7 +1000,20 @@ static hipError_t launch_bwd_t(int bias, int phases, BwdArgs& a, hipStream_t st)
     b.sched = (slots % 8 == 0) ? 1 : 0;
     const dim3 grid((unsigned)(slots * b.nblk)), block(DKDV_NW * 64);
     const bool sparse = a.bmask != nullptr;
-    if (bias == kBiasTensor && slots != BH)
+    if (phases & FA_BWD_DQ_ATOMIC) {
+      const size_t n4 = (size_t)BH * a.Nq * D / 4;
+      const unsigned zb = (unsigned)std::min<size_t>((n4 + 255) / 256, 4096);
+      hipLaunchKernelGGL(zero_f32x4_kernel, dim3(zb), dim3(256), 0, st,
+                         static_cast<f32x4*>(a.dq), n4);
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+    if (phases & FA_BWD_DQ_ATOMIC) {
+      if (bias)
+        hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, kDkdvBR, DKDV_NW, DKDV_WPE, kBiasSlope, false, false, true>), grid, block, 0, st, b);
+      else
+        hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, kDkdvBR, DKDV_NW, DKDV_WPE, kBiasNone, false, false, true>), grid, block, 0, st, b);
+    } else if (bias == kBiasTensor && slots != BH)
       hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, kDkdvBR, DKDV_NW, DKDV_WPE, kBiasTensor, false, true>), grid, block, 0, st, b);
     else if (bias == kBiasTensor)
       hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, kDkdvBR, DKDV_NW, DKDV_WPE, kBiasTensor, false>), grid, block, 0, st, b);

@@ -275,13 +275,25 @@ FA_API fa_status fa_bwd(const void* q, const void* k, const void* v, const void*
  *  FA_BWD_PREP: D = rowsum(dO * O) and the key-range summary, into the workspace;
  *  FA_BWD_DKDV: dK and dV (needs a completed FA_BWD_PREP on the same workspace);
  *  FA_BWD_DQ:   dQ (needs a completed FA_BWD_PREP on the same workspace).
+ *  FA_BWD_DQ_ATOMIC (with FA_BWD_DKDV, in place of FA_BWD_DQ): the dK/dV launch also
+ *               forms dQ = scale dS K for its block of keys and adds it into dq with
+ *               float32 atomic adds; dq must be float32 (grad_dtype FA_F32) and is cleared
+ *               by the call first. The order of the additions varies from run to run, so
+ *               dQ is not bitwise reproducible (dK, dV are). 16-bit inputs without a
+ *               block bitmap or a bias tensor (else FA_ERR_UNSUPPORTED); without
+ *               FA_BWD_DKDV, or together with FA_BWD_DQ: FA_ERR_ARG. This is the
+ *               recomputation backward with the dQ accumulation kept in the key-outer
+ *               pass (marketmaker.cc attention page, the section on the backward pass
+ *               recomputing rather than storing); FA_BWD_DQ recomputes S and dP in a
+ *               query-outer pass instead, deterministically.
  *  Phases given together run in that order. fa_bwd(...) is fa_bwd_phases(FA_BWD_ALL, ...).
- *  `phases` must be a non-empty subset of FA_BWD_ALL (else FA_ERR_ARG); the other
- *  arguments are validated exactly as for fa_bwd. */
+ *  `phases` must be a non-empty subset of FA_BWD_ALL | FA_BWD_DQ_ATOMIC (else
+ *  FA_ERR_ARG); the other arguments are validated exactly as for fa_bwd. */
 #define FA_BWD_PREP 1
 #define FA_BWD_DKDV 2
 #define FA_BWD_DQ 4
 #define FA_BWD_ALL 7
+#define FA_BWD_DQ_ATOMIC 8
 FA_API fa_status fa_bwd_phases(int phases, const void* q, const void* k, const void* v,
                                const void* o, const float* lse, const void* dout, void* dq,
                                void* dk, void* dv, fa_dtype grad_dtype, void* workspace,

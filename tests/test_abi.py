@@ -188,6 +188,32 @@ def test_bwd_rejects_invalid_arguments(kw, status):
     assert bwd(**kw) == status
 
 
+def test_bwd_atomic_dq_phase_validation():
+    A = fa.FA_BWD_DQ_ATOMIC
+    assert bwd_phases(A) == 10                                   # without the dK/dV pass
+    assert bwd_phases(fa.FA_BWD_ALL | A) == 10                   # with the separate dQ pass
+    assert bwd_phases(16) == 10
+    assert bwd_phases(fa.FA_BWD_DKDV | A, gdt=fa.FA_BF16) == 8   # float32 dq only
+    assert bwd_phases(fa.FA_BWD_DKDV | A, dtype=fa.FA_F32) == 8
+    d = fa.MaskBiasDesc()
+    d.block_mask, d.block_q, d.block_k = P, 64, 64
+    assert bwd_phases(fa.FA_BWD_DKDV | A, mb=ctypes.byref(d)) == 8
+    # a valid request reaches the workspace check (16 bytes: too small, nothing launches)
+    assert bwd_phases(fa.FA_BWD_PREP | fa.FA_BWD_DKDV | A, wsb=16) == 7
+
+
+def bwd_phases(phases, **kw):
+    lib = fa.load_library()
+    a = dict(q=P, k=P, v=P, o=P, lse=P, do=P, dq=P, dk=P, dv=P, gdt=fa.FA_F32, ws=P, wsb=1 << 20,
+             B=1, H=1, Nq=16, Nk=16, d=128, scale=0.1, causal=1, mb=None, dtype=fa.FA_BF16,
+             stream=None)
+    a.update(kw)
+    return lib.fa_bwd_phases(phases, a["q"], a["k"], a["v"], a["o"], a["lse"], a["do"], a["dq"],
+                             a["dk"], a["dv"], a["gdt"], a["ws"], a["wsb"], a["B"], a["H"],
+                             a["Nq"], a["Nk"], a["d"], a["scale"], a["causal"], a["mb"],
+                             a["dtype"], a["stream"])
+
+
 @pytest.mark.parametrize("args,status", [
     ((None, P, 10, 10, 4, P, None), 1),
     ((P, P, 0, 10, 4, P, None), 2),
