@@ -29,7 +29,7 @@ COMMON = [
     "-I", INCLUDE, "-I", CSRC, "-Wall", "-Wno-unused-function",
 ]
 
-SOURCES = ["fa_api.hip", "fa_fwd.hip", "fa_bwd.hip", "fa_fp8.hip"]
+SOURCES = ["fa_api.hip", "fa_fwd.hip", "fa_bwd.hip", "fa_bwd32.hip", "fa_fp8.hip"]
 
 
 def _compile(src: str, obj: str, extra=()) -> str:

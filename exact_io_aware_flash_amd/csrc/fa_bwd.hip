@@ -31,12 +31,6 @@ namespace fa {
 // ---------------------------------------------------------------------------------
 // 1. D = rowsum(dO * O)
 // ---------------------------------------------------------------------------------
-// Exponent offset of a row in the recomputed probabilities, p = exp2(s * scale * log2(e)
-// + bias * log2(e) - offset). A row with no visible key has LSE = -inf (its output is 0);
-// its offset is +inf, so every probability of the row is exactly 0 whatever the bias
-// (-inf - (-inf) would be NaN, and a finite score minus -inf would be +inf).
-__device__ inline float lse_offset2(float lse) { return lse == kNegInf ? -kNegInf : lse * kLog2e; }
-
 // Also writes the exponent offset per row (lse_offset2: LSE * log2(e)), which the dK/dV
 // pass reads.
 template <typename T, int D>
@@ -928,7 +922,6 @@ void bwd_dq_kernel(const BwdArgs a) {
 // ---------------------------------------------------------------------------------
 // launch
 // ---------------------------------------------------------------------------------
-constexpr int kDkdvBR = 64;  // query rows per LDS tile of the dK/dV pass
 
 size_t bwd_qsum_offset(int B, int H, int Nq) {
   return (((size_t)B * H * Nq * sizeof(float)) + 255) & ~(size_t)255;
@@ -947,7 +940,7 @@ size_t bwd_workspace_bytes(int B, int H, int Nq, int Nk) {
 
 // dL/dslope from the dK/dV pass's per-workgroup partials, one thread per slope, summed in
 // a fixed order (batch, then key block; all heads for a shared slope)
-__global__ void dslope_reduce_kernel(const float* __restrict__ part, int B, int H, int nblk,
+static __global__ void dslope_reduce_kernel(const float* __restrict__ part, int B, int H, int nblk,
                                      int n_slopes, float* __restrict__ out) {
   const int s = threadIdx.x;
   if (s >= n_slopes) return;
@@ -1028,9 +1021,7 @@ static hipError_t launch_bwd_t(int bias, int phases, BwdArgs& a, hipStream_t st)
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (bias == kBiasSlope && a.dslopes != nullptr) {
-      hipLaunchKernelGGL(dslope_reduce_kernel, dim3(1), dim3(FA_MAX_SLOPES), 0, st,
-                         b.dslope_part, a.B, a.H, b.nblk, a.n_slopes, a.dslopes);
-      e = hipGetLastError();
+      e = launch_dslope_reduce(b.dslope_part, a.B, a.H, b.nblk, a.n_slopes, a.dslopes, st);
       if (e != hipSuccess) return e;
     }
   }
@@ -1067,9 +1058,18 @@ hipError_t launch_bwd(fa_dtype dt, int d, int bias, int phases, BwdArgs& a, hipS
     case FA_F16:
       return d == 128 ? launch_bwd_t<_Float16, 128, 4, 1, 64, 8, 2>(bias, phases, a, st)
                       : launch_bwd_t<_Float16, 64, 4, 1, 128, 8, 2>(bias, phases, a, st);
+    case FA_F32:
+      return launch_bwd32(d, bias, phases, a, st);
     default:
-      return hipErrorNotSupported;  // float32 backward is not implemented
+      return hipErrorNotSupported;
   }
+}
+
+hipError_t launch_dslope_reduce(const float* part, int B, int H, int nblk, int n_slopes,
+                                float* out, hipStream_t st) {
+  hipLaunchKernelGGL(dslope_reduce_kernel, dim3(1), dim3(FA_MAX_SLOPES), 0, st, part, B, H, nblk,
+                     n_slopes, out);
+  return hipGetLastError();
 }
 
 }  // namespace fa

@@ -21,6 +21,7 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
@@ -97,6 +98,13 @@ __device__ inline float xhalf_max(float v) { return __builtin_fmaxf(v, xhalf(v))
 __device__ inline float xhalf_sum(float v) { return v + xhalf(v); }
 
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Exponent offset of a row in the recomputed probabilities of the backward passes,
+// p = exp2(s * scale * log2(e) + bias * log2(e) - offset). A row with no visible key has
+// LSE = -inf (its output is 0); its offset is +inf, so every probability of the row is
+// exactly 0 whatever the bias (-inf - (-inf) would be NaN, and a finite score minus -inf
+// would be +inf).
+__device__ inline float lse_offset2(float lse) { return lse == kNegInf ? -kNegInf : lse * kLog2e; }
 
 __device__ inline bool wave_any(bool p) { return __builtin_amdgcn_ballot_w64(p) != 0; }
 

@@ -107,6 +107,14 @@ hipError_t launch_fwd(fa_dtype dt, int d, int bias_mode, FwdArgs& a, hipStream_t
 // Tiles of the block-sparse forward list per workgroup (keys per tile >= 32).
 constexpr int kSparseMaxTiles = FA_MAX_SPARSE_N / 32;
 hipError_t launch_bwd(fa_dtype dt, int d, int bias_mode, int phases, BwdArgs& a, hipStream_t st);
+// float32 inputs (fa_bwd32.hip): prep, dK/dV and dQ passes on float32 MFMA
+hipError_t launch_bwd32(int d, int bias_mode, int phases, BwdArgs& a, hipStream_t st);
+// dL/dslope from the dK/dV pass's per-workgroup partials [B*H][nblk], in a fixed order
+hipError_t launch_dslope_reduce(const float* part, int B, int H, int nblk, int n_slopes,
+                                float* out, hipStream_t st);
+// query rows per LDS tile of the 16-bit dK/dV pass: the granularity of the key-range
+// summary in the backward workspace
+constexpr int kDkdvBR = 64;
 hipError_t launch_mask_summary(const int32_t* ks, const int32_t* ke, int Nq, int Nk, int block,
                                int32_t* out, hipStream_t st);
 

@@ -264,7 +264,12 @@ FA_API size_t fa_bwd_workspace_bytes(int B, int H, int N_q, int N_k, int d);
  *  its contents on entry do not matter.
  *  Gradients of L = sum(O * dout): dV = P^T dO; dP = dO V^T; D_i = rowsum(dO_i * O_i);
  *  dS = P * (dP - D); dQ = scale * dS K; dK = scale * dS^T Q, with
- *  P = exp(S - LSE) recomputed tile by tile. No gradient flows to bias or mask. */
+ *  P = exp(S - LSE) recomputed tile by tile. No gradient flows to bias or mask (dbias and
+ *  dslopes in the descriptor ask for the bias gradients explicitly).
+ *  16-bit inputs: products on 16-bit MFMA with P and dS rounded to the input type,
+ *  float32 accumulation. float32 inputs: every product on float32 MFMA, nothing rounded
+ *  below float32 (gradients float32; dbias dense only: dbias_reduce != 0 gives
+ *  FA_ERR_UNSUPPORTED). The result is deterministic (a fixed order of every sum). */
 FA_API fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
                  const void* dout, void* dq, void* dk, void* dv, fa_dtype grad_dtype,
                  void* workspace, size_t workspace_bytes,

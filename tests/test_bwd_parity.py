@@ -109,14 +109,6 @@ def test_full_causal_bf16_n8192_backward():
         check_grads(got, want, f"{w.name} b{b} h{h}")
 
 
-def test_fp32_backward_reports_unsupported():
-    q = torch.zeros(1, 1, 8, 64, device=DEV)
-    o, lse = fa.fa_fwd(q, q, q)
-    with pytest.raises(fa.FaError) as e:
-        fa.fa_bwd(q, q, q, q, o, lse)
-    assert e.value.status == 8
-
-
 @pytest.mark.parametrize("dtype,d", [(torch.bfloat16, 128), (torch.float16, 64)])
 @pytest.mark.parametrize("causal,ranged,per_head", [(True, False, True), (False, True, False),
                                                     (True, True, True)])
