@@ -40,10 +40,10 @@ PEAK_FP8_TFLOPS = 2 * PEAK_BF16_TFLOPS  # dense E4M3 MFMA (published 5.0 PFLOP/s
 # the kernel source they were measured on. A changed source means stale counters -> null.
 TRAFFIC = {
     # kernel: (source hash, bytes read, bytes written) -- profiles/attention_fwd_bwd_bf16_causal_B2H16N8192d128.md
-    "fwd": ("95f972e2f93c5058", 292.7e6, 68.2e6),
-    "bwd_prep": ("e457124e31a2aaa3", 136.3e6, 2.1e6),
-    "bwd_dkdv": ("e457124e31a2aaa3", 270.9e6, 268.4e6),
-    "bwd_dq": ("e457124e31a2aaa3", 411.5e6, 138.2e6),
+    "fwd": ("47e58733019d059a", 282.0e6, 68.2e6),
+    "bwd_prep": ("5605dc2e8bd54061", 136.3e6, 2.1e6),
+    "bwd_dkdv": ("5605dc2e8bd54061", 270.9e6, 268.4e6),
+    "bwd_dq": ("5605dc2e8bd54061", 397.2e6, 138.2e6),
 }
 
 
