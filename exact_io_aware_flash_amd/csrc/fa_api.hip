@@ -320,7 +320,6 @@ fa_status fa_fwd_split(const void* q, const void* k, const void* v, void* o, flo
   if (!q || !k || !v || !o) return FA_ERR_NULL;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return FA_ERR_ALIGN;
   if (lse != nullptr && (reinterpret_cast<uintptr_t>(lse) & 3u)) return FA_ERR_ALIGN;
-  if (dtype == FA_F32) return FA_ERR_UNSUPPORTED;
   if (workspace == nullptr ||
       workspace_bytes < fa_fwd_split_workspace_bytes(B, H, N_q, N_k, d, n_split))
     return FA_ERR_WORKSPACE;

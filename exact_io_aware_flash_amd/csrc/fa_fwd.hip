@@ -93,8 +93,10 @@ void fwd_kernel(const FwdArgs a) {
   const bool causal = a.causal != 0;
   const bool ranged = a.key_start != nullptr;
 
-  int bh, qb;
-  map_block(blockIdx.x, a.B * a.H, a.nqb, a.sched, true, bh, qb);
+  // work unit = (b, h, query block, key range); heaviest query blocks first
+  int bh, unit;
+  map_block(blockIdx.x, a.B * a.H, a.nqb * a.n_split, a.sched, true, bh, unit);
+  const int qb = unit / a.n_split, split = unit - qb * a.n_split;
   const int head = bh % a.H;
   const int q0 = qb * C::kBR;
   const T* __restrict__ Q = static_cast<const T*>(a.q) + (size_t)bh * Nq * D;
@@ -147,6 +149,10 @@ void fwd_kernel(const FwdArgs a) {
   if (ranged) {
     w_lo = max(w_lo, w_min_s);
     w_hi = min(w_hi, w_max_e);
+  }
+  if (a.n_split > 1) {  // this unit's key range (whole tiles)
+    w_lo = max(w_lo, split * a.split_keys);
+    w_hi = min(w_hi, (split + 1) * a.split_keys);
   }
   if (!wave_live || w_hi <= w_lo) { w_lo = Nk; w_hi = 0; }
   if (lane == 0) { wg_win[wid][0] = w_lo; wg_win[wid][1] = w_hi; }
@@ -443,7 +449,22 @@ void fwd_kernel(const FwdArgs a) {
     const float lt = l[qs] + xhalf(l[qs]);
     const float inv = lt > 0.f ? 1.f / lt : 0.f;
     const int row = qrow[qs];
-    if (row < Nq) {
+    if (row < Nq && a.n_split > 1) {
+      // normalised float32 partial of this key range and its LSE (nothing visible in the
+      // range: O = 0, LSE = -inf, which gives it zero weight in the merge)
+      const size_t prow = (size_t)split * ((size_t)a.B * a.H * Nq) + (size_t)bh * Nq + row;
+#pragma unroll
+      for (int db = 0; db < C::kDB; ++db)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int d0 = db * 32 + 8 * g4 + 4 * h;
+          *reinterpret_cast<f32x4*>(a.o_part + prow * D + d0) =
+              f32x4{o[qs][db][4 * g4] * inv, o[qs][db][4 * g4 + 1] * inv,
+                    o[qs][db][4 * g4 + 2] * inv, o[qs][db][4 * g4 + 3] * inv};
+        }
+      if (h == 0)
+        a.lse_part[prow] = lt > 0.f ? (m2[qs] + __builtin_amdgcn_logf(lt)) * kLn2 : kNegInf;
+    } else if (row < Nq) {
 #pragma unroll
       for (int db = 0; db < C::kDB; ++db) {
 #pragma unroll
@@ -902,26 +923,44 @@ hipError_t launch_mask_summary(const int32_t* ks, const int32_t* ke, int Nq, int
 // ---------------------------------------------------------------------------------
 // tile configurations per (dtype, d) and the launcher
 // ---------------------------------------------------------------------------------
+template <typename T, int D>
+static hipError_t launch_merge(const FwdArgs& a, hipStream_t st);
+
 template <typename T, int D, int BC, int QSUB, int NW, int WPE>
 static hipError_t launch_cfg(int bias, FwdArgs& a, hipStream_t st) {
   using C = FwdCfg<T, D, BC, QSUB, NW>;
+  static_assert(kFwdTileKeys % BC == 0, "split ranges are whole tiles");
   a.nqb = (a.Nq + C::kBR - 1) / C::kBR;
+  if (a.n_split < 1) a.n_split = 1;
   const int BH = a.B * a.H;
   a.sched = (BH % 8 == 0) ? kSchedXcd : kSchedHeadMajor;
-  const dim3 grid((unsigned)(BH * a.nqb)), block(C::kNT);
+  const dim3 grid((unsigned)(BH * a.nqb * a.n_split)), block(C::kNT);
   if (bias == kBiasTensor)
     hipLaunchKernelGGL((fwd_kernel<T, D, BC, QSUB, NW, WPE, kBiasTensor>), grid, block, 0, st, a);
   else if (bias)
     hipLaunchKernelGGL((fwd_kernel<T, D, BC, QSUB, NW, WPE, kBiasSlope>), grid, block, 0, st, a);
   else
     hipLaunchKernelGGL((fwd_kernel<T, D, BC, QSUB, NW, WPE, kBiasNone>), grid, block, 0, st, a);
-  return hipGetLastError();
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.n_split == 1) return e;
+  return launch_merge<T, D>(a, st);
 }
 
 // ---------------------------------------------------------------------------------
 // Merge of split-key partials: LSE = log sum_r exp(LSE_r), O = sum_r exp(LSE_r - LSE) O_r.
 // D/4 threads per row, one float4 of the row each; n_split <= ceil(N_k / 64).
 // ---------------------------------------------------------------------------------
+// four merged output values in the output type (16-bit: rounded to nearest even)
+template <typename T>
+__device__ inline void store_merged(T* p, f32x4 v) {
+  if constexpr (sizeof(T) == 4) {
+    *reinterpret_cast<f32x4*>(p) = v;
+  } else {
+    using E = Elt<T>;
+    stg8(p, u32x2{E::pack2(v[0], v[1]), E::pack2(v[2], v[3])});
+  }
+}
+
 template <typename T, int D>
 __global__ __launch_bounds__(256) void fwd_merge_kernel(const float* __restrict__ o_part,
                                                         const float* __restrict__ lse_part,
@@ -946,9 +985,7 @@ __global__ __launch_bounds__(256) void fwd_merge_kernel(const float* __restrict_
     }
   }
   const float inv = den > 0.f ? 1.f / den : 0.f;
-  using E = Elt<T>;
-  stg8(o + (size_t)r * D + c, u32x2{E::pack2(acc[0] * inv, acc[1] * inv),
-                                    E::pack2(acc[2] * inv, acc[3] * inv)});
+  store_merged(o + (size_t)r * D + c, acc * inv);
   if (c == 0 && lse != nullptr)
     lse[r] = den > 0.f ? m + __builtin_amdgcn_logf(den) * kLn2 : kNegInf;
 }
@@ -996,9 +1033,7 @@ __global__ __launch_bounds__(256) void fwd_merge_wide_kernel(const float* __rest
     den += den_s[j];
   }
   const float inv = den > 0.f ? 1.f / den : 0.f;
-  using E = Elt<T>;
-  stg8(o + (size_t)r * D + c, u32x2{E::pack2(acc[0] * inv, acc[1] * inv),
-                                    E::pack2(acc[2] * inv, acc[3] * inv)});
+  store_merged(o + (size_t)r * D + c, acc * inv);
   if (t == 0 && lse != nullptr)
     lse[r] = den > 0.f ? m + __builtin_amdgcn_logf(den) * kLn2 : kNegInf;
 }

@@ -236,8 +236,7 @@ FA_API fa_status fa_fwd_tile_counts(const void* q, const void* k, const void* v,
  *           for the same sizes and n_split; contents on entry do not matter; the call
  *           overwrites it. Calls sharing one workspace must not overlap on the device.
  *  Errors: as fa_fwd; FA_ERR_WORKSPACE if the workspace is NULL or too small (effective
- *  count > 1); FA_ERR_UNSUPPORTED for float32 inputs with an effective count > 1;
- *  FA_ERR_ARG if n_split < 0. */
+ *  count > 1); FA_ERR_ARG if n_split < 0. */
 FA_API fa_status fa_fwd_split(const void* q, const void* k, const void* v, void* o, float* lse,
                               int B, int H, int N_q, int N_k, int d, float scale, int causal,
                               const fa_mask_bias_desc* mb, fa_dtype dtype, int n_split,

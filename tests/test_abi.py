@@ -274,7 +274,7 @@ def fwd_split(**kw):
 
 @pytest.mark.parametrize("kw,status", [
     (dict(n=-1), 10), (dict(q=None), 1), (dict(Nq=0), 2), (dict(d=80), 4),
-    (dict(dtype=fa.FA_F32), 8),
+    (dict(dtype=fa.FA_F32, wsb=1024), 7),  # float32 splits too: stops at the workspace
     (dict(ws=None), 7), (dict(wsb=1024), 7), (dict(ws=MIS), 6), (dict(v=MIS), 6),
     (dict(scale=float("nan")), 10),
     (dict(n=1, q=None), 1),  # effective count 1: validated as fa_fwd

@@ -37,6 +37,10 @@ CASES = [
     (3, 2, 1, 130, 128, False, torch.bfloat16, 2),   # second range holds 2 keys
     (1, 1, 300, 2000, 128, True, torch.bfloat16, 4),  # two query blocks, causal diagonal
     (1, 2, 33, 5000, 128, False, torch.float16, 5),   # 33 rows: a second, 1-row wave
+    # float32 inputs (float32 MFMA; 32-key tiles inside the 64-key-multiple ranges)
+    (2, 3, 1, 4096, 128, True, torch.float32, 0),
+    (1, 2, 40, 1000, 64, False, torch.float32, 7),
+    (1, 1, 300, 2000, 128, True, torch.float32, 4),
 ]
 
 
