@@ -105,7 +105,6 @@ fa_status read_desc(const fa_mask_bias_desc* mb, int H, int N_q, int N_k, fa_dty
     if (mb->bias == nullptr) return FA_ERR_NULL;
     if (reinterpret_cast<uintptr_t>(mb->bias) & 3u) return FA_ERR_ALIGN;
     if (mb->bias_stride_b < 0 || mb->bias_stride_h < 0 || mb->bias_stride_i < 0) return FA_ERR_MASK;
-    if (mb->block_mask != nullptr) return FA_ERR_UNSUPPORTED;
     // a bias tile (up to 64 rows) is addressed by 32-bit byte offsets from its first row
     if (mb->bias_stride_i * 64 + N_k >= (1LL << 30)) return FA_ERR_UNSUPPORTED;
     a.tbias = mb->bias;
@@ -400,8 +399,13 @@ fa_status bwd_check(int phases, const void* q, const void* k, const void* v, con
   if (dqa && (raw(grad_dtype) != FA_F32 || raw(dtype) == FA_F32 || a.bmask != nullptr ||
               bias == kBiasTensor))
     return FA_ERR_UNSUPPORTED;
-  // float32 inputs: dbias dense only
-  if (raw(dtype) == FA_F32 && mb != nullptr && mb->dbias_reduce != 0) return FA_ERR_UNSUPPORTED;
+  // float32 inputs: dbias dense only; with a block bitmap, dbias not summed over batches
+  // or heads
+  if (mb != nullptr && mb->dbias_reduce != 0 &&
+      (raw(dtype) == FA_F32 ||
+       (mb->block_mask != nullptr &&
+        (mb->dbias_reduce & (FA_DBIAS_SUM_BATCH | FA_DBIAS_SUM_HEADS)) != 0)))
+    return FA_ERR_UNSUPPORTED;
   return FA_OK;
 }
 

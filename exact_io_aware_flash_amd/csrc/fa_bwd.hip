@@ -490,8 +490,9 @@ void bwd_dkdv_kernel(const BwdArgs a) {
     };
     // zero dbias of query tile t for this wave's keys (lanes 0-31 and 32-63: alternate rows)
     // (only the first member: later ones add nothing there; rows summed: written at the end)
+    // (with a bitmap the launch clears dbias first: tiles no wave lists are never visited)
     auto zero_dbias_tile = [&](int t) {
-      if (dB == nullptr || rrows || !first || key >= Nk) return;
+      if (SPARSE || dB == nullptr || rrows || !first || key >= Nk) return;
       for (int i = 0; i < BR / 2; ++i) {
         const int qi = t * BR + 2 * i + h;
         if (qi < Nq) dB[(size_t)qi * Nk + key] = 0.f;
@@ -952,6 +953,14 @@ static __global__ void dslope_reduce_kernel(const float* __restrict__ part, int 
   out[s] = acc;
 }
 
+// Clears n floats (a dense dbias before a block-sparse dK/dV pass writes the visible
+// entries; a kernel rather than a memset node, so that a captured graph replays it
+// correctly).
+__global__ __launch_bounds__(256) void zero_f32_kernel(float* __restrict__ p, size_t n) {
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256)
+    p[i] = 0.f;
+}
+
 // Clears n4 float4 (dq before the dK/dV pass adds into it with atomics; a kernel rather
 // than a memset node, so that a captured graph replays it correctly).
 __global__ __launch_bounds__(256) void zero_f32x4_kernel(f32x4* __restrict__ p, size_t n4) {
@@ -1006,10 +1015,22 @@ static hipError_t launch_bwd_t(int bias, int phases, BwdArgs& a, hipStream_t st)
         hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, kDkdvBR, DKDV_NW, DKDV_WPE, kBiasSlope, false, false, true>), grid, block, 0, st, b);
       else
         hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, kDkdvBR, DKDV_NW, DKDV_WPE, kBiasNone, false, false, true>), grid, block, 0, st, b);
-    } else if (bias == kBiasTensor && slots != BH)
+    } else if (bias == kBiasTensor && slots != BH) {
       hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, kDkdvBR, DKDV_NW, DKDV_WPE, kBiasTensor, false, true>), grid, block, 0, st, b);
-    else if (bias == kBiasTensor)
+    } else if (bias == kBiasTensor && sparse) {
+      // a dense dbias is cleared first: tiles no wave of a workgroup lists are never
+      // visited, so the kernel does not write their zeros itself
+      if (a.dbias != nullptr && (a.db_red & FA_DBIAS_SUM_ROWS) == 0) {
+        const size_t nd = (size_t)BH * a.Nq * a.Nk;
+        const unsigned zb = (unsigned)std::min<size_t>((nd + 255) / 256, 8192);
+        hipLaunchKernelGGL(zero_f32_kernel, dim3(zb), dim3(256), 0, st, a.dbias, nd);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+      }
+      hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, kDkdvBR, DKDV_NW, DKDV_WPE, kBiasTensor, true>), grid, block, 0, st, b);
+    } else if (bias == kBiasTensor) {
       hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, kDkdvBR, DKDV_NW, DKDV_WPE, kBiasTensor, false>), grid, block, 0, st, b);
+    }
     else if (bias && sparse)
       hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, kDkdvBR, DKDV_NW, DKDV_WPE, kBiasSlope, true>), grid, block, 0, st, b);
     else if (bias)
@@ -1035,7 +1056,9 @@ static hipError_t launch_bwd_t(int bias, int phases, BwdArgs& a, hipStream_t st)
     b.sched = sched;
     const dim3 grid((unsigned)(BH * b.nblk)), block(nw * 64);
     // (the block-sparse form always uses 64-key tiles, which lie inside one block)
-    if (bias == kBiasTensor)
+    if (bias == kBiasTensor && a.bmask != nullptr)
+      hipLaunchKernelGGL((bwd_dq_kernel<T, D, 64, 4, DQ_WPE, kBiasTensor, true>), grid, block, 0, st, b);
+    else if (bias == kBiasTensor)
       hipLaunchKernelGGL((bwd_dq_kernel<T, D, 64, 4, DQ_WPE, kBiasTensor, false>), grid, block, 0, st, b);
     else if (a.bmask != nullptr && bias)
       hipLaunchKernelGGL((bwd_dq_kernel<T, D, 64, DQ_NW, DQ_WPE, kBiasSlope, true>), grid, block, 0, st, b);

@@ -1074,11 +1074,15 @@ static hipError_t launch16(int bias, FwdArgs& a, hipStream_t st) {
   const dim3 grid((unsigned)(BH * a.nqb * a.n_split)), block(C::kNT);
   const bool sparse = a.bmask != nullptr;
   if (bias == kBiasTensor) {
-    // (a bias tensor comes without a bitmap; its tile rides in a two-stage ring)
-    if constexpr (ST == 2 && NW == 4)
-      hipLaunchKernelGGL((fwd16_kernel<T, D, BC, NW, ST, kBiasTensor, false>), grid, block, 0, st, a);
-    else
+    // (the bias tensor's tile rides in a two-stage ring)
+    if constexpr (ST == 2 && NW == 4) {
+      if (sparse)
+        hipLaunchKernelGGL((fwd16_kernel<T, D, BC, NW, ST, kBiasTensor, true>), grid, block, 0, st, a);
+      else
+        hipLaunchKernelGGL((fwd16_kernel<T, D, BC, NW, ST, kBiasTensor, false>), grid, block, 0, st, a);
+    } else {
       return hipErrorNotSupported;
+    }
   } else if (bias && sparse)
     hipLaunchKernelGGL((fwd16_kernel<T, D, BC, NW, ST, kBiasSlope, true>), grid, block, 0, st, a);
   else if (bias)

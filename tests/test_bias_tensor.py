@@ -416,3 +416,76 @@ def test_dbias_beyond_2_31_elements_matches_the_head_alone():
     for a, b in zip(g1, (dq, dk, dv)):
         assert torch.equal(a, one(b))
     del dbias
+
+
+SPARSE_BIAS_CASES = [
+    # dtype, d, causal, nq, nk, bq, bk, density, layout, dbias ("dense", "rows" or None)
+    (torch.bfloat16, 128, True, 300, 330, 64, 64, 0.6, "head", "dense"),
+    (torch.float16, 64, False, 257, 520, 128, 64, 0.5, "batch_head", "rows"),
+    (torch.bfloat16, 128, False, 200, 700, 64, 192, 0.4, "shared", None),
+]
+
+
+@pytest.mark.parametrize("dtype,d,causal,nq,nk,bq,bk,density,layout,db", SPARSE_BIAS_CASES)
+def test_block_bitmap_with_bias_tensor(dtype, d, causal, nq, nk, bq, bk, density, layout, db):
+    # a block bitmap and a bias tensor together: forward (plain and split), backward and
+    # dbias against the oracle, which applies both
+    B, H = 2, 2
+    seed = 23001 + nq + 5 * nk + bq + bk + d
+    q, k, v, do = (normal((B, H, n, d), dtype, seed + i) for i, n in enumerate((nq, nk, nk, nq)))
+    nbq, nbk = -(-nq // bq), -(-nk // bk)
+    shape = {"shared": (nbq, nbk), "head": (H, nbq, nbk), "batch_head": (B, H, nbq, nbk)}[layout]
+    bm = (np.random.default_rng(seed + 5).random(shape) < density).astype(np.uint8)
+    bias = bias_tensor((1, H, nq, nk), seed + 6, 2.0, 0.05)
+    scale = 1.0 / math.sqrt(d)
+    qd, kd, vd, dod, bd = (t.to(DEV) for t in (q, k, v, do, bias))
+    kw = dict(causal=causal, scale=scale, bias=bd,
+              block_mask=(torch.from_numpy(bm).to(DEV), bq, bk))
+    o, lse = fa.fa_fwd(qd, kd, vd, **kw)
+    o2, lse2 = fa.fa_fwd_split(qd, kd, vd, n_split=3, **kw)
+    dbias = None
+    if db == "dense":
+        dbias = torch.full((B, H, nq, nk), float("nan"), dtype=torch.float32, device=DEV)
+    elif db == "rows":
+        dbias = torch.full((B, H, 1, nk), float("nan"), dtype=torch.float32, device=DEV)
+    dq, dk, dv = fa.fa_bwd(dod, qd, kd, vd, o, lse, dbias=dbias, **kw)
+    torch.cuda.synchronize()
+    bn = bias.double().numpy()
+    qn, kn, vn, don = np64(q), np64(k), np64(v), np64(do)
+    o_ref, lse_ref = oracle.attention_forward(qn, kn, vn, scale, causal=causal, bias=bn,
+                                              block_mask=(bm, bq, bk))
+    what = f"bitmap+bias {layout} {nq}x{nk} {bq}x{bk} c{causal} d{d}"
+    assert_fwd_close(np64(o), np64(lse), o_ref, lse_ref, dtype, what)
+    assert_fwd_close(np64(o2), np64(lse2), o_ref, lse_ref, dtype, what + " split")
+    *want, dref = oracle.attention_backward(qn, kn, vn, don, scale, causal=causal, bias=bn,
+                                            block_mask=(bm, bq, bk), return_dbias=True)
+    check((dq, dk, dv), want, ("dQ", "dK", "dV"), what)
+    if db is None:
+        return
+    tol, masked = dbias_tol_masked(qn, kn, vn, don, scale, causal, bn, bm, bq, bk)
+    g = np64(dbias)
+    assert np.isfinite(g).all(), what
+    if db == "dense":
+        assert np.all(np.abs(g - dref) <= tol), what
+        assert np.all(g[masked] == 0), what
+    else:
+        ref = dref.sum(axis=2, keepdims=True)
+        bound = tol.sum(axis=2, keepdims=True) + nq * 2.0 ** -23 * np.abs(dref).sum(axis=2,
+                                                                                  keepdims=True)
+        assert np.all(np.abs(g - ref) <= bound), what
+
+
+def dbias_tol_masked(q, k, v, do, scale, causal, bias, bm, bq, bk):
+    """dbias_tol (module docstring) with the block bitmap applied too."""
+    B, H, nq, _ = q.shape
+    nk = k.shape[2]
+    tol = np.empty((B, H, nq, nk))
+    masked = np.empty((B, H, nq, nk), dtype=bool)
+    for b in range(B):
+        for h in range(H):
+            p = oracle.attention_probabilities(q, k, scale, b, h, causal, bias=bias,
+                                               block_mask=(bm, bq, bk))
+            a = (np.abs(do[b, h]) * (p @ np.abs(v[b, h]))).sum(axis=1)
+            tol[b, h] = p * (2.0 ** -8 * a[:, None] + 1e-3) + 1e-6
+            masked[b, h] = p == 0
+    return tol, masked
