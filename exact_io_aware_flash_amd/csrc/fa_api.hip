@@ -72,7 +72,6 @@ fa_status read_desc(const fa_mask_bias_desc* mb, int H, int N_q, int N_k, fa_dty
     if (mb->block_q < 64 || mb->block_q % 64 != 0 || mb->block_k < 64 || mb->block_k % 64 != 0)
       return FA_ERR_MASK;
     if (mb->mask_stride_b < 0 || mb->mask_stride_h < 0) return FA_ERR_MASK;
-    if (dtype == FA_F32) return FA_ERR_UNSUPPORTED;
     if (N_q > FA_MAX_SPARSE_N || N_k > FA_MAX_SPARSE_N) return FA_ERR_UNSUPPORTED;
     a.bmask = mb->block_mask;
     a.bq = mb->block_q;

@@ -220,6 +220,12 @@ void dkdv32_kernel(const BwdArgs a) {
       const int* sm = a.qsum + 4 * (t / 2);
       skip |= kw1 <= sm[0] || kw0 >= sm[3];
     }
+    // block bitmap (a 32-row tile and a wave's 32 keys lie inside one block), as a mask
+    if (a.bmask != nullptr && !skip) {
+      const int bb = bh / a.H, hh = bh - bb * a.H;
+      skip = a.bmask[bb * a.bm_sb + hh * a.bm_sh + (long long)(q0t / a.bq) * a.nkb +
+                     min(kw0, Nk - 1) / a.bk] == 0;
+    }
     if (!skip) {
       f32x16 sc = f32x16{}, dp = f32x16{};
 #pragma unroll
@@ -371,6 +377,13 @@ void dq32_kernel(const BwdArgs a) {
     const int kt0 = t * BC;
     const float* Ks = smem + stg * STAGE;
     const float* Vs = Ks + TILE;
+    // block bitmap: this lane's row and the tile's 32 keys lie inside one block
+    bool blk = true;
+    if (a.bmask != nullptr) {
+      const int bb = bh / a.H, hh = bh - bb * a.H;
+      blk = a.bmask[bb * a.bm_sb + hh * a.bm_sh + (long long)((int)qr / a.bq) * a.nkb +
+                    min(kt0, Nk - 1) / a.bk] != 0;
+    }
     if (!(kt0 >= w_hi || kt0 + BC <= w_lo)) {
       f32x16 st = f32x16{}, dpt = f32x16{};
 #pragma unroll
@@ -383,7 +396,7 @@ void dq32_kernel(const BwdArgs a) {
       for (int g = 0; g < 16; ++g) {
         const int key = kt0 + res_row(g, h);
         const float x = __builtin_fmaf(st[g], sl2, bias2<BM>(a, TB, slope2, qrow, key) - lq);
-        const bool vis = key < Nk && qrow < Nq && (!causal || key <= qrow + off) &&
+        const bool vis = blk && key < Nk && qrow < Nq && (!causal || key <= qrow + off) &&
                          key >= kst && key < ken;
         const float p = vis ? fast_exp2(x) : 0.f;
         ds[g] = p * (dpt[g] - dd);

@@ -288,7 +288,7 @@ void fwd_kernel(const FwdArgs a) {
     const int kt1 = kt0 + BC;
     const bool skip = kt0 >= w_hi || kt1 <= w_lo;
     if (!skip) {
-      const bool full = kt1 <= Nk && kt1 <= w_full_c &&
+      const bool full = a.bmask == nullptr && kt1 <= Nk && kt1 <= w_full_c &&
                         (!ranged || (w_max_s <= kt0 && w_min_e >= kt1));
       const char* Ks = smem + stage * C::kStage;
       const char* Vs = Ks + C::kKBytes;
@@ -352,13 +352,23 @@ void fwd_kernel(const FwdArgs a) {
           const int lo = kst[qs], hi = min(ken[qs], Nk);
           const int cl = causal ? qrow[qs] + off : Nk;
 #pragma unroll
-          for (int kb = 0; kb < C::kKB; ++kb)
+          for (int kb = 0; kb < C::kKB; ++kb) {
+            // block bitmap: the 32 keys of a block lie inside one block of >= 64 keys;
+            // applied here as a mask (these tiles are still loaded)
+            bool blk = true;
+            if (a.bmask != nullptr) {
+              const int bb = bh / a.H, hh = bh - bb * a.H;
+              const int r = min(qrow[qs], Nq - 1) / a.bq;
+              const int c = min(kt0 + kb * 32, Nk - 1) / a.bk;
+              blk = a.bmask[bb * a.bm_sb + hh * a.bm_sh + (long long)r * a.nkb + c] != 0;
+            }
 #pragma unroll
             for (int g = 0; g < 16; ++g) {
               const int j = kt0 + kb * 32 + res_row(g, h);
-              const bool vis = j >= lo && j < hi && j <= cl;
+              const bool vis = blk && j >= lo && j < hi && j <= cl;
               s[qs][kb][g] = vis ? s[qs][kb][g] : kNegInf;
             }
+          }
         }
       }
 

@@ -108,7 +108,8 @@ typedef enum fa_bias_kind {
  *  mask_stride_b, mask_stride_h : bitmap strides in bytes between batches and heads;
  *              0 shares one bitmap over that axis (negative: FA_ERR_MASK).
  *              The bitmap is read during the enqueued work; it must stay valid until the
- *              stream has passed the call. 16-bit inputs only (float32: FA_ERR_UNSUPPORTED);
+ *              stream has passed the call. 16-bit inputs skip the tiles of invisible
+ *              blocks; float32 inputs apply the bitmap as a mask (same result).
  *              N_q and N_k at most FA_MAX_SPARSE_N (FA_ERR_UNSUPPORTED beyond).
  *  dslopes : DEVICE pointer to n_slopes floats, or NULL. fa_bwd (and fa_bwd_phases with
  *              FA_BWD_DKDV) writes there the gradient of the same loss with respect to the

@@ -120,7 +120,7 @@ def test_block_mask_descriptor_validation():
         d = desc(**bad)
         assert fwd(mb=ctypes.byref(d)) == 5, bad
     d = desc()
-    assert fwd(mb=ctypes.byref(d), dtype=fa.FA_F32) == 8  # 16-bit inputs only
+    assert fwd(mb=ctypes.byref(d), dtype=fa.FA_F32, d=96) == 4  # float32 too: shape checks
     assert fwd(mb=ctypes.byref(d), Nk=65536 + 64) == 8    # beyond FA_MAX_SPARSE_N
     assert fwd(mb=ctypes.byref(d), Nq=65536 + 1) == 8
     assert ctypes.sizeof(fa.MaskBiasDesc) == 120  # the C layout of fa_mask_bias_desc

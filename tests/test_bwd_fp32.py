@@ -22,7 +22,7 @@ import torch
 
 import oracle
 from synth import WORKLOADS, bias_tensor, key_ranges, normal, qkv_inputs
-from tests.util import np64
+from tests.util import assert_fwd_close, np64
 
 pytestmark = pytest.mark.gpu
 
@@ -187,3 +187,29 @@ def test_fp32_backward_is_deterministic_and_phases_agree():
     torch.cuda.synchronize()
     for x, y, z in zip(a, b, grads):
         assert torch.equal(x, y) and torch.equal(x, z)
+
+
+@pytest.mark.parametrize("causal,layout", [(True, "head"), (False, "batch_head")])
+def test_fp32_block_bitmap_forward_and_backward(causal, layout):
+    # float32 inputs apply a block bitmap as a mask (forward, split forward, backward)
+    B, H, nq, nk, d, bq, bk = 2, 2, 300, 330, 64, 64, 128
+    q, k, v, do = (normal((B, H, n, d), torch.float32, 7400 + i)
+                   for i, n in enumerate((nq, nk, nk, nq)))
+    nbq, nbk = -(-nq // bq), -(-nk // bk)
+    shape = {"head": (H, nbq, nbk), "batch_head": (B, H, nbq, nbk)}[layout]
+    bm = (np.random.default_rng(7405).random(shape) < 0.6).astype(np.uint8)
+    scale = 1.0 / math.sqrt(d)
+    qd, kd, vd, dod = (t.to(DEV) for t in (q, k, v, do))
+    kw = dict(causal=causal, scale=scale, block_mask=(torch.from_numpy(bm).to(DEV), bq, bk))
+    o, lse = fa.fa_fwd(qd, kd, vd, **kw)
+    o2, lse2 = fa.fa_fwd_split(qd, kd, vd, n_split=3, **kw)
+    got = fa.fa_bwd(dod, qd, kd, vd, o, lse, **kw)
+    torch.cuda.synchronize()
+    qn, kn, vn, don = np64(q), np64(k), np64(v), np64(do)
+    mask = dict(block_mask=(bm, bq, bk))
+    o_ref, lse_ref = oracle.attention_forward(qn, kn, vn, scale, causal=causal, **mask)
+    what = f"fp32 bitmap {layout} c{causal}"
+    assert_fwd_close(np64(o), np64(lse), o_ref, lse_ref, torch.float32, what)
+    assert_fwd_close(np64(o2), np64(lse2), o_ref, lse_ref, torch.float32, what + " split")
+    want = oracle.attention_backward(qn, kn, vn, don, scale, causal=causal, **mask)
+    check32(got, want, grad_bounds(qn, kn, vn, don, scale, causal, **mask), what)
