@@ -40,10 +40,10 @@ PEAK_FP8_TFLOPS = 2 * PEAK_BF16_TFLOPS  # dense E4M3 MFMA (published 5.0 PFLOP/s
 # the kernel source they were measured on. A changed source means stale counters -> null.
 TRAFFIC = {
     # kernel: (source hash, bytes read, bytes written) -- profiles/attention_fwd_bwd_bf16_causal_B2H16N8192d128.md
-    "fwd": ("47e58733019d059a", 282.0e6, 68.2e6),
-    "bwd_prep": ("5605dc2e8bd54061", 136.3e6, 2.1e6),
-    "bwd_dkdv": ("5605dc2e8bd54061", 270.9e6, 268.4e6),
-    "bwd_dq": ("5605dc2e8bd54061", 397.2e6, 138.2e6),
+    "fwd": ("53b1b7f9417b93e4", 490.7e6, 68.2e6),
+    "bwd_prep": ("a0c1eb94246b0815", 136.3e6, 2.1e6),
+    "bwd_dkdv": ("a0c1eb94246b0815", 270.9e6, 268.4e6),
+    "bwd_dq": ("a0c1eb94246b0815", 675.1e6, 139.2e6),
 }
 
 
@@ -79,6 +79,8 @@ def parse():
                     help="only time the block-sparse shapes and print them as one JSON line")
     ap.add_argument("--no-sweep", action="store_true",
                     help="skip the supplementary forward timings of the five workloads")
+    ap.add_argument("--sweep-only", action="store_true",
+                    help="only time the five workloads and print them as one JSON line")
     ap.add_argument("--no-fp8", action="store_true",
                     help="skip the supplementary FP8 forward timings")
     ap.add_argument("--fp8-only", action="store_true",
@@ -149,6 +151,13 @@ def main():
             print("no GPU visible", file=sys.stderr)
             sys.exit(1)
         print(json.dumps({"bias_tensor": bias_tensor_bench(fa, torch)}), flush=True)
+        return
+    if args.sweep_only:
+        fa.load_library()  # fails loudly if the HIP library is missing
+        if not torch.cuda.is_available():
+            print("no GPU visible", file=sys.stderr)
+            sys.exit(1)
+        print(json.dumps({"sweep": workload_sweep(fa, torch)}), flush=True)
         return
     if args.sparse_only:
         fa.load_library()  # fails loudly if the HIP library is missing

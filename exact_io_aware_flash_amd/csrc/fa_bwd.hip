@@ -985,7 +985,7 @@ static hipError_t launch_bwd_t(int bias, int phases, BwdArgs& a, hipStream_t st)
       if (e != hipSuccess) return e;
     }
   }
-  const int sched = (BH % 8 == 0) ? 1 : 0;
+  const int sched = (BH % 8 == 0) ? kSchedXcdLpt : kSchedHeadMajor;
   // dK, dV
   if (phases & FA_BWD_DKDV) {
     constexpr int BK = 32 * DKDV_NW;

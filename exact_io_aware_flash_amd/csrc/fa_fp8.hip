@@ -462,7 +462,7 @@ static hipError_t launch_fwd8_t(Fp8FwdArgs& a, hipStream_t st) {
   // shape: 344 us, against 353 us with 2 or 3 tiles in flight and 370-386 us with 8 waves)
   constexpr int NW = 4, ST = 2;
   a.nqb = (a.Nq + 32 * NW - 1) / (32 * NW);
-  a.sched = ((a.B * a.H) % 8 == 0) ? kSchedXcd : kSchedHeadMajor;
+  a.sched = ((a.B * a.H) % 8 == 0) ? kSchedXcdLpt : kSchedHeadMajor;
   const dim3 grid((unsigned)(a.B * a.H * a.nqb)), block(NW * 64);
   hipLaunchKernelGGL((fwd8_kernel<T, D, NW, ST>), grid, block, 0, st, a);
   return hipGetLastError();

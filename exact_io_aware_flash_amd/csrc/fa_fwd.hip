@@ -943,7 +943,7 @@ static hipError_t launch_cfg(int bias, FwdArgs& a, hipStream_t st) {
   a.nqb = (a.Nq + C::kBR - 1) / C::kBR;
   if (a.n_split < 1) a.n_split = 1;
   const int BH = a.B * a.H;
-  a.sched = (BH % 8 == 0) ? kSchedXcd : kSchedHeadMajor;
+  a.sched = (BH % 8 == 0) ? kSchedXcdLpt : kSchedHeadMajor;
   const dim3 grid((unsigned)(BH * a.nqb * a.n_split)), block(C::kNT);
   if (bias == kBiasTensor)
     hipLaunchKernelGGL((fwd_kernel<T, D, BC, QSUB, NW, WPE, kBiasTensor>), grid, block, 0, st, a);
@@ -1080,7 +1080,7 @@ static hipError_t launch16(int bias, FwdArgs& a, hipStream_t st) {
   a.keys_tile = BC;
   if (a.n_split < 1) a.n_split = 1;
   const int BH = a.B * a.H;
-  a.sched = (BH % 8 == 0) ? kSchedXcd : kSchedHeadMajor;
+  a.sched = (BH % 8 == 0) ? kSchedXcdLpt : kSchedHeadMajor;
   const dim3 grid((unsigned)(BH * a.nqb * a.n_split)), block(C::kNT);
   const bool sparse = a.bmask != nullptr;
   if (bias == kBiasTensor) {

@@ -11,7 +11,8 @@ namespace fa {
 // Work-to-workgroup mapping of the forward/backward grids.
 enum Sched : int {
   kSchedHeadMajor = 0,  // block L -> head L / nblk, heaviest query block first
-  kSchedXcd = 1         // heads pinned to one of the 8 XCDs (L % 8), heaviest first
+  kSchedXcd = 1,        // heads pinned to one of the 8 XCDs (L % 8), heaviest first
+  kSchedXcdLpt = 2      // as kSchedXcd, blocks of all the XCD's heads by weight
 };
 
 struct FwdArgs {
