@@ -59,11 +59,22 @@ def sanitizer_runtime() -> str:
     return found[-1]
 
 
-def build(verbose: bool = False, sanitize: bool = False, out: str = LIB) -> str:
+# The race-check library: every ring step of the kernels also waits for all of its loads
+# and passes a full workgroup barrier (FA_SYNC_CHECK in fa_device.h); a GPU test compares
+# its results with the normal library's bit for bit.
+SYNC_CHECK_LIB = os.path.join(PKG, "libfa_synccheck.so")
+
+
+def build(verbose: bool = False, sanitize: bool = False, out: str = LIB,
+          sync_check: bool = False) -> str:
     """Compile every HIP source for gfx950 and link ``libfa.so`` (or ``out``); returns its
-    path. ``sanitize``: host code built with AddressSanitizer and UBSan (SANITIZE)."""
-    extra = SANITIZE if sanitize else []
-    bdir = os.path.join(PKG, "_build_san" if sanitize else "_build")
+    path. ``sanitize``: host code built with AddressSanitizer and UBSan (SANITIZE).
+    ``sync_check``: the race-check variant (FA_SYNC_CHECK=1)."""
+    extra = list(SANITIZE if sanitize else [])
+    if sync_check:
+        extra.append("-DFA_SYNC_CHECK=1")
+    bdir = os.path.join(PKG, "_build_san" if sanitize else "_build_sync" if sync_check
+                        else "_build")
     os.makedirs(bdir, exist_ok=True)
     objs = [os.path.join(bdir, s.replace(".hip", ".o")) for s in SOURCES]
     with cf.ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 1)) as ex:

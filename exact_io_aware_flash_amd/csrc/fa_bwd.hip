@@ -517,6 +517,7 @@ void bwd_dkdv_kernel(const BwdArgs a) {
       // barrier
       if constexpr (SPARSE) lw.slide(p);
       if (p + P < n_pos) issue(p + P);
+      sync_check();
       if constexpr (DQA) {
         if (p > 0) dq_tile(p - 1);
         dsw = dst_s + (p & 1) * kDsBuf;
@@ -892,6 +893,7 @@ void bwd_dq_kernel(const BwdArgs a) {
     // barrier
     if constexpr (SPARSE) lw.slide(p);
     if (p + P < n_pos) issue(p + P);
+    sync_check();
     const int t = tile_at(p);
     const int kt0 = t * BC, kt1 = kt0 + BC;
     bool skip = kt0 >= w_hi || kt1 <= w_lo;

@@ -209,6 +209,7 @@ void dkdv32_kernel(const BwdArgs a) {
     const int stg = (t - t_lo) & 1;
     const bool more = t + 1 < t_hi;
     if (more) load(t + 1);
+    sync_check();
     const int q0t = t * BR;
     const float* Qs = smem + stg * STAGE;
     const float* Ds = Qs + TILE;
@@ -374,6 +375,7 @@ void dq32_kernel(const BwdArgs a) {
     const int stg = (t - t_lo) & 1;
     const bool more = t + 1 < t_hi;
     if (more) tl.load(K, V, (t + 1) * BC, Nk, tid);
+    sync_check();
     const int kt0 = t * BC;
     const float* Ks = smem + stg * STAGE;
     const float* Vs = Ks + TILE;

@@ -212,6 +212,21 @@ __device__ inline void wait_vmem() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
+// Race-check build (compiled with FA_SYNC_CHECK=1 into a library of its own, which a test
+// compares with the normal one): every ring step also waits for all of its loads and
+// passes a full workgroup barrier right after issuing the next tile, so copies no longer
+// overlap compute and no wave runs ahead of another. The normal build must give the
+// same bits; a difference means an access that depends on timing.
+#ifndef FA_SYNC_CHECK
+#define FA_SYNC_CHECK 0
+#endif
+__device__ inline void sync_check() {
+  if constexpr (FA_SYNC_CHECK != 0) {
+    wait_vmem<0>();
+    __syncthreads();
+  }
+}
+
 // A read-and-wait LDS load written as inline assembly, for small tables that are filled
 // before a loop and only read inside it. Written through the builtin path, such a read
 // looks to the compiler as if it could alias the ring stages being filled by direct

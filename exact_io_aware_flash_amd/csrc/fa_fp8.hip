@@ -408,6 +408,7 @@ void fwd8_kernel(const Fp8FwdArgs a) {
   auto step = [&](auto J, int t) __attribute__((always_inline)) {
     constexpr int j = decltype(J)::value;
     if (t + P < n_t) issue(std::integral_constant<int, j + P>{}, t + P);
+    sync_check();
     if (live_tile(t)) tile(sptr(J), t, !full_tile(t));
     if (t + 1 < n_t) land(min(t + P, n_t - 1) - (t + 1));
   };

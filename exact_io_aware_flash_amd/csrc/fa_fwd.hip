@@ -283,6 +283,7 @@ void fwd_kernel(const FwdArgs a) {
     const int stage = (t - t_lo) & 1;
     const bool more = t + 1 < t_hi;
     if (more) load_tile(t + 1);
+    sync_check();
 
     const int kt0 = t * BC;
     const int kt1 = kt0 + BC;
@@ -840,6 +841,7 @@ void fwd16_kernel(const FwdArgs a) {
     // the stage of position p+P held position p-1, which every wave finished before the
     // barrier
     if (p + P < n_pos) issue(std::integral_constant<int, j + P>{}, tile_at(p + P));
+    sync_check();
     if (wave_needs(p, t)) {
       ++n_comp;
       const char* sb = sptr(J);
