@@ -198,9 +198,13 @@ def main():
         if ev is not None:
             ev[len(phases)][1].record()
 
+    torch.cuda.synchronize()
+    torch.cuda.reset_peak_memory_stats(dev)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    peak_bytes = torch.cuda.max_memory_allocated(dev)
+    io_bytes = sum(t.numel() * t.element_size() for t in (q, k, v, do, o, lse) + grads)
 
     events = [[[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in names]
               for _ in range(args.steps)]
@@ -289,6 +293,11 @@ def main():
         "fwd_frac_of_bf16_peak": round(fwd_tflops / PEAK_BF16_TFLOPS, 4),
         "bwd_tflops": round(bwd_flops / (bwd_ms * 1e-3) / 1e12, 1),
         "kernels": kernels,
+        # device memory held during the step: inputs, outputs and gradients, plus the
+        # backward workspace (D and the scaled LSE); no N x N matrix is ever allocated
+        "memory": {"peak_allocated_bytes": int(peak_bytes), "io_bytes": int(io_bytes),
+                   "workspace_bytes": int(ws.numel()),
+                   "score_matrix_bytes_bf16": int(2 * B * H * N * N)},
         "backward_forms": forms,
         "roofline": roofline,
         "cpu_baseline": cpu,

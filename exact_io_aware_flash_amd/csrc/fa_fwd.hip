@@ -9,20 +9,20 @@
 // never loaded or computed. The score matrix never leaves registers.
 //
 // gfx950 mapping (not the Hopper design the pages describe):
-//  * one workgroup = NW waves = NW*32*QSUB query rows of one (batch, head); the grid runs
-//    over (batch, head, query block) so batch 1-4 still fills 256 CUs;
-//  * each wave owns its own 32*QSUB query rows (no cross-wave reduction of scores);
+//  * one workgroup = NW waves x 32 query rows of one (batch, head); the grid runs over
+//    (batch, head, query block[, key range]) so batch 1-4 still fills 256 CUs;
+//  * each wave owns its own 32 query rows (no cross-wave reduction of scores);
 //  * scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_{bf16,f16}:
-//    a lane then holds 16 keys of ONE query row per 32x32 tile, so the row max needs one
-//    exchange between the two wave halves and the row sum none until the epilogue;
-//  * the probabilities feed O^T += V^T P^T directly from those result registers; V is
-//    stored transposed in LDS (with keys relabelled so that every lane reads 16
-//    contiguous bytes) by an in-register 4x8 transpose during the global->LDS copy;
-//  * K and V^T tiles are double-buffered in LDS: the global loads of tile j+1 are issued
-//    before tile j is computed and written to the other buffer after it;
-//  * the running max is only moved when a row's tile max exceeds it by more than 2^8
-//    (exact: numerator and denominator share the same stale max), which removes almost
-//    every rescale of the 64-128 accumulator registers per lane;
+//    a lane then holds 16 keys of ONE query row per 32x32 tile, so the row statistics
+//    are per lane except for one exchange between the two wave halves;
+//  * the probabilities feed O^T += V^T P^T directly from those result registers; V stays
+//    row-major in LDS and its transposed operand comes from ds_read_b64_tr_b16;
+//  * K and V tiles go from HBM straight into a ring of LDS stages (buffer loads that
+//    write LDS), one or more tiles ahead of the tile being computed, one barrier a tile;
+//  * the running max is only moved when a row's scores exceed it by more than 2^8
+//    (exact: numerator and denominator share the same stale max); once every row holds
+//    a finite max, a tile's own max is not even computed: a score above m + 8 makes the
+//    lane's probability sum exceed 2^8, and only then is the max taken and the tile redone;
 //  * Q stays in registers for the whole loop; O^T and S^T live in registers.
 #include <type_traits>
 
@@ -758,39 +758,58 @@ void fwd16_kernel(const FwdArgs a) {
           sc[kb][g] = (j >= lo && j < hi) ? sc[kb][g] : kNegInf;
         }
     }
-    // The lane's half of the row decides whether the running max must move: some row's
-    // max exceeds m + tau exactly when some half-row's does, so the exchange between the
-    // two wave halves is only needed in the (rare) rescale branch.
-    float mx = kNegInf;
+    u32x4 pb[KB][2];
+    // probabilities against the running max m2 (packed into pb) and the lane's sum
+    auto probs = [&]() __attribute__((always_inline)) -> float {
+      const float nb = m2 == kNegInf ? 0.f : -m2;
+      float t = 0.f;
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
+      for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-      for (int g = 0; g < 16; ++g) mx = __builtin_fmaxf(mx, sc[kb][g]);
-    const float hmax = PRE ? mx : mx * sl2;
-    if (__builtin_expect(wave_any(hmax > m2 + kTau), 0)) {  // rare after the first tiles
-      const float tmax = xhalf_max(hmax);  // the whole row
+        for (int st = 0; st < 2; ++st)
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            const int g = 8 * st + 2 * w;
+            const float x0 = PRE ? sc[kb][g] + nb : __builtin_fmaf(sc[kb][g], sl2, nb);
+            const float x1 = PRE ? sc[kb][g + 1] + nb : __builtin_fmaf(sc[kb][g + 1], sl2, nb);
+            const float p0 = fast_exp2(x0), p1 = fast_exp2(x1);
+            pb[kb][st][w] = E::pack2(p0, p1);
+            t += p0 + p1;  // float32 row sum (the LSE needs the unrounded probabilities)
+          }
+      return t;
+    };
+    // move the running max to the row's max (both wave halves) and rescale
+    auto remax = [&]() __attribute__((always_inline)) {
+      float mx = kNegInf;
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int g = 0; g < 16; ++g) mx = __builtin_fmaxf(mx, sc[kb][g]);
+      const float tmax = xhalf_max(PRE ? mx : mx * sl2);
       const float mnew = __builtin_fmaxf(m2, tmax);
       const float alpha = mnew == kNegInf ? 1.f : fast_exp2(m2 - mnew);
       l *= alpha;
 #pragma unroll
       for (int db = 0; db < DB; ++db) o[db] *= alpha;
       m2 = mnew;
+    };
+    float t;
+    if (__builtin_expect(wave_any(m2 == kNegInf), 0)) {
+      // a row without a finite running max yet: take the tile's max first
+      remax();
+      t = probs();
+    } else {
+      // Every row already holds a probability >= 1 (from the key that set m2), so the
+      // tile needs no max of its own unless a score exceeds m2 + tau: then some p > 2^tau
+      // and the lane's sum of p exceeds 2^tau too (an infinite p included). Only then is
+      // the max taken, the accumulators rescaled and the tile's probabilities redone.
+      t = probs();
+      if (__builtin_expect(wave_any(!(t <= 256.f)), 0)) {
+        remax();
+        t = probs();
+      }
     }
-    const float nb = m2 == kNegInf ? 0.f : -m2;
-    u32x4 pb[KB][2];
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-      for (int st = 0; st < 2; ++st)
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          const int g = 8 * st + 2 * w;
-          const float x0 = PRE ? sc[kb][g] + nb : __builtin_fmaf(sc[kb][g], sl2, nb);
-          const float x1 = PRE ? sc[kb][g + 1] + nb : __builtin_fmaf(sc[kb][g + 1], sl2, nb);
-          const float p0 = fast_exp2(x0), p1 = fast_exp2(x1);
-          pb[kb][st][w] = E::pack2(p0, p1);
-          l += p0 + p1;  // float32 row sum (the LSE needs the unrounded probabilities)
-        }
+    l += t;
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
 #pragma unroll

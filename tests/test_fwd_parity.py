@@ -132,6 +132,26 @@ def test_large_magnitude_scores_stay_finite():
     assert_fwd_close(np64(o), np64(lse), o_ref, lse_ref, torch.bfloat16, "large scores")
 
 
+@pytest.mark.parametrize("dtype,d", [(torch.bfloat16, 128), (torch.float16, 64)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_scores_growing_along_keys(dtype, d, causal):
+    # Key j carries 8*j in coordinate 0 and every query a positive coordinate 0 (up to 4),
+    # so each 64-key tile raises a row's scores by up to ~260 (log2 units) over the last:
+    # the running max must move on almost every tile, by more than 128 on the rows whose
+    # first probabilities against the stale max overflow to infinity.
+    B, H, n = 1, 2, 700
+    q = normal((B, H, n, d), torch.float32, 61)
+    k = normal((B, H, n, d), torch.float32, 62)
+    q[..., 0] = torch.linspace(0.0, 4.0, n)
+    k[..., 0] = 8.0 * torch.arange(n, dtype=torch.float32)
+    q, k = q.to(dtype), k.to(dtype)
+    v = normal((B, H, n, d), dtype, 63)
+    o, lse = run(q, k, v, causal=causal)
+    o_ref, lse_ref = oracle.attention_forward(np64(q), np64(k), np64(v), 1 / math.sqrt(d),
+                                              causal=causal)
+    assert_fwd_close(np64(o), np64(lse), o_ref, lse_ref, dtype, f"growing scores c{causal}")
+
+
 def test_forward_is_deterministic():
     w = WORKLOADS[2].scaled(B=1, H=4, N_q=1000, N_k=1000)
     q, k, v, _ = qkv_inputs(w)
