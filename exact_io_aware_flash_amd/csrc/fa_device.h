@@ -31,6 +31,7 @@ constexpr float kNegInf = -__builtin_huge_valf();
 // Lazy rescale of the online softmax: the running max (log2 units) only moves when a
 // row's new scores exceed it by more than kTau, so probabilities stay <= 2^kTau.
 constexpr float kTau = 8.0f;
+constexpr float kTauP = 256.0f;  // 2^kTau: a probability above it means the max moved
 
 // Element-type traits: 16-bit types go through the 32x32x16 MFMA, float through 32x32x2.
 template <typename T> struct Elt;

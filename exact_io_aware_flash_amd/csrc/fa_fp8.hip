@@ -340,39 +340,58 @@ void fwd8_kernel(const Fp8FwdArgs a) {
         for (int g = 0; g < 16; ++g)
           sc[kh][g] = (kh * 32 + res_row(g, h) < hi) ? sc[kh][g] : kNegInf;
     }
-    float mx = kNegInf;
+    // probabilities (<= 2^8) rounded to E4M3, packed in key order kappa: bytes 0-15 from
+    // the first 32-key block, 16-31 from the second; returns the lane's sum
+    i32x8 pf;
+    auto probs = [&]() __attribute__((always_inline)) -> float {
+      const float nb = m2 == kNegInf ? 0.f : -m2;
+      float t = 0.f;
 #pragma unroll
-    for (int kh = 0; kh < 2; ++kh)
+      for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
-      for (int g = 0; g < 16; ++g) mx = __builtin_fmaxf(mx, sc[kh][g]);
-    const float hmax = mx * ct;
-    if (__builtin_expect(wave_any(hmax > m2 + kTau), 0)) {
-      const float tmax = xhalf_max(hmax);
+        for (int w = 0; w < 4; ++w) {
+          const int g = 4 * w;
+          const float p0 = fast_exp2(__builtin_fmaf(sc[kh][g], ct, nb));
+          const float p1 = fast_exp2(__builtin_fmaf(sc[kh][g + 1], ct, nb));
+          const float p2 = fast_exp2(__builtin_fmaf(sc[kh][g + 2], ct, nb));
+          const float p3 = fast_exp2(__builtin_fmaf(sc[kh][g + 3], ct, nb));
+          t += (p0 + p1) + (p2 + p3);
+          int pk = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, 0, false);
+          pk = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, pk, true);
+          pf[4 * kh + w] = pk;
+        }
+      return t;
+    };
+    // moves the running max to the row's max (both wave halves) and rescales
+    auto remax = [&]() __attribute__((always_inline)) {
+      float mx = kNegInf;
+#pragma unroll
+      for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+        for (int g = 0; g < 16; ++g) mx = __builtin_fmaxf(mx, sc[kh][g]);
+      const float tmax = xhalf_max(mx * ct);
       const float mnew = __builtin_fmaxf(m2, tmax);
       const float alpha = mnew == kNegInf ? 1.f : fast_exp2(m2 - mnew);
       l *= alpha;
 #pragma unroll
       for (int db = 0; db < DB; ++db) o[db] *= alpha;
       m2 = mnew;
-    }
-    const float nb = m2 == kNegInf ? 0.f : -m2;
-    // probabilities (<= 2^8) rounded to E4M3, packed in key order kappa: bytes 0-15 from
-    // the first 32-key block, 16-31 from the second
-    i32x8 pf;
-#pragma unroll
-    for (int kh = 0; kh < 2; ++kh)
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const int g = 4 * w;
-        const float p0 = fast_exp2(__builtin_fmaf(sc[kh][g], ct, nb));
-        const float p1 = fast_exp2(__builtin_fmaf(sc[kh][g + 1], ct, nb));
-        const float p2 = fast_exp2(__builtin_fmaf(sc[kh][g + 2], ct, nb));
-        const float p3 = fast_exp2(__builtin_fmaf(sc[kh][g + 3], ct, nb));
-        l += (p0 + p1) + (p2 + p3);
-        int pk = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, 0, false);
-        pk = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, pk, true);
-        pf[4 * kh + w] = pk;
+    };
+    // A row with a finite running max holds a probability >= 1 already, so the tile's max
+    // is only needed when a score exceeds m2 + tau: then some p > 2^tau and the lane's sum
+    // exceeds 2^tau too. Rows without a finite max yet take the max first.
+    float tsum;
+    if (__builtin_expect(wave_any(m2 == kNegInf), 0)) {
+      remax();
+      tsum = probs();
+    } else {
+      tsum = probs();
+      if (__builtin_expect(wave_any(!(tsum <= kTauP)), 0)) {
+        remax();
+        tsum = probs();
       }
+    }
+    l += tsum;
     i32x8 vf[DB];
 #pragma unroll
     for (int db = 0; db < DB; ++db)

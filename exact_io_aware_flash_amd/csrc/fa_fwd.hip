@@ -804,7 +804,7 @@ void fwd16_kernel(const FwdArgs a) {
       // and the lane's sum of p exceeds 2^tau too (an infinite p included). Only then is
       // the max taken, the accumulators rescaled and the tile's probabilities redone.
       t = probs();
-      if (__builtin_expect(wave_any(!(t <= 256.f)), 0)) {
+      if (__builtin_expect(wave_any(!(t <= kTauP)), 0)) {
         remax();
         t = probs();
       }
