@@ -31,8 +31,9 @@ namespace fa {
 // ---------------------------------------------------------------------------------
 // 1. D = rowsum(dO * O)
 // ---------------------------------------------------------------------------------
-// Also writes the exponent offset per row (lse_offset2: LSE * log2(e)), which the dK/dV
-// pass reads.
+// D is stored negated: the dK/dV pass starts its dP accumulation from it, so the MFMA
+// chain delivers dP - D directly. Also writes the exponent offset per row (lse_offset2:
+// LSE * log2(e)), which the dK/dV pass reads.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void bwd_prep_kernel(const T* __restrict__ o,
                                                        const T* __restrict__ dout,
@@ -61,7 +62,7 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const T* __restrict__ o,
 #pragma unroll
   for (int s = TPR / 2; s >= 1; s >>= 1) acc += __shfl_xor(acc, s, 64);
   if (row < rows && c == 0) {
-    delta[row] = acc;
+    delta[row] = -acc;
     lse2[row] = lse_offset2(lse[row]);
   }
 }
@@ -302,7 +303,16 @@ void bwd_dkdv_kernel(const BwdArgs a) {
     float pre[TENSOR ? QB : 1][16];  // dbias values a later member adds to (see below)
     auto qblock = [&](const char* sb, int q0t, int qb, auto mask_tag) {
       constexpr bool MASK = decltype(mask_tag)::value;
-      f32x16 sc = f32x16{}, dp = f32x16{};
+      // dp starts at -D of the 16 queries this lane holds (rows res_row(g, h) of the block:
+      // register g of the 32x32 result is row 8(g/4) + 4h + g%4, four consecutive rows per
+      // 16-byte read), so the dP MFMA chain delivers dP - D
+      f32x16 sc = f32x16{}, dp;
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const f32x4 nd = *reinterpret_cast<const f32x4*>(sb + L::DLT + (32 * qb + 8 * q4 + 4 * h) * 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dp[4 * q4 + e] = nd[e];
+      }
       {
         u32x4 qa[DK], da[DK];
 #pragma unroll
@@ -317,13 +327,12 @@ void bwd_dkdv_kernel(const BwdArgs a) {
           dp = E::mma(da[ks], vf[ks], dp);
         }
       }
-      // statistics of the 16 queries this lane holds (rows res_row(g, h) of the block)
-      f32x4 l4[4], d4[4];
+      // LSE * log2(e) of the 16 queries this lane holds
+      f32x4 l4[4];
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
         const int r0 = 32 * qb + 8 * q4 + 4 * h;
         l4[q4] = *reinterpret_cast<const f32x4*>(sb + L::LSE + r0 * 4);
-        d4[q4] = *reinterpret_cast<const f32x4*>(sb + L::DLT + r0 * 4);
       }
       float p[16], ds[16], adist[BIAS ? 16 : 1];
       const char* bs = sb + L::STAGE + wid_s * BT::kWaveBytes;  // this wave's bias windows
@@ -364,7 +373,7 @@ void bwd_dkdv_kernel(const BwdArgs a) {
         }
       }
 #pragma unroll
-      for (int g = 0; g < 16; ++g) ds[g] = p[g] * (dp[g] - d4[g / 4][g % 4]);
+      for (int g = 0; g < 16; ++g) ds[g] = p[g] * dp[g];  // dp holds dP - D
       if constexpr (DQA) {
         // dS^T row 32 w + n (this lane's key), queries 32 qb + 8 t4 + 4 h + (0..3)
         const int rr = 32 * wid_s + n;
@@ -698,7 +707,10 @@ void bwd_dq_kernel(const BwdArgs a) {
     dof[ks] = ldg16(dO + qr * D + 16 * ks + 8 * h);
   }
   const float lq = lse_offset2(a.lse[(size_t)bh * Nq + qr]);
-  const float dq_d = a.delta[(size_t)bh * Nq + qr];
+  // -D of this lane's query row (the prep pass stores D negated). Starting the dP^T
+  // accumulation from it, as the dK/dV pass does, would keep 16 more registers live and
+  // spill at this kernel's 256.
+  const float nd = a.delta[(size_t)bh * Nq + qr];
 
   // key window of this wave / workgroup (same rules as the forward pass)
   int kst = 0, ken = Nk;
@@ -847,7 +859,7 @@ void bwd_dq_kernel(const BwdArgs a) {
         }
       }
 #pragma unroll
-      for (int g = 0; g < 16; ++g) sc[kb][g] = sc[kb][g] * (dp[kb][g] - dq_d);  // dS^T
+      for (int g = 0; g < 16; ++g) sc[kb][g] = sc[kb][g] * (dp[kb][g] + nd);  // dS^T
     }
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {

@@ -67,7 +67,7 @@ struct BwdArgs {
   const void* o;
   const void* dout;
   const float* lse;
-  float* delta;   // [B,H,Nq] rowsum(dO * O), workspace
+  float* delta;   // [B,H,Nq] rowsum(dO * O), workspace (negated by the 16-bit prep pass)
   float* lse2;    // [B,H,Nq] LSE * log2(e), workspace
   int32_t* qsum;  // key-range summary per query tile of the dK/dV pass, workspace
   void* dq;
