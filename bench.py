@@ -40,10 +40,10 @@ PEAK_FP8_TFLOPS = 2 * PEAK_BF16_TFLOPS  # dense E4M3 MFMA (published 5.0 PFLOP/s
 # the kernel source they were measured on. A changed source means stale counters -> null.
 TRAFFIC = {
     # kernel: (source hash, bytes read, bytes written) -- profiles/attention_fwd_bwd_bf16_causal_B2H16N8192d128.md
-    "fwd": ("49e850d86f95ec87", 489.6e6, 68.2e6),
-    "bwd_prep": ("4e9a551cf8760cf6", 136.3e6, 2.1e6),
-    "bwd_dkdv": ("4e9a551cf8760cf6", 270.9e6, 268.4e6),
-    "bwd_dq": ("4e9a551cf8760cf6", 661.6e6, 139.3e6),
+    "fwd": ("f0c3c2fc90adc34a", 504.9e6, 68.2e6),
+    "bwd_prep": ("3d1a0df25fbc8249", 136.3e6, 2.1e6),
+    "bwd_dkdv": ("3d1a0df25fbc8249", 270.9e6, 268.4e6),
+    "bwd_dq": ("3d1a0df25fbc8249", 685.8e6, 139.3e6),
 }
 
 

@@ -8,7 +8,8 @@
 // dQ = scale * dS K, dK = scale * dS^T Q.
 //
 // Three launches, no atomics, deterministic:
-//  1. prep:  D_i = rowsum(dO_i * O_i) in float32 (one HBM pass);
+//  1. prep:  D_i = rowsum(dO_i * O_i) in float32 (one HBM pass), stored negated, and
+//            LSE_i * log2(e);
 //  2. dkdv:  one workgroup per (b, h, block of 32*NW keys); each wave keeps its 32 keys'
 //            K and V rows in registers and accumulates dK^T/dV^T while walking the query
 //            tiles. S = Q K^T and dP = dO V^T come out with the key on the lane and the
@@ -16,8 +17,9 @@
 //            registers; Q and dO are staged in LDS both row-major (A operands of S, dP)
 //            and transposed (B operands of dV, dK);
 //  3. dq:    forward-shaped: one workgroup per (b, h, block of 32*NW queries); Q, dO, LSE
-//            and D of the wave's 32 queries stay in registers; K (row-major and
-//            transposed) and V tiles are double-buffered in LDS; dQ^T += K^T dS^T.
+//            and D of the wave's 32 queries stay in registers; K (read as rows and by
+//            transposing gathers) and V tiles stream through a ring of LDS stages;
+//            dQ^T += K^T dS^T.
 // The dq pass recomputes S and dP a second time (7 matrix products instead of 5) in
 // exchange for no float32 atomics on dQ.
 #include <algorithm>

@@ -529,7 +529,7 @@ void fwd16_kernel(const FwdArgs a) {
   using E = Elt<T>;
   using BT = BiasRowTile<BC>;
   constexpr bool SLOPE = BM == kBiasSlope, TENSOR = BM == kBiasTensor;
-  constexpr bool PRE = BM != kBiasNone;  // scores scaled to log2 units before the row max
+  constexpr bool PRE = BM != kBiasNone;  // bias added to the scores in log2 units before the exponentials
   constexpr int KB = C::kKB, DB = C::kDB, DK = C::kDK, RB = C::kRB;
   constexpr int P = ST - 1;                                  // tiles in flight ahead
   // direct loads per wave per tile: K and V windows (+ the bias tile's rows)
