@@ -198,6 +198,9 @@ def main():
         if ev is not None:
             ev[len(phases)][1].record()
 
+    fwd_flops = 4.0 * B * H * N * N * d / 2.0
+    bwd_flops = 2.5 * fwd_flops
+
     torch.cuda.synchronize()
     torch.cuda.reset_peak_memory_stats(dev)
     for _ in range(args.warmup):
@@ -218,8 +221,6 @@ def main():
     kern_ms = {n: float(np.mean([events[s][i][0].elapsed_time(events[s][i][1])
                                  for s in range(args.steps)])) for i, n in enumerate(names)}
 
-    fwd_flops = 4.0 * B * H * N * N * d / 2.0
-    bwd_flops = 2.5 * fwd_flops
     step_flops = fwd_flops + bwd_flops
     value = step_flops / (ms_per_step * 1e-3) / 1e12
 
@@ -310,24 +311,29 @@ def main():
     print(json.dumps(line), flush=True)
 
 
-def time_us(torch, fn, reps=10, rounds=3):
-    """Average microseconds per call of `fn` over `reps` back-to-back calls, timed with HIP
-    events on the launch stream (torch's current stream); median over `rounds` after 5
-    warm-up calls. Back-to-back calls keep the GPU busy, as in a real pass: a sync between
-    single calls would let the clocks drop and add the host's launch time."""
-    for _ in range(5):
-        fn()
-    torch.cuda.synchronize()
-    ts = []
-    for _ in range(rounds):
+def time_us(torch, fn, rounds=5, settle_ms=50.0, round_ms=10.0):
+    """Average microseconds per call of `fn` over back-to-back calls, timed with HIP events
+    on the launch stream (torch's current stream); median over `rounds`. Back-to-back calls
+    keep the GPU busy, as in a real pass: a sync between single calls would let the clocks
+    drop and add the host's launch time. The clocks also need tens of milliseconds of load
+    to settle (back to back from idle, the causal B2 H16 N8192 d128 forward took 690 us,
+    then 490 us after about 30 ms), so the calls
+    are first repeated for `settle_ms`, and each round lasts at least `round_ms`."""
+    def run(n):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
-        for _ in range(reps):
+        for _ in range(n):
             fn()
         e1.record()
         e1.synchronize()
-        ts.append(e0.elapsed_time(e1) * 1e3 / reps)
-    return sorted(ts)[len(ts) // 2]
+        return e0.elapsed_time(e1) / n  # ms per call
+
+    run(3)
+    est = max(run(3), 1e-3)
+    run(min(5000, max(5, math.ceil(settle_ms / est))))
+    reps = min(2000, max(10, math.ceil(round_ms / est)))
+    ts = sorted(run(reps) * 1e3 for _ in range(rounds))
+    return ts[len(ts) // 2]
 
 
 def backward_forms(fa, torch, q, k, v, do, o, lse, grads, ws, kw, bwd_flops):
