@@ -21,17 +21,25 @@ Readings (the page names the idea only):
   numbers are an input). The 1/sqrt(d) normalisation is left out of the stored values
   (the block scale absorbs it): the rotated vector is x diag(signs) H_d, and scores of
   rotated operands are divided by d.
-* Blocks: 64 consecutive rows (of one (b, h)) by all d columns for Q and K, with
-  amax = max |value| over the block and scale = amax / 448. V is not rotated (that would
-  need the inverse rotation of O) and is quantised with one scale per (b, h): the
-  largest of its 64-row block amaxes, over 448.
+* Blocks: 64 consecutive rows (of one (b, h)) by all d columns, with amax = max |value|
+  over the block. Q and K: scale = amax / 448. V is not rotated (that would need the
+  inverse rotation of O); its block scale is a power of two, 2^e with e the smallest
+  integer (at least -127) such that amax <= 448 * 2^e, and its codes are those of
+  x * 2^-e. A power of two is the form of block scale that a scaled matrix product
+  applies to its operand itself (an E8M0 exponent), so the V scale of each 64-key block
+  enters the P V product exactly. Since E4M3 is a floating-point format, a block scale
+  that maps the amax anywhere into (224, 448] changes only which of the block's smallest
+  values fall below E4M3's normal range.
 * Precision of the code decision (a float decides an integer): the rotated value is the
   exact float64 sum, rounded once to float32; amax, 448 / amax and the product with it
   are float32 (IEEE, correctly rounded); the float32 result is clamped and rounded to
-  E4M3. A block with amax = 0 stores zeros and scale 0.
+  E4M3. For V the product with 2^-e is exact. A block with amax = 0 stores zeros (scale
+  0 for Q and K, 2^0 for V).
 """
 
 from __future__ import annotations
+
+import math
 
 import numpy as np
 
@@ -101,7 +109,8 @@ def quantize(x, signs=None, per_head: bool = False):
     Rows are padded with zeros to a multiple of 64. Returns (codes [B, H, Np, d] uint8,
     amax [B, H, Np/64] float32 of the (rotated) values per 64-row block, scale used per
     block [B, H, Np/64] float32). With per_head the scale of every block of a (b, h) is
-    the largest block amax of that (b, h), over 448.
+    the largest block amax of that (b, h), over 448 (plain FP8 with one scale per head,
+    the form the rotated block quantisation is compared against).
     """
     x = np.asarray(x, dtype=np.float64)
     B, H, N, d = x.shape
@@ -117,6 +126,40 @@ def quantize(x, signs=None, per_head: bool = False):
         inv = np.where(used > 0, np.float32(E4M3_MAX) / np.where(used > 0, used, 1),
                        0).astype(np.float32)
     scaled = (blocks * inv[..., None, None]).astype(np.float32)
+    codes = e4m3_round(scaled).reshape(B, H, n_p, d)
+    return codes, amax, scale
+
+
+def v_block_exponent(amax: float) -> int:
+    """The exponent e of a V block's scale 2^e: the smallest integer e >= -127 with
+    amax <= 448 * 2^e; 0 for an all-zero block. Found by exact comparisons in float64."""
+    a = float(amax)
+    if a == 0.0:
+        return 0
+    e = math.frexp(a)[1] - 9  # a < 2^(e + 9), and 448 * 2^e = 0.875 * 2^(e + 9)
+    while a > math.ldexp(E4M3_MAX, e):
+        e += 1
+    while e > -127 and a <= math.ldexp(E4M3_MAX, e - 1):
+        e -= 1
+    return max(e, -127)
+
+
+def quantize_v(x):
+    """Block-quantise V [B, H, N, d] to E4M3 with power-of-two block scales.
+
+    Rows are padded with zeros to a multiple of 64. Returns (codes [B, H, Np, d] uint8,
+    amax [B, H, Np/64] float32, scale [B, H, Np/64] float64 = 2^e per block).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    B, H, N, d = x.shape
+    n_p = -(-N // QBLOCK) * QBLOCK
+    y = _pad_rows(x.astype(np.float32), n_p)
+    nb = n_p // QBLOCK
+    blocks = y.reshape(B, H, nb, QBLOCK, d)
+    amax = np.abs(blocks).max(axis=(3, 4)).astype(np.float32)
+    expo = np.vectorize(v_block_exponent, otypes=[np.int64])(amax)
+    scale = np.ldexp(1.0, expo)
+    scaled = (blocks.astype(np.float64) * np.ldexp(1.0, -expo)[..., None, None]).astype(np.float32)
     codes = e4m3_round(scaled).reshape(B, H, n_p, d)
     return codes, amax, scale
 
@@ -139,7 +182,7 @@ def fp8_attention_operands(q, k, v, signs=None):
     n_q, n_k, d = q.shape[2], k.shape[2], q.shape[3]
     cq, _, sq = quantize(q, signs)
     ck, _, sk = quantize(k, signs)
-    cv, _, sv = quantize(v, None, per_head=True)
+    cv, _, sv = quantize_v(v)
     qh = dequantize(cq, sq)[:, :, :n_q]
     kh = dequantize(ck, sk)[:, :, :n_k]
     vh = dequantize(cv, sv)[:, :, :n_k]

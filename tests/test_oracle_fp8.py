@@ -153,6 +153,58 @@ def test_zero_block_gives_zero_codes_and_scale():
     assert not codes.any() and amax[0, 0, 0] == 0 and scale[0, 0, 0] == 0
 
 
+# ---- V: power-of-two block scales -------------------------------------------------------
+def _v_exponent_brute(a):
+    # linear scan over every admissible exponent, exact float64 comparisons
+    for e in range(-127, 200):
+        if float(a) <= 448.0 * 2.0 ** e:
+            return e
+    raise AssertionError
+
+
+def test_v_block_exponent_by_brute_force():
+    rng = np.random.default_rng(27)
+    vals = [np.float32(448.0), np.float32(224.0), np.float32(1.0), np.float32(0.875),
+            np.nextafter(np.float32(448.0), np.float32(1e9)),
+            np.nextafter(np.float32(448.0), np.float32(0.0)),
+            np.float32(448.0 * 2.0 ** -20), np.float32(3.0e38), np.float32(1e-40),
+            np.float32(448.0 * 2.0 ** -127), np.float32(448.0 * 2.0 ** -128)]
+    vals += list((rng.random(200) * 2.0 ** rng.integers(-60, 60, 200)).astype(np.float32))
+    for a in vals:
+        assert F.v_block_exponent(a) == _v_exponent_brute(a), a
+    assert F.v_block_exponent(0.0) == 0
+
+
+def test_v_codes_by_brute_force_and_blocks_independent():
+    B, H, N, d = 1, 2, 200, 64
+    x = _inputs((B, H, N, d), 28)
+    codes, amax, scale = F.quantize_v(x)
+    assert codes.shape == (B, H, 256, d) and scale.shape == (B, H, 4)
+    for h, blk in itertools.product(range(H), range(4)):
+        rows = x[0, h, 64 * blk:64 * blk + 64].astype(np.float32)
+        e = _v_exponent_brute(np.abs(rows).max())
+        assert amax[0, h, blk] == np.abs(rows).max() and scale[0, h, blk] == 2.0 ** e
+        want = F.e4m3_round((rows.astype(np.float64) / 2.0 ** e).astype(np.float32))
+        assert np.array_equal(codes[0, h, 64 * blk:64 * blk + len(rows)], want)
+        top = np.abs(F.e4m3_decode(want)).max()
+        assert 224.0 < top <= 448.0  # the block amax lands in the top binade of E4M3
+    # a block scaled by 2^5 keeps its codes, its scale grows 32-fold, the others stay
+    y = x.copy()
+    y[0, 1, 64:128] *= 32.0
+    c2, _, s2 = F.quantize_v(y)
+    assert np.array_equal(c2, codes)
+    assert s2[0, 1, 1] == 32.0 * scale[0, 1, 1]
+    assert np.array_equal(np.delete(s2.ravel(), 5), np.delete(scale.ravel(), 5))
+
+
+def test_v_dequantised_error_within_half_a_step():
+    x = _inputs((1, 3, 256, 128), 29)
+    codes, _, scale = F.quantize_v(x)
+    back = F.dequantize(codes, scale)
+    step = np.maximum(np.abs(back), 2.0 ** -6 * np.repeat(scale, 64, axis=2)[..., None])
+    assert np.all(np.abs(back - x) <= 2.0 ** -4 * step + 1e-12)
+
+
 def test_one_hot_rotated_operands_are_exact():
     # rows 7 * signs * H[j] rotate to 7 d e_j = 448 e_j: block scale 1 and code 448, so
     # the quantised operands give exactly the scores of the original inputs
@@ -162,7 +214,7 @@ def test_one_hot_rotated_operands_are_exact():
     rng = np.random.default_rng(26)
     q = (7.0 * s * hd[rng.integers(0, d, n)])[None, None]
     k = (7.0 * s * hd[rng.integers(0, d, n)])[None, None]
-    # V: exact E4M3 values with 448 among them, so the per-head scale is 1
+    # V: exact E4M3 values with 448 among them, so the block scale is 2^0
     v = np.asarray(F.e4m3_decode(rng.integers(0, 0xFF, (1, 1, n, d)).astype(np.uint8) & 0xF7))
     v[0, 0, 5, 7] = 448.0
     qh, kh, vh, div = F.fp8_attention_operands(q, k, v, s)

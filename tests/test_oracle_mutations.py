@@ -170,6 +170,13 @@ def mut_rotation_signs_ignored(monkeypatch):
                         _orig_hadamard(np.asarray(x).shape[-1]))
 
 
+_orig_v_exp = F8.v_block_exponent
+
+
+def mut_v_exponent_one_too_high(monkeypatch):
+    monkeypatch.setattr(F8, "v_block_exponent", lambda a: _orig_v_exp(a) + (a != 0))
+
+
 FP8_PINS = [
     lambda: [fp8_pins.test_decode_known_values(c, v) for c, v in
              [(0x01, 2.0 ** -9), (0x38, 1.0), (0x7E, 448.0)]],
@@ -178,11 +185,14 @@ FP8_PINS = [
     lambda: fp8_pins.test_hadamard_is_orthogonal_with_pm1_entries(64),
     lambda: fp8_pins.test_rotation_of_a_signed_hadamard_row_is_one_hot(),
     lambda: fp8_pins.test_block_amax_and_codes_by_brute_force(True),
+    lambda: fp8_pins.test_v_block_exponent_by_brute_force(),
+    lambda: fp8_pins.test_v_codes_by_brute_force_and_blocks_independent(),
 ]
 
 
 @pytest.mark.parametrize("mutation", [
     mut_e4m3_bias_8, mut_e4m3_ties_away, mut_hadamard_no_minus, mut_rotation_signs_ignored,
+    mut_v_exponent_one_too_high,
 ])
 def test_planted_fp8_mistake_is_caught(monkeypatch, mutation):
     mutation(monkeypatch)
