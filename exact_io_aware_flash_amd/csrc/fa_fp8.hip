@@ -9,15 +9,18 @@
 // diag(signs) H_d (H_d the Sylvester Hadamard matrix; the 1/sqrt(d) factor is left to
 // the scores): the fast Walsh-Hadamard transform runs in float64, where the sums of d
 // 16-bit inputs are exact, and is rounded once to float32. Each 64-row block gets
-// amax = max |x| and codes RNE(clamp(x * (448 / amax))). Q is stored row-major; K and V
-// are stored as the LDS images of the forward's tiles (see fa.h), so the forward copies
-// them with plain linear direct loads.
+// amax = max |x|; Q and K codes are RNE(clamp(x * (448 / amax))), V codes RNE(x * 2^-e)
+// with 2^e the smallest power of two such that amax <= 448 * 2^e, the block scale the
+// P V product applies itself. Q is stored row-major; K and V are stored as the LDS images
+// of the forward's tiles (see fa.h), so the forward copies them with plain linear direct
+// loads.
 //
 // Forward: the 16-bit forward's structure (query rows per wave, online softmax with
 // lazy rescale, K/V tiles through a ring of LDS stages by direct loads) with
 // v_mfma_f32_32x32x64_f8f6f4 for S^T = K Q^T (k = 64 bytes of d per step) and for
-// O^T += V^T P^T (k = all 64 keys of a tile in one step). The probabilities (at most
-// 2^8 with the lazy rescale) are rounded to E4M3 straight from the score registers; the
+// O^T += V^T P^T (k = all 64 keys of a tile in one step, with the tile's V block scale
+// given to the product as its E8M0 operand scale). The probabilities (at most 2^8 with
+// the lazy rescale) are rounded to E4M3 straight from the score registers; the
 // transposed, key-permuted V tile puts each lane's 32 keys in the same byte order.
 #include <hip/hip_runtime.h>
 
@@ -29,6 +32,18 @@ namespace fa {
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 constexpr float kE4m3Max = 448.f;
+
+// Exponent e of a V block's scale 2^e: the smallest e >= -127 (the E8M0 floor) with
+// amax <= 448 * 2^e, and 0 for an all-zero block. With 448 = 1.75 * 2^8 and amax =
+// 1.m * 2^(E - 127) (E its biased exponent field) that is E - 135, plus one when the
+// mantissa exceeds 1.75 (field above 0x600000).
+__device__ inline int v_block_exp(float amax) {
+  if (!(amax > 0.f)) return 0;
+  const uint32_t b = __float_as_uint(amax);
+  const int eb = (int)(b >> 23);
+  if (eb == 0) return -127;  // subnormal: below 2^-126 < 448 * 2^-127
+  return max(eb - 135 + ((b & 0x7fffffu) > 0x600000u ? 1 : 0), -127);
+}
 
 // ---------------------------------------------------------------------------------
 // byte layouts of the quantised K and V tiles (64 rows of one (b, h))
@@ -104,28 +119,6 @@ __device__ inline float block_max256(float x, float* red) {
   return r;
 }
 
-// pass 1 of the V layout: amax of every 64-row block (no codes)
-template <typename T, int D>
-__global__ __launch_bounds__(256) void fp8_amax_kernel(const Fp8QuantArgs a) {
-  __shared__ float red[4];
-  constexpr int PER = D / 4;
-  const int nb = a.Np / 64;
-  const int bh = blockIdx.x / nb, blk = blockIdx.x - bh * nb;
-  const int r = threadIdx.x >> 2, q = threadIdx.x & 3, row = blk * 64 + r;
-  double v[PER];
-  if (row < a.N) {
-    load_quarter_row<T, D>(static_cast<const T*>(a.x) + ((size_t)bh * a.N + row) * D, q, v);
-  } else {
-#pragma unroll
-    for (int i = 0; i < PER; ++i) v[i] = 0.0;
-  }
-  float m = 0.f;
-#pragma unroll
-  for (int i = 0; i < PER; ++i) m = __builtin_fmaxf(m, __builtin_fabsf((float)v[i]));
-  m = block_max256(m, red);
-  if (threadIdx.x == 0) a.amax[(size_t)bh * nb + blk] = m;
-}
-
 template <typename T, int D>
 __global__ __launch_bounds__(256) void fp8_quant_kernel(const Fp8QuantArgs a) {
   constexpr int PER = D / 4;
@@ -149,18 +142,12 @@ __global__ __launch_bounds__(256) void fp8_quant_kernel(const Fp8QuantArgs a) {
     f[i] = (float)v[i];  // one rounding of the exact value
     m = __builtin_fmaxf(m, __builtin_fabsf(f[i]));
   }
-  float amax;
-  if (a.layout == FA_FP8_V) {
-    // one scale per (b, h): the largest block amax written by the first pass
-    float hm = 0.f;
-    const float* am = a.amax + (size_t)bh * nb;
-    for (int i = threadIdx.x; i < nb; i += 256) hm = __builtin_fmaxf(hm, am[i]);
-    amax = block_max256(hm, red);
-  } else {
-    amax = block_max256(m, red);
-    if (threadIdx.x == 0) a.amax[(size_t)bh * nb + blk] = amax;
-  }
-  const float inv = amax > 0.f ? kE4m3Max / amax : 0.f;
+  const float amax = block_max256(m, red);
+  if (threadIdx.x == 0) a.amax[(size_t)bh * nb + blk] = amax;
+  // Q, K: x * (448 / amax); V: x * 2^-e, exact (127 - e lies in [7, 254], a normal float)
+  const float inv = a.layout == FA_FP8_V
+                        ? __uint_as_float((uint32_t)(127 - v_block_exp(amax)) << 23)
+                        : (amax > 0.f ? kE4m3Max / amax : 0.f);
   uint32_t w[PER / 4];
 #pragma unroll
   for (int i = 0; i < PER / 4; ++i) {
@@ -205,6 +192,12 @@ __global__ __launch_bounds__(256) void fp8_quant_kernel(const Fp8QuantArgs a) {
 __device__ inline f32x16 mma8(i32x8 a, i32x8 b, f32x16 c) {
   // A and B in E4M3 (format code 0), no block scales
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+// the same with E8M0 operand scales: A times 2^(sa - 127), B times 2^(sb - 127) (byte 0 of
+// each; every lane passes the same value here). Both must be run-time values: a constant
+// scale operand would be encoded as a float32 constant.
+__device__ inline f32x16 mma8s(i32x8 a, i32x8 b, f32x16 c, int sa, int sb) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, sa, 0, sb);
 }
 __device__ inline i32x8 cat8(u32x4 lo, u32x4 hi) {
   return i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
@@ -264,13 +257,11 @@ void fwd8_kernel(const Fp8FwdArgs a) {
     w_full_c = max(0, min(Nk, wq0 + off + 1));
   }
   if (!wave_live || w_hi <= 0) w_hi = 0;
-  // V scale: the largest block amax of the head, over 448 (as the quantiser used it)
-  float vm = 0.f;
-  {
-    const float* vam = a.v_amax + (size_t)bh * (a.Nkp / 64);
-    for (int i = lane; i < a.Nkp / 64; i += 64) vm = __builtin_fmaxf(vm, vam[i]);
-    vm = wave_fmax(vm);
-  }
+  // V block amaxes the same way: tile t's block scale exponent for the P V product
+  const __attribute__((address_space(4))) float* vam =
+      (const __attribute__((address_space(4))) float*)(a.v_amax + (size_t)bh * (a.Nkp / 64));
+  int e8_one = 127;  // E8M0 for 2^0, kept opaque to the compiler (see mma8s)
+  asm volatile("" : "+v"(e8_one));
   if (lane == 0) wg_hi[wid] = w_hi;
   __syncthreads();
   int g_hi = 0;
@@ -283,7 +274,6 @@ void fwd8_kernel(const Fp8FwdArgs a) {
   // the score scale of this wave's rows: scale * log2(e) (/ d if rotated) * q block scale
   const float sq = wave_live ? a.q_amax[(size_t)bh * (a.Nqp / 64) + wq0 / 64] / kE4m3Max : 0.f;
   const float csq = a.sl2 * sq;
-  const float sv = vm / kE4m3Max;
 
   // Q operand (B of S^T = K Q^T): query row n, bytes 64c + 32h .. +31 of each k-step
   i32x8 qf[DC];
@@ -396,8 +386,9 @@ void fwd8_kernel(const Fp8FwdArgs a) {
 #pragma unroll
     for (int db = 0; db < DB; ++db)
       vf[db] = cat8(lds_ld16(sb, db * 32 * 64 + va[0]), lds_ld16(sb, db * 32 * 64 + va[1]));
+    const int e8_v = v_block_exp(vam[t]) + 127;  // V block scale 2^e as E8M0
 #pragma unroll
-    for (int db = 0; db < DB; ++db) o[db] = mma8(vf[db], pf, o[db]);
+    for (int db = 0; db < DB; ++db) o[db] = mma8s(vf[db], pf, o[db], e8_v, e8_one);
   };
 
   // ring: tile t's K and V images copied linearly, stage t % ST
@@ -438,9 +429,9 @@ void fwd8_kernel(const Fp8FwdArgs a) {
     if constexpr (ST > 3) if (t + 3 < n_t) step(I3{}, t + 3);
   }
 
-  // epilogue: O = sv * O^T / l, LSE = (m + log2 l) ln 2
+  // epilogue: O = O^T / l, LSE = (m + log2 l) ln 2
   const float lt = xhalf_sum(l);
-  const float inv = lt > 0.f ? sv / lt : 0.f;
+  const float inv = lt > 0.f ? 1.f / lt : 0.f;
   if (qrow < Nq) {
 #pragma unroll
     for (int db = 0; db < DB; ++db)
@@ -462,11 +453,6 @@ void fwd8_kernel(const Fp8FwdArgs a) {
 template <typename T, int D>
 static hipError_t launch_quant_t(Fp8QuantArgs& a, hipStream_t st) {
   const dim3 grid((unsigned)(a.B * a.H * (a.Np / 64))), block(256);
-  if (a.layout == FA_FP8_V) {
-    hipLaunchKernelGGL((fp8_amax_kernel<T, D>), grid, block, 0, st, a);
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
   hipLaunchKernelGGL((fp8_quant_kernel<T, D>), grid, block, 0, st, a);
   return hipGetLastError();
 }

@@ -350,10 +350,13 @@ FA_API fa_status fa_mask_summary(const int32_t* key_start, const int32_t* key_en
  * Format: OCP FP8 E4M3 (1 sign, 4 exponent bits with bias 7, 3 mantissa bits;
  * largest finite 448; no infinities). A tensor [B,H,N,d] is quantised in blocks of 64
  * rows of one (b, h): N is padded with zero rows to Np = fa_fp8_rows(N) (a multiple of
- * 64), block i covers rows 64i .. 64i+63, amax[b,h,i] = max |x| over the block, and a
- * value x becomes code RNE(clamp(x * (448 / s), -448, 448)) with s the block's amax
- * (FA_FP8_Q, FA_FP8_K) or the largest block amax of the (b, h) (FA_FP8_V); the stored
- * value of a code c is decode(c) * s / 448. For Q and K the rows may first be rotated:
+ * 64), block i covers rows 64i .. 64i+63, and amax[b,h,i] = max |x| over the block.
+ * FA_FP8_Q, FA_FP8_K: a value x becomes code RNE(clamp(x * (448 / amax), -448, 448)),
+ * whose stored value is decode(c) * amax / 448. FA_FP8_V: the block scale is a power of
+ * two, 2^e with e the smallest integer >= -127 such that amax <= 448 * 2^e (e = 0 for an
+ * all-zero block); x becomes code RNE(x * 2^-e), stored value decode(c) * 2^e (the P V
+ * product of fa_fwd_fp8 applies 2^e as its E8M0 operand scale, exactly). For Q and K
+ * the rows may first be rotated:
  * x -> x diag(signs) H_d, with H_d the Sylvester Hadamard matrix (entries +-1,
  * H_d H_d^T = d I) and signs a caller-drawn vector of +-1; Q and K must use the same
  * signs, and then (Q M)(K M)^T = d Q K^T, which fa_fwd_fp8 divides out.
@@ -381,8 +384,8 @@ FA_API int fa_fp8_rows(int N);
  *  signs: HOST pointer to d floats, each exactly +1 or -1 (read during the call), to
  *        rotate (FA_FP8_Q and FA_FP8_K only; NULL: no rotation; with FA_FP8_V: FA_ERR_ARG).
  * The rotation is computed exactly (float64 sums of the 16-bit inputs) and rounded once
- * to float32; amax, 448/amax and the products are float32. FA_FP8_V takes two launches
- * (the block amaxes, then the codes with the head-wide scale). */
+ * to float32; amax, 448/amax and the products are float32 (for V the product with
+ * 2^-e is exact). One launch, one workgroup per block. */
 FA_API fa_status fa_fp8_quantize(const void* x, int B, int H, int N, int d, fa_dtype dtype,
                                  fa_fp8_layout layout, const float* signs, void* x8, float* amax,
                                  void* stream);
@@ -394,8 +397,8 @@ FA_API fa_status fa_fp8_quantize(const void* x, int B, int H, int N, int d, fa_d
  * o [B,H,N_q,d] device in out_dtype (FA_BF16 or FA_F16), lse [B,H,N_q] float32 or NULL.
  * Both products run on E4M3 MFMA with float32 accumulation: S^T = K Q^T on the codes,
  * scaled by the block scales; the probabilities (at most 2^8 with the lazy rescale) are
- * rounded to E4M3 for O^T += V^T P^T, while the row sum uses them unrounded; O is the
- * result times V's scale over the row sum. */
+ * rounded to E4M3 for O^T += V^T P^T (each key tile's V block scale applied by the
+ * product), while the row sum uses them unrounded; O is the result over the row sum. */
 FA_API fa_status fa_fwd_fp8(const void* q8, const void* k8, const void* v8, const float* q_amax,
                             const float* k_amax, const float* v_amax, void* o, float* lse, int B,
                             int H, int N_q, int N_k, int d, float scale, int causal, int rotated,
