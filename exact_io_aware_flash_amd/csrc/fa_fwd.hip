@@ -529,7 +529,6 @@ void fwd16_kernel(const FwdArgs a) {
   using E = Elt<T>;
   using BT = BiasRowTile<BC>;
   constexpr bool SLOPE = BM == kBiasSlope, TENSOR = BM == kBiasTensor;
-  constexpr bool PRE = BM != kBiasNone;  // bias added to the scores in log2 units before the exponentials
   constexpr int KB = C::kKB, DB = C::kDB, DK = C::kDK, RB = C::kRB;
   constexpr int P = ST - 1;                                  // tiles in flight ahead
   // direct loads per wave per tile: K and V windows (+ the bias tile's rows)
@@ -724,15 +723,37 @@ void fwd16_kernel(const FwdArgs a) {
         for (int ks = 0; ks < DK; ++ks) sc[kb] = E::mma(kf[kb][ks], qf[ks], sc[kb]);
       }
     }
+    // The exponents, in place: x = s * scale * log2(e) + bias - m2 (m2 taken as 0 for rows
+    // without a finite running max yet), formed right after the products.
+    const float nb0 = m2 == kNegInf ? 0.f : -m2;
     if constexpr (SLOPE) {
+      // slope2 * |i - j| with i - j = base - (kb*32 + 8*(g/4) + g%4); when every key of the
+      // tile lies on one side of every row of the wave (a wave-uniform test), |i - j| is
+      // +-(i - j) and bias and offset together are one multiply-add per score
       const float base = (float)(qrow - kt0 - 4 * h);
+      const bool below = kt0 + BC <= wq0 + 1, above = kt0 >= wq0 + 31;
+      if (below || above) {
+        const float sg = below ? slope2 : -slope2, a = __builtin_fmaf(sg, base, nb0);
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+          for (int g = 0; g < 16; ++g)
+            sc[kb][g] = __builtin_fmaf(sc[kb][g], sl2,
+                                       __builtin_fmaf(-sg, (float)(kb * 32 + 8 * (g / 4) + (g % 4)), a));
+      } else {
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+          for (int g = 0; g < 16; ++g) {
+            const float dist = base - (float)(kb * 32 + 8 * (g / 4) + (g % 4));
+            sc[kb][g] = __builtin_fmaf(sc[kb][g], sl2, __builtin_fmaf(slope2, __builtin_fabsf(dist), nb0));
+          }
+      }
+    } else if constexpr (!TENSOR) {
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-        for (int g = 0; g < 16; ++g) {
-          const float dist = base - (float)(kb * 32 + 8 * (g / 4) + (g % 4));
-          sc[kb][g] = __builtin_fmaf(sc[kb][g], sl2, slope2 * __builtin_fabsf(dist));
-        }
+        for (int g = 0; g < 16; ++g) sc[kb][g] = __builtin_fmaf(sc[kb][g], sl2, nb0);
     }
     if constexpr (TENSOR) {
       // keys kb*32 + 8 g4 + 4h .. +3 of row n, from this wave's bias rows in the stage
@@ -743,7 +764,7 @@ void fwd16_kernel(const FwdArgs a) {
           const f32x4 bv = BT::read(Bs, n, kb * 32 + 8 * g4 + 4 * h);
 #pragma unroll
           for (int e = 0; e < 4; ++e)
-            sc[kb][4 * g4 + e] = __builtin_fmaf(sc[kb][4 * g4 + e], sl2, bv[e] * kLog2e);
+            sc[kb][4 * g4 + e] = __builtin_fmaf(sc[kb][4 * g4 + e], sl2, __builtin_fmaf(bv[e], kLog2e, nb0));
         }
     }
     if (masked) {
@@ -759,9 +780,9 @@ void fwd16_kernel(const FwdArgs a) {
         }
     }
     u32x4 pb[KB][2];
-    // probabilities against the running max m2 (packed into pb) and the lane's sum
-    auto probs = [&]() __attribute__((always_inline)) -> float {
-      const float nb = m2 == kNegInf ? 0.f : -m2;
+    // probabilities 2^(x + sh) (packed into pb) and the lane's sum; sh moves the exponents
+    // to a new running max (SH false: none)
+    auto probs = [&](auto SH, float sh) __attribute__((always_inline)) -> float {
       float t = 0.f;
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
@@ -770,44 +791,44 @@ void fwd16_kernel(const FwdArgs a) {
 #pragma unroll
           for (int w = 0; w < 4; ++w) {
             const int g = 8 * st + 2 * w;
-            const float x0 = PRE ? sc[kb][g] + nb : __builtin_fmaf(sc[kb][g], sl2, nb);
-            const float x1 = PRE ? sc[kb][g + 1] + nb : __builtin_fmaf(sc[kb][g + 1], sl2, nb);
+            const float x0 = decltype(SH)::value ? sc[kb][g] + sh : sc[kb][g];
+            const float x1 = decltype(SH)::value ? sc[kb][g + 1] + sh : sc[kb][g + 1];
             const float p0 = fast_exp2(x0), p1 = fast_exp2(x1);
             pb[kb][st][w] = E::pack2(p0, p1);
             t += p0 + p1;  // float32 row sum (the LSE needs the unrounded probabilities)
           }
       return t;
     };
-    // move the running max to the row's max (both wave halves) and rescale
-    auto remax = [&]() __attribute__((always_inline)) {
+    // move the running max to the row's max (both wave halves) and rescale; returns the
+    // shift of the exponents to the new max
+    auto remax = [&]() __attribute__((always_inline)) -> float {
       float mx = kNegInf;
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int g = 0; g < 16; ++g) mx = __builtin_fmaxf(mx, sc[kb][g]);
-      const float tmax = xhalf_max(PRE ? mx : mx * sl2);
+      const float tmax = xhalf_max(mx) - nb0;  // the row's largest s * scale * log2(e) + bias
       const float mnew = __builtin_fmaxf(m2, tmax);
       const float alpha = mnew == kNegInf ? 1.f : fast_exp2(m2 - mnew);
       l *= alpha;
 #pragma unroll
       for (int db = 0; db < DB; ++db) o[db] *= alpha;
       m2 = mnew;
+      return (mnew == kNegInf ? 0.f : -mnew) - nb0;
     };
+    using NoShift = std::false_type;
+    using Shift = std::true_type;
     float t;
     if (__builtin_expect(wave_any(m2 == kNegInf), 0)) {
       // a row without a finite running max yet: take the tile's max first
-      remax();
-      t = probs();
+      t = probs(Shift{}, remax());
     } else {
       // Every row already holds a probability >= 1 (from the key that set m2), so the
       // tile needs no max of its own unless a score exceeds m2 + tau: then some p > 2^tau
       // and the lane's sum of p exceeds 2^tau too (an infinite p included). Only then is
       // the max taken, the accumulators rescaled and the tile's probabilities redone.
-      t = probs();
-      if (__builtin_expect(wave_any(!(t <= kTauP)), 0)) {
-        remax();
-        t = probs();
-      }
+      t = probs(NoShift{}, 0.f);
+      if (__builtin_expect(wave_any(!(t <= kTauP)), 0)) t = probs(Shift{}, remax());
     }
     l += t;
 #pragma unroll
