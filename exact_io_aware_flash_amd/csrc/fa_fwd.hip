@@ -23,6 +23,8 @@
 //    (exact: numerator and denominator share the same stale max); once every row holds
 //    a finite max, a tile's own max is not even computed: a score above m + 8 makes the
 //    lane's probability sum exceed 2^8, and only then is the max taken and the tile redone;
+//  * the exponents (scaled score + bias - running max) are formed in place right after
+//    the score products, so the probability pass is exp2, sum and packing only;
 //  * Q stays in registers for the whole loop; O^T and S^T live in registers.
 #include <type_traits>
 
