@@ -852,12 +852,23 @@ void bwd_dq_kernel(const BwdArgs a) {
         sc[kb][g] = fast_exp2(x);
       }
       if (masked) {
-        const int lo = kst - kt0;
-        const int hi = min(min(ken, Nk), causal ? qrow + off + 1 : Nk) - kt0;
+        // tile-local visible keys [lo, hi) of this row; register g holds key
+        // kb*32 + res_row(g, h) = c + 4h (c constant), so the bounds are shifted by 4h
+        const int hi4 = min(min(ken, Nk), causal ? qrow + off + 1 : Nk) - kt0 - 4 * h;
+        if (ranged) {
+          const int lo4 = kst - kt0 - 4 * h;
+          const unsigned span = (unsigned)max(hi4 - lo4, 0);  // c visible iff c - lo4 < span
 #pragma unroll
-        for (int g = 0; g < 16; ++g) {
-          const int j = kb * 32 + res_row(g, h);
-          sc[kb][g] = (j >= lo && j < hi) ? sc[kb][g] : 0.f;
+          for (int g = 0; g < 16; ++g) {
+            const int c = kb * 32 + res_row(g, 0);
+            sc[kb][g] = (unsigned)(c - lo4) < span ? sc[kb][g] : 0.f;
+          }
+        } else {
+#pragma unroll
+          for (int g = 0; g < 16; ++g) {
+            const int c = kb * 32 + res_row(g, 0);
+            sc[kb][g] = c < hi4 ? sc[kb][g] : 0.f;
+          }
         }
       }
 #pragma unroll

@@ -770,16 +770,29 @@ void fwd16_kernel(const FwdArgs a) {
         }
     }
     if (masked) {
-      // visible keys of this row inside the tile: tile-local [lo, hi)
-      const int lo = kst - kt0;
-      const int hi = min(min(ken, Nk), causal ? qrow + off + 1 : Nk) - kt0;
+      // visible keys of this row inside the tile: tile-local [lo, hi). Register g of block
+      // kb holds key kb*32 + res_row(g, h) = c + 4h with c a constant per register, so the
+      // bounds are shifted by 4h once and each register compares its constant c.
+      const int hi4 = min(min(ken, Nk), causal ? qrow + off + 1 : Nk) - kt0 - 4 * h;
+      if (ranged) {
+        const int lo4 = kst - kt0 - 4 * h;
+        const unsigned span = (unsigned)max(hi4 - lo4, 0);  // c visible iff c - lo4 < span
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
+        for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-        for (int g = 0; g < 16; ++g) {
-          const int j = kb * 32 + res_row(g, h);
-          sc[kb][g] = (j >= lo && j < hi) ? sc[kb][g] : kNegInf;
-        }
+          for (int g = 0; g < 16; ++g) {
+            const int c = kb * 32 + res_row(g, 0);
+            sc[kb][g] = (unsigned)(c - lo4) < span ? sc[kb][g] : kNegInf;
+          }
+      } else {
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+          for (int g = 0; g < 16; ++g) {
+            const int c = kb * 32 + res_row(g, 0);
+            sc[kb][g] = c < hi4 ? sc[kb][g] : kNegInf;
+          }
+      }
     }
     u32x4 pb[KB][2];
     // probabilities 2^(x + sh) (packed into pb) and the lane's sum; sh moves the exponents
