@@ -40,10 +40,10 @@ PEAK_FP8_TFLOPS = 2 * PEAK_BF16_TFLOPS  # dense E4M3 MFMA (published 5.0 PFLOP/s
 # the kernel source they were measured on. A changed source means stale counters -> null.
 TRAFFIC = {
     # kernel: (source hash, bytes read, bytes written) -- profiles/attention_fwd_bwd_bf16_causal_B2H16N8192d128.md
-    "fwd": ("f0c3c2fc90adc34a", 480.6e6, 68.2e6),
-    "bwd_prep": ("3d1a0df25fbc8249", 136.3e6, 2.1e6),
-    "bwd_dkdv": ("3d1a0df25fbc8249", 270.9e6, 268.4e6),
-    "bwd_dq": ("3d1a0df25fbc8249", 682.5e6, 139.3e6),
+    "fwd": ("ce35e01e02c6d7f7", 477.6e6, 68.2e6),
+    "bwd_prep": ("9e427430576fa2b1", 136.3e6, 2.1e6),
+    "bwd_dkdv": ("9e427430576fa2b1", 270.9e6, 268.4e6),
+    "bwd_dq": ("9e427430576fa2b1", 673.3e6, 134.7e6),
 }
 
 
