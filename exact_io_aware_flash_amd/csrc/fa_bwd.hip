@@ -159,7 +159,9 @@ void bwd_dkdv_kernel(const BwdArgs a) {
 
   for (int m = 0; m < n_mem; ++m) {
     if (m > 0) __syncthreads();  // every wave is done with the ring and the tile list
-    const bool first = m == 0;   // the first member writes dbias, later ones add to it
+    // the first member writes dbias, later ones add to it; with a bitmap a member may skip
+    // tiles another one visits, so the launch clears dbias and every member adds
+    const bool first = m == 0 && !(SPARSE && MEM);
     const int bh = (rb | rh) ? (rb ? m / mem_h : slot / slot_h) * a.H
                                    + (rh ? m % mem_h : slot % slot_h)
                              : slot;
@@ -1042,6 +1044,16 @@ static hipError_t launch_bwd_t(int bias, int phases, BwdArgs& a, hipStream_t st)
         hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, kDkdvBR, DKDV_NW, DKDV_WPE, kBiasSlope, false, false, true>), grid, block, 0, st, b);
       else
         hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, kDkdvBR, DKDV_NW, DKDV_WPE, kBiasNone, false, false, true>), grid, block, 0, st, b);
+    } else if (bias == kBiasTensor && slots != BH && sparse) {
+      // dbias summed over batches or heads with a bitmap: cleared first, every member adds
+      if ((a.db_red & FA_DBIAS_SUM_ROWS) == 0) {
+        const size_t nd = (size_t)slots * a.Nq * a.Nk;
+        const unsigned zb = (unsigned)std::min<size_t>((nd + 255) / 256, 8192);
+        hipLaunchKernelGGL(zero_f32_kernel, dim3(zb), dim3(256), 0, st, a.dbias, nd);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+      }
+      hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, kDkdvBR, DKDV_NW, DKDV_WPE, kBiasTensor, true, true>), grid, block, 0, st, b);
     } else if (bias == kBiasTensor && slots != BH) {
       hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, kDkdvBR, DKDV_NW, DKDV_WPE, kBiasTensor, false, true>), grid, block, 0, st, b);
     } else if (bias == kBiasTensor && sparse) {

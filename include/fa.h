@@ -126,8 +126,7 @@ typedef enum fa_bias_kind {
  *              (scifaro.com related-papers page for FlashMask, arXiv 2410.01359: the
  *              abstract on attention with bias); -inf entries act as a mask; +inf or NaN
  *              entries give undefined results. Read during the enqueued work. Works
- *              together with a block bitmap (16-bit inputs), except that dbias summed over
- *              batches or heads with a bitmap gives FA_ERR_UNSUPPORTED.
+ *              together with a block bitmap, dbias and its summed forms included.
  *  bias_stride_b, bias_stride_h, bias_stride_i : element strides, >= 0 (else FA_ERR_MASK);
  *              64 * bias_stride_i + N_k must stay below 2^30 (else FA_ERR_UNSUPPORTED).
  *  dbias :     DEVICE pointer to a dense float32 array (4-byte aligned), or NULL. fa_bwd

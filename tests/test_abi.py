@@ -138,15 +138,14 @@ def test_bias_tensor_descriptor_validation():
     for bad in (dict(sb=-1), dict(sh=-16), dict(si=-1)):
         assert fwd(mb=ctypes.byref(desc(**bad))) == 5, bad
     assert fwd(mb=ctypes.byref(desc(si=1 << 24))) == 8  # tile offsets would pass 32 bits
-    # a bitmap together with a bias tensor is accepted (a valid backward stops at the
-    # 16-byte workspace: nothing launches); dbias summed over batches or heads with a
-    # bitmap is not implemented (rejected before anything launches)
+    # a bitmap together with a bias tensor and any summed dbias is accepted (a valid
+    # backward stops at the 16-byte workspace: nothing launches)
     d = desc()
     d.block_mask, d.block_q, d.block_k = P, 64, 64
-    d.dbias, d.dbias_reduce = P, fa.FA_DBIAS_SUM_HEADS
-    assert bwd(mb=ctypes.byref(d)) == 8
-    d.dbias_reduce = fa.FA_DBIAS_SUM_ROWS
-    assert bwd(mb=ctypes.byref(d), wsb=16) == 7
+    for bits in (fa.FA_DBIAS_SUM_HEADS, fa.FA_DBIAS_SUM_BATCH | fa.FA_DBIAS_SUM_HEADS,
+                 fa.FA_DBIAS_SUM_ROWS):
+        d.dbias, d.dbias_reduce = P, bits
+        assert bwd(mb=ctypes.byref(d), wsb=16) == 7, bits
     # dbias needs the bias tensor, 4-byte aligned; misaligned bias rejected in the backward
     d = desc()
     d.dbias = P + 2

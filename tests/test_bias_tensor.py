@@ -419,10 +419,16 @@ def test_dbias_beyond_2_31_elements_matches_the_head_alone():
 
 
 SPARSE_BIAS_CASES = [
-    # dtype, d, causal, nq, nk, bq, bk, density, layout, dbias ("dense", "rows" or None)
+    # dtype, d, causal, nq, nk, bq, bk, density, layout, dbias: "dense", "rows" (summed over
+    # query rows), the summed axes (b batches, h heads, i query rows) or None. With a
+    # bitmap per (b, h) the members of a summed dbias visit different tiles.
     (torch.bfloat16, 128, True, 300, 330, 64, 64, 0.6, "head", "dense"),
     (torch.float16, 64, False, 257, 520, 128, 64, 0.5, "batch_head", "rows"),
     (torch.bfloat16, 128, False, 200, 700, 64, 192, 0.4, "shared", None),
+    (torch.bfloat16, 128, True, 300, 330, 64, 64, 0.6, "batch_head", "b"),
+    (torch.float16, 64, False, 257, 520, 128, 64, 0.5, "batch_head", "bh"),
+    (torch.bfloat16, 128, False, 200, 300, 64, 128, 0.5, "head", "h"),
+    (torch.bfloat16, 128, True, 130, 260, 64, 64, 0.5, "batch_head", "bhi"),
 ]
 
 
@@ -444,10 +450,10 @@ def test_block_bitmap_with_bias_tensor(dtype, d, causal, nq, nk, bq, bk, density
     o, lse = fa.fa_fwd(qd, kd, vd, **kw)
     o2, lse2 = fa.fa_fwd_split(qd, kd, vd, n_split=3, **kw)
     dbias = None
-    if db == "dense":
-        dbias = torch.full((B, H, nq, nk), float("nan"), dtype=torch.float32, device=DEV)
-    elif db == "rows":
-        dbias = torch.full((B, H, 1, nk), float("nan"), dtype=torch.float32, device=DEV)
+    axes = {"dense": "", "rows": "i"}.get(db, db)
+    if db is not None:
+        dshape = (1 if "b" in axes else B, 1 if "h" in axes else H, 1 if "i" in axes else nq, nk)
+        dbias = torch.full(dshape, float("nan"), dtype=torch.float32, device=DEV)
     dq, dk, dv = fa.fa_bwd(dod, qd, kd, vd, o, lse, dbias=dbias, **kw)
     torch.cuda.synchronize()
     bn = bias.double().numpy()
@@ -465,14 +471,26 @@ def test_block_bitmap_with_bias_tensor(dtype, d, causal, nq, nk, bq, bk, density
     tol, masked = dbias_tol_masked(qn, kn, vn, don, scale, causal, bn, bm, bq, bk)
     g = np64(dbias)
     assert np.isfinite(g).all(), what
-    if db == "dense":
+    if axes == "":
         assert np.all(np.abs(g - dref) <= tol), what
         assert np.all(g[masked] == 0), what
     else:
-        ref = dref.sum(axis=2, keepdims=True)
-        bound = tol.sum(axis=2, keepdims=True) + nq * 2.0 ** -23 * np.abs(dref).sum(axis=2,
-                                                                                  keepdims=True)
+        # summed: the sum of the per-element bounds plus the float32 rounding of a sum of
+        # n terms; an element whose every summand is masked is exactly zero
+        red = tuple(ax for ax, c in enumerate("bhi") if c in axes)
+        n_terms = int(np.prod([(B, H, nq)[ax] for ax in red]))
+        ref = dref.sum(axis=red, keepdims=True)
+        bound = (tol.sum(axis=red, keepdims=True)
+                 + n_terms * 2.0 ** -23 * np.abs(dref).sum(axis=red, keepdims=True))
+        assert g.shape == ref.shape, what
         assert np.all(np.abs(g - ref) <= bound), what
+        assert np.all(g[masked.all(axis=red, keepdims=True)] == 0), what
+        if "b" in axes or "h" in axes:
+            # deterministic: a second call gives the same bits
+            dbias2 = torch.full(dshape, float("nan"), dtype=torch.float32, device=DEV)
+            fa.fa_bwd(dod, qd, kd, vd, o, lse, dbias=dbias2, **kw)
+            torch.cuda.synchronize()
+            assert torch.equal(dbias, dbias2), what
 
 
 def dbias_tol_masked(q, k, v, do, scale, causal, bias, bm, bq, bk):
