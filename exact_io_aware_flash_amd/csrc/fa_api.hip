@@ -398,8 +398,6 @@ fa_status bwd_check(int phases, const void* q, const void* k, const void* v, con
   if (dqa && (raw(grad_dtype) != FA_F32 || raw(dtype) == FA_F32 || a.bmask != nullptr ||
               bias == kBiasTensor))
     return FA_ERR_UNSUPPORTED;
-  // float32 inputs: dbias dense only
-  if (mb != nullptr && mb->dbias_reduce != 0 && raw(dtype) == FA_F32) return FA_ERR_UNSUPPORTED;
   return FA_OK;
 }
 

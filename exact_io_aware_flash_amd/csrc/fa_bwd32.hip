@@ -125,171 +125,206 @@ void dkdv32_kernel(const BwdArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wid = wave_id(), n = lane & 31, h = lane >> 5;
   const int Nq = a.Nq, Nk = a.Nk, off = Nk - Nq;
   const bool causal = a.causal != 0, ranged = a.key_start != nullptr;
-  int bh, kb;
-  map_block(blockIdx.x, a.B * a.H, a.nblk, a.sched, false, bh, kb);
-  const int head = bh % a.H;
-  const float* Q = static_cast<const float*>(a.q) + (size_t)bh * Nq * D;
-  const float* K = static_cast<const float*>(a.k) + (size_t)bh * Nk * D;
-  const float* V = static_cast<const float*>(a.v) + (size_t)bh * Nk * D;
-  const float* dO = static_cast<const float*>(a.dout) + (size_t)bh * Nq * D;
-  const float* lse2 = a.lse2 + (size_t)bh * Nq;
-  const float* dlt = a.delta + (size_t)bh * Nq;
-  const float sl2 = a.sl2;
-  const float slope2 = SLOPE ? a.slope2[a.n_slopes == 1 ? 0 : head] : 0.f;
-  const float* TB = TENSOR ? a.tbias + (long long)(bh / a.H) * a.tb_sb + (long long)head * a.tb_sh
-                           : nullptr;
-  float* dB = (TENSOR && a.dbias != nullptr) ? a.dbias + (size_t)bh * Nq * Nk : nullptr;
+  // dbias summed over batches and/or heads: the workgroup owns one dbias slice (slot) and
+  // computes, one after the other, every (b, h) that shares it (its members), adding each
+  // member's dS in a fixed order; otherwise a slot is one (b, h)
+  const int rb = TENSOR ? (a.db_red & FA_DBIAS_SUM_BATCH) : 0;
+  const int rh = TENSOR ? (a.db_red & FA_DBIAS_SUM_HEADS) : 0;
+  const bool rrows = TENSOR && (a.db_red & FA_DBIAS_SUM_ROWS) != 0;
+  const int slot_h = rh ? 1 : a.H;
+  const int n_slots = (rb ? 1 : a.B) * slot_h;
+  const int mem_h = rh ? a.H : 1, n_mem = (rb ? a.B : 1) * mem_h;
+  int slot, kb;
+  map_block(blockIdx.x, n_slots, a.nblk, a.sched, false, slot, kb);
+  // the slot's dbias [Nq' rows][Nk] (NULL: dbias not wanted); dense and summed forms are
+  // cleared by the launch, so every member adds (rows summed: written once at the end)
+  float* dB = (TENSOR && a.dbias != nullptr) ? a.dbias + (size_t)slot * (rrows ? 1 : Nq) * Nk
+                                             : nullptr;
+  float dbr = 0.f;  // rows summed: this lane's share of its key's dbias, over all members
 
-  const int k0 = kb * 128, k1 = min(k0 + 128, Nk);
-  const int kw0 = k0 + 32 * wid, kw1 = min(kw0 + 32, Nk);
-  const int key = kw0 + n;
+  for (int m = 0; m < n_mem; ++m) {
+    if (m > 0) __syncthreads();  // every wave is done with the stages and the window
+    const int bh = (rb | rh) ? (rb ? m / mem_h : slot / slot_h) * a.H
+                                   + (rh ? m % mem_h : slot % slot_h)
+                             : slot;
+    const int head = bh % a.H;
+    const float* Q = static_cast<const float*>(a.q) + (size_t)bh * Nq * D;
+    const float* K = static_cast<const float*>(a.k) + (size_t)bh * Nk * D;
+    const float* V = static_cast<const float*>(a.v) + (size_t)bh * Nk * D;
+    const float* dO = static_cast<const float*>(a.dout) + (size_t)bh * Nq * D;
+    const float* lse2 = a.lse2 + (size_t)bh * Nq;
+    const float* dlt = a.delta + (size_t)bh * Nq;
+    const float sl2 = a.sl2;
+    const float slope2 = SLOPE ? a.slope2[a.n_slopes == 1 ? 0 : head] : 0.f;
+    const float* TB = TENSOR ? a.tbias + (long long)(bh / a.H) * a.tb_sb
+                                   + (long long)head * a.tb_sh
+                             : nullptr;
 
-  // K and V of this lane's key: B operands of S = Q K^T and dP = dO V^T (element 2s + h)
-  float kf[NS], vf[NS];
-  {
-    const size_t r = (size_t)min(key, Nk - 1);
-#pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      kf[s] = K[r * D + 2 * s + h];
-      vf[s] = V[r * D + 2 * s + h];
-    }
-  }
+    const int k0 = kb * 128, k1 = min(k0 + 128, Nk);
+    const int kw0 = k0 + 32 * wid, kw1 = min(kw0 + 32, Nk);
+    const int key = kw0 + n;
 
-  // query tiles that can see a key of this block (range summaries are per 64 rows)
-  const int nqt = (Nq + BR - 1) / BR;
-  int t_lo = 0, t_hi = nqt;
-  if (causal) t_lo = max(0, k0 - off) / BR;
-  if (causal && k0 - off >= Nq) t_hi = 0;
-  if (ranged) {
-    if (tid < 64) {
-      int lo = nqt, hi = -1;
-      for (int t = lane; t < nqt; t += 64) {
-        const int* sm = a.qsum + 4 * (t / 2);  // {min start, max start, min end, max end}
-        if (!(k1 <= sm[0] || k0 >= sm[3])) { lo = min(lo, t); hi = max(hi, t); }
-      }
-      lo = wave_min(lo);
-      hi = wave_max(hi);
-      if (lane == 0) { win[0] = lo; win[1] = hi + 1; }
-    }
-    __syncthreads();
-    t_lo = max(t_lo, win[0]);
-    t_hi = min(t_hi, win[1]);
-  }
-  if (k0 >= Nk) t_hi = t_lo;
-
-  Tile32<D, RS> tl;
-  float areg = 0.f;  // threads 0-127: one entry of the tile's row arrays
-  auto load = [&](int t) {
-    const int q0t = t * BR;
-    tl.load(Q, dO, q0t, Nq, tid);
-    if (tid < 4 * BR) {
-      const int arr = tid / BR, r = min(q0t + tid % BR, Nq - 1);
-      if (arr == 0) areg = lse2[r];
-      else if (arr == 1) areg = dlt[r];
-      else if (ranged) areg = __builtin_bit_cast(float, arr == 2 ? a.key_start[r] : a.key_end[r]);
-    }
-  };
-  auto store = [&](int stg) {
-    float* sb = smem + stg * STAGE;
-    tl.store(sb, sb + TILE, tid);
-    if (tid < 4 * BR) sb[2 * TILE + tid] = areg;
-  };
-
-  f32x16 dv[DB], dk[DB];
-#pragma unroll
-  for (int db = 0; db < DB; ++db) { dv[db] = f32x16{}; dk[db] = f32x16{}; }
-  float sgrad = 0.f;
-
-  if (t_lo < t_hi) {
-    load(t_lo);
-    store(0);
-  }
-  __syncthreads();
-  for (int t = t_lo; t < t_hi; ++t) {
-    const int stg = (t - t_lo) & 1;
-    const bool more = t + 1 < t_hi;
-    if (more) load(t + 1);
-    sync_check();
-    const int q0t = t * BR;
-    const float* Qs = smem + stg * STAGE;
-    const float* Ds = Qs + TILE;
-    const float* Ar = Qs + 2 * TILE;  // LSE*log2(e), D, key_start, key_end (32 each)
-
-    bool skip = kw0 >= Nk;
-    if (causal) skip |= q0t + BR - 1 + off < kw0;
-    if (ranged) {
-      const int* sm = a.qsum + 4 * (t / 2);
-      skip |= kw1 <= sm[0] || kw0 >= sm[3];
-    }
-    // block bitmap (a 32-row tile and a wave's 32 keys lie inside one block), as a mask
-    if (a.bmask != nullptr && !skip) {
-      const int bb = bh / a.H, hh = bh - bb * a.H;
-      skip = a.bmask[bb * a.bm_sb + hh * a.bm_sh + (long long)(q0t / a.bq) * a.nkb +
-                     min(kw0, Nk - 1) / a.bk] == 0;
-    }
-    if (!skip) {
-      f32x16 sc = f32x16{}, dp = f32x16{};
+    // K and V of this lane's key: B operands of S = Q K^T and dP = dO V^T (element 2s + h)
+    float kf[NS], vf[NS];
+    {
+      const size_t r = (size_t)min(key, Nk - 1);
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
-        sc = mma32(Qs[n * RS + 2 * s + h], kf[s], sc);
-        dp = mma32(Ds[n * RS + 2 * s + h], vf[s], dp);
+        kf[s] = K[r * D + 2 * s + h];
+        vf[s] = V[r * D + 2 * s + h];
       }
-      float p[16], ds[16];
-#pragma unroll
-      for (int g = 0; g < 16; ++g) {
-        const int r = res_row(g, h), qi = q0t + r;
-        const float x = __builtin_fmaf(sc[g], sl2, bias2<BM>(a, TB, slope2, qi, key) - Ar[r]);
-        bool vis = key < Nk && qi < Nq && (!causal || key <= qi + off);
-        if (ranged) {
-          const int lo = min(max(__builtin_bit_cast(int, Ar[2 * BR + r]), 0), Nk);
-          const int hi = min(max(__builtin_bit_cast(int, Ar[3 * BR + r]), 0), Nk);
-          vis = vis && key >= lo && key < hi;
+    }
+
+    // query tiles that can see a key of this block (range summaries are per 64 rows)
+    const int nqt = (Nq + BR - 1) / BR;
+    int t_lo = 0, t_hi = nqt;
+    if (causal) t_lo = max(0, k0 - off) / BR;
+    if (causal && k0 - off >= Nq) t_hi = 0;
+    if (ranged) {
+      if (tid < 64) {
+        int lo = nqt, hi = -1;
+        for (int t = lane; t < nqt; t += 64) {
+          const int* sm = a.qsum + 4 * (t / 2);  // {min start, max start, min end, max end}
+          if (!(k1 <= sm[0] || k0 >= sm[3])) { lo = min(lo, t); hi = max(hi, t); }
         }
-        p[g] = vis ? fast_exp2(x) : 0.f;
-        ds[g] = p[g] * (dp[g] - Ar[BR + r]);
-        if constexpr (TENSOR) {
-          if (dB != nullptr && key < Nk && qi < Nq) dB[(size_t)qi * Nk + key] = ds[g];
-        }
-        if constexpr (SLOPE) sgrad = __builtin_fmaf(ds[g], __builtin_fabsf((float)(qi - key)), sgrad);
+        lo = wave_min(lo);
+        hi = wave_max(hi);
+        if (lane == 0) { win[0] = lo; win[1] = hi + 1; }
       }
+      __syncthreads();
+      t_lo = max(t_lo, win[0]);
+      t_hi = min(t_hi, win[1]);
+    }
+    if (k0 >= Nk) t_hi = t_lo;
+
+    Tile32<D, RS> tl;
+    float areg = 0.f;  // threads 0-127: one entry of the tile's row arrays
+    auto load = [&](int t) {
+      const int q0t = t * BR;
+      tl.load(Q, dO, q0t, Nq, tid);
+      if (tid < 4 * BR) {
+        const int arr = tid / BR, r = min(q0t + tid % BR, Nq - 1);
+        if (arr == 0) areg = lse2[r];
+        else if (arr == 1) areg = dlt[r];
+        else if (ranged) areg = __builtin_bit_cast(float, arr == 2 ? a.key_start[r] : a.key_end[r]);
+      }
+    };
+    auto store = [&](int stg) {
+      float* sb = smem + stg * STAGE;
+      tl.store(sb, sb + TILE, tid);
+      if (tid < 4 * BR) sb[2 * TILE + tid] = areg;
+    };
+
+    f32x16 dv[DB], dk[DB];
 #pragma unroll
-      for (int db = 0; db < DB; ++db) {
+    for (int db = 0; db < DB; ++db) { dv[db] = f32x16{}; dk[db] = f32x16{}; }
+    float sgrad = 0.f;
+
+    if (t_lo < t_hi) {
+      load(t_lo);
+      store(0);
+    }
+    __syncthreads();
+    for (int t = t_lo; t < t_hi; ++t) {
+      const int stg = (t - t_lo) & 1;
+      const bool more = t + 1 < t_hi;
+      if (more) load(t + 1);
+      sync_check();
+      const int q0t = t * BR;
+      const float* Qs = smem + stg * STAGE;
+      const float* Ds = Qs + TILE;
+      const float* Ar = Qs + 2 * TILE;  // LSE*log2(e), D, key_start, key_end (32 each)
+
+      bool skip = kw0 >= Nk;
+      if (causal) skip |= q0t + BR - 1 + off < kw0;
+      if (ranged) {
+        const int* sm = a.qsum + 4 * (t / 2);
+        skip |= kw1 <= sm[0] || kw0 >= sm[3];
+      }
+      // block bitmap (a 32-row tile and a wave's 32 keys lie inside one block), as a mask
+      if (a.bmask != nullptr && !skip) {
+        const int bb = bh / a.H, hh = bh - bb * a.H;
+        skip = a.bmask[bb * a.bm_sb + hh * a.bm_sh + (long long)(q0t / a.bq) * a.nkb +
+                       min(kw0, Nk - 1) / a.bk] == 0;
+      }
+      if (!skip) {
+        f32x16 sc = f32x16{}, dp = f32x16{};
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+          sc = mma32(Qs[n * RS + 2 * s + h], kf[s], sc);
+          dp = mma32(Ds[n * RS + 2 * s + h], vf[s], dp);
+        }
+        float p[16], ds[16];
 #pragma unroll
         for (int g = 0; g < 16; ++g) {
-          const int r = res_row(g, h);
-          dv[db] = mma32(p[g], Ds[r * RS + 32 * db + n], dv[db]);
-          dk[db] = mma32(ds[g], Qs[r * RS + 32 * db + n], dk[db]);
+          const int r = res_row(g, h), qi = q0t + r;
+          const float x = __builtin_fmaf(sc[g], sl2, bias2<BM>(a, TB, slope2, qi, key) - Ar[r]);
+          bool vis = key < Nk && qi < Nq && (!causal || key <= qi + off);
+          if (ranged) {
+            const int lo = min(max(__builtin_bit_cast(int, Ar[2 * BR + r]), 0), Nk);
+            const int hi = min(max(__builtin_bit_cast(int, Ar[3 * BR + r]), 0), Nk);
+            vis = vis && key >= lo && key < hi;
+          }
+          p[g] = vis ? fast_exp2(x) : 0.f;
+          ds[g] = p[g] * (dp[g] - Ar[BR + r]);
+          if constexpr (TENSOR) {
+            if (dB != nullptr && key < Nk && qi < Nq) {
+              if (rrows) dbr += ds[g];
+              else if (n_mem > 1) dB[(size_t)qi * Nk + key] += ds[g];
+              else dB[(size_t)qi * Nk + key] = ds[g];
+            }
+          }
+          if constexpr (SLOPE)
+            sgrad = __builtin_fmaf(ds[g], __builtin_fabsf((float)(qi - key)), sgrad);
+        }
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+#pragma unroll
+          for (int g = 0; g < 16; ++g) {
+            const int r = res_row(g, h);
+            dv[db] = mma32(p[g], Ds[r * RS + 32 * db + n], dv[db]);
+            dk[db] = mma32(ds[g], Qs[r * RS + 32 * db + n], dk[db]);
+          }
+        }
+      }
+      // the other stage was last read before the previous barrier
+      if (more) store(stg ^ 1);
+      __syncthreads();
+    }
+
+    if constexpr (SLOPE) {
+      if (a.dslope_part != nullptr) {
+        __shared__ float sred[4];
+        const float w = wave_fsum(sgrad);
+        if (lane == 0) sred[wid] = w;
+        __syncthreads();
+        if (tid == 0)
+          a.dslope_part[(size_t)bh * a.nblk + kb] = sred[0] + sred[1] + sred[2] + sred[3];
+      }
+    }
+
+    const float scale = a.scale;
+    float* dK = static_cast<float*>(a.dk);
+    float* dV = static_cast<float*>(a.dv);
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+#pragma unroll
+      for (int g = 0; g < 16; ++g) {
+        const int kr = kw0 + res_row(g, h);
+        if (kr < Nk) {
+          const size_t idx = ((size_t)bh * Nk + kr) * D + 32 * db + n;
+          dK[idx] = dk[db][g] * scale;
+          dV[idx] = dv[db][g];
         }
       }
     }
-    // the other stage was last read before the previous barrier
-    if (more) store(stg ^ 1);
-    __syncthreads();
-  }
-
-  if constexpr (SLOPE) {
-    if (a.dslope_part != nullptr) {
-      __shared__ float sred[4];
-      const float w = wave_fsum(sgrad);
-      if (lane == 0) sred[wid] = w;
-      __syncthreads();
-      if (tid == 0) a.dslope_part[(size_t)bh * a.nblk + kb] = sred[0] + sred[1] + sred[2] + sred[3];
-    }
-  }
-
-  const float scale = a.scale;
-  float* dK = static_cast<float*>(a.dk);
-  float* dV = static_cast<float*>(a.dv);
-#pragma unroll
-  for (int db = 0; db < DB; ++db) {
-#pragma unroll
-    for (int g = 0; g < 16; ++g) {
-      const int kr = kw0 + res_row(g, h);
-      if (kr < Nk) {
-        const size_t idx = ((size_t)bh * Nk + kr) * D + 32 * db + n;
-        dK[idx] = dk[db][g] * scale;
-        dV[idx] = dv[db][g];
-      }
+  }  // members
+  // rows summed: the two lanes of a key hold the sums of alternate row groups
+  if constexpr (TENSOR) {
+    if (rrows && dB != nullptr) {
+      const float tot = dbr + __shfl_xor(dbr, 32, 64);
+      const int key = kb * 128 + 32 * wid + n;
+      if (h == 0 && key < Nk) dB[key] = tot;
     }
   }
 }
@@ -441,15 +476,25 @@ hipError_t launch_passes(int phases, BwdArgs& a, hipStream_t st) {
   if (phases & FA_BWD_DKDV) {
     BwdArgs b = a;
     b.nblk = (a.Nk + 127) / 128;
-    b.sched = sched;
+    // a workgroup per dbias slice and key block (a slice is one (b, h) unless dbias is
+    // summed over batches or heads)
+    int slots = BH;
     if (BM == kBiasTensor && a.dbias != nullptr) {
-      const size_t nd = (size_t)BH * a.Nq * a.Nk;
-      const unsigned zb = (unsigned)std::min<size_t>((nd + 255) / 256, 8192);
-      hipLaunchKernelGGL(zero_f32_kernel, dim3(zb), dim3(256), 0, st, a.dbias, nd);
-      e = hipGetLastError();
-      if (e != hipSuccess) return e;
+      slots = ((a.db_red & FA_DBIAS_SUM_BATCH) ? 1 : a.B) *
+              ((a.db_red & FA_DBIAS_SUM_HEADS) ? 1 : a.H);
+      if ((a.db_red & FA_DBIAS_SUM_ROWS) == 0) {  // rows summed: every element is written
+        const size_t nd = (size_t)slots * a.Nq * a.Nk;
+        const unsigned zb = (unsigned)std::min<size_t>((nd + 255) / 256, 8192);
+        hipLaunchKernelGGL(zero_f32_kernel, dim3(zb), dim3(256), 0, st, a.dbias, nd);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+      }
+    } else {
+      b.db_red = 0;
     }
-    hipLaunchKernelGGL((dkdv32_kernel<D, BM>), dim3((unsigned)(BH * b.nblk)), dim3(256), 0, st, b);
+    b.sched = (slots % 8 == 0) ? 1 : 0;
+    hipLaunchKernelGGL((dkdv32_kernel<D, BM>), dim3((unsigned)(slots * b.nblk)), dim3(256), 0, st,
+                       b);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (BM == kBiasSlope && a.dslopes != nullptr) {

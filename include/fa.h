@@ -268,8 +268,8 @@ FA_API size_t fa_bwd_workspace_bytes(int B, int H, int N_q, int N_k, int d);
  *  dslopes in the descriptor ask for the bias gradients explicitly).
  *  16-bit inputs: products on 16-bit MFMA with P and dS rounded to the input type,
  *  float32 accumulation. float32 inputs: every product on float32 MFMA, nothing rounded
- *  below float32 (gradients float32; dbias dense only: dbias_reduce != 0 gives
- *  FA_ERR_UNSUPPORTED). The result is deterministic (a fixed order of every sum). */
+ *  below float32 (gradients float32). The result is deterministic (a fixed order of every
+ *  sum, dbias summed over batches or heads included). */
 FA_API fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
                  const void* dout, void* dq, void* dk, void* dv, fa_dtype grad_dtype,
                  void* workspace, size_t workspace_bytes,

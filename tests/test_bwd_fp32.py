@@ -137,6 +137,7 @@ def test_fp32_backward_slope_bias_ranges_and_dslopes(causal):
 
 
 def test_fp32_backward_bias_tensor_and_dbias():
+    # dense dbias, then dbias summed over each broadcast axis set
     B, H, nq, nk, d = 2, 2, 257, 300, 64
     q, k, v, do = (normal((B, H, n, d), torch.float32, 7200 + i)
                    for i, n in enumerate((nq, nk, nk, nq)))
@@ -158,10 +159,31 @@ def test_fp32_backward_bias_tensor_and_dbias():
     assert np.all(g[masked] == 0)  # masked entries (and the empty row) exactly zero
     err = np.abs(g - dref)
     assert np.all(err <= bds), float((err - bds).max())
-    with pytest.raises(fa.FaError) as e:  # summed dbias: 16-bit inputs only
-        fa.fa_bwd(dod, qd, kd, vd, o, lse, causal=True, scale=scale, bias=bd,
-                  dbias=torch.zeros((1, H, nq, nk), dtype=torch.float32, device=DEV))
-    assert e.value.status == 8
+    # dbias summed over broadcast axes (b batches, h heads, i query rows): the sum of the
+    # per-element bounds plus the float32 rounding of a sum of n terms; an element whose
+    # every summand is masked is exactly zero; a second call gives the same bits
+    for axes in ("b", "bh", "i", "bhi"):
+        red = tuple(ax for ax, c in enumerate("bhi") if c in axes)
+        shape = tuple(1 if i in red else n for i, n in enumerate((B, H, nq, nk)))
+        n_terms = int(np.prod([(B, H, nq)[ax] for ax in red]))
+        sums = []
+        for _ in range(2):
+            db = torch.full(shape, float("nan"), dtype=torch.float32, device=DEV)
+            got2 = fa.fa_bwd(dod, qd, kd, vd, o, lse, causal=True, scale=scale, bias=bd,
+                             dbias=db)
+            torch.cuda.synchronize()
+            sums.append(db)
+        for a, b in zip(got2, got):
+            assert torch.equal(a, b), axes  # the gradients do not depend on dbias
+        assert torch.equal(sums[0], sums[1]), axes
+        g = np64(sums[0])
+        ref = dref.sum(axis=red, keepdims=True)
+        bound = (bds.sum(axis=red, keepdims=True)
+                 + n_terms * 2.0 ** -23 * np.abs(dref).sum(axis=red, keepdims=True))
+        assert g.shape == ref.shape and np.isfinite(g).all(), axes
+        err = np.abs(g - ref)
+        assert np.all(err <= bound), (axes, float((err - bound).max()))
+        assert np.all(g[masked.all(axis=red, keepdims=True)] == 0), axes
 
 
 def test_fp32_backward_c1_workload():
